@@ -1,0 +1,83 @@
+"""Seeded synthetic inputs for the NVFP4 / Q4_1 x Q8_0 product.
+
+This module only draws random numbers; it holds none of the product's arithmetic
+(no decode, no quantization, no dot products).  Both the GPU path's tests/benchmark
+and the oracle's tests take their inputs from here, so the two sides always see the
+same bytes.
+
+Workload recipes (the shapes and value distributions of the decode/prefill
+workloads this library targets):
+
+* NVFP4 weights: every 4-bit code uniform over all 16 codes; one UE4M3 scale per
+  16 weights with its unbiased exponent uniform in [-4, 4] and its 3-bit mantissa
+  uniform, i.e. byte = ((e + 7) << 3) | m; a float32 per-tensor scale (1.0, or
+  uniform in [0.5, 2] for the layer-set workloads).
+* Activations: float32 N(0, 1); the prefill workload also multiplies
+  round(0.001 * M * K) distinct, seeded positions by 50 (sign kept).
+* Q4_1 weights: codes uniform 0..15, per 32 weights d ~ U[1e-3, 2e-2] and
+  m ~ U[-0.1, 0], drawn in float32 and stored as binary16 (numpy's
+  round-to-nearest-even conversion).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Decode GEMV set of one transformer layer at hidden 5120, ffn 17408 (N, K).
+LAYER = (("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120), ("down", 5120, 17408))
+
+WORKLOADS = {
+    "gemv_small": dict(M=1, N=4864, K=896),
+    "layer": dict(M=1, mats=LAYER),
+    "prefill": dict(Ms=(256, 2048), N=17408, K=5120),
+    "q4_1": dict(Ms=(1, 512), N=4096, K=4096),
+    "stack": dict(Ms=(1, 8), layers=64, mats=LAYER),
+}
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def nvfp4_weights(N: int, K: int, seed: int, w_scale: str | float = 1.0):
+    """Returns (codes uint8 [N, K] in 0..15, scales uint8 [N, K/16], w_scale float32)."""
+    assert K % 16 == 0
+    r = rng(seed)
+    codes = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    e = r.integers(-4, 5, size=(N, K // 16), dtype=np.int16)
+    m = r.integers(0, 8, size=(N, K // 16), dtype=np.int16)
+    scales = (((e + 7) << 3) | m).astype(np.uint8)
+    if w_scale == "uniform":
+        ws = np.float32(r.uniform(0.5, 2.0))
+    else:
+        ws = np.float32(w_scale)
+    return codes, scales, ws
+
+
+def activations(M: int, K: int, seed: int, outliers: bool = False) -> np.ndarray:
+    """float32 [M, K], N(0,1); with ``outliers`` 0.1 % of positions scaled by 50."""
+    r = rng(seed)
+    x = r.standard_normal(size=(M, K), dtype=np.float32)
+    if outliers:
+        n = int(round(0.001 * M * K))
+        if n:
+            idx = r.choice(M * K, size=n, replace=False)
+            x.reshape(-1)[idx] *= np.float32(50.0)
+    return x
+
+
+def q4_1_weights(N: int, K: int, seed: int):
+    """Returns (qw uint8 [N, K] in 0..15, dw uint16 [N, K/32], mw uint16 [N, K/32])."""
+    assert K % 32 == 0
+    r = rng(seed)
+    qw = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    d = r.uniform(1e-3, 2e-2, size=(N, K // 32)).astype(np.float32)
+    m = r.uniform(-0.1, 0.0, size=(N, K // 32)).astype(np.float32)
+    return qw, d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)
+
+
+def seed_for(workload: str, tensor: str, index: int = 0) -> int:
+    """Fixed, documented seed per (workload, tensor, index)."""
+    base = {"gemv_small": 100, "layer": 200, "prefill": 300, "q4_1": 400, "stack": 500,
+            "test": 900}[workload]
+    tag = sum((i + 1) * ord(ch) for i, ch in enumerate(tensor)) % 997
+    return base * 1_000_003 + tag * 1009 + index

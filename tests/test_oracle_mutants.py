@@ -1,0 +1,42 @@
+"""Planted mistakes: each is a one-line change to a copy of the oracle source,
+compiled on the CPU; the pin battery must reject every one of them."""
+import os
+
+import pytest
+
+import oracle as O
+import oracle_pins
+
+MUTANTS = {
+    "e2m1_bias": ("ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)"),
+    "e2m1_sign_dropped": ("    return s ? -v : v;\n}\n\n/* NVFP4 subblock", "    return v;\n}\n\n/* NVFP4 subblock"),
+    "ue4m3_subnormal": ("return ldexp((double)m, -9);", "return ldexp((double)m, -10);"),
+    "ue4m3_bias": ("return ldexp(1.0 + m / 8.0, e - 7);", "return ldexp(1.0 + m / 8.0, e - 8);"),
+    "f16_tie_rule": ("if (rem > 0x1000u || (rem == 0x1000u && (res & 1u)))", "if (rem >= 0x1000u)"),
+    "f16_subnormal_shift": ("int shift = 14 - e;", "int shift = 13 - e;"),
+    "q8_round_half_away": ("float r = rintf(t);", "float r = roundf(t);"),
+    "q8_divide_by_f16": ("float t = xb[j] / d;", "float t = xb[j] / (float)nvqo_f16_to_f64(nvqo_f32_to_f16(d));"),
+    "q8_bsum_offset": ("bsum16[m * (K / 16) + 2 * b + h] = (int16_t)s;", "bsum16[m * (K / 16) + 2 * b + (1 - h)] = (int16_t)s;"),
+    "isums_index": ("acc += l * (int32_t)q[m * K + k];", "acc += l * (int32_t)q[m * K + (k ^ 1)];"),
+    "act_scale_index": ("a[k] = nvqo_f16_to_f64(d16[k / 32]) * (double)q[k];", "a[k] = nvqo_f16_to_f64(d16[k / 16 % (K / 32)]) * (double)q[k];"),
+    "weight_scale_index": ("w[k] = (double)w_scale * nvqo_ue4m3(scales[k / 16]) * nvqo_e2m1(codes[k]);",
+                           "w[k] = (double)w_scale * nvqo_ue4m3(scales[k / 32]) * nvqo_e2m1(codes[k]);"),
+    "q4_1_offset_dropped": ("w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k] + nvqo_f16_to_f64(mw[k / 32]);",
+                            "w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k];"),
+    "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* ----",
+                           "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* ----"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(O.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmutant.so")
+    O.build(out=lib, src=str(mpath))
+    results = oracle_pins.battery(O.Oracle(lib))
+    failed = [n for n, ok, _ in results if not ok]
+    assert failed, f"mutant {name} passed every pin"
