@@ -1,0 +1,111 @@
+// nvq_device.h -- device helpers shared by the gfx950 kernels of libnvq.
+//
+// Everything here is written for CDNA4 (gfx950) only: 64-wide wavefronts,
+// v_perm_b32 byte selection, v_dot4_i32_i8, the OCP E4M3 / E2M1 conversion
+// instructions and the 16x16x32 fp16 MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Byte permute and integer dot product.
+// v_perm_b32(s0, s1, sel): result byte i = pool[sel_i] where pool bytes 0..3 come
+// from s1 and 4..7 from s0; selector 12 gives 0x00 and selectors >= 13 give 0xFF;
+// selectors 8..11 replicate the sign bit of pool bytes 1, 3, 5, 7.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// E2M1 -> signed integer L(c) = 2 * E2M1(c) in -12..12, four codes per dword
+// (one code per byte, values 0..15).  Two v_perm_b32 lookups whose sum is L:
+//   PA indexed by the whole code:   codes 0..7 give 0,2,4,6,8,11,15,23; codes
+//     8..12 give 0 (sign bits of non-negative pool bytes, or selector 12);
+//     codes 13..15 give 0xFF = -1.
+//   PB indexed by (code & 7):       0,-1,-2,-3,-4,-5,-7,-11.
+// Sum: 0,1,2,3,4,6,8,12 for codes 0..7 and 0,-1,-2,-3,-4,-6,-8,-12 for 8..15.
+// The two halves are summed inside the integer dot products (two v_dot4 per
+// operand), so no byte-wise add (and no carry) is ever needed.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPA_lo = 0x06040200u, kPA_hi = 0x170F0B08u;
+constexpr uint32_t kPB_lo = 0xFDFEFF00u, kPB_hi = 0xF5F9FBFCu;
+
+// One dword of 8 packed codes (byte i: code of weight 2i in bits 0..3, weight 2i+1
+// in bits 4..7) against activation dwords qe (the 4 even-position codes) and qo
+// (the 4 odd-position codes).  Returns acc + sum_j L(code_j) * q_j.
+__device__ __forceinline__ int dot8_e2m1(uint32_t c, uint32_t qe, uint32_t qo, int acc) {
+  const uint32_t lo = c & 0x0F0F0F0Fu;
+  const uint32_t lo7 = c & 0x07070707u;
+  const uint32_t t = c >> 4;
+  const uint32_t hi = t & 0x0F0F0F0Fu;
+  const uint32_t hi7 = t & 0x07070707u;
+  acc = dot4(perm(kPA_hi, kPA_lo, lo), qe, acc);
+  acc = dot4(perm(kPB_hi, kPB_lo, lo7), qe, acc);
+  acc = dot4(perm(kPA_hi, kPA_lo, hi), qo, acc);
+  acc = dot4(perm(kPB_hi, kPB_lo, hi7), qo, acc);
+  return acc;
+}
+
+// Split 8 activation bytes (two dwords, natural order) into even / odd positions.
+__device__ __forceinline__ void split_even_odd(uint32_t a, uint32_t b, uint32_t& e, uint32_t& o) {
+  e = perm(b, a, 0x06040200u);  // bytes a0 a2 b0 b2
+  o = perm(b, a, 0x07050301u);  // bytes a1 a3 b1 b3
+}
+
+// ---------------------------------------------------------------------------
+// UE4M3 scale byte -> float.  gfx950's v_cvt_f32_fp8 decodes OCP E4M3 (bias 7,
+// subnormals, 0x7F NaN); a UE4M3 byte with bit 7 clear has the same bits.
+// sel picks the byte of the dword.
+// ---------------------------------------------------------------------------
+template <int SEL>
+__device__ __forceinline__ float ue4m3_to_f32(uint32_t v) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, SEL);
+}
+
+// ---------------------------------------------------------------------------
+// Two E2M1 codes of byte SEL of v -> two fp16 values (low nibble first).  The
+// instruction's scale operand only contributes its power-of-two exponent, so it
+// is always 1.0 here and any other scale is applied with an exact fp16 multiply.
+// ---------------------------------------------------------------------------
+template <int SEL>
+__device__ __forceinline__ half2_t e2m1x2_to_f16(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, SEL);
+}
+
+// binary16 bits -> float (exact)
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Four signed bytes -> four fp16 (exact for |v| <= 2048): bias to unsigned,
+// splice under the exponent byte of 1024 (0x64) and subtract 1024 + 128.
+__device__ __forceinline__ void i8x4_to_f16x4(uint32_t v, half2_t& lo, half2_t& hi) {
+  const uint32_t u = v ^ 0x80808080u;
+  const uint32_t a = perm(0x64646464u, u, 0x04010400u);  // [u0, 0x64, u1, 0x64]
+  const uint32_t b = perm(0x64646464u, u, 0x04030402u);  // [u2, 0x64, u3, 0x64]
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(half2_t, a) - bias;
+  hi = __builtin_bit_cast(half2_t, b) - bias;
+}
+
+// Reduce a float over groups of LANES consecutive lanes (LANES = 16, 32 or 64);
+// every lane of a group ends with the group sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = LANES / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace nvq

@@ -1,0 +1,36 @@
+// nvq_launch.h -- host-side launchers of the gfx950 kernels (internal to libnvq).
+// Argument validation is done by the C ABI layer before any of these is called;
+// each launcher only picks a kernel configuration and enqueues it on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvq {
+
+hipError_t launch_act_quant(const float* x, int64_t M, int64_t K, int8_t* q, uint16_t* d16,
+                            int16_t* bsum16, hipStream_t stream);
+
+// NVFP4, M == 1, integer-dot path.  isums != nullptr selects the debug variant
+// (writes per-16 integer sums instead of y).
+hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
+                                const uint16_t* d16, int64_t N, int64_t K, float* y,
+                                int32_t* isums, hipStream_t stream);
+
+// NVFP4, MFMA tiled path (any M >= 1; used for M >= 2).  isums != nullptr selects
+// the debug variant.
+hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
+                             const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
+                             int32_t* isums, hipStream_t stream);
+
+// Q4_1, M == 1, integer-dot path.
+hipError_t launch_gemv_q4_1_m1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                               const int16_t* bsum16, int64_t N, int64_t K, float* y,
+                               int32_t* isums, hipStream_t stream);
+
+// Q4_1, MFMA tiled path (any M >= 1).
+hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream);
+
+}  // namespace nvq

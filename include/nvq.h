@@ -1,0 +1,180 @@
+/*
+ * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 x Q8_0) quantized matrix
+ * products on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Weights W [N][K] ("out x in", row-major) are stored 4-bit;
+ * activations X [M][K] (M tokens) are quantized on the fly to Q8_0; the product is
+ *     y[m][n] = sum_k W[n][k] * A[m][k],   y float32 [M][N] row-major,
+ * where A = d * q is the Q8_0-dequantized activation.  Sources (web pages, cited
+ * by title and section):
+ *   "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3 ("Code map" and the
+ *     bias-trick paragraph): NVFP4 weights in 64-weight blocks, one UE4M3 scale
+ *     per 16 weights, integer partial sums per 16-subblock, per-16 activation code
+ *     sums; batch-1 decode uses a vector dot, larger batches a tiled matmul;
+ *     section 1 names the Q4_1 kernels of the same work.
+ *   The llama.cpp 2-bit GGUF tutorial (spke.com, article 4846), GGML type table:
+ *     Q8_0 is 32 values in 34 bytes (32 int8 codes + one fp16 scale).
+ *
+ * Element formats (bit-exact definitions):
+ *   E2M1 code c (4 bits): sign = bit 3, exponent e = bits 2..1 (bias 1), mantissa
+ *     m = bit 0; e == 0 gives m/2, otherwise (1 + m/2) * 2^(e-1).  Code 8 is 0.
+ *   UE4M3 byte b (bit 7 must be 0, 0x7F is not allowed): exponent E = b >> 3
+ *     (bias 7), mantissa M = b & 7; E == 0 gives M * 2^-9, otherwise
+ *     (1 + M/8) * 2^(E-7).  Range 2^-9 .. 448.
+ *   NVFP4 weight: W[n][k] = S * UE4M3(scale[n][k/16]) * E2M1(code[n][k]),
+ *     S = float32 per-tensor scale (argument w_scale).
+ *   Q4_1 weight: W[n][k] = d[n][k/32] * q[n][k] + m[n][k/32], q in 0..15,
+ *     d and m IEEE binary16.
+ *   Q8_0 activation, per row and per 32 consecutive k:
+ *     amax = max |x|; d32 = amax / 127 (IEEE float32 division);
+ *     d = binary16(d32) rounded to nearest even (stored);
+ *     q = clamp(rint(x / d32), -127, 127) with IEEE float32 division by the
+ *         unrounded d32 and ties to even; amax == 0 gives d = 0, q = 0.
+ *     A[m][k] = d[m][k/32] * q[m][k].  bsum16[m][j] = sum of the 16 codes
+ *     q[m][16j .. 16j+15] (int16).
+ *
+ * Packed weight buffers (produced on the host by nvq_pack_*; one contiguous
+ * buffer, which the caller copies to device memory):
+ *   NVFP4, nvq_nvfp4_weight_bytes(N, K) = N*K/2 + N*K/16 bytes:
+ *     [0, N*K/2)            codes: row n at n*K/2; byte i of a row holds the code
+ *                           of weight k = 2i in bits 0..3 and of k = 2i+1 in bits 4..7.
+ *     [N*K/2, +N*K/16)      UE4M3 scales, row-major [N][K/16].
+ *   Q4_1, nvq_q4_1_weight_bytes(N, K) = N*K/2 + N*K/8 bytes:
+ *     [0, N*K/2)            codes, same nibble order as NVFP4.
+ *     [N*K/2, +N*K/8)       per 32 weights a 4-byte pair: binary16 d in the low
+ *                           half, binary16 m in the high half, row-major [N][K/32].
+ *
+ * Conventions for every entry point:
+ *   - All array arguments of the compute entries are DEVICE pointers owned by the
+ *     caller; the packers take HOST pointers.  The library allocates no device
+ *     memory and keeps no pointer after it returns; its only state is a
+ *     per-device "is this gfx950" flag written on first use.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Compute entries only enqueue work; results are valid once the stream is
+ *     synchronised.
+ *   - Device pointers w, q, x and y must be 16-byte aligned, d_f16 and bsum16
+ *     2-byte aligned and isums 4-byte aligned (NVQ_ERR_ALIGN otherwise).
+ *   - Return value: NVQ_OK (0) or a negative nvq_status.  On any error nothing is
+ *     enqueued and no output is touched (except NVQ_ERR_HIP, which reports a
+ *     launch failure after validation passed).  nvq_last_error() returns a
+ *     thread-local message describing the last error of the calling thread.
+ *   - Results are deterministic: identical inputs give bitwise identical outputs.
+ *   - The compute entries run only on gfx950 devices (NVQ_ERR_DEVICE otherwise);
+ *     there is no other code path.
+ */
+#ifndef NVQ_H
+#define NVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int nvq_status;
+
+#define NVQ_OK             0
+#define NVQ_ERR_NULL      -1  /* a required pointer is NULL */
+#define NVQ_ERR_SHAPE     -2  /* M, N or K out of range or K not a multiple of the block */
+#define NVQ_ERR_RANGE     -3  /* invalid code / scale byte, or bad enum argument */
+#define NVQ_ERR_ALIGN     -4  /* pointer alignment requirement not met */
+#define NVQ_ERR_DEVICE    -5  /* current device is not gfx950 */
+#define NVQ_ERR_HIP       -6  /* HIP runtime error (see nvq_last_error) */
+#define NVQ_ERR_WORKSPACE -7  /* workspace missing or too small */
+
+#define NVQ_FMT_NVFP4 0
+#define NVQ_FMT_Q4_1  1
+#define NVQ_PATH_GEMV 0
+#define NVQ_PATH_GEMM 1
+
+/* Largest M accepted by the GEMV entries; the GEMM entries accept M >= 16. */
+#define NVQ_GEMV_MAX_M 15
+
+/* ---- sizes (pure functions) ------------------------------------------------ */
+
+/* Bytes of a packed NVFP4 weight buffer [N][K]: N*K*9/16.  0 if N < 1 or K is not
+ * a positive multiple of 64. */
+size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
+
+/* Bytes of a packed Q4_1 weight buffer [N][K]: N*K*5/8.  0 if N < 1 or K is not a
+ * positive multiple of 32. */
+size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt is
+ * NVQ_FMT_*).  May be 0; the workspace pointer may then be NULL. */
+size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+/* ---- packers (host memory in, host memory out) ------------------------------ */
+
+/* codes: [N][K] bytes, one E2M1 code (0..15) per byte; ue4m3: [N][K/16] bytes.
+ * Writes nvq_nvfp4_weight_bytes(N, K) bytes to dst_host.  K % 64 == 0.
+ * NVQ_ERR_RANGE if a code exceeds 15 or a scale byte has bit 7 set or equals 0x7F
+ * (dst_host is then left unspecified). */
+nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3,
+                          int64_t N, int64_t K, void* dst_host);
+
+/* q: [N][K] bytes (0..15); d_f16, m_f16: [N][K/32] binary16 bit patterns.
+ * Writes nvq_q4_1_weight_bytes(N, K) bytes to dst_host.  K % 32 == 0.
+ * NVQ_ERR_RANGE if a code exceeds 15. */
+nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t* m_f16,
+                         int64_t N, int64_t K, void* dst_host);
+
+/* ---- activation quantization ------------------------------------------------ */
+
+/* Q8_0 quantization of x [M][K] float32 into q [M][K] int8, d_f16 [M][K/32]
+ * (binary16 bits) and, if bsum16 is not NULL, bsum16 [M][K/16] int16.  M >= 1,
+ * K % 32 == 0.  Bit-exact with the definition above.  Non-finite x, or
+ * amax > 65504 * 127, are outside the contract. */
+nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
+                                 int8_t* q, uint16_t* d_f16, int16_t* bsum16, void* stream);
+
+/* ---- NVFP4 products ----------------------------------------------------------- */
+
+/* Decode GEMV (the single-token case takes the vector-dot form): 1 <= M <= NVQ_GEMV_MAX_M, N >= 1,
+ * K % 64 == 0.  w: packed NVFP4 [N][K]; q, d_f16: Q8_0 activations [M][K];
+ * y [M][N] float32 (overwritten).  Per output the error against the exact product
+ * is at most 1e-5 * sum_k |W*A| + 1e-6 (float32 accumulation of exact per-16
+ * integer sums). */
+nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
+                          int64_t M, int64_t N, int64_t K, float* y, void* stream);
+
+/* Prefill GEMM (many tokens take the tiled form): M >= 16, N >= 1,
+ * K % 64 == 0; arguments as for the GEMV plus a device workspace of at least
+ * nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K) bytes. */
+nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
+                          int64_t M, int64_t N, int64_t K, float* y,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- Q4_1 products ------------------------------------------------------------ */
+
+/* Q4_1 GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 32 == 0.
+ * bsum16 [M][K/16] (from nvq_quantize_act_q8_0) is required: the offset m of each
+ * 32-block multiplies the sum of that block's activation codes. */
+nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream);
+nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- debug: integer per-16 partial sums --------------------------------------- */
+
+/* isums [M][N][K/16] int32 = for each 16-subblock, sum_j L(code) * q (NVFP4, with
+ * L(c) = 2*E2M1(c), an integer in -12..12) or sum_j code * q (Q4_1, unsigned codes).
+ * fmt: NVQ_FMT_*; path: NVQ_PATH_GEMV or NVQ_PATH_GEMM selects which production
+ * kernel's data path (weight load, code expansion, integer/MFMA contraction)
+ * produces the sums, run with unit scales.  Any M >= 1 is accepted for either
+ * path; K % 64 == 0 (NVFP4) or K % 32 == 0 (Q4_1). */
+nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q,
+                           int64_t M, int64_t N, int64_t K, int32_t* isums, void* stream);
+
+/* ---- errors ------------------------------------------------------------------- */
+
+const char* nvq_status_str(nvq_status s);
+const char* nvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVQ_H */

@@ -1,0 +1,98 @@
+"""Shared helpers of the GPU parity tests: build seeded cases, run the library
+through its C ABI binding, compute the oracle on the same bytes, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import gemm_q8_act_amd as nvq
+from gemm_q8_act_amd import synth
+
+TOL_REL = 1e-5
+TOL_ABS = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_dev():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU test needs a visible gfx950 device"
+    return torch
+
+
+def to_dev(a: np.ndarray):
+    torch = torch_dev()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def quantize_gpu(x: np.ndarray):
+    torch = torch_dev()
+    M, K = x.shape
+    xd = to_dev(x)
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
+    b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
+    nvq.nvq_quantize_act_q8_0(xd, q, d, b)
+    return q, d, b
+
+
+def host(t) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, awa: np.ndarray, what: str):
+    """|y_gpu - y_oracle| <= 1e-5 * sum|w*a| + 1e-6 element by element; also rejects
+    an all-zero result (a silent no-op would otherwise pass on zero inputs)."""
+    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+    assert np.isfinite(y_gpu).all(), f"{what}: non-finite output"
+    err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
+    bound = TOL_REL * awa + TOL_ABS
+    worst = float((err / bound).max()) if err.size else 0.0
+    bad = int((err > bound).sum())
+    assert bad == 0, f"{what}: {bad} of {err.size} outputs outside the bound (worst err/bound {worst:.3g})"
+    if np.abs(y_ref).max() > 0:
+        assert np.abs(y_gpu).max() > 0, f"{what}: output all zero"
+    return worst
+
+
+class NvCase:
+    """Seeded NVFP4 case: logical weights (oracle side), packed weights on the GPU."""
+
+    def __init__(self, M, N, K, seed, w_scale=1.0, outliers=False):
+        self.M, self.N, self.K = M, N, K
+        self.codes, self.scales, self.ws = synth.nvfp4_weights(N, K, seed, w_scale)
+        self.x = synth.activations(M, K, seed + 1, outliers=outliers)
+        self.w = to_dev(nvq.nvq_pack_nvfp4(self.codes, self.scales))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_nvfp4(self.codes, self.scales, self.ws, self.qh, self.dh, cols=cols)
+
+
+class Q41Case:
+    def __init__(self, M, N, K, seed):
+        self.M, self.N, self.K = M, N, K
+        self.qw, self.dw, self.mw = synth.q4_1_weights(N, K, seed)
+        self.x = synth.activations(M, K, seed + 1)
+        self.w = to_dev(nvq.nvq_pack_q4_1(self.qw, self.dw, self.mw))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_q4_1(self.qw, self.dw, self.mw, self.qh, self.dh, cols=cols)
+
+
+def sample_cols(N: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
+    """First/last columns, both sides of tile boundaries, plus seeded random ones."""
+    base = {0, 1, N - 1, N - 2}
+    for t in (tile, 2 * tile, (N // tile) * tile):
+        base |= {t - 1, t}
+    r = np.random.Generator(np.random.PCG64(seed))
+    base |= set(int(v) for v in r.integers(0, N, count))
+    return np.array(sorted(c for c in base if 0 <= c < N), np.int64)

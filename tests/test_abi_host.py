@@ -1,0 +1,149 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the sizes and packers follow the documented layout, and every
+argument error is reported before any HIP call (so these run on a CPU host)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import gemm_q8_act_amd as nvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvq.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_symbols() == sorted(nvq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = nvq.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", nvq.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (nvq_[a-z0-9_]+)\b", out))
+    assert set(declared_symbols()) <= exported
+
+
+def test_library_has_only_gfx950_code(tmp_path):
+    fb = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", "-O", "binary", "--only-section=.hip_fatbin", nvq.LIB_PATH, str(fb)], check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o",
+                          f"--input={fb}"], capture_output=True, text=True, check=True)
+    targets = [t for t in out.stdout.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), targets
+
+
+def test_sizes():
+    assert nvq.nvq_nvfp4_weight_bytes(4864, 896) == 4864 * 896 * 9 // 16
+    assert nvq.nvq_nvfp4_weight_bytes(7, 64) == 7 * 36
+    assert nvq.nvq_nvfp4_weight_bytes(7, 96) == 0          # K % 64 != 0
+    assert nvq.nvq_nvfp4_weight_bytes(0, 64) == 0
+    assert nvq.nvq_q4_1_weight_bytes(4096, 4096) == 4096 * 4096 * 5 // 8
+    assert nvq.nvq_q4_1_weight_bytes(3, 32) == 3 * 20
+    assert nvq.nvq_q4_1_weight_bytes(3, 48) == 0
+    assert nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) >= 0
+
+
+def test_pack_nvfp4_layout():
+    r = np.random.Generator(np.random.PCG64(5))
+    N, K = 3, 128
+    codes = r.integers(0, 16, (N, K), dtype=np.uint8)
+    scales = r.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
+    buf = nvq.nvq_pack_nvfp4(codes, scales)
+    assert buf.size == N * K * 9 // 16
+    cb = buf[: N * K // 2].reshape(N, K // 2)
+    assert (cb & 0xF == codes[:, 0::2]).all()          # weight 2i in the low nibble
+    assert (cb >> 4 == codes[:, 1::2]).all()           # weight 2i+1 in the high nibble
+    assert (buf[N * K // 2:].reshape(N, K // 16) == scales).all()
+
+
+def test_pack_q4_1_layout():
+    r = np.random.Generator(np.random.PCG64(6))
+    N, K = 2, 96
+    q = r.integers(0, 16, (N, K), dtype=np.uint8)
+    d = r.integers(0, 65536, (N, K // 32), dtype=np.uint32).astype(np.uint16)
+    m = r.integers(0, 65536, (N, K // 32), dtype=np.uint32).astype(np.uint16)
+    buf = nvq.nvq_pack_q4_1(q, d, m)
+    assert buf.size == N * K * 5 // 8
+    cb = buf[: N * K // 2].reshape(N, K // 2)
+    assert (cb & 0xF == q[:, 0::2]).all() and (cb >> 4 == q[:, 1::2]).all()
+    pairs = buf[N * K // 2:].view(np.uint32).reshape(N, K // 32)
+    assert ((pairs & 0xFFFF) == d).all() and ((pairs >> 16) == m).all()
+
+
+@pytest.mark.parametrize("bad", ["code16", "scale_bit7", "scale_nan"])
+def test_pack_nvfp4_rejects_invalid(bad):
+    codes = np.zeros((1, 64), np.uint8)
+    scales = np.full((1, 4), 0x38, np.uint8)
+    if bad == "code16":
+        codes[0, 5] = 16
+    elif bad == "scale_bit7":
+        scales[0, 2] = 0xB8
+    else:
+        scales[0, 1] = 0x7F
+    with pytest.raises(nvq.NvqError) as e:
+        nvq.nvq_pack_nvfp4(codes, scales)
+    assert e.value.status == -3
+
+
+def test_pack_shape_errors():
+    L = nvq.lib()
+    codes = np.zeros((1, 96), np.uint8)
+    scales = np.zeros((1, 6), np.uint8)
+    dst = np.zeros(128, np.uint8)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert L.nvq_pack_nvfp4(p(codes), p(scales), 1, 96, p(dst)) == -2
+    assert L.nvq_pack_nvfp4(None, p(scales), 1, 64, p(dst)) == -1
+    assert "NULL" in nvq.last_error()
+
+
+# Fake but well-aligned "device" addresses: validation must reject the call before
+# any of them is dereferenced or any HIP call is made.
+A16 = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20002)
+MIS = ctypes.c_void_p(0x30004)
+
+
+def test_gemv_validation_without_gpu():
+    L = nvq.lib()
+    st = None
+    assert L.nvq_gemv_nvfp4(None, 1.0, A16, A16, 1, 8, 64, A16, st) == -1
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, A16, 1, 8, 96, A16, st) == -2     # K % 64
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, A16, 0, 8, 64, A16, st) == -2     # M = 0
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, A16, 16, 8, 64, A16, st) == -2    # M > 15
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, A16, 1, 0, 64, A16, st) == -2     # N = 0
+    assert L.nvq_gemv_nvfp4(MIS, 1.0, A16, A16, 1, 8, 64, A16, st) == -4     # w alignment
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, ctypes.c_void_p(0x20001), 1, 8, 64, A16, st) == -4
+    assert L.nvq_gemv_q4_1(A16, A16, A16, None, 1, 8, 32, A16, st) == -1     # bsum16 required
+    assert L.nvq_gemv_q4_1(A16, A16, A16, A2, 1, 8, 48, A16, st) == -2       # K % 32
+
+
+def test_gemm_validation_without_gpu():
+    L = nvq.lib()
+    assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 15, 8, 64, A16, None, 0, None) == -2   # M < 16
+    assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 32, A16, None, 0, None) == -2   # K % 64
+    assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 64, MIS, None, 0, None) == -4   # y alignment
+    assert L.nvq_gemm_q4_1(A16, A16, A16, A2, 8, 8, 32, A16, None, 0, None) == -2
+    assert L.nvq_quantize_act_q8_0(A16, 1, 48, A16, A16, None, None) == -2
+    assert L.nvq_quantize_act_q8_0(MIS, 1, 64, A16, A16, None, None) == -4
+    assert L.nvq_quantize_act_q8_0(None, 1, 64, A16, A16, None, None) == -1
+    assert L.nvq_debug_isums(7, 0, A16, A16, 1, 8, 64, A16, None) == -3
+    assert L.nvq_debug_isums(0, 9, A16, A16, 1, 8, 64, A16, None) == -3
+    assert L.nvq_debug_isums(1, 0, A16, A16, 1, 8, 48, A16, None) == -2
+
+
+def test_status_strings():
+    for s, name in [(0, "NVQ_OK"), (-1, "NVQ_ERR_NULL"), (-2, "NVQ_ERR_SHAPE"), (-3, "NVQ_ERR_RANGE"),
+                    (-4, "NVQ_ERR_ALIGN"), (-5, "NVQ_ERR_DEVICE"), (-6, "NVQ_ERR_HIP"),
+                    (-7, "NVQ_ERR_WORKSPACE")]:
+        assert nvq.status_str(s) == name
