@@ -23,12 +23,13 @@ NVQ_FMT_NVFP4 = 0
 NVQ_FMT_Q4_1 = 1
 NVQ_PATH_GEMV = 0
 NVQ_PATH_GEMM = 1
+NVQ_PATH_GEMV_DOT4 = 2
 NVQ_GEMV_MAX_M = 15
 
 # Every symbol include/nvq.h declares.
 EXPORTS = (
     "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_gemm_workspace_bytes",
-    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4",
+    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_dot4",
     "nvq_gemm_nvfp4", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
     "nvq_status_str", "nvq_last_error",
 )
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "nvq_pack_q4_1": (ctypes.c_int, [P, P, P, I64, I64, P]),
             "nvq_quantize_act_q8_0": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
+            "nvq_gemv_nvfp4_dot4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_gemv_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
@@ -211,6 +213,17 @@ def nvq_gemv_nvfp4(w, w_scale: float, q, d_f16, y, stream=None) -> None:
     _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
     _check(lib().nvq_gemv_nvfp4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
                                 _stream(stream, y)), "nvq_gemv_nvfp4")
+
+
+def nvq_gemv_nvfp4_dot4(w, w_scale: float, q, d_f16, y, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_nvfp4_dot4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
+                                     _stream(stream, y)), "nvq_gemv_nvfp4_dot4")
 
 
 def nvq_gemm_nvfp4(w, w_scale: float, q, d_f16, y, workspace=None, stream=None) -> None:

@@ -17,12 +17,12 @@
 //     (columns = m), every lane owns a single column m, so one d value per lane
 //     scales all of that lane's accumulators.
 //
-// Tiling: a 256-thread block computes BN weight rows x BM tokens.  Per 64-k step
-// the block loads BN x 32 B of codes + BN x 4 scale bytes and BM x 64 B of
-// activation codes, expands both to fp16 in LDS (double-buffered, rows padded
-// to 144 B so 16-byte fragment reads are bank-conflict free), and each of the 4
-// wavefronts runs (BN/64) x (BM/16) MFMAs per chunk.  Global loads of step k+1 are
-// issued before the MFMAs of step k.
+// Tiling: a 256-thread block computes BN weight rows x BM tokens.  Per 128-k step
+// the block loads BN/16 tile-chunks of the packed layout (1 KB of codes + 128 scale
+// bytes each, contiguous) and BM x 128 B of activation codes, expands both to fp16
+// in LDS (double-buffered, rows padded to 272 B so 16-byte fragment reads are
+// bank-conflict free), and each of the 4 wavefronts runs (BN/64) x (BM/16) MFMAs
+// per 32-k block.  Global loads of step k+1 are issued before the MFMAs of step k.
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
@@ -36,28 +36,29 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
                                                          int64_t M, float w_scale,
                                                          float* __restrict__ y,
                                                          int32_t* __restrict__ isums) {
-  constexpr int BK = 64;
+  constexpr int BK = 128;        // one tile-chunk of the packed layout per step
   constexpr int WN = BN / 4;     // weight rows per wavefront
   constexpr int NT = WN / 16;    // 16-row subtiles per wavefront
   constexpr int MT = BM / 16;    // 16-token subtiles
-  constexpr int LDH = BK + 8;    // fp16 per LDS row (144 B)
-  constexpr int WT = (BN * 2 + 255) / 256;  // 32-weight weight tasks per thread
-  constexpr int AT = (BM * 4 + 255) / 256;  // 16-code activation tasks per thread
+  constexpr int LDH = BK + 8;    // fp16 per LDS row (272 B: conflict-free 16-byte reads)
+  constexpr int WT = (BN * 4 + 255) / 256;  // 32-weight lane slots per thread
+  constexpr int AT = (BM * 8 + 255) / 256;  // 16-code activation segments per thread
   static_assert(NT >= 1 && MT >= 1, "tile");
 
   __shared__ __align__(16) _Float16 lw[2][BN * LDH];
   __shared__ __align__(16) _Float16 la[2][BM * LDH];
-  __shared__ float ldv[2][BM * 2];
+  __shared__ float ldv[2][BM * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t n0 = (int64_t)blockIdx.x * BN;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int64_t crow = K >> 1, srow = K >> 4;
   const int64_t nb32 = K >> 5;
-  const int nks = K / BK;
-  const uint8_t* __restrict__ sc = w + N * crow;
+  const int64_t nsb = K >> 4;
+  const int nch = (K + BK - 1) / BK;
+  const int64_t ntiles = (N + 15) >> 4;
+  const uint8_t* __restrict__ sc = w + ntiles * nch * 1024;
 
   uint4 wreg[WT];
   uint32_t sreg[WT];
@@ -68,11 +69,11 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < WT; ++i) {
       const int task = tid + 256 * i;
-      const int r = task >> 1, h = task & 1;
-      const int64_t row = n0 + r;
-      if (task < BN * 2 && row < N) {
-        wreg[i] = *reinterpret_cast<const uint4*>(w + row * crow + (int64_t)ks * 32 + 16 * h);
-        sreg[i] = *reinterpret_cast<const uint16_t*>(sc + row * srow + (int64_t)ks * 4 + 2 * h);
+      const int64_t tile = n0 / 16 + (task >> 6);
+      if (task < BN * 4 && tile < ntiles) {
+        const int64_t blk = tile * nch + ks;
+        wreg[i] = *reinterpret_cast<const uint4*>(w + blk * 1024 + 16 * (task & 63));
+        sreg[i] = *reinterpret_cast<const uint16_t*>(sc + blk * 128 + 2 * (task & 63));
       } else {
         wreg[i] = make_uint4(0u, 0u, 0u, 0u);
         sreg[i] = 0u;
@@ -81,16 +82,18 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < AT; ++i) {
       const int task = tid + 256 * i;
-      const int r = task >> 2, p = task & 3;
+      const int r = task >> 3, p = task & 7;
       const int64_t m = m0 + r;
-      if (task < BM * 4 && m < M)
-        areg[i] = *reinterpret_cast<const uint4*>(q + m * K + (int64_t)ks * 64 + 16 * p);
+      const int64_t k = (int64_t)ks * BK + 16 * p;
+      if (task < BM * 8 && m < M && k < K)
+        areg[i] = *reinterpret_cast<const uint4*>(q + m * K + k);
       else
         areg[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    if (!DEBUG && tid < BM * 2) {
-      const int64_t m = m0 + (tid >> 1);
-      dval = (m < M) ? f16_bits_to_f32(d16[m * nb32 + 2 * ks + (tid & 1)]) : 0.0f;
+    if (!DEBUG && tid < BM * 4) {
+      const int64_t m = m0 + (tid >> 2);
+      const int64_t b = (int64_t)ks * 4 + (tid & 3);
+      dval = (m < M && b < nb32) ? f16_bits_to_f32(d16[m * nb32 + b]) : 0.0f;
     }
   };
 
@@ -98,13 +101,15 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < WT; ++i) {
       const int task = tid + 256 * i;
-      if (task < BN * 2) {
-        const int r = task >> 1, h = task & 1;
+      if (task < BN * 4) {
+        const int l = task & 63;
+        const int r = 16 * (task >> 6) + (l & 15);   // row within the block tile
+        const int kq = l >> 4;                        // 32-k quarter of the chunk
         const _Float16 u0 = DEBUG ? (_Float16)1.0f : (_Float16)ue4m3_to_f32<0>(sreg[i]);
         const _Float16 u1 = DEBUG ? (_Float16)1.0f : (_Float16)ue4m3_to_f32<1>(sreg[i]);
         const half2_t s0 = {u0, u0}, s1 = {u1, u1};
         const uint32_t c[4] = {wreg[i].x, wreg[i].y, wreg[i].z, wreg[i].w};
-        _Float16* dst = &lw[buf][r * LDH + 32 * h];
+        _Float16* dst = &lw[buf][r * LDH + 32 * kq];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           const half2_t s = d < 2 ? s0 : s1;
@@ -122,8 +127,8 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < AT; ++i) {
       const int task = tid + 256 * i;
-      if (task < BM * 4) {
-        const int r = task >> 2, p = task & 3;
+      if (task < BM * 8) {
+        const int r = task >> 3, p = task & 7;
         const uint32_t c[4] = {areg[i].x, areg[i].y, areg[i].z, areg[i].w};
         _Float16* dst = &la[buf][r * LDH + 16 * p];
 #pragma unroll
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
         }
       }
     }
-    if (!DEBUG && tid < BM * 2) ldv[buf][tid] = dval;
+    if (!DEBUG && tid < BM * 4) ldv[buf][tid] = dval;
   };
 
   floatx4 acc[NT][MT];
@@ -148,12 +153,12 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
     for (int t = 0; t < MT; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15;   // fragment row (A) / column (B)
-  const int fg = lane >> 4;   // k group: k = 8*fg .. 8*fg+7 of the chunk
+  const int fg = lane >> 4;   // k group: k = 8*fg .. 8*fg+7 of the 32-k block
   const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int buf, int ks) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < BK / 32; ++c) {
       half8_t a[NT], b[MT];
 #pragma unroll
       for (int i = 0; i < NT; ++i)
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
       if (!DEBUG) {
         float dv[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) dv[t] = ldv[buf][(16 * t + fr) * 2 + c];
+        for (int t = 0; t < MT; ++t) dv[t] = ldv[buf][(16 * t + fr) * 4 + c];
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
@@ -184,11 +189,11 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
               const half8_t bb = ((fg >> 1) == hsub) ? b[t] : z8;
               const floatx4 p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bb, zero4, 0, 0, 0);
               const int64_t m = m0 + 16 * t + fr;
-              const int64_t s = (int64_t)ks * 4 + 2 * c + hsub;
+              const int64_t s = (int64_t)ks * 8 + 2 * c + hsub;
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const int64_t n = n0 + wave * WN + 16 * i + 4 * fg + rr;
-                if (m < M && n < N) isums[(m * N + n) * srow + s] = (int32_t)(2.0f * p[rr]);
+                if (m < M && n < N && s < nsb) isums[(m * N + n) * nsb + s] = (int32_t)(2.0f * p[rr]);
               }
             }
           }
@@ -199,8 +204,8 @@ __global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restri
   gload(0);
   lstore(0);
   __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const bool more = ks + 1 < nks;
+  for (int ks = 0; ks < nch; ++ks) {
+    const bool more = ks + 1 < nch;
     if (more) gload(ks + 1);
     compute(ks & 1, ks);
     if (more) lstore((ks + 1) & 1);

@@ -1,236 +1,208 @@
 // gemv_nvfp4.hip -- batch-1 decode GEMV, NVFP4 weights x Q8_0 activations, gfx950.
 //
-// Method ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map and
-// bias-trick paragraph): per 16-weight subblock an exact integer sum of
-// L(code) * q with L = 2 * E2M1, then one float scale per subblock,
-//     y[n] = S * sum_s 0.5 * UE4M3(scale[n][s]) * d[s/2] * isum16[n][s].
-// The page's x86 kernel biases codes to 0..24 because the VNNI multiply is
-// unsigned x signed; v_dot4_i32_i8 is signed x signed, so the signed L is used
-// directly and the bias (and the bsum16 correction) is not needed here.
+// What is computed ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3,
+// Code map and bias-trick paragraph): for every 16-weight subblock an exact integer
+// sum of the weight codes' values times the activation codes, then one float scale
+// per subblock:
+//     y[n] = S * sum_s UE4M3(scale[n][s]) * d[s/2] * sum_{k in s} E2M1(code[n][k]) * q[k].
 //
-// Mapping (HBM-bound stream of 9/16 byte per weight):
-//   * a "unit" is 32 consecutive weights of a row: 16 B of codes (one 128-bit
-//     load) + 2 UE4M3 bytes + one Q8_0 block of activations;
-//   * LPR lanes share a row and take units sub, sub + LPR, ... so each load
-//     instruction of a wavefront reads 64/LPR runs of LPR*16 contiguous bytes;
-//   * every lane keeps the activation codes of its units in VGPRs (pre-split into
-//     even/odd positions to match the nibble order) and reuses them for all the
-//     rows it visits; RG row groups are loaded before any is reduced so that
-//     RG*UPL 128-bit loads per lane are in flight;
-//   * E2M1 -> int8 is two v_perm_b32 table lookups per 4 codes whose sum is L,
-//     consumed by two v_dot4_i32_i8 (see nvq_device.h);
-//   * per unit: 2 integer sums -> float, times UE4M3 (v_cvt_f32_fp8) and the
-//     lane's 0.5*d, accumulated in float; the LPR partial sums of a row are
-//     reduced across lanes and the first lane writes y.
+// Weights use the tile-interleaved packed layout (include/nvq.h): a 16-row x 128-k
+// tile-chunk is 1 KB of codes in MFMA lane order (lane l = 16*g + n holds row n,
+// k = 32g..32g+31) followed elsewhere by its 128 scale bytes (lane l: the two scales
+// of subblocks 2g, 2g+1).  Every wavefront load is therefore 1 KB contiguous.
+//
+// Two inner loops share one skeleton (a 256-thread block owns one 16-row tile; its
+// four wavefronts take the chunks c = wave, wave+4, ...; each wavefront issues the
+// loads of P chunks before computing them; an activation table built once per
+// block in LDS; partial sums reduced through LDS at the end):
+//
+//  * MODE_MX (production).  gfx950's matrix cores read E2M1 natively: the 16 packed
+//    bytes a lane loads are, unchanged, its FP4 operand of one
+//    v_mfma_scale_f32_16x16x128_f8f6f4.  The FP8 (E4M3) operand carries the
+//    activations: each code q = 16*h + l with h = q >> 4 in [-8, 7] and l = q & 15,
+//    both exact in E4M3 (a byte b <= 15 encodes exactly b * 2^-9, which the
+//    operand's MX scale 2^9 undoes; h is stored sign-magnitude).  Its 16 rows are
+//    (subblock sb, part) variants that are zero outside subblock sb, so one MFMA
+//    returns, for 16 weight rows, the 8 per-subblock sums of both parts:
+//    isum = 16 * D_h + D_l is exact.  The vector unit only applies
+//    UE4M3 * d per subblock (about 10 instructions per 2048 weights), so the
+//    kernel stays under the HBM stream instead of being bound by code expansion.
+//
+//  * MODE_DOT4.  The same sums with the vector unit only: E2M1 -> int8 by two
+//    v_perm_b32 table lookups per four codes, summed inside v_dot4_i32_i8 (see
+//    nvq_device.h).  About 13 full-rate instructions per 8 weights: on MI355X this
+//    costs as much time as streaming the bytes, so it is the slower of the two.
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
 namespace nvq {
 
-constexpr int kGemvMaxUPL = 10;
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__host__ __device__ constexpr int gemv_rg(int upl) { return upl >= 7 ? 1 : (upl >= 4 ? 2 : 4); }
+constexpr int kGemvP = 5;  // chunks per load batch and wavefront
 
-template <int LPR, int UPL, bool DEBUG>
-__global__ __launch_bounds__(256) void gemv_nvfp4_m1_kernel(const uint8_t* __restrict__ w,
-                                                            int64_t N, int K,
-                                                            const int8_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ d16,
-                                                            float w_scale, float* __restrict__ y,
-                                                            int32_t* __restrict__ isums) {
-  constexpr int RG = gemv_rg(UPL);
-  constexpr int RPG = 64 / LPR;   // rows side by side in one wavefront
-  constexpr int RPW = RPG * RG;   // rows per wavefront
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane % LPR;
-  const int slot = lane / LPR;
-  const int units = K >> 5;
-  const int64_t crow = K >> 1;   // code bytes per row
-  const int64_t srow = K >> 4;   // scale bytes per row
-  const uint8_t* __restrict__ sc = w + N * crow;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
+// Four activation codes -> the high parts h = q >> 4 as sign-magnitude E4M3 bytes
+// (|h| <= 8, value |h| * 2^-9 with the sign bit).
+__device__ __forceinline__ uint32_t act_hi_e4m3(uint32_t q) {
+  const uint32_t nib = (q >> 4) & 0x0F0F0F0Fu;   // h as a two's complement nibble
+  const uint32_t neg = (nib >> 3) & 0x01010101u;  // 1 where h < 0
+  const uint32_t m = (neg << 4) - neg;            // 0x0F where h < 0
+  const uint32_t mag = (nib ^ m) + neg;           // |h|
+  return mag | (neg << 7);
+}
 
-  // 1. weight loads of all RG row groups first (RG*UPL 16-byte loads in flight)
-  uint4 cw[RG][UPL];
-  uint32_t sw[RG][UPL];
+template <int MODE, bool DEBUG>
+__global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
+                                                         int K, const int8_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ d16,
+                                                         float w_scale, float* __restrict__ y,
+                                                         int32_t* __restrict__ isums) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int nch = (K + 127) >> 7;
+  const int nsb = K >> 4;
+  // LDS: activation table [nch][256 B] | 16 zero bytes | d [nch*4] | partial sums [4][64]
+  uint8_t* tab = smem;
+  float* dtab = reinterpret_cast<float*>(smem + nch * 256 + 16);
+  float* red = dtab + nch * 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t tile = blockIdx.x;
+  const int64_t ntiles = (N + 15) >> 4;
+  const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
+  const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
+
+  // 1. first batch of weight loads, issued before anything else
+  u32x4 bb[kGemvP];
+  uint32_t ss[kGemvP];
+  auto issue = [&](int c0) {
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int64_t row = row0 + r * RPG + slot;
-#pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const int u = sub + LPR * j;
-      if (row < N && u < units) {
-        cw[r][j] = *reinterpret_cast<const uint4*>(w + row * crow + 16 * (int64_t)u);
-        sw[r][j] = *reinterpret_cast<const uint16_t*>(sc + row * srow + 2 * (int64_t)u);
+    for (int p = 0; p < kGemvP; ++p) {
+      const int c = c0 + 4 * p;
+      if (c < nch) {
+        bb[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt + (int64_t)c * 1024));
+        ss[p] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + (int64_t)c * 128));
       } else {
-        cw[r][j] = make_uint4(0u, 0u, 0u, 0u);
-        sw[r][j] = 0u;
+        bb[p] = u32x4{0u, 0u, 0u, 0u};
+        ss[p] = 0u;
       }
     }
-  }
+  };
+  int c0 = wave;
+  issue(c0);
 
-  // 2. activation codes of this lane's units, split into even / odd positions
-  uint32_t qe[UPL][4], qo[UPL][4];
-  float dq[UPL];
-#pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int u = sub + LPR * j;
-    if (u < units) {
-      const uint4 a = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u);
-      const uint4 b = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u + 16);
-      split_even_odd(a.x, a.y, qe[j][0], qo[j][0]);
-      split_even_odd(a.z, a.w, qe[j][1], qo[j][1]);
-      split_even_odd(b.x, b.y, qe[j][2], qo[j][2]);
-      split_even_odd(b.z, b.w, qe[j][3], qo[j][3]);
-      dq[j] = DEBUG ? 0.0f : 0.5f * f16_bits_to_f32(d16[u]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qe[j][i] = qo[j][i] = 0u;
-      dq[j] = 0.0f;
+  // 2. activation table: per 128-k chunk, MX: [h parts 128 B | l parts 128 B];
+  //    DOT4: per 32-k quarter g, [even codes 16 B | odd codes 16 B]
+  for (int t = tid; t < nch * 32; t += 256) {
+    const int k = 4 * t;
+    const uint32_t qv = (k < K) ? *reinterpret_cast<const uint32_t*>(q + k) : 0u;
+    const int c = k >> 7, o = k & 127;
+    if (MODE == 0) {
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = act_hi_e4m3(qv);
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = qv & 0x0F0F0F0Fu;
+    } else if ((t & 1) == 0) {
+      // pairs of dwords (8 codes) -> one even and one odd dword
+      const uint32_t qv2 = (k + 4 < K) ? *reinterpret_cast<const uint32_t*>(q + k + 4) : 0u;
+      uint32_t e, od;
+      split_even_odd(qv, qv2, e, od);
+      const int gq = o >> 5, j = (o & 31) >> 3;  // quarter, 8-code group within it
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + gq * 64 + 4 * j) = e;
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + gq * 64 + 16 + 4 * j) = od;
     }
   }
+  if (tid < 4) reinterpret_cast<uint32_t*>(tab + nch * 256)[tid] = 0u;
+  if (!DEBUG)
+    for (int b = tid; b < nch * 4; b += 256) dtab[b] = (b < (K >> 5)) ? f16_bits_to_f32(d16[b]) : 0.0f;
+  __syncthreads();
 
-  // 3. integer dots, per-subblock scaling, row reduction
+  // 3. compute
+  const int sbv = nl >> 1, part = nl & 1;
+  const uint8_t* zero16 = tab + nch * 256;
+  const uint32_t pal = in_vgpr(kPA_lo), pah = in_vgpr(kPA_hi);
+  const uint32_t pbl = in_vgpr(kPB_lo), pbh = in_vgpr(kPB_hi);
+  const uint32_t m4 = in_vgpr(0x0F0F0F0Fu), m3 = in_vgpr(0x07070707u);
+  const int64_t row = tile * 16 + nl;
+  float acc = 0.0f;
+  while (true) {
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int64_t row = row0 + r * RPG + slot;
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      int i0 = dot8_e2m1(cw[r][j].x, qe[j][0], qo[j][0], 0);
-      i0 = dot8_e2m1(cw[r][j].y, qe[j][1], qo[j][1], i0);
-      int i1 = dot8_e2m1(cw[r][j].z, qe[j][2], qo[j][2], 0);
-      i1 = dot8_e2m1(cw[r][j].w, qe[j][3], qo[j][3], i1);
+    for (int p = 0; p < kGemvP; ++p) {
+      const int c = c0 + 4 * p;
+      if (c >= nch) continue;
+      float i0, i1;  // the two per-16 sums (E2M1 units) of subblocks 8c+2g, 8c+2g+1
+      if (MODE == 0) {
+        const uint8_t* pa = (sbv == g) ? tab + c * 256 + part * 128 + 16 * g : zero16;
+        const uint8_t* pb = (sbv == g + 4) ? tab + c * 256 + part * 128 + 64 + 16 * g : zero16;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(pb);
+        const v8i av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                        (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        const v8i bv = {(int)bb[p][0], (int)bb[p][1], (int)bb[p][2], (int)bb[p][3], 0, 0, 0, 0};
+        // A: FP8 activation variants (scale 2^9), B: FP4 weights (scale 1)
+        const floatx4 D = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127 + 9, 0, 127);
+        i0 = fmaf(D[0], 16.0f, D[1]);
+        i1 = fmaf(D[2], 16.0f, D[3]);
+      } else {
+        const u32x4 qe = *reinterpret_cast<const u32x4*>(tab + c * 256 + g * 64);
+        const u32x4 qo = *reinterpret_cast<const u32x4*>(tab + c * 256 + g * 64 + 16);
+        int a0 = 0, b0 = 0, a1 = 0, b1 = 0;
+        dot8_e2m1_ab(bb[p][0], qe[0], qo[0], a0, b0, pal, pah, pbl, pbh, m4, m3);
+        dot8_e2m1_ab(bb[p][1], qe[1], qo[1], a0, b0, pal, pah, pbl, pbh, m4, m3);
+        dot8_e2m1_ab(bb[p][2], qe[2], qo[2], a1, b1, pal, pah, pbl, pbh, m4, m3);
+        dot8_e2m1_ab(bb[p][3], qe[3], qo[3], a1, b1, pal, pah, pbl, pbh, m4, m3);
+        i0 = 0.5f * (float)(a0 + b0);  // L = 2 * E2M1
+        i1 = 0.5f * (float)(a1 + b1);
+      }
       if (DEBUG) {
-        const int u = sub + LPR * j;
-        if (row < N && u < units) {
-          isums[row * srow + 2 * u] = i0;
-          isums[row * srow + 2 * u + 1] = i1;
+        const int s0 = 8 * c + 2 * g;
+        if (row < N && s0 < nsb) {
+          isums[row * nsb + s0] = (int32_t)(2.0f * i0);
+          isums[row * nsb + s0 + 1] = (int32_t)(2.0f * i1);
         }
       } else {
-        const float u0 = ue4m3_to_f32<0>(sw[r][j]);
-        const float u1 = ue4m3_to_f32<1>(sw[r][j]);
-        acc = fmaf(fmaf((float)i0, u0, (float)i1 * u1), dq[j], acc);
+        const float t = fmaf(i0, ue4m3_to_f32<0>(ss[p]), i1 * ue4m3_to_f32<1>(ss[p]));
+        acc = fmaf(t, dtab[4 * c + g], acc);
       }
     }
-    if (!DEBUG) {
-      acc = group_sum<LPR>(acc);
-      if (sub == 0 && row < N) y[row] = acc * w_scale;
-    }
+    c0 += 4 * kGemvP;
+    if (c0 >= nch) break;
+    issue(c0);
+  }
+  if (DEBUG) return;
+
+  // 4. reduce the 16 partial sums of each row (4 lane groups x 4 wavefronts)
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float s = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) s += red[ww * 64 + gg * 16 + tid];
+    const int64_t r = tile * 16 + tid;
+    if (r < N) y[r] = s * w_scale;
   }
 }
 
-// Generic fallback for K beyond kGemvMaxUPL*64*32 weights: one wavefront per row,
-// activations re-read per unit (from cache).  Same arithmetic as the fast kernel.
-template <bool DEBUG>
-__global__ __launch_bounds__(256) void gemv_nvfp4_m1_long_kernel(
-    const uint8_t* __restrict__ w, int64_t N, int K, const int8_t* __restrict__ q,
-    const uint16_t* __restrict__ d16, float w_scale, float* __restrict__ y,
-    int32_t* __restrict__ isums) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= N) return;  // whole wavefront exits together
-  const int units = K >> 5;
-  const int64_t crow = K >> 1, srow = K >> 4;
-  const uint8_t* __restrict__ sc = w + N * crow;
-  float acc = 0.0f;
-  for (int u = lane; u < units; u += 64) {
-    const uint4 c = *reinterpret_cast<const uint4*>(w + row * crow + 16 * (int64_t)u);
-    const uint32_t s = *reinterpret_cast<const uint16_t*>(sc + row * srow + 2 * (int64_t)u);
-    const uint4 a = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u);
-    const uint4 b = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u + 16);
-    uint32_t e0, o0, e1, o1, e2, o2, e3, o3;
-    split_even_odd(a.x, a.y, e0, o0);
-    split_even_odd(a.z, a.w, e1, o1);
-    split_even_odd(b.x, b.y, e2, o2);
-    split_even_odd(b.z, b.w, e3, o3);
-    int i0 = dot8_e2m1(c.y, e1, o1, dot8_e2m1(c.x, e0, o0, 0));
-    int i1 = dot8_e2m1(c.w, e3, o3, dot8_e2m1(c.z, e2, o2, 0));
-    if (DEBUG) {
-      isums[row * srow + 2 * u] = i0;
-      isums[row * srow + 2 * u + 1] = i1;
-    } else {
-      const float dqv = 0.5f * f16_bits_to_f32(d16[u]);
-      acc = fmaf(fmaf((float)i0, ue4m3_to_f32<0>(s), (float)i1 * ue4m3_to_f32<1>(s)), dqv, acc);
-    }
-  }
-  if (!DEBUG) {
-    acc = group_sum<64>(acc);
-    if (lane == 0) y[row] = acc * w_scale;
-  }
-}
-
-namespace {
-
-typedef void (*gemv_fn)(const uint8_t*, int64_t, int, const int8_t*, const uint16_t*, float,
-                        float*, int32_t*);
-
-template <int LPR, bool DEBUG>
-gemv_fn pick_upl(int upl) {
-  switch (upl) {
-    case 1: return gemv_nvfp4_m1_kernel<LPR, 1, DEBUG>;
-    case 2: return gemv_nvfp4_m1_kernel<LPR, 2, DEBUG>;
-    case 3: return gemv_nvfp4_m1_kernel<LPR, 3, DEBUG>;
-    case 4: return gemv_nvfp4_m1_kernel<LPR, 4, DEBUG>;
-    case 5: return gemv_nvfp4_m1_kernel<LPR, 5, DEBUG>;
-    case 6: return gemv_nvfp4_m1_kernel<LPR, 6, DEBUG>;
-    case 7: return gemv_nvfp4_m1_kernel<LPR, 7, DEBUG>;
-    case 8: return gemv_nvfp4_m1_kernel<LPR, 8, DEBUG>;
-    case 9: return gemv_nvfp4_m1_kernel<LPR, 9, DEBUG>;
-    case 10: return gemv_nvfp4_m1_kernel<LPR, 10, DEBUG>;
-    default: return nullptr;
-  }
-}
-
-}  // namespace
-
-// Choose lanes-per-row and units-per-lane for a K: the LPR in {64, 32, 16} with
-// the fewest idle unit slots (ties to the wider LPR), subject to UPL <= 10.
-void gemv_m1_config(int64_t K, int* lpr_out, int* upl_out) {
-  const int units = (int)(K / 32);
-  int best_lpr = 0, best_upl = 0;
-  double best_eff = -1.0;
-  const int lprs[3] = {64, 32, 16};
-  for (int i = 0; i < 3; ++i) {
-    const int lpr = lprs[i];
-    const int upl = (units + lpr - 1) / lpr;
-    if (upl > kGemvMaxUPL) continue;
-    const double eff = (double)units / (double)(lpr * upl);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best_lpr = lpr;
-      best_upl = upl;
-    }
-  }
-  *lpr_out = best_lpr;
-  *upl_out = best_upl;
+size_t gemv_lds_bytes(int64_t K) {
+  const int64_t nch = (K + 127) / 128;
+  return (size_t)(nch * 256 + 16 + nch * 16 + 4 * 64 * 4);
 }
 
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
-                                int32_t* isums, hipStream_t stream) {
-  const bool debug = isums != nullptr;
-  int lpr = 0, upl = 0;
-  gemv_m1_config(K, &lpr, &upl);
-  if (lpr == 0) {
-    const int64_t grid = (N + 3) / 4;
-    if (debug)
-      hipLaunchKernelGGL(gemv_nvfp4_m1_long_kernel<true>, dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, N, (int)K, q, d16, w_scale, y, isums);
-    else
-      hipLaunchKernelGGL(gemv_nvfp4_m1_long_kernel<false>, dim3((unsigned)grid), dim3(256), 0,
-                         stream, w, N, (int)K, q, d16, w_scale, y, isums);
-    return hipGetLastError();
+                                int32_t* isums, int mode, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const size_t lds = gemv_lds_bytes(K);
+  const bool dbg = isums != nullptr;
+  auto fn = mode == 0 ? (dbg ? gemv_nvfp4_kernel<0, true> : gemv_nvfp4_kernel<0, false>)
+                      : (dbg ? gemv_nvfp4_kernel<1, true> : gemv_nvfp4_kernel<1, false>);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
-  gemv_fn fn = nullptr;
-  if (lpr == 64) fn = debug ? pick_upl<64, true>(upl) : pick_upl<64, false>(upl);
-  if (lpr == 32) fn = debug ? pick_upl<32, true>(upl) : pick_upl<32, false>(upl);
-  if (lpr == 16) fn = debug ? pick_upl<16, true>(upl) : pick_upl<16, false>(upl);
-  if (!fn) return hipErrorInvalidValue;
-  const int64_t rows_per_block = 4 * (64 / lpr) * gemv_rg(upl);
-  const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, stream, w, N, (int)K, q, d16,
+  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles), dim3(256), lds, stream, w, N, (int)K, q, d16,
                      w_scale, y, isums);
   return hipGetLastError();
 }

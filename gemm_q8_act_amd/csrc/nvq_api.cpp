@@ -102,7 +102,8 @@ const char* nvq_last_error(void) { return g_err; }
 
 size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < 64 || K % 64 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
-  return (size_t)(N * K / 2 + N * K / 16);
+  const int64_t np = (N + 15) / 16 * 16, kp = (K + 127) / 128 * 128;
+  return (size_t)(np * kp / 2 + np * kp / 16);
 }
 
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K) {
@@ -119,19 +120,33 @@ nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3, int64_t N,
                           void* dst_host) {
   if (!codes || !ue4m3 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_nvfp4: NULL pointer");
   if (nvq_nvfp4_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_nvfp4: N=%lld K=%lld (K %% 64 == 0 required)", (long long)N, (long long)K);
+  for (int64_t i = 0; i < N * K; ++i)
+    if (codes[i] > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_nvfp4: code > 15 at weight %lld", (long long)i);
+  for (int64_t i = 0; i < N * K / 16; ++i)
+    if ((ue4m3[i] & 0x80) || ue4m3[i] == 0x7F) return fail(NVQ_ERR_RANGE, "nvq_pack_nvfp4: invalid UE4M3 byte 0x%02x at scale %lld", ue4m3[i], (long long)i);
+  // Tile-interleaved layout: 16-row x 128-k tile-chunks; codes of lane l = 16*g + n
+  // (row n, k = 32g .. 32g+31 of the chunk) at 16*l, scales (subblocks 2g, 2g+1)
+  // at 2*l of the chunk's 128-byte scale block.  Padding rows / k are zero.
   uint8_t* dst = static_cast<uint8_t*>(dst_host);
-  const int64_t nc = N * K / 2;
-  for (int64_t i = 0; i < nc; ++i) {
-    const uint8_t a = codes[2 * i], b = codes[2 * i + 1];
-    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_nvfp4: code > 15 at weight %lld", (long long)(2 * i));
-    dst[i] = (uint8_t)(a | (b << 4));
-  }
-  const int64_t ns = N * K / 16;
-  for (int64_t i = 0; i < ns; ++i) {
-    const uint8_t s = ue4m3[i];
-    if ((s & 0x80) || s == 0x7F) return fail(NVQ_ERR_RANGE, "nvq_pack_nvfp4: invalid UE4M3 byte 0x%02x at scale %lld", s, (long long)i);
-    dst[nc + i] = s;
-  }
+  const int64_t ntiles = (N + 15) / 16, nch = (K + 127) / 128, ns = K / 16;
+  uint8_t* sc = dst + ntiles * nch * 1024;
+  for (int64_t t = 0; t < ntiles; ++t)
+    for (int64_t c = 0; c < nch; ++c) {
+      uint8_t* blk = dst + (t * nch + c) * 1024;
+      uint8_t* sblk = sc + (t * nch + c) * 128;
+      for (int l = 0; l < 64; ++l) {
+        const int64_t row = t * 16 + (l & 15);
+        const int64_t k0 = c * 128 + 32 * (l >> 4);
+        const bool live = row < N && k0 < K;
+        const uint8_t* cr = codes + row * K + k0;
+        for (int b = 0; b < 16; ++b)
+          blk[16 * l + b] = live ? (uint8_t)(cr[2 * b] | (cr[2 * b + 1] << 4)) : 0;
+        for (int j = 0; j < 2; ++j) {
+          const int64_t s = k0 / 16 + j;
+          sblk[2 * l + j] = (live && s < ns) ? ue4m3[row * ns + s] : 0;
+        }
+      }
+    }
   g_err[0] = '\0';
   return NVQ_OK;
 }
@@ -174,15 +189,34 @@ static nvq_status check_common(const void* w, const int8_t* q, const uint16_t* d
   return NVQ_OK;
 }
 
+// The decode GEMV kernels keep the whole activation table of a row in LDS.
+static bool gemv_fits_lds(int64_t K) { return nvq::gemv_lds_bytes(K) <= 160 * 1024 - 1024; }
+
 nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y, void* stream) {
   NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_nvfp4"));
   NVQ_TRY(check_dims(M, N, K, 64, 1, NVQ_GEMV_MAX_M));
   NVQ_TRY(check_device());
   const uint8_t* wb = static_cast<const uint8_t*>(w);
-  if (M == 1)
-    return launched(nvq::launch_gemv_nvfp4_m1(wb, w_scale, q, d_f16, N, K, y, nullptr, (hipStream_t)stream), "gemv_nvfp4");
+  if (M == 1 && gemv_fits_lds(K))
+    return launched(nvq::launch_gemv_nvfp4_m1(wb, w_scale, q, d_f16, N, K, y, nullptr, 0, (hipStream_t)stream), "gemv_nvfp4");
   return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
+}
+
+nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
+                               int64_t M, int64_t N, int64_t K, float* y, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_nvfp4_dot4"));
+  NVQ_TRY(check_dims(M, N, K, 64, 1, NVQ_GEMV_MAX_M));
+  if (!gemv_fits_lds(K)) return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4_dot4: K=%lld too large for the LDS activation table", (long long)K);
+  NVQ_TRY(check_device());
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  for (int64_t m = 0; m < M; ++m) {
+    hipError_t e = nvq::launch_gemv_nvfp4_m1(wb, w_scale, q + m * K, d_f16 + m * (K / 32), N, K, y + m * N,
+                                             nullptr, 1, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(NVQ_ERR_HIP, "gemv_nvfp4_dot4 launch: %s", hipGetErrorString(e));
+  }
+  g_err[0] = '\0';
+  return NVQ_OK;
 }
 
 nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
@@ -226,7 +260,8 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,
                            int64_t N, int64_t K, int32_t* isums, void* stream) {
   if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1) return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d", fmt);
-  if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM) return fail(NVQ_ERR_RANGE, "nvq_debug_isums: path=%d", path);
+  if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM && !(path == NVQ_PATH_GEMV_DOT4 && fmt == NVQ_FMT_NVFP4))
+    return fail(NVQ_ERR_RANGE, "nvq_debug_isums: path=%d", path);
   if (!w || !q || !isums) return fail(NVQ_ERR_NULL, "nvq_debug_isums: NULL pointer");
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(isums, 4)) return fail(NVQ_ERR_ALIGN, "nvq_debug_isums: w and q must be 16-byte aligned, isums 4-byte");
   NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : 32, 1, kMaxM));
@@ -239,9 +274,12 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
     return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemm_q4_1");
   }
   const int64_t per_m = N * (K / 16);
+  if (fmt == NVQ_FMT_NVFP4 && !gemv_fits_lds(K))
+    return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the decode GEMV kernels", (long long)K);
   for (int64_t m = 0; m < M; ++m) {
     hipError_t e = (fmt == NVQ_FMT_NVFP4)
-        ? nvq::launch_gemv_nvfp4_m1(wb, 1.0f, q + m * K, nullptr, N, K, nullptr, isums + m * per_m, st)
+        ? nvq::launch_gemv_nvfp4_m1(wb, 1.0f, q + m * K, nullptr, N, K, nullptr, isums + m * per_m,
+                                    path == NVQ_PATH_GEMV_DOT4 ? 1 : 0, st)
         : nvq::launch_gemv_q4_1_m1(wb, q + m * K, nullptr, nullptr, N, K, nullptr, isums + m * per_m, st);
     if (e != hipSuccess) return fail(NVQ_ERR_HIP, "debug gemv launch: %s", hipGetErrorString(e));
   }

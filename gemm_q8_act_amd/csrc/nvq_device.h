@@ -43,18 +43,26 @@ constexpr uint32_t kPB_lo = 0xFDFEFF00u, kPB_hi = 0xF5F9FBFCu;
 
 // One dword of 8 packed codes (byte i: code of weight 2i in bits 0..3, weight 2i+1
 // in bits 4..7) against activation dwords qe (the 4 even-position codes) and qo
-// (the 4 odd-position codes).  Returns acc + sum_j L(code_j) * q_j.
-__device__ __forceinline__ int dot8_e2m1(uint32_t c, uint32_t qe, uint32_t qo, int acc) {
-  const uint32_t lo = c & 0x0F0F0F0Fu;
-  const uint32_t lo7 = c & 0x07070707u;
+// (the 4 odd-position codes).  Adds the PA part of L(code)*q to a and the PB part
+// to b; a + b is the integer dot product.  pal/pah/pbl/pbh are the pools and
+// m4/m3 the nibble masks, held in VGPRs by the caller.
+__device__ __forceinline__ void dot8_e2m1_ab(uint32_t c, uint32_t qe, uint32_t qo, int& a, int& b,
+                                             uint32_t pal, uint32_t pah, uint32_t pbl, uint32_t pbh,
+                                             uint32_t m4, uint32_t m3) {
+  const uint32_t lo = c & m4, lo7 = c & m3;
   const uint32_t t = c >> 4;
-  const uint32_t hi = t & 0x0F0F0F0Fu;
-  const uint32_t hi7 = t & 0x07070707u;
-  acc = dot4(perm(kPA_hi, kPA_lo, lo), qe, acc);
-  acc = dot4(perm(kPB_hi, kPB_lo, lo7), qe, acc);
-  acc = dot4(perm(kPA_hi, kPA_lo, hi), qo, acc);
-  acc = dot4(perm(kPB_hi, kPB_lo, hi7), qo, acc);
-  return acc;
+  const uint32_t hi = t & m4, hi7 = t & m3;
+  a = dot4(perm(pah, pal, lo), qe, a);
+  b = dot4(perm(pbh, pbl, lo7), qe, b);
+  a = dot4(perm(pah, pal, hi), qo, a);
+  b = dot4(perm(pbh, pbl, hi7), qo, b);
+}
+
+// Same, returning acc + sum_j L(code_j) * q_j (pools taken as constants).
+__device__ __forceinline__ int dot8_e2m1(uint32_t c, uint32_t qe, uint32_t qo, int acc) {
+  int a = acc, b = 0;
+  dot8_e2m1_ab(c, qe, qo, a, b, kPA_lo, kPA_hi, kPB_lo, kPB_hi, 0x0F0F0F0Fu, 0x07070707u);
+  return a + b;
 }
 
 // Split 8 activation bytes (two dwords, natural order) into even / odd positions.
@@ -99,13 +107,37 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t v, half2_t& lo, half2_t& 
   hi = __builtin_bit_cast(half2_t, b) - bias;
 }
 
-// Reduce a float over groups of LANES consecutive lanes (LANES = 16, 32 or 64);
-// every lane of a group ends with the group sum.
+// Keep a value in a VGPR (stops the compiler from re-materialising a constant
+// operand of v_perm_b32 before every use).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the sum.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+// Reduce a float over groups of LANES consecutive lanes (LANES = 16, 32 or 64).
+// The result is valid in the first lane of each group (lane % LANES == 0).
+// Rows of 16 are reduced with DPP (no LDS traffic); rows are combined with
+// v_readlane into uniform values.
 template <int LANES>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = LANES / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = row16_sum(v);
+  if (LANES == 16) return v;
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  if (LANES == 32) return (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
+  return (r0 + r1) + (r2 + r3);
 }
 
 }  // namespace nvq

@@ -11,11 +11,14 @@ namespace nvq {
 hipError_t launch_act_quant(const float* x, int64_t M, int64_t K, int8_t* q, uint16_t* d16,
                             int16_t* bsum16, hipStream_t stream);
 
-// NVFP4, M == 1, integer-dot path.  isums != nullptr selects the debug variant
-// (writes per-16 integer sums instead of y).
+// NVFP4, M == 1 decode GEMV on the tile-interleaved layout.  mode 0: FP4 MFMA
+// inner loop (production); mode 1: v_perm + v_dot4 inner loop.  isums != nullptr
+// selects the debug variant (writes per-16 integer sums instead of y).
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
-                                int32_t* isums, hipStream_t stream);
+                                int32_t* isums, int mode, hipStream_t stream);
+// LDS bytes the decode GEMV needs for a row length K.
+size_t gemv_lds_bytes(int64_t K);
 
 // NVFP4, MFMA tiled path (any M >= 1; used for M >= 2).  isums != nullptr selects
 // the debug variant.

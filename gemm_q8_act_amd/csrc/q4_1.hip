@@ -355,7 +355,27 @@ hipError_t launch_q41_tile(const uint8_t* w, const int8_t* q, const uint16_t* d1
 }
 }  // namespace
 
-void gemv_m1_config(int64_t K, int* lpr_out, int* upl_out);
+// Lanes-per-row and units-per-lane for a row of K weights: the LPR in {64, 32, 16}
+// with the fewest idle unit slots (ties to the wider LPR), subject to UPL <= 10.
+static void gemv_m1_config(int64_t K, int* lpr_out, int* upl_out) {
+  const int units = (int)(K / 32);
+  int best_lpr = 0, best_upl = 0;
+  double best_eff = -1.0;
+  const int lprs[3] = {64, 32, 16};
+  for (int i = 0; i < 3; ++i) {
+    const int lpr = lprs[i];
+    const int upl = (units + lpr - 1) / lpr;
+    if (upl > kQ41MaxUPL) continue;
+    const double eff = (double)units / (double)(lpr * upl);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best_lpr = lpr;
+      best_upl = upl;
+    }
+  }
+  *lpr_out = best_lpr;
+  *upl_out = best_upl;
+}
 
 hipError_t launch_gemv_q4_1_m1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                                const int16_t* bsum16, int64_t N, int64_t K, float* y,

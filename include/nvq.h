@@ -35,12 +35,23 @@
  *
  * Packed weight buffers (produced on the host by nvq_pack_*; one contiguous
  * buffer, which the caller copies to device memory):
- *   NVFP4, nvq_nvfp4_weight_bytes(N, K) = N*K/2 + N*K/16 bytes:
- *     [0, N*K/2)            codes: row n at n*K/2; byte i of a row holds the code
- *                           of weight k = 2i in bits 0..3 and of k = 2i+1 in bits 4..7.
- *     [N*K/2, +N*K/16)      UE4M3 scales, row-major [N][K/16].
- *   Q4_1, nvq_q4_1_weight_bytes(N, K) = N*K/2 + N*K/8 bytes:
- *     [0, N*K/2)            codes, same nibble order as NVFP4.
+ *   NVFP4, tile-interleaved.  Let Np = N rounded up to 16, Kp = K rounded up to 128,
+ *     T = Np/16 row tiles, C = Kp/128 chunks.  nvq_nvfp4_weight_bytes(N, K) =
+ *     Np*Kp/2 + Np*Kp/16 bytes:
+ *     [0, T*C*1024)         codes: tile t, chunk c at (t*C + c)*1024: 64 slots of
+ *                           16 bytes; slot l = 16*g + n holds row 16t + n,
+ *                           k = 128c + 32g .. 128c + 32g + 31; byte i of a slot holds
+ *                           the code of k0 + 2i in bits 0..3 and of k0 + 2i + 1 in
+ *                           bits 4..7.
+ *     [T*C*1024, +T*C*128)  UE4M3 scales: tile t, chunk c at (t*C + c)*128: slot l
+ *                           (2 bytes) holds the scales of the two 16-subblocks of
+ *                           slot l's 32 codes, in k order.
+ *     Rows >= N and k >= K are zero padding.  One slot is the 16-byte FP4 operand a
+ *     lane of a 16x16x128 matrix-core instruction takes, so every 64-lane load of
+ *     a tile-chunk reads 1 KB of contiguous memory.
+ *   Q4_1, row-major, nvq_q4_1_weight_bytes(N, K) = N*K/2 + N*K/8 bytes:
+ *     [0, N*K/2)            codes: row n at n*K/2; byte i of a row holds the code of
+ *                           k = 2i in bits 0..3 and of k = 2i+1 in bits 4..7.
  *     [N*K/2, +N*K/8)       per 32 weights a 4-byte pair: binary16 d in the low
  *                           half, binary16 m in the high half, row-major [N][K/32].
  *
@@ -85,16 +96,18 @@ typedef int nvq_status;
 
 #define NVQ_FMT_NVFP4 0
 #define NVQ_FMT_Q4_1  1
-#define NVQ_PATH_GEMV 0
-#define NVQ_PATH_GEMM 1
+#define NVQ_PATH_GEMV      0  /* decode GEMV, matrix-core inner loop (production) */
+#define NVQ_PATH_GEMM      1  /* tiled GEMM */
+#define NVQ_PATH_GEMV_DOT4 2  /* decode GEMV, v_perm + v_dot4 inner loop (NVFP4 only) */
 
 /* Largest M accepted by the GEMV entries; the GEMM entries accept M >= 16. */
 #define NVQ_GEMV_MAX_M 15
 
 /* ---- sizes (pure functions) ------------------------------------------------ */
 
-/* Bytes of a packed NVFP4 weight buffer [N][K]: N*K*9/16.  0 if N < 1 or K is not
- * a positive multiple of 64. */
+/* Bytes of a packed NVFP4 weight buffer [N][K]: Np*Kp*9/16 with Np = N rounded up
+ * to 16 and Kp = K rounded up to 128.  0 if N < 1 or K is not a positive multiple
+ * of 64. */
 size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
 
 /* Bytes of a packed Q4_1 weight buffer [N][K]: N*K*5/8.  0 if N < 1 or K is not a
@@ -131,13 +144,22 @@ nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
 
 /* ---- NVFP4 products ----------------------------------------------------------- */
 
-/* Decode GEMV (the single-token case takes the vector-dot form): 1 <= M <= NVQ_GEMV_MAX_M, N >= 1,
- * K % 64 == 0.  w: packed NVFP4 [N][K]; q, d_f16: Q8_0 activations [M][K];
- * y [M][N] float32 (overwritten).  Per output the error against the exact product
- * is at most 1e-5 * sum_k |W*A| + 1e-6 (float32 accumulation of exact per-16
- * integer sums). */
+/* Decode GEMV (the single-token case of the product): 1 <= M <= NVQ_GEMV_MAX_M,
+ * N >= 1, K % 64 == 0.  w: packed NVFP4 [N][K]; q, d_f16: Q8_0 activations [M][K];
+ * y [M][N] float32 (overwritten).  M == 1 runs the decode kernel whose per-16
+ * integer sums come from the matrix cores reading the FP4 codes directly; M >= 2
+ * runs the tiled kernel.  Per output the error against the exact product is at
+ * most 1e-5 * sum_k |W*A| + 1e-6 (float32 accumulation of exact per-16 sums). */
 nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y, void* stream);
+
+/* The same decode GEMV with the per-16 integer sums computed on the vector unit:
+ * E2M1 -> int8 by v_perm_b32 table lookups and v_dot4_i32_i8 (one launch per
+ * token).  Same arguments, results within the same bound.  K is limited to what
+ * the on-chip activation table holds (NVQ_ERR_SHAPE beyond, about 70000). */
+nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q,
+                               const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
+                               float* y, void* stream);
 
 /* Prefill GEMM (many tokens take the tiled form): M >= 16, N >= 1,
  * K % 64 == 0; arguments as for the GEMV plus a device workspace of at least
@@ -162,10 +184,11 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
 
 /* isums [M][N][K/16] int32 = for each 16-subblock, sum_j L(code) * q (NVFP4, with
  * L(c) = 2*E2M1(c), an integer in -12..12) or sum_j code * q (Q4_1, unsigned codes).
- * fmt: NVQ_FMT_*; path: NVQ_PATH_GEMV or NVQ_PATH_GEMM selects which production
- * kernel's data path (weight load, code expansion, integer/MFMA contraction)
- * produces the sums, run with unit scales.  Any M >= 1 is accepted for either
- * path; K % 64 == 0 (NVFP4) or K % 32 == 0 (Q4_1). */
+ * fmt: NVQ_FMT_*; path: NVQ_PATH_GEMV, NVQ_PATH_GEMM or (NVFP4 only)
+ * NVQ_PATH_GEMV_DOT4 selects which production kernel's data path (weight load,
+ * code expansion, integer / matrix-core contraction) produces the sums, run with
+ * unit scales.  Any M >= 1 is accepted for every path; K % 64 == 0 (NVFP4) or
+ * K % 32 == 0 (Q4_1). */
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q,
                            int64_t M, int64_t N, int64_t K, int32_t* isums, void* stream);
 

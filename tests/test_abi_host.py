@@ -45,7 +45,9 @@ def test_library_has_only_gfx950_code(tmp_path):
 
 def test_sizes():
     assert nvq.nvq_nvfp4_weight_bytes(4864, 896) == 4864 * 896 * 9 // 16
-    assert nvq.nvq_nvfp4_weight_bytes(7, 64) == 7 * 36
+    assert nvq.nvq_nvfp4_weight_bytes(34816, 5120) == 34816 * 5120 * 9 // 16
+    assert nvq.nvq_nvfp4_weight_bytes(7, 64) == 16 * 128 * 9 // 16      # padded to a 16 x 128 tile
+    assert nvq.nvq_nvfp4_weight_bytes(17, 192) == 32 * 256 * 9 // 16
     assert nvq.nvq_nvfp4_weight_bytes(7, 96) == 0          # K % 64 != 0
     assert nvq.nvq_nvfp4_weight_bytes(0, 64) == 0
     assert nvq.nvq_q4_1_weight_bytes(4096, 4096) == 4096 * 4096 * 5 // 8
@@ -54,17 +56,36 @@ def test_sizes():
     assert nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) >= 0
 
 
-def test_pack_nvfp4_layout():
-    r = np.random.Generator(np.random.PCG64(5))
-    N, K = 3, 128
+def unpack_tiled(buf, N, K):
+    """Inverse of the tile-interleaved layout, written from the header's description."""
+    Np, Kp = -(-N // 16) * 16, -(-K // 128) * 128
+    T, C = Np // 16, Kp // 128
+    codes = np.zeros((Np, Kp), np.uint8)
+    scales = np.zeros((Np, Kp // 16), np.uint8)
+    cb = buf[: T * C * 1024].reshape(T, C, 64, 16)
+    sb = buf[T * C * 1024: T * C * 1152].reshape(T, C, 64, 2)
+    for t in range(T):
+        for c in range(C):
+            for l in range(64):
+                n, g = l % 16, l // 16
+                k0 = 128 * c + 32 * g
+                codes[16 * t + n, k0:k0 + 32:2] = cb[t, c, l] & 0xF
+                codes[16 * t + n, k0 + 1:k0 + 32:2] = cb[t, c, l] >> 4
+                scales[16 * t + n, k0 // 16: k0 // 16 + 2] = sb[t, c, l]
+    return codes, scales
+
+
+@pytest.mark.parametrize("N,K", [(3, 128), (16, 256), (37, 320), (5, 64)])
+def test_pack_nvfp4_layout(N, K):
+    r = np.random.Generator(np.random.PCG64(5 + N))
     codes = r.integers(0, 16, (N, K), dtype=np.uint8)
     scales = r.integers(0, 0x7F, (N, K // 16), dtype=np.uint8)
     buf = nvq.nvq_pack_nvfp4(codes, scales)
-    assert buf.size == N * K * 9 // 16
-    cb = buf[: N * K // 2].reshape(N, K // 2)
-    assert (cb & 0xF == codes[:, 0::2]).all()          # weight 2i in the low nibble
-    assert (cb >> 4 == codes[:, 1::2]).all()           # weight 2i+1 in the high nibble
-    assert (buf[N * K // 2:].reshape(N, K // 16) == scales).all()
+    assert buf.size == nvq.nvq_nvfp4_weight_bytes(N, K)
+    c2, s2 = unpack_tiled(buf, N, K)
+    assert (c2[:N, :K] == codes).all() and (s2[:N, :K // 16] == scales).all()
+    assert not c2[N:].any() and not c2[:, K:].any()           # zero padding
+    assert not s2[N:].any() and not s2[:, K // 16:].any()
 
 
 def test_pack_q4_1_layout():
@@ -139,6 +160,8 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_quantize_act_q8_0(None, 1, 64, A16, A16, None, None) == -1
     assert L.nvq_debug_isums(7, 0, A16, A16, 1, 8, 64, A16, None) == -3
     assert L.nvq_debug_isums(0, 9, A16, A16, 1, 8, 64, A16, None) == -3
+    assert L.nvq_debug_isums(1, 2, A16, A16, 1, 8, 64, A16, None) == -3    # dot4 path is NVFP4 only
+    assert L.nvq_gemv_nvfp4_dot4(A16, 1.0, A16, A16, 16, 8, 64, A16, None) == -2
     assert L.nvq_debug_isums(1, 0, A16, A16, 1, 8, 48, A16, None) == -2
 
 

@@ -75,26 +75,32 @@ def test_act_quant_without_bsum(oracle):
 # NVFP4 decode GEMV, M = 1 (integer-dot kernel)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N,K", [(4864, 896), (1, 64), (37, 128), (129, 640), (1000, 4096),
-                                 (300, 5120), (130, 17408), (20, 20544)])
-def test_gemv_nvfp4_m1(oracle, N, K):
-    say(f"gemv_nvfp4 M=1 N={N} K={K}")
+GEMV_SHAPES = [(4864, 896), (1, 64), (37, 128), (129, 640), (33, 320), (1000, 4096),
+               (300, 5120), (130, 17408), (20, 20544)]
+
+
+@pytest.mark.parametrize("N,K", GEMV_SHAPES)
+@pytest.mark.parametrize("kernel", ["mfma", "dot4"])
+def test_gemv_nvfp4_m1(oracle, N, K, kernel):
+    say(f"gemv_nvfp4 ({kernel}) M=1 N={N} K={K}")
     torch = torch_dev()
     c = NvCase(1, N, K, synth.seed_for("test", "gemv", N * 7 + K), w_scale="uniform")
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    fn = nvq.nvq_gemv_nvfp4 if kernel == "mfma" else nvq.nvq_gemv_nvfp4_dot4
+    fn(c.w, c.ws, c.q, c.d, y)
     yo, awa = c.oracle_y(oracle)
-    check_y(host(y), yo, awa, f"gemv N={N} K={K}")
+    check_y(host(y), yo, awa, f"gemv {kernel} N={N} K={K}")
 
 
 @pytest.mark.parametrize("M", [1, 3])
-def test_gemv_isums_bit_exact(oracle, M):
-    say(f"debug isums GEMV path M={M}")
+@pytest.mark.parametrize("path", [nvq.NVQ_PATH_GEMV, nvq.NVQ_PATH_GEMV_DOT4])
+def test_gemv_isums_bit_exact(oracle, M, path):
+    say(f"debug isums GEMV path={path} M={M}")
     torch = torch_dev()
-    for N, K in [(37, 128), (70, 5120), (9, 20544)]:
+    for N, K in [(37, 128), (33, 320), (70, 5120), (9, 20544)]:
         c = NvCase(M, N, K, 1234 + N)
         isums = torch.empty((M, N, K // 16), dtype=torch.int32, device="cuda")
-        nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, nvq.NVQ_PATH_GEMV, c.w, c.q, N, isums)
+        nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, path, c.w, c.q, N, isums)
         ref = oracle.isums_nvfp4(c.codes, c.qh)
         assert (host(isums) == ref).all(), (N, K)
         assert np.abs(ref).max() > 0
@@ -104,19 +110,21 @@ def test_gemv_isums_bit_exact(oracle, M):
 # NVFP4 tiled MFMA path: GEMV with 2 <= M <= 15 and GEMM with M >= 16
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,N,K", [(2, 300, 512), (8, 129, 1024), (15, 64, 64), (8, 77, 5120)])
-def test_gemv_nvfp4_small_batch(oracle, M, N, K):
-    say(f"gemv_nvfp4 M={M} N={N} K={K}")
+@pytest.mark.parametrize("M,N,K", [(2, 300, 512), (8, 129, 1024), (15, 64, 64), (8, 77, 5120), (3, 50, 320)])
+@pytest.mark.parametrize("kernel", ["mfma", "dot4"])
+def test_gemv_nvfp4_small_batch(oracle, M, N, K, kernel):
+    say(f"gemv_nvfp4 ({kernel}) M={M} N={N} K={K}")
     torch = torch_dev()
     c = NvCase(M, N, K, 4321 + M * N, w_scale="uniform")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    fn = nvq.nvq_gemv_nvfp4 if kernel == "mfma" else nvq.nvq_gemv_nvfp4_dot4
+    fn(c.w, c.ws, c.q, c.d, y)
     yo, awa = c.oracle_y(oracle)
     check_y(host(y), yo, awa, f"gemv M={M} N={N} K={K}")
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 64, 64), (17, 77, 192), (100, 300, 640), (64, 128, 2048),
-                                   (129, 257, 1024)])
+                                   (129, 257, 1024), (40, 70, 320)])
 def test_gemm_nvfp4(oracle, M, N, K):
     say(f"gemm_nvfp4 M={M} N={N} K={K}")
     torch = torch_dev()
@@ -127,7 +135,7 @@ def test_gemm_nvfp4(oracle, M, N, K):
     check_y(host(y), yo, awa, f"gemm M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 70, 128), (17, 33, 192), (5, 64, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 70, 128), (17, 33, 192), (5, 64, 1024), (3, 20, 320)])
 def test_gemm_isums_bit_exact(oracle, M, N, K):
     say(f"debug isums GEMM path M={M} N={N} K={K}")
     torch = torch_dev()
@@ -142,12 +150,14 @@ def test_gemm_isums_bit_exact(oracle, M, N, K):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,N,K", list(synth.LAYER))
-def test_layer_gemv_full_size(oracle, name, N, K):
-    say(f"layer gemv {name} N={N} K={K}")
+@pytest.mark.parametrize("kernel", ["mfma", "dot4"])
+def test_layer_gemv_full_size(oracle, name, N, K, kernel):
+    say(f"layer gemv ({kernel}) {name} N={N} K={K}")
     torch = torch_dev()
     c = NvCase(1, N, K, synth.seed_for("layer", name), w_scale="uniform")
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    fn = nvq.nvq_gemv_nvfp4 if kernel == "mfma" else nvq.nvq_gemv_nvfp4_dot4
+    fn(c.w, c.ws, c.q, c.d, y)
     cols = sample_cols(N, 64, N)
     yo, awa = c.oracle_y(oracle, cols=cols)
     check_y(host(y)[:, cols], yo, awa, f"layer {name}")
@@ -249,7 +259,7 @@ def test_determinism_and_guard_bands(oracle):
 def test_validation_leaves_output_untouched():
     torch = torch_dev()
     y = torch.full((16, 64), 7.0, dtype=torch.float32, device="cuda")
-    w = torch.zeros(nvq.nvq_nvfp4_weight_bytes(64, 96 + 32), dtype=torch.uint8, device="cuda")
+    w = torch.zeros(nvq.nvq_nvfp4_weight_bytes(64, 128), dtype=torch.uint8, device="cuda")
     q = torch.zeros((16, 96), dtype=torch.int8, device="cuda")
     d = torch.zeros((16, 3), dtype=torch.int16, device="cuda")
     with pytest.raises(nvq.NvqError) as e:
