@@ -1,0 +1,595 @@
+"""Benchmark of the NVFP4 x Q8_0 hot path on one MI355X.
+
+Headline (``value``): decode weight-streaming throughput, GB/s of NVFP4 weight
+bytes, for one transformer layer at hidden 5120 / ffn 17408 with M = 1 token:
+one step = Q8_0 quantization of the four GEMV inputs + the QKV [7168x5120],
+O [5120x5120], gate+up [34816x5120] and down [5120x17408] GEMVs.  The layer's
+185.8 MB of weights are replicated ``--copies`` times in HBM and step s uses copy
+s % copies, so consecutive steps never find their weights in the 256 MB
+Infinity Cache.  Inputs are resident in HBM before the timed region.
+
+Also measured in the same run (reported as sub-objects of the JSON line): the
+prefill GEMM TFLOP/s at M = 2048 (and 256), N = 17408, K = 5120; the small
+GEMV (N = 4864, K = 896) and the Q4_1 GEMV / GEMM (N = K = 4096); the oracle's
+CPU throughput on the same layer.  ``--stack`` instead measures the 64-layer
+stack (M = 1 or 8) of the same layer shapes.
+
+Roofline: per-kernel durations come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream).  Peaks: HBM 8000 GB/s, dense
+fp16 MFMA 2500 TFLOP/s (the GEMM computes in fp16 x fp16 -> fp32).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+METRIC = "NVFP4×Q8_0 GEMV weight GB/s (M=1) and GEMM TOPS (M=2048), % of roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=8, help="distinct HBM copies of the layer weights")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every kernel from Python instead of replaying a captured HIP graph")
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--stack", action="store_true", help="64-layer stack instead of one layer")
+    p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
+    p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="for rocprofv3 --pmc runs: one 256 MiB device copy (calibration) and 4 gate+up "
+                        "GEMV launches over distinct weight copies, then exit")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def dev_tensor(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def nvfp4_bytes(N, K):
+    return N * K * 9 // 16
+
+
+def gemv_alg_bytes(M, N, K):
+    """Bytes the product must move: packed weights + Q8_0 activations (codes +
+    binary16 scale per 32) + float32 outputs."""
+    return nvfp4_bytes(N, K) + M * K * 17 // 16 + 4 * M * N
+
+
+class Layer:
+    """Device-resident decode layer: packed weights (``copies`` replicas), activations."""
+
+    def __init__(self, M, copies, seed_base=0, share_from=None):
+        import torch
+
+        import gemm_q8_act_amd as nvq
+        from gemm_q8_act_amd import synth
+
+        self.M = M
+        self.mats = []
+        for i, (name, N, K) in enumerate(synth.LAYER):
+            if share_from is None:
+                codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name, seed_base), "uniform")
+                packed = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+            else:
+                packed, ws = share_from.mats[i]["w"][0], share_from.mats[i]["ws"]
+            if share_from is None:
+                ws_list = [packed] + [packed.clone() for _ in range(copies - 1)]
+            else:
+                ws_list = [packed.clone() for _ in range(copies)]
+            x = dev_tensor(synth.activations(M, K, synth.seed_for("layer", "x_" + name, seed_base)))
+            self.mats.append(dict(
+                name=name, N=N, K=K, w=ws_list, ws=float(ws), x=x,
+                q=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                d=torch.empty((M, K // 32), dtype=torch.int16, device="cuda"),
+                b=torch.empty((M, K // 16), dtype=torch.int16, device="cuda"),
+                y=torch.empty((M, N), dtype=torch.float32, device="cuda")))
+
+    def weight_bytes(self):
+        return sum(nvfp4_bytes(m["N"], m["K"]) for m in self.mats)
+
+    def step(self, copy, events=None):
+        import gemm_q8_act_amd as nvq
+
+        for j, m in enumerate(self.mats):
+            nvq.nvq_quantize_act_q8_0(m["x"], m["q"], m["d"], m["b"])
+            if events is not None:
+                events[j][0].record()
+            nvq.nvq_gemv_nvfp4(m["w"][copy], m["ws"], m["q"], m["d"], m["y"])
+            if events is not None:
+                events[j][1].record()
+
+
+def kernel_src_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "gemm_q8_act_amd", "csrc"))):
+        with open(os.path.join(ROOT, "gemm_q8_act_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+    recorded under profiles/ with the hash of the kernel sources it was taken on;
+    None once the kernels have changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e or e.get("src_hash") != kernel_src_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# measurements
+# ---------------------------------------------------------------------------
+
+def time_layer(args):
+    import torch
+
+    M = 1
+    layer = Layer(M, args.copies)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        layer.step(s % args.copies)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        # one graph holds `copies` consecutive steps (one per weight copy)
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s_cap):
+                for c in range(args.copies):
+                    layer.step(c)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    steps = args.steps
+    if graph is not None:
+        reps = max(1, steps // args.copies)
+        steps = reps * args.copies
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for s in range(steps):
+            layer.step(s % args.copies)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-kernel durations: HIP events on the launch stream around batches of
+    # back-to-back launches of one GEMV over >= 1 GB of weight copies
+    per = {}
+    for m in layer.mats:
+        per[m["name"]] = gemv_batch_time(layer, m)
+        per[m["name"]]["dot4_us"] = gemv_batch_time(layer, m, dot4=True)["us_avg"]
+    return layer, steps, elapsed, per
+
+
+def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
+    """Average launch duration of one GEMV: HIP events (on the launch stream) around a
+    batch of back-to-back launches that rotate through at least ``min_bytes`` of
+    distinct weight copies, so no launch finds its weights in the 256 MB Infinity
+    Cache.  A sleep kernel queued before each batch lets the host enqueue the whole
+    batch before the GPU reaches it, so the batch runs at the GPU's pace."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+
+    fn = nvq.nvq_gemv_nvfp4_dot4 if dot4 else nvq.nvq_gemv_nvfp4
+    wbytes = nvfp4_bytes(m["N"], m["K"])
+    extra = max(0, -(-min_bytes // wbytes) - len(m["w"]))
+    ws = list(m["w"]) + [m["w"][i % len(m["w"])].clone() for i in range(extra)]
+    for w in ws:
+        fn(w, m["ws"], m["q"], m["d"], m["y"])
+    torch.cuda.synchronize()
+    cyc = int(sleep_cycles_per_ms() * 3.0)  # 3 ms backlog
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(cyc)
+        e0.record()
+        for w in ws:
+            fn(w, m["ws"], m["q"], m["d"], m["y"])
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / len(ws))
+    nlaunch = len(ws)
+    del ws
+    us = 1e3 * float(np.mean(ms))
+    ab = gemv_alg_bytes(layer.M, m["N"], m["K"])
+    return dict(N=m["N"], K=m["K"], us_avg=us, us_p50=1e3 * float(np.median(ms)), alg_bytes=ab,
+                GBps=ab / (us * 1e-6) / 1e9, launches_per_batch=nlaunch)
+
+
+_SLEEP_RATE = []
+
+
+def sleep_cycles_per_ms():
+    """Rate of torch.cuda._sleep (its spin counter ticks per ms), measured once."""
+    import torch
+
+    if not _SLEEP_RATE:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1000000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SLEEP_RATE.append(1e6 / max(e0.elapsed_time(e1), 1e-3))
+    return _SLEEP_RATE[0]
+
+
+def hbm_ceiling():
+    """Measured ceilings (the roofline-by-measurement method): device-to-device copy
+    of 1 GiB (read + write bytes) and a read-only reduction over 1 GiB."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    v = a.view(torch.float32)
+    for _ in range(2):
+        b.copy_(a)
+        v.sum()
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    for _ in range(5):
+        v.sum()
+    e2.record()
+    torch.cuda.synchronize()
+    copy_s = e0.elapsed_time(e1) / 5 * 1e-3
+    read_s = e1.elapsed_time(e2) / 5 * 1e-3
+    return dict(copy_GBps=2 * n / copy_s / 1e9, read_GBps=n / read_s / 1e9,
+                note="1 GiB device copy (read+write bytes) and float32 sum reduction (read bytes), torch kernels")
+
+
+def time_gemm(M, N=17408, K=5120, reps=10, warm=3):
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("prefill", "w") + M)
+    w = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+    x = dev_tensor(synth.activations(M, K, synth.seed_for("prefill", "x") + M, outliers=True))
+    q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
+    b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_quantize_act_q8_0(x, q, d, b)
+    for _ in range(warm):
+        nvq.nvq_gemm_nvfp4(w, ws, q, d, y)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        nvq.nvq_gemm_nvfp4(w, ws, q, d, y)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    us = 1e3 * float(np.mean(ms))
+    tflops = 2.0 * M * N * K / (us * 1e-6) / 1e12
+    return dict(M=M, N=N, K=K, us_avg=us, us_p50=1e3 * float(np.median(ms)), TFLOPs=tflops,
+                frac=tflops / FP16_PEAK_TFLOPS)
+
+
+def time_extras():
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    out = {}
+    # small decode GEMV N=4864 K=896 (L2-resident, launch-bound)
+    N, K = 4864, 896
+    codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("gemv_small", "w"))
+    w = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+    x = dev_tensor(synth.activations(1, K, synth.seed_for("gemv_small", "x")))
+    q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((1, K // 32), dtype=torch.int16, device="cuda")
+    b = torch.empty((1, K // 16), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_quantize_act_q8_0(x, q, d, b)
+    us = _event_time(lambda: nvq.nvq_gemv_nvfp4(w, ws, q, d, y), 200)
+    out["gemv_small_N4864_K896"] = dict(us_avg=us, GBps=gemv_alg_bytes(1, N, K) / (us * 1e-6) / 1e9)
+    # Q4_1 N = K = 4096: GEMV M=1 and GEMM M=512
+    N = K = 4096
+    qw, dw, mw = synth.q4_1_weights(N, K, synth.seed_for("q4_1", "w"))
+    w = dev_tensor(nvq.nvq_pack_q4_1(qw, dw, mw))
+    for M in (1, 512):
+        x = dev_tensor(synth.activations(M, K, synth.seed_for("q4_1", "x") + M))
+        q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
+        b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        nvq.nvq_quantize_act_q8_0(x, q, d, b)
+        if M == 1:
+            us = _event_time(lambda: nvq.nvq_gemv_q4_1(w, q, d, b, y), 200)
+            byts = N * K * 5 // 8 + K * 17 // 16 + K // 8 + 4 * N
+            out["q4_1_gemv_N4096_K4096"] = dict(us_avg=us, GBps=byts / (us * 1e-6) / 1e9,
+                                                note="10.5 MB of weights: Infinity-Cache resident across repeats")
+        else:
+            us = _event_time(lambda: nvq.nvq_gemm_q4_1(w, q, d, b, y), 20)
+            tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+            out["q4_1_gemm_M512_N4096_K4096"] = dict(us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS)
+    return out
+
+
+def _event_time(fn, reps):
+    import torch
+
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(sleep_cycles_per_ms() * 5.0))  # backlog: launches queue behind it
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline():
+    """The oracle (plain scalar C, untouched) on the same decode layer: Q8_0
+    quantization of the four inputs + all output rows of the four GEMVs, split over
+    host threads by output rows."""
+    import oracle
+    from gemm_q8_act_amd import synth
+
+    o = oracle.load()
+    threads = min(16, os.cpu_count() or 1)
+    mats = []
+    for name, N, K in synth.LAYER:
+        codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name, 0), "uniform")
+        x = synth.activations(1, K, synth.seed_for("layer", "x_" + name, 0))
+        mats.append((N, K, codes, scales, ws, x))
+    t0 = time.perf_counter()
+    wbytes = 0
+    passes = 0
+    while True:  # whole-layer passes until about 10 s of wall time have gone by
+        for N, K, codes, scales, ws, x in mats:
+            q, d, _ = o.quantize_q8_0(x)
+            o.matmul_threads("nvfp4", (codes, scales, ws), q, d, np.arange(N), threads)
+            wbytes += nvfp4_bytes(N, K)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0:
+            break
+    return dict(value=wbytes / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{passes} passes over the full decode layer (Q8_0 of the 4 inputs + all 52224 output "
+                       f"rows of the QKV/O/gate+up/down GEMVs), M=1; {el:.2f} s wall on {threads} host threads")
+
+
+def run_stack(args):
+    """64-layer stack of the layer shapes, one token step = 256 GEMVs (+ their
+    input quantization) back to back on one stream."""
+    import torch
+
+    M = args.tokens
+    # layer 0's packed weights are cloned into 63 more distinct HBM buffers
+    # (11.9 GB in all); activations differ per layer
+    layers = [Layer(M, 1)]
+    layers += [Layer(M, 1, seed_base=i, share_from=layers[0]) for i in range(1, 64)]
+    torch.cuda.synchronize()
+    wbytes = sum(l.weight_bytes() for l in layers)
+    for _ in range(2):
+        for l in layers:
+            l.step(0)
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 50)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for l in layers:
+            l.step(0)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    gbps = wbytes * steps / el / 1e9
+    line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=2,
+                ms_per_step=1e3 * el / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="int8/fp32", data="synthetic",
+                config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408",
+                            weight_bytes=wbytes),
+                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=gbps / HBM_PEAK_GBS, traffic=None))
+    print(json.dumps(line), flush=True)
+
+
+def traffic_probe():
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)  # calibration: n bytes read, n bytes written
+    torch.cuda.synchronize()
+    name, N, K = [t for t in synth.LAYER if t[0] == "gate_up"][0]
+    codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name, 0), "uniform")
+    w0 = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+    wl = [w0] + [w0.clone() for _ in range(3)]
+    x = dev_tensor(synth.activations(1, K, synth.seed_for("layer", "x_" + name, 0)))
+    q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((1, K // 32), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_quantize_act_q8_0(x, q, d, None)
+    torch.cuda.synchronize()
+    for w in wl:
+        nvq.nvq_gemv_nvfp4(w, float(ws), q, d, y)
+    torch.cuda.synchronize()
+    log(f"traffic probe: copy {n} B; 4 x gate+up GEMV N={N} K={K}, {nvfp4_bytes(N, K)} weight bytes each")
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """HBM bytes per dispatch from two rocprofv3 --pmc runs of --traffic-probe
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the factor that
+    maps the counter to the known bytes of the 256 MiB calibration copy."""
+    import collections
+    import csv
+
+    def dispatches(path, counter):  # [(kernel name, grid, value summed over instances)]
+        acc = collections.defaultdict(float)
+        names = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
+                names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], r.get("Grid_Size", ""))
+        return [(names[i][0], names[i][1], v) for i, v in acc.items()]
+
+    f = dispatches(fetch_csv, "FETCH_SIZE")
+    wr = dispatches(write_csv, "WRITE_SIZE")
+    n = 256 << 20
+    # the calibration copy is the largest copyBuffer dispatch of each run
+    cf = max(v for k, g, v in f if "copyBuffer" in k)
+    cw = max(v for k, g, v in wr if "copyBuffer" in k)
+    ff, fw = (n / 1024) / cf, (n / 1024) / cw
+    res = dict(calibration=dict(copy_bytes=n, fetch_kib=cf, write_kib=cw, fetch_factor=ff, write_factor=fw))
+    gf = [(k, g, v) for k, g, v in f if "gemv_nvfp4_kernel" in k]
+    gw = [v for k, g, v in wr if "gemv_nvfp4_kernel" in k]
+    if gf:
+        vf, vw = float(np.mean([v for _, _, v in gf])), float(np.mean(gw)) if gw else 0.0
+        res["gemv_nvfp4_gate_up"] = dict(
+            kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
+            bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=gemv_alg_bytes(1, 34816, 5120),
+            src_hash=kernel_src_hash())
+    print(json.dumps(res, indent=1))
+
+
+def summarize_trace(path):
+    """Per-(kernel, grid) summary of a rocprofv3 kernel_trace.csv."""
+    import collections
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    agg = collections.defaultdict(list)
+    for r in rows:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
+        agg[(r["Kernel_Name"].split("(")[0], grid)].append(dur)
+    out = []
+    for (name, grid), d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(d, np.float64) / 1e3
+        out.append(f"{name[:60]:60s} grid={grid:>16s} n={len(d):5d} avg_us={d.mean():9.2f} "
+                   f"p50_us={np.median(d):9.2f} min_us={d.min():9.2f} total_us={d.sum():11.1f}")
+    print("\n".join(out))
+
+
+def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2])
+        return
+    if len(sys.argv) == 4 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2], sys.argv[3])
+        return
+    args = parse()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {ws}).", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+
+    import gemm_q8_act_amd as nvq
+
+    nvq.lib()  # fails loudly if libnvq.so is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.traffic_probe:
+        traffic_probe()
+        return
+    if args.stack:
+        run_stack(args)
+        return
+    if args.only_gemm:
+        for M in (2048, 256):
+            log(json.dumps(time_gemm(M)))
+        return
+
+    log("decode layer ...")
+    layer, steps, elapsed, per = time_layer(args)
+    wbytes = layer.weight_bytes()
+    gbps = wbytes * steps / elapsed / 1e9
+    # dominant kernel: the gate+up GEMV (54 % of the step's weight bytes)
+    gu = per["gate_up"]
+    roofline = dict(bound="hbm", achieved=gu["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=gu["GBps"] / HBM_PEAK_GBS, traffic=load_traffic("gemv_nvfp4_gate_up"),
+                    kernel="gemv_nvfp4_kernel<0,false,4,5> (matrix-core decode GEMV), gate+up N=34816 K=5120",
+                    us_per_launch=gu["us_avg"], alg_bytes_per_launch=gu["alg_bytes"])
+    line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=args.warmup,
+                ms_per_step=1e3 * elapsed / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
+                dtype="int8/fp32", data="synthetic",
+                config=dict(workload="decode layer hidden=5120 ffn=17408, M=1: Q8_0 + QKV/O/gate_up/down GEMVs",
+                            weight_bytes_per_step=wbytes, weight_copies=args.copies,
+                            graph=not args.eager),
+                roofline=roofline, per_kernel=per)
+    if not args.no_extras:
+        line["hbm_ceiling"] = hbm_ceiling()
+    if not args.no_gemm:
+        log("prefill gemm ...")
+        g = {f"M{M}": time_gemm(M) for M in (2048, 256)}
+        g2 = g["M2048"]
+        line["gemm"] = dict(metric="NVFP4xQ8_0 prefill GEMM TFLOP/s (M=2048, N=17408, K=5120)",
+                            value=g2["TFLOPs"], unit="TFLOP/s",
+                            roofline=dict(bound="mfma", achieved=g2["TFLOPs"], peak=FP16_PEAK_TFLOPS,
+                                          unit="TFLOP/s", frac=g2["frac"], traffic=None,
+                                          kernel="gemm_nvfp4_kernel (fp16 MFMA 16x16x32)"),
+                            runs=g)
+    if not args.no_extras:
+        log("extras ...")
+        line["extras"] = time_extras()
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,10 +11,13 @@
 // k = 32g..32g+31) followed elsewhere by its 128 scale bytes (lane l: the two scales
 // of subblocks 2g, 2g+1).  Every wavefront load is therefore 1 KB contiguous.
 //
-// Two inner loops share one skeleton (a 256-thread block owns one 16-row tile; its
-// four wavefronts take the chunks c = wave, wave+4, ...; each wavefront issues the
-// loads of P chunks before computing them; an activation table built once per
-// block in LDS; partial sums reduced through LDS at the end):
+// Two inner loops share one skeleton.  A block of W wavefronts owns one 16-row tile;
+// wavefront v takes the chunks c = v, v + W, ... in batches of P, issuing the loads of
+// a batch before computing it.  The activation table is built once per block in LDS.
+// Order of the prologue matters: the activation codes are loaded first and every
+// global load is unconditional (indices are clamped into the buffers), so the table
+// build waits only for those codes (loads retire in order) and runs while the first
+// weight batch is still in flight.  Partial sums are reduced through LDS at the end.
 //
 //  * MODE_MX (production).  gfx950's matrix cores read E2M1 natively: the 16 packed
 //    bytes a lane loads are, unchanged, its FP4 operand of one
@@ -40,8 +43,6 @@ namespace nvq {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGemvP = 5;  // chunks per load batch and wavefront
-
 // Four activation codes -> the high parts h = q >> 4 as sign-magnitude E4M3 bytes
 // (|h| <= 8, value |h| * 2^-9 with the sign bit).
 __device__ __forceinline__ uint32_t act_hi_e4m3(uint32_t q) {
@@ -52,19 +53,29 @@ __device__ __forceinline__ uint32_t act_hi_e4m3(uint32_t q) {
   return mag | (neg << 7);
 }
 
-template <int MODE, bool DEBUG>
-__global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
-                                                         int K, const int8_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ d16,
-                                                         float w_scale, float* __restrict__ y,
-                                                         int32_t* __restrict__ isums) {
+// LDS carve-up shared by kernel and launcher: activation table [nch + 1][256 B] (the
+// last chunk slot takes the writes of out-of-range threads), 16 zero bytes, d table
+// [nch * 4 + 4] floats (the last 4 likewise), partial sums [W][64] floats.
+__host__ __device__ constexpr int64_t gemv_tab_bytes(int64_t nch) { return (nch + 1) * 256; }
+__host__ __device__ constexpr int64_t gemv_dtab_off(int64_t nch) { return gemv_tab_bytes(nch) + 16; }
+__host__ __device__ constexpr int64_t gemv_red_off(int64_t nch) { return gemv_dtab_off(nch) + (nch * 4 + 4) * 4; }
+
+template <int MODE, bool DEBUG, int W, int P>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
+                                                            int K, const int8_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ d16,
+                                                            float w_scale, float* __restrict__ y,
+                                                            int32_t* __restrict__ isums) {
+  constexpr int NT = 64 * W;
   extern __shared__ __align__(16) uint8_t smem[];
   const int nch = (K + 127) >> 7;
   const int nsb = K >> 4;
-  // LDS: activation table [nch][256 B] | 16 zero bytes | d [nch*4] | partial sums [4][64]
+  const int nq16 = K >> 4;  // 16-code groups of the activation row
+  const int nd = K >> 5;    // activation scales
   uint8_t* tab = smem;
-  float* dtab = reinterpret_cast<float*>(smem + nch * 256 + 16);
-  float* red = dtab + nch * 4;
+  uint8_t* zero16 = smem + gemv_tab_bytes(nch);
+  float* dtab = reinterpret_cast<float*>(smem + gemv_dtab_off(nch));
+  float* red = reinterpret_cast<float*>(smem + gemv_red_off(nch));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int64_t tile = blockIdx.x;
@@ -72,52 +83,63 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restri
   const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
   const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
 
-  // 1. first batch of weight loads, issued before anything else
-  u32x4 bb[kGemvP];
-  uint32_t ss[kGemvP];
+  // 1. activation codes and scales first (at most two 16-code groups per thread here)
+  const u32x4* __restrict__ q16 = reinterpret_cast<const u32x4*>(q);
+  const u32x4 qa = q16[min(tid, nq16 - 1)];
+  const u32x4 qb = q16[min(tid + NT, nq16 - 1)];
+  uint32_t da = 0u;
+  if (!DEBUG) da = d16[min(tid, nd - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. first batch of weight loads (chunk indices clamped: loads past the row's last
+  //    chunk re-read it and are never consumed)
+  u32x4 bb[P];
+  uint32_t ss[P];
   auto issue = [&](int c0) {
 #pragma unroll
-    for (int p = 0; p < kGemvP; ++p) {
-      const int c = c0 + 4 * p;
-      if (c < nch) {
-        bb[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt + (int64_t)c * 1024));
-        ss[p] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + (int64_t)c * 128));
-      } else {
-        bb[p] = u32x4{0u, 0u, 0u, 0u};
-        ss[p] = 0u;
-      }
+    for (int p = 0; p < P; ++p) {
+      const int c = min(c0 + W * p, nch - 1);
+      bb[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt + (int64_t)c * 1024));
+      ss[p] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + (int64_t)c * 128));
     }
   };
   int c0 = wave;
   issue(c0);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // 2. activation table: per 128-k chunk, MX: [h parts 128 B | l parts 128 B];
-  //    DOT4: per 32-k quarter g, [even codes 16 B | odd codes 16 B]
-  for (int t = tid; t < nch * 32; t += 256) {
-    const int k = 4 * t;
-    const uint32_t qv = (k < K) ? *reinterpret_cast<const uint32_t*>(q + k) : 0u;
-    const int c = k >> 7, o = k & 127;
+  // 3. activation table.  MX: per 128-k chunk [h parts 128 B | l parts 128 B].
+  //    DOT4: per 32-k quarter [even codes 16 B | odd codes 16 B].
+  auto put = [&](int j, const u32x4& v) {  // the 16 codes k = 16 j .. 16 j + 15
+    const int k = 16 * j, c = k >> 7, o = k & 127;
     if (MODE == 0) {
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = act_hi_e4m3(qv);
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = qv & 0x0F0F0F0Fu;
-    } else if ((t & 1) == 0) {
-      // pairs of dwords (8 codes) -> one even and one odd dword
-      const uint32_t qv2 = (k + 4 < K) ? *reinterpret_cast<const uint32_t*>(q + k + 4) : 0u;
-      uint32_t e, od;
-      split_even_odd(qv, qv2, e, od);
-      const int gq = o >> 5, j = (o & 31) >> 3;  // quarter, 8-code group within it
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + gq * 64 + 4 * j) = e;
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + gq * 64 + 16 + 4 * j) = od;
+      const u32x4 hi = {act_hi_e4m3(v[0]), act_hi_e4m3(v[1]), act_hi_e4m3(v[2]), act_hi_e4m3(v[3])};
+      const u32x4 lo = {v[0] & 0x0F0F0F0Fu, v[1] & 0x0F0F0F0Fu, v[2] & 0x0F0F0F0Fu, v[3] & 0x0F0F0F0Fu};
+      *reinterpret_cast<u32x4*>(tab + c * 256 + o) = hi;
+      *reinterpret_cast<u32x4*>(tab + c * 256 + 128 + o) = lo;
+    } else {
+      uint32_t e0, o0, e1, o1;
+      split_even_odd(v[0], v[1], e0, o0);
+      split_even_odd(v[2], v[3], e1, o1);
+      const int base = c * 256 + (o >> 5) * 64 + 8 * ((o & 31) >> 4);
+      *reinterpret_cast<uint2*>(tab + base) = make_uint2(e0, e1);
+      *reinterpret_cast<uint2*>(tab + base + 16) = make_uint2(o0, o1);
     }
+  };
+  const int junk = nch * 8;  // 16-code group index of the spare chunk slot
+  put(tid < nq16 ? tid : junk, qa);
+  put(tid + NT < nq16 ? tid + NT : junk, qb);
+  for (int j = tid + 2 * NT; j < nq16; j += NT) put(j, q16[j]);
+  for (int j = nq16 + tid; j < nch * 8; j += NT) put(j, u32x4{0u, 0u, 0u, 0u});
+  if (!DEBUG) {
+    dtab[tid < nd ? tid : nch * 4] = f16_bits_to_f32((uint16_t)da);
+    for (int b = tid + NT; b < nd; b += NT) dtab[b] = f16_bits_to_f32(d16[b]);
+    for (int b = nd + tid; b < nch * 4; b += NT) dtab[b] = 0.0f;
   }
-  if (tid < 4) reinterpret_cast<uint32_t*>(tab + nch * 256)[tid] = 0u;
-  if (!DEBUG)
-    for (int b = tid; b < nch * 4; b += 256) dtab[b] = (b < (K >> 5)) ? f16_bits_to_f32(d16[b]) : 0.0f;
+  if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
   __syncthreads();
 
-  // 3. compute
+  // 4. compute
   const int sbv = nl >> 1, part = nl & 1;
-  const uint8_t* zero16 = tab + nch * 256;
   const uint32_t pal = in_vgpr(kPA_lo), pah = in_vgpr(kPA_hi);
   const uint32_t pbl = in_vgpr(kPB_lo), pbh = in_vgpr(kPB_hi);
   const uint32_t m4 = in_vgpr(0x0F0F0F0Fu), m3 = in_vgpr(0x07070707u);
@@ -125,8 +147,8 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restri
   float acc = 0.0f;
   while (true) {
 #pragma unroll
-    for (int p = 0; p < kGemvP; ++p) {
-      const int c = c0 + 4 * p;
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + W * p;
       if (c >= nch) continue;
       float i0, i1;  // the two per-16 sums (E2M1 units) of subblocks 8c+2g, 8c+2g+1
       if (MODE == 0) {
@@ -164,19 +186,19 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restri
         acc = fmaf(t, dtab[4 * c + g], acc);
       }
     }
-    c0 += 4 * kGemvP;
+    c0 += W * P;
     if (c0 >= nch) break;
     issue(c0);
   }
   if (DEBUG) return;
 
-  // 4. reduce the 16 partial sums of each row (4 lane groups x 4 wavefronts)
+  // 5. reduce the 4 W partial sums of each row (4 lane groups x W wavefronts)
   red[wave * 64 + lane] = acc;
   __syncthreads();
   if (tid < 16) {
     float s = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww)
+    for (int ww = 0; ww < W; ++ww)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) s += red[ww * 64 + gg * 16 + tid];
     const int64_t r = tile * 16 + tid;
@@ -184,27 +206,44 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(const uint8_t* __restri
   }
 }
 
+// Launch shape: 4 wavefronts x 5-chunk batches, or 8 x 3 for long rows over few tiles
+// (the down projection: K = 17408 over 320 tiles), where more wavefronts per tile keep
+// more loads in flight per block.
+static bool gemv_wide(int64_t ntiles, int64_t nch) { return nch >= 64 && ntiles <= 1024; }
+
 size_t gemv_lds_bytes(int64_t K) {
   const int64_t nch = (K + 127) / 128;
-  return (size_t)(nch * 256 + 16 + nch * 16 + 4 * 64 * 4);
+  return (size_t)(gemv_red_off(nch) + 8 * 64 * 4);  // room for the widest block (W = 8)
+}
+
+template <int MODE, bool DEBUG, int W, int P>
+static hipError_t launch_gemv(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
+                              int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nch = (K + 127) / 128;
+  const size_t lds = (size_t)(gemv_red_off(nch) + W * 64 * 4);
+  auto fn = gemv_nvfp4_kernel<MODE, DEBUG, W, P>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles), dim3(64 * W), lds, stream, w, N, (int)K, q, d16,
+                     w_scale, y, isums);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
                                 int32_t* isums, int mode, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
-  const size_t lds = gemv_lds_bytes(K);
-  const bool dbg = isums != nullptr;
-  auto fn = mode == 0 ? (dbg ? gemv_nvfp4_kernel<0, true> : gemv_nvfp4_kernel<0, false>)
-                      : (dbg ? gemv_nvfp4_kernel<1, true> : gemv_nvfp4_kernel<1, false>);
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles), dim3(256), lds, stream, w, N, (int)K, q, d16,
-                     w_scale, y, isums);
-  return hipGetLastError();
+  const int64_t nch = (K + 127) / 128;
+  if (isums != nullptr)
+    return mode == 0 ? launch_gemv<0, true, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream)
+                     : launch_gemv<1, true, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
+  if (mode != 0) return launch_gemv<1, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
+  if (gemv_wide(ntiles, nch)) return launch_gemv<0, false, 8, 3>(w, w_scale, q, d16, N, K, y, isums, stream);
+  return launch_gemv<0, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
 }
 
 }  // namespace nvq
