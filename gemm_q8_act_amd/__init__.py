@@ -233,6 +233,10 @@ def nvq_gemm_nvfp4(w, w_scale: float, q, d_f16, y, workspace=None, stream=None) 
     N = y.shape[1]
     _need(y, torch.float32, (M, N), "y")
     _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
+    if workspace is None:  # the split-K partial tiles; torch's caching allocator makes this cheap
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvq_gemm_nvfp4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
                                 _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_nvfp4")

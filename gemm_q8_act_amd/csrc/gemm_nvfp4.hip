@@ -1,35 +1,33 @@
-// gemm_nvfp4.hip -- tiled MFMA product, NVFP4 weights x Q8_0 activations, gfx950.
+// gemm_nvfp4.hip -- tiled MFMA products, NVFP4 weights x Q8_0 activations, gfx950.
 //
 // Method ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map:
 // the tiled path unpacks weight and activation tiles, then runs a microkernel with
 // a per-16 weight scale cached beside the unpacked tile).  On gfx950 the
-// contraction runs on the matrix cores:
+// contraction runs on the matrix cores, on an exact fp16 expansion of the weights:
+// w16 = E2M1(code) * UE4M3(scale) has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in fp16; activation codes q (|q| <= 127) are exact
+// in fp16 too.  Two kernels:
 //
-//   * Exact fp16 expansion.  w16 = E2M1(code) * UE4M3(scale) has at most 6
-//     significant bits and lies in [2^-10, 2688], so it is exact in fp16; the
-//     UE4M3 scale is folded into the weights once per tile.  Activation codes q
-//     (|q| <= 127) are exact in fp16 too.
-//   * Per 32-k chunk (one Q8_0 block) one v_mfma_f32_16x16x32_f16 with a zero
-//     accumulator gives P[n][m] = sum_k w16 * q; products are exact in fp32.
-//   * The chunk's activation scale d[m] differs per chunk, so it is applied on the
-//     vector unit: acc[n][m] += d[m][chunk] * P[n][m]; y = S * acc at the end.
-//     With weights as the MFMA A operand (rows = n) and activations as B
-//     (columns = m), every lane owns a single column m, so one d value per lane
-//     scales all of that lane's accumulators.
-//
-// Tiling: a 256-thread block computes BN weight rows x BM tokens.  Per 128-k step
-// the block loads BN/16 tile-chunks of the packed layout (1 KB of codes + 128 scale
-// bytes each, contiguous) and BM x 128 B of activation codes, expands both to fp16
-// in LDS (double-buffered, rows padded to 272 B so 16-byte fragment reads are
-// bank-conflict free), and each of the 4 wavefronts runs (BN/64) x (BM/16) MFMAs
-// per 32-k block.  Global loads of step k+1 are issued before the MFMAs of step k.
+//   * gemm_nvfp4_tile_kernel (M <= 64, the GEMV entry for 2 <= M <= 15, and the
+//     debug sums).  Per 32-k chunk (one Q8_0 block) one v_mfma_f32_16x16x32_f16
+//     with a zero accumulator gives P[n][m] = sum_k w16 * q, exact in fp32; the
+//     chunk's activation scale is applied on the vector unit,
+//     acc[n][m] += d[m][chunk] * P[n][m].  Weights are the MFMA A operand (rows n)
+//     and activations B (columns m), so one d value per lane scales all of that
+//     lane's accumulators.  A 256-thread block computes BN weight rows x BM tokens
+//     per 128-k step from double-buffered LDS.
+//   * gemm_nvfp4_kernel (M > 64), below: the activation scale is folded into an
+//     exact two-term fp16 split of the activations so the matrix core accumulates
+//     the whole row by itself.
+#include <algorithm>
+
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
 namespace nvq {
 
 template <int BM, int BN, bool DEBUG>
-__global__ __launch_bounds__(256) void gemm_nvfp4_kernel(const uint8_t* __restrict__ w,
+__global__ __launch_bounds__(256) void gemm_nvfp4_tile_kernel(const uint8_t* __restrict__ w,
                                                          int64_t N, int K,
                                                          const int8_t* __restrict__ q,
                                                          const uint16_t* __restrict__ d16,
@@ -239,18 +237,331 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
                        int64_t M, int64_t N, int64_t K, float* y, int32_t* isums,
                        hipStream_t stream) {
   dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_nvfp4_kernel<BM, BN, DEBUG>), grid, dim3(256), 0, stream, w, N, (int)K,
+  hipLaunchKernelGGL((gemm_nvfp4_tile_kernel<BM, BN, DEBUG>), grid, dim3(256), 0, stream, w, N, (int)K,
                      q, d16, M, w_scale, y, isums);
   return hipGetLastError();
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------------
+// Large-M kernel: exact two-term split of the scaled activations.
+//
+// The per-32 activation scale d is folded into the activation operand instead of
+// being applied to partial products on the vector unit: d * q has at most 18
+// significant bits (11 of the binary16 d, 7 of |q| <= 127), so it is the exact sum
+// of two binary16 values, hi = fp16(d * q) (one v_pk_mul_f16, round to nearest)
+// and lo = fma(d, q, -hi) (one v_pk_fma_f16; the exact difference is representable,
+// so the fused result is exact).  Then y = S * (W16 . hi + W16 . lo) with the
+// matrix core accumulating across the whole row: twice the MFMA work of a single
+// pass, but no per-block vector FMA and no partial-product registers.  Exact as long
+// as |d * q| stays below 65520 (|x| < 65504); beyond that hi is infinite and the
+// affected outputs become non-finite rather than silently wrong.
+//
+// Block: 512 threads (8 wavefronts, 2 along n x 4 along m), tile 256 weight rows x
+// 256 tokens, wavefront tile 128 x 64 (4 x 2 v_mfma_f32_32x32x16_f16 tiles).
+// LDS holds two 64-k stages (double buffered): weights expanded to fp16 (E2M1 *
+// UE4M3, exact), raw int8 activation codes and their binary16 scales.  Each
+// wavefront splits its own activation fragments into (hi, lo) in registers.
+// Fragments of the next 32-k substep are read while the MFMAs of the current one
+// issue; global loads run two stages ahead; staging of stage t+1 overlaps the
+// MFMAs of stage t.
+//
+// Work items: full tiles, then -- for the tiles of an incomplete last round over
+// the 256 compute units -- K-split parts whose fp32 partial tiles go to the
+// workspace and are summed in part order by gemm_nvfp4_reduce_kernel
+// (deterministic: no atomics).
+// ---------------------------------------------------------------------------------
+namespace {
+constexpr int kBigBN = 256, kBigBM = 256, kBigThreads = 512;
+constexpr int kBigLRW = 72;   // halves per LDS weight row (64 k + 8 pad)
+constexpr int kBigLRA = 80;   // bytes per LDS activation row (64 codes + 16 pad)
+constexpr int kBigStageW = kBigBN * kBigLRW * 2, kBigStageA = kBigBM * kBigLRA, kBigStageD = kBigBM * 4;
+constexpr int kBigStage = kBigStageW + kBigStageA + kBigStageD;
+constexpr int kBigLds = 2 * kBigStage;
+constexpr int kBigAcc = 128;  // fp32 accumulators per thread (4 x 2 tiles x 16)
+constexpr int kSlots = 256;   // compute units of the chip: work items of the last round
+constexpr int kMaxSplit = 8;
+
+struct BigPlan {
+  int64_t tiles_n, tiles, full, split_tiles;
+  int split;  // K parts per split tile (1: no split)
+  int stages;
+};
+
+BigPlan big_plan(int64_t M, int64_t N, int64_t K) {
+  BigPlan p;
+  p.tiles_n = (N + kBigBN - 1) / kBigBN;
+  p.tiles = p.tiles_n * ((M + kBigBM - 1) / kBigBM);
+  p.stages = (int)(K / 64);
+  const int64_t r = p.tiles % kSlots;
+  p.split = 1;
+  if (r != 0) p.split = (int)std::min<int64_t>({kSlots / r, (int64_t)kMaxSplit, (int64_t)p.stages});
+  if (p.split < 2) p.split = 1;
+  p.split_tiles = p.split > 1 ? r : 0;
+  p.full = p.tiles - p.split_tiles;
+  return p;
+}
+}  // namespace
+
+size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64) return 0;
+  const BigPlan p = big_plan(M, N, K);
+  return (size_t)(p.split_tiles * p.split) * kBigThreads * kBigAcc * sizeof(float);
+}
+
+__global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
+                                                            int K, const int8_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ d16, int64_t M,
+                                                            float w_scale, float* __restrict__ y,
+                                                            float* __restrict__ part_ws, BigPlan plan) {
+  constexpr int BN = kBigBN, BM = kBigBM, WM = 4, TN = 4, TM = 2;
+  constexpr int LRW = kBigLRW, LRA = kBigLRA;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+  // work item -> tile and stage range
+  const int64_t item = blockIdx.x;
+  int64_t tile, part = -1;
+  int t0 = 0, t1 = plan.stages;
+  if (item < plan.full) {
+    tile = item;
+  } else {
+    const int64_t it = item - plan.full;
+    tile = plan.full + it / plan.split;
+    part = it % plan.split;
+    t0 = (int)(part * plan.stages / plan.split);
+    t1 = (int)((part + 1) * plan.stages / plan.split);
+  }
+  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
+  const int nch = (K + 127) >> 7;
+  const int64_t ntiles = (N + 15) >> 4;
+  const uint8_t* __restrict__ sc = w + ntiles * nch * 1024;
+  const int nb32 = K >> 5;
+
+  // staging task of this thread: 32 weight codes (one 16 B lane slot) of row wrow and
+  // k-quarter (2 (t & 1) + whh) of chunk t >> 1; 32 activation codes of row arow;
+  // one activation scale.  Rows beyond N / M are clamped to valid memory: their
+  // results are never stored.
+  const int wrow = tid >> 1, whh = tid & 1;
+  const int64_t wtile = min(n0 / 16 + (wrow >> 4), ntiles - 1);
+  const uint8_t* __restrict__ wbase = w + wtile * nch * 1024 + 16 * (wrow & 15);
+  const uint8_t* __restrict__ sbase = sc + wtile * nch * 128 + 2 * (wrow & 15);
+  const int arow = tid >> 1, ahh = tid & 1;
+  const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + 32 * ahh;
+  const int drow = tid & 255, dblk = tid >> 8;
+  const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  struct Stage { uint4 wr; uint32_t sr; uint4 a0, a1; uint32_t dr; };
+  auto gload = [&](int t, Stage& x) {
+    const int c = t >> 1, g = 2 * (t & 1) + whh;
+    x.wr = *reinterpret_cast<const uint4*>(wbase + (int64_t)c * 1024 + 256 * g);
+    x.sr = *reinterpret_cast<const uint16_t*>(sbase + (int64_t)c * 128 + 32 * g);
+    const uint4* ap = reinterpret_cast<const uint4*>(abase + 64 * t);
+    x.a0 = ap[0];
+    x.a1 = ap[1];
+    x.dr = dbase[2 * t];
+  };
+  auto lstore = [&](int b, const Stage& x) {
+    uint8_t* st = smem + b * kBigStage;
+    _Float16* lw = reinterpret_cast<_Float16*>(st);
+    uint8_t* la = st + kBigStageW;
+    uint16_t* ld = reinterpret_cast<uint16_t*>(st + kBigStageW + kBigStageA);
+    const _Float16 u0 = (_Float16)ue4m3_to_f32<0>(x.sr), u1 = (_Float16)ue4m3_to_f32<1>(x.sr);
+    const half2_t s0 = {u0, u0}, s1 = {u1, u1};
+    const uint32_t cc[4] = {x.wr.x, x.wr.y, x.wr.z, x.wr.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const half2_t s = d < 2 ? s0 : s1;
+      const half2_t p0 = e2m1x2_to_f16<0>(cc[d]) * s;
+      const half2_t p1 = e2m1x2_to_f16<1>(cc[d]) * s;
+      const half2_t p2 = e2m1x2_to_f16<2>(cc[d]) * s;
+      const half2_t p3 = e2m1x2_to_f16<3>(cc[d]) * s;
+      const half8_t v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      *reinterpret_cast<half8_t*>(lw + wrow * LRW + 32 * whh + 8 * d) = v;
+    }
+    *reinterpret_cast<uint4*>(la + arow * LRA + 32 * ahh) = x.a0;
+    *reinterpret_cast<uint4*>(la + arow * LRA + 32 * ahh + 16) = x.a1;
+    ld[2 * drow + dblk] = (uint16_t)x.dr;
+  };
+
+  floatx16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = floatx16{};
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  // fragments of one 32-k substep u of a stage: weights for both 16-k halves, raw
+  // activation codes, activation scales
+  struct Frag { half8_t af[2][TN]; uint2 raw[2][TM]; uint32_t dd[TM]; };
+  auto fread = [&](int b, int u, Frag& f) {
+    const uint8_t* st = smem + b * kBigStage;
+    const _Float16* lw = reinterpret_cast<const _Float16*>(st);
+    const uint8_t* la = st + kBigStageW;
+    const uint16_t* ld = reinterpret_cast<const uint16_t*>(st + kBigStageW + kBigStageA);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+        f.af[h][i] = *reinterpret_cast<const half8_t*>(lw + (wn * (BN / 2) + 32 * i + fr) * LRW + 32 * u + 16 * h + fk);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int r = wm * (BM / WM) + 32 * j + fr;
+      f.dd[j] = ld[2 * r + u];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
+    }
+  };
+  auto mfmas = [&](const Frag& f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      half8_t bh[TM], bl[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)f.dd[j]);
+        const half2_t d2 = {dh, dh};
+        half2_t a0, a1, c0, c1;
+        i8x4_to_f16x4(f.raw[h][j].x, a0, a1);
+        i8x4_to_f16x4(f.raw[h][j].y, c0, c1);
+        const half2_t h0 = a0 * d2, h1 = a1 * d2, h2 = c0 * d2, h3 = c1 * d2;
+        const half2_t l0 = __builtin_elementwise_fma(a0, d2, -h0);
+        const half2_t l1 = __builtin_elementwise_fma(a1, d2, -h1);
+        const half2_t l2 = __builtin_elementwise_fma(c0, d2, -h2);
+        const half2_t l3 = __builtin_elementwise_fma(c1, d2, -h3);
+        bh[j] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+        bl[j] = half8_t{l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bh[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bl[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // pipeline over stages t0 .. t1-1 (every global load index is clamped to the range,
+  // so no load is conditional and the in-order load counter stays exact)
+  Stage x;
+  gload(t0, x);
+  lstore(0, x);
+  gload(min(t0 + 1, t1 - 1), x);
+  __syncthreads();
+  Frag f0, f1;
+  fread(0, 0, f0);
+  for (int t = t0; t < t1; ++t) {
+    const int b = (t - t0) & 1;
+    fread(b, 1, f1);
+    if (t + 1 < t1) lstore(b ^ 1, x);  // stage t+1, loaded one stage ago
+    mfmas(f0);
+    gload(min(t + 2, t1 - 1), x);
+    __syncthreads();                   // stage t+1 visible; stage t-1's buffer free
+    if (t + 1 < t1) fread(b ^ 1, 0, f0);
+    mfmas(f1);
+  }
+
+  if (part >= 0) {
+    // partial tile: thread-private accumulators to the workspace, element-major
+    float* dst = part_ws + ((item - plan.full) * kBigAcc) * kBigThreads + tid;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dst[((i * TM + j) * 16 + e) * kBigThreads] = acc[i][j][e];
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = m0 + wm * (BM / WM) + 32 * j + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t n = n0 + wn * (BN / 2) + 32 * i + 8 * e4 + 4 * (lane >> 5);
+        const floatx4 v = {acc[i][j][4 * e4] * w_scale, acc[i][j][4 * e4 + 1] * w_scale,
+                           acc[i][j][4 * e4 + 2] * w_scale, acc[i][j][4 * e4 + 3] * w_scale};
+        if ((N & 3) == 0 && n + 3 < N) {
+          *reinterpret_cast<floatx4*>(y + m * N + n) = v;
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (n + rr < N) y[m * N + n + rr] = v[rr];
+        }
+      }
+  }
+}
+
+// Sums the K parts of every split tile in part order (fp32, p = 0, 1, ...) and stores
+// the tile.  Block (split tile, group of 8 accumulator slots): each thread reduces the
+// same 8 slots of one producer thread, so every load of a part is one coalesced 2 KB
+// row of the element-major workspace.
+constexpr int kReduceGroups = kBigAcc / 8;
+
+__global__ __launch_bounds__(512) void gemm_nvfp4_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
+                                                                int64_t M, float w_scale,
+                                                                float* __restrict__ y, BigPlan plan) {
+  constexpr int BN = kBigBN, BM = kBigBM, WM = 4, TM = 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+  const int64_t st = blockIdx.x / kReduceGroups;  // split tile index
+  const int grp = blockIdx.x % kReduceGroups;     // accumulator slots 8 grp .. 8 grp + 7
+  const int ij = grp >> 1, i = ij / TM, j = ij % TM, e0 = 8 * grp;
+  const int64_t tile = plan.full + st;
+  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
+  const float* src = part_ws + (st * plan.split * kBigAcc + e0) * kBigThreads + tid;
+  float v[8][kMaxSplit];
+#pragma unroll
+  for (int p = 0; p < kMaxSplit; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e][p] = p < plan.split ? src[((int64_t)p * kBigAcc + e) * kBigThreads] : 0.0f;
+  const int64_t m = m0 + wm * (BM / WM) + 32 * j + (lane & 31);
+  if (m >= M) return;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float o[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float s = v[4 * h + rr][0];
+#pragma unroll
+      for (int p = 1; p < kMaxSplit; ++p)
+        if (p < plan.split) s += v[4 * h + rr][p];
+      o[rr] = s * w_scale;
+    }
+    // slot e0 + 4 h + rr of thread tid holds row 8 ((e0 % 16) / 4 + h) + 4 (lane >> 5) + rr
+    const int64_t n = n0 + wn * (BN / 2) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
+    if ((N & 3) == 0 && n + 3 < N) {
+      *reinterpret_cast<floatx4*>(y + m * N + n) = floatx4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (n + rr < N) y[m * N + n + rr] = o[rr];
+    }
+  }
+}
+
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
-                             int32_t* isums, hipStream_t stream) {
+                             int32_t* isums, float* workspace, hipStream_t stream) {
   if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
   if (M <= 16) return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
-  return launch_tile<64, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+  if (M <= 64) return launch_tile<64, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+  const BigPlan plan = big_plan(M, N, K);
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kBigLds);
+  if (ea != hipSuccess) return ea;
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)items), dim3(kBigThreads), kBigLds, stream, w, N,
+                     (int)K, q, d16, M, w_scale, y, workspace, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.split_tiles == 0) return e;
+  hipLaunchKernelGGL(gemm_nvfp4_reduce_kernel, dim3((unsigned)(plan.split_tiles * kReduceGroups)),
+                     dim3(kBigThreads), 0, stream, workspace, N, M, w_scale, y, plan);
+  return hipGetLastError();
 }
 
 }  // namespace nvq

@@ -112,8 +112,10 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K) {
 }
 
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  (void)fmt; (void)M; (void)N; (void)K;
-  return 0;  // the tiled kernels keep all partial sums on chip
+  // NVFP4 with M > 64: fp32 partial tiles of the K-split work items that fill the
+  // last round over the compute units.  Q4_1 keeps all partial sums on chip.
+  if (fmt != NVQ_FMT_NVFP4 || M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
+  return nvq::gemm_nvfp4_workspace(M, N, K);
 }
 
 nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3, int64_t N, int64_t K,
@@ -200,7 +202,7 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   if (M == 1 && gemv_fits_lds(K))
     return launched(nvq::launch_gemv_nvfp4_m1(wb, w_scale, q, d_f16, N, K, y, nullptr, 0, (hipStream_t)stream), "gemv_nvfp4");
-  return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
+  return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
 }
 
 nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
@@ -224,10 +226,14 @@ nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const u
                           size_t ws_bytes, void* stream) {
   NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_nvfp4"));
   NVQ_TRY(check_dims(M, N, K, 64, 16, kMaxM));
+  if ((M + 255) / 256 > (int64_t)1 << 31 || (N + 255) / 256 > (((int64_t)1 << 31) - 1) / ((M + 255) / 256))
+    return fail(NVQ_ERR_SHAPE, "nvq_gemm_nvfp4: M=%lld x N=%lld has too many 256 x 256 tiles for one launch", (long long)M, (long long)N);
   const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K);
   if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_nvfp4: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_nvfp4: workspace must be 16-byte aligned");
   NVQ_TRY(check_device());
-  return launched(nvq::launch_gemm_nvfp4(static_cast<const uint8_t*>(w), w_scale, q, d_f16, M, N, K, y, nullptr, (hipStream_t)stream), "gemm_nvfp4");
+  return launched(nvq::launch_gemm_nvfp4(static_cast<const uint8_t*>(w), w_scale, q, d_f16, M, N, K, y, nullptr,
+                                         static_cast<float*>(workspace), (hipStream_t)stream), "gemm_nvfp4");
 }
 
 nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
@@ -270,7 +276,7 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   hipStream_t st = (hipStream_t)stream;
   if (path == NVQ_PATH_GEMM) {
-    if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, st), "debug gemm_nvfp4");
+    if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_nvfp4");
     return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemm_q4_1");
   }
   const int64_t per_m = N * (K / 16);

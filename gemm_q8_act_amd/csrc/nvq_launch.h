@@ -20,11 +20,13 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
 // LDS bytes the decode GEMV needs for a row length K.
 size_t gemv_lds_bytes(int64_t K);
 
-// NVFP4, MFMA tiled path (any M >= 1; used for M >= 2).  isums != nullptr selects
-// the debug variant.
+// NVFP4, MFMA tiled paths (any M >= 1; used for M >= 2).  isums != nullptr selects
+// the debug variant.  M > 64 uses the split-activation kernel, whose K-split parts
+// need gemm_nvfp4_workspace(M, N, K) bytes of device workspace (may be 0).
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
-                             int32_t* isums, hipStream_t stream);
+                             int32_t* isums, float* workspace, hipStream_t stream);
+size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
 
 // Q4_1, M == 1, integer-dot path.
 hipError_t launch_gemv_q4_1_m1(const uint8_t* w, const int8_t* q, const uint16_t* d16,

@@ -114,8 +114,11 @@ size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
  * positive multiple of 32. */
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
 
-/* Workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt is
- * NVQ_FMT_*).  May be 0; the workspace pointer may then be NULL. */
+/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt
+ * is NVQ_FMT_*): for NVFP4 with M > 64, the fp32 partial tiles of the K-split work
+ * items that even out the last round of 256 x 256 tiles over the chip's 256
+ * compute units (at most 64 MiB); otherwise 0.  Pure function.  When it is 0 the
+ * workspace pointer may be NULL. */
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ---- packers (host memory in, host memory out) ------------------------------ */
@@ -162,8 +165,15 @@ nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q,
                                float* y, void* stream);
 
 /* Prefill GEMM (many tokens take the tiled form): M >= 16, N >= 1,
- * K % 64 == 0; arguments as for the GEMV plus a device workspace of at least
- * nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K) bytes. */
+ * K % 64 == 0; arguments as for the GEMV plus a device workspace (16-byte aligned,
+ * contents on entry irrelevant, overwritten) of at least
+ * nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K) bytes; NULL is accepted when
+ * that size is 0.  Calls that share a workspace must not overlap in time.
+ * For M > 64 the kernel folds each activation scale into an exact pair of binary16
+ * values (hi + lo = d * q); this is exact for |d * q| < 65520, i.e. activations
+ * below the binary16 range limit.  A row with larger activations yields
+ * non-finite outputs in that row (never silently wrong values); the GEMV entry
+ * points have no such limit. */
 nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y,
                           void* workspace, size_t ws_bytes, void* stream);

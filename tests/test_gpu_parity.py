@@ -123,8 +123,12 @@ def test_gemv_nvfp4_small_batch(oracle, M, N, K, kernel):
     check_y(host(y), yo, awa, f"gemv M={M} N={N} K={K}")
 
 
+# M <= 64: per-block scaled tile kernel; M > 64: split-activation kernel, whose
+# small shapes always take the K-split + ordered-reduction route (fewer tiles than
+# compute units), except K = 64 (one stage: no split)
 @pytest.mark.parametrize("M,N,K", [(16, 64, 64), (17, 77, 192), (100, 300, 640), (64, 128, 2048),
-                                   (129, 257, 1024), (40, 70, 320)])
+                                   (129, 257, 1024), (40, 70, 320), (300, 600, 384), (65, 33, 64),
+                                   (257, 1000, 448), (520, 129, 128)])
 def test_gemm_nvfp4(oracle, M, N, K):
     say(f"gemm_nvfp4 M={M} N={N} K={K}")
     torch = torch_dev()
@@ -254,6 +258,52 @@ def test_determinism_and_guard_bands(oracle):
     nvq.nvq_gemv_nvfp4(c.w, 1.0, c.q[:1], c.d[:1], y1)
     nvq.nvq_gemv_nvfp4(c.w, 4.0, c.q[:1], c.d[:1], y2)
     assert (host(y2) == 4.0 * host(y1)).all()
+
+
+def test_gemm_split_kernel_determinism_and_guard_bands(oracle):
+    """M > 64 with K-split parts: bitwise-identical repeats, nothing written outside y."""
+    say("gemm (M > 64, K-split) determinism + guard bands")
+    torch = torch_dev()
+    M, N, K = 300, 520, 1024
+    c = NvCase(M, N, K, 4242, w_scale=1.25, outliers=True)
+    guard = 4096
+    outs = []
+    for rep in range(2):
+        buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+        y = buf[guard:guard + M * N].view(M, N)
+        ws = torch.full((nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, M, N, K),), 0x7F, dtype=torch.uint8,
+                        device="cuda")  # junk on entry must not matter
+        nvq.nvq_gemm_nvfp4(c.w, c.ws, c.q, c.d, y, workspace=ws)
+        torch.cuda.synchronize()
+        b = host(buf)
+        assert (b[:guard] == 12345.0).all() and (b[guard + M * N:] == 12345.0).all()
+        outs.append(b[guard:guard + M * N].copy())
+    assert (outs[0].view(np.uint32) == outs[1].view(np.uint32)).all()
+    yo, awa = c.oracle_y(oracle, cols=np.arange(0, N, 7))
+    check_y(outs[0].reshape(M, N)[:, ::7], yo, awa, "gemm split determinism case")
+
+
+def test_gemm_split_kernel_activation_range():
+    """Rows whose scaled activations exceed the binary16 range come out non-finite
+    (documented contract of the M > 64 GEMM); every other row is unaffected."""
+    say("gemm (M > 64) activation range contract")
+    torch = torch_dev()
+    M, N, K = 96, 64, 128
+    c = NvCase(M, N, K, 77)
+    x = synth.activations(M, K, 78)
+    x[5, 3] = 1.0e6  # |d * q| far above 65504 in row 5
+    q, d, _ = quantize_gpu(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_nvfp4(c.w, c.ws, q, d, y)
+    y_ref = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    x2 = x.copy()
+    x2[5] = 0.0
+    q2, d2, _ = quantize_gpu(x2)
+    nvq.nvq_gemm_nvfp4(c.w, c.ws, q2, d2, y_ref)
+    yh, yr = host(y), host(y_ref)
+    assert not np.isfinite(yh[5]).all()
+    rows = [r for r in range(M) if r != 5]
+    assert (yh[rows] == yr[rows]).all()
 
 
 def test_validation_leaves_output_untouched():
