@@ -420,11 +420,27 @@ def run_stack(args):
         for l in layers:
             l.step(0)
     torch.cuda.synchronize()
-    steps = max(1, args.steps // 50)
+    graph = None
+    if not args.eager:  # one stack step (256 quantizations + 256 GEMVs) per graph replay
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s_cap):
+                for l in layers:
+                    l.step(0)
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    steps = max(2, args.steps // 20)
     t0 = time.perf_counter()
     for _ in range(steps):
-        for l in layers:
-            l.step(0)
+        if graph is not None:
+            graph.replay()
+        else:
+            for l in layers:
+                l.step(0)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gbps = wbytes * steps / el / 1e9
@@ -432,7 +448,7 @@ def run_stack(args):
                 ms_per_step=1e3 * el / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="int8/fp32", data="synthetic",
                 config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408",
-                            weight_bytes=wbytes),
+                            weight_bytes=wbytes, graph=not args.eager),
                 roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=gbps / HBM_PEAK_GBS, traffic=None))
     print(json.dumps(line), flush=True)
