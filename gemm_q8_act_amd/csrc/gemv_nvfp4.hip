@@ -311,20 +311,30 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_batch_kernel(const uint8_t*
       const int cl = wave + W * i;  // chunk within the slice
       const v8i bv = {(int)x.bb[i][0], (int)x.bb[i][1], (int)x.bb[i][2], (int)x.bb[i][3], 0, 0, 0, 0};
       const float u0 = ue4m3_to_f32<0>(x.ss[i]), u1 = ue4m3_to_f32<1>(x.ss[i]);
+      // all MT tokens, branch-free (tokens >= M have zero tables), in three phases
+      // (operand reads, MFMAs, scaling) so that the MFMAs of different tokens are in
+      // flight together instead of each waiting for the previous token's result
+      floatx4 D[MT];
+      {
+        v8i av[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint8_t* base = tab + (t * SL + cl) * 256 + part * 128;
+          const uint8_t* pa = (sbv == g) ? base + 16 * g : zero16;
+          const uint8_t* pb = (sbv == g + 4) ? base + 64 + 16 * g : zero16;
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(pb);
+          av[t] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          D[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[t], bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
+                                                                  127 + 9, 0, 127);
+      }
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        if (t >= M) break;
-        const uint8_t* base = tab + (t * SL + cl) * 256 + part * 128;
-        const uint8_t* pa = (sbv == g) ? base + 16 * g : zero16;
-        const uint8_t* pb = (sbv == g + 4) ? base + 64 + 16 * g : zero16;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(pb);
-        const v8i av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                        (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        const floatx4 D = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            av, bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127 + 9, 0, 127);
-        const float i0 = fmaf(D[0], 16.0f, D[1]);
-        const float i1 = fmaf(D[2], 16.0f, D[3]);
+        const float i0 = fmaf(D[t][0], 16.0f, D[t][1]);
+        const float i1 = fmaf(D[t][2], 16.0f, D[t][3]);
         acc[t] = fmaf(fmaf(i0, u0, i1 * u1), dtab[t * SL * 4 + 4 * cl + g], acc[t]);
       }
     }
