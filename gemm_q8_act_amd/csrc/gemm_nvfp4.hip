@@ -274,7 +274,8 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 namespace {
 constexpr int kBigBN = 256, kBigBM = 256, kBigThreads = 512;
 constexpr int kBigLRW = 72;   // halves per LDS weight row (64 k + 8 pad)
-constexpr int kBigLRA = 80;   // bytes per LDS activation row (64 codes + 16 pad)
+constexpr int kBigLRA = 72;   // bytes per LDS activation row (64 codes + 8 pad: 18 dwords, so the
+                              // 8-byte fragment reads of 16 consecutive rows hit distinct banks)
 constexpr int kBigStageW = kBigBN * kBigLRW * 2, kBigStageA = kBigBM * kBigLRA, kBigStageD = kBigBM * 4;
 constexpr int kBigStage = kBigStageW + kBigStageA + kBigStageD;
 constexpr int kBigLds = 2 * kBigStage;

@@ -53,7 +53,20 @@ def test_sizes():
     assert nvq.nvq_q4_1_weight_bytes(4096, 4096) == 4096 * 4096 * 5 // 8
     assert nvq.nvq_q4_1_weight_bytes(3, 32) == 3 * 20
     assert nvq.nvq_q4_1_weight_bytes(3, 48) == 0
-    assert nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) >= 0
+    # K-split workspace of the M > 64 GEMM: fp32 partial tiles of 256 x 256 (one per
+    # 512-thread work item x 128 accumulators), for the tiles of an incomplete last
+    # round over 256 compute units, split up to 8 ways (at most one per 64-k stage)
+    tile_bytes = 512 * 128 * 4
+    ws = nvq.nvq_gemm_workspace_bytes
+    assert ws(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) == 32 * 8 * tile_bytes      # 544 tiles: 32 left over
+    assert ws(nvq.NVQ_FMT_NVFP4, 256, 17408, 5120) == 68 * 3 * tile_bytes       # 68 tiles, 256 // 68 = 3
+    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 640) == 1 * 8 * tile_bytes             # 1 tile, 10 stages
+    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 192) == 1 * 3 * tile_bytes             # split <= stages
+    assert ws(nvq.NVQ_FMT_NVFP4, 65, 33, 64) == 0                               # one stage: no split
+    assert ws(nvq.NVQ_FMT_NVFP4, 4096, 4096, 1024) == 0                         # 256 tiles: full rounds
+    assert ws(nvq.NVQ_FMT_NVFP4, 64, 17408, 5120) == 0                          # M <= 64: tile kernel
+    assert ws(nvq.NVQ_FMT_Q4_1, 2048, 4096, 4096) == 0
+    assert ws(nvq.NVQ_FMT_NVFP4, 2048, 17408, 96) == 0                          # invalid K
 
 
 def unpack_tiled(buf, N, K):
@@ -154,6 +167,10 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 15, 8, 64, A16, None, 0, None) == -2   # M < 16
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 32, A16, None, 0, None) == -2   # K % 64
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 64, MIS, None, 0, None) == -4   # y alignment
+    # M > 64 with K-split parts needs a workspace: missing -> NVQ_ERR_WORKSPACE before any device call
+    assert L.nvq_gemm_workspace_bytes(0, 100, 8, 640) > 0
+    assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, None, 0, None) == -7
+    assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, A16, 16, None) == -7   # too small
     assert L.nvq_gemm_q4_1(A16, A16, A16, A2, 8, 8, 32, A16, None, 0, None) == -2
     assert L.nvq_quantize_act_q8_0(A16, 1, 48, A16, A16, None, None) == -2
     assert L.nvq_quantize_act_q8_0(MIS, 1, 64, A16, A16, None, None) == -4

@@ -306,6 +306,54 @@ def test_gemm_split_kernel_activation_range():
     assert (yh[rows] == yr[rows]).all()
 
 
+@pytest.mark.parametrize("K", [65536, 98304])
+def test_gemv_long_rows(oracle, K):
+    """K = 65536 keeps the decode GEMV's activation table in LDS; K = 98304 does not
+    and takes the tiled kernel instead (both must agree with the oracle)."""
+    say(f"gemv long row N=40 K={K}")
+    torch = torch_dev()
+    c = NvCase(1, 40, K, 31 + K // 1024)
+    y = torch.empty((1, 40), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"gemv K={K}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 100])
+def test_zero_weights_give_exact_zero(M):
+    """Codes 0 and 8 (+0, -0) only: every output is exactly 0 on every path."""
+    say(f"zero weights M={M}")
+    torch = torch_dev()
+    N, K = 70, 640
+    codes, scales, ws = synth.nvfp4_weights(N, K, 5)
+    codes = (codes & 8).astype(np.uint8)  # 0 or 8
+    w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    q, d, _ = quantize_gpu(synth.activations(M, K, 6, outliers=True))
+    y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemv_nvfp4 if M <= 15 else nvq.nvq_gemm_nvfp4)(w, float(ws), q, d, y)
+    yh = host(y)
+    assert (yh == 0.0).all()
+
+
+@pytest.mark.parametrize("M", [1, 5, 90])
+def test_subnormal_ue4m3_scales(oracle, M):
+    """UE4M3 bytes 0x01..0x07 (M * 2^-9) mixed with normal scales."""
+    say(f"subnormal UE4M3 scales M={M}")
+    torch = torch_dev()
+    N, K = 50, 384
+    codes, scales, ws = synth.nvfp4_weights(N, K, 9)
+    r = np.random.Generator(np.random.PCG64(10))
+    sub = r.random(scales.shape) < 0.5
+    scales = np.where(sub, r.integers(1, 8, scales.shape), scales).astype(np.uint8)
+    c = NvCase(M, N, K, 11)
+    c.codes, c.scales, c.ws = codes, scales, ws
+    c.w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemv_nvfp4 if M <= 15 else nvq.nvq_gemm_nvfp4)(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"subnormal scales M={M}")
+
+
 def test_validation_leaves_output_untouched():
     torch = torch_dev()
     y = torch.full((16, 64), 7.0, dtype=torch.float32, device="cuda")
