@@ -107,22 +107,17 @@ class Layer:
                 name=name, N=N, K=K, w=ws_list, ws=float(ws), x=x,
                 q=torch.empty((M, K), dtype=torch.int8, device="cuda"),
                 d=torch.empty((M, K // 32), dtype=torch.int16, device="cuda"),
-                b=torch.empty((M, K // 16), dtype=torch.int16, device="cuda"),
                 y=torch.empty((M, N), dtype=torch.float32, device="cuda")))
 
     def weight_bytes(self):
         return sum(nvfp4_bytes(m["N"], m["K"]) for m in self.mats)
 
-    def step(self, copy, events=None):
+    def step(self, copy):
         import gemm_q8_act_amd as nvq
 
-        for j, m in enumerate(self.mats):
-            nvq.nvq_quantize_act_q8_0(m["x"], m["q"], m["d"], m["b"])
-            if events is not None:
-                events[j][0].record()
+        for m in self.mats:
+            nvq.nvq_quantize_act_q8_0(m["x"], m["q"], m["d"])
             nvq.nvq_gemv_nvfp4(m["w"][copy], m["ws"], m["q"], m["d"], m["y"])
-            if events is not None:
-                events[j][1].record()
 
 
 def kernel_src_hash():
