@@ -1,0 +1,225 @@
+// gemv_batch_f16.hip -- batched decode GEMV (2 <= M <= 8 tokens per launch), NVFP4
+// weights x Q8_0 activations, on gfx950's fp16 matrix cores.
+//
+// What is computed ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3):
+//     y[m][n] = S * sum_s UE4M3(scale[n][s]) * sum_{k in s} E2M1(code[n][k]) * d[m][k/32] * q[m][k].
+//
+// Both scales are folded into exact fp16 operands, so the matrix core accumulates the
+// whole row and the vector unit never touches a partial product:
+//  * weights: w16 = E2M1 * UE4M3 has at most 6 significant bits and lies in
+//    [2^-10, 2688], so it is an exact binary16 value (v_cvt_scalef32_pk_f16_fp4, then
+//    one v_pk_mul_f16 by the UE4M3 value);
+//  * activations: d * q has at most 18 significant bits (11 of the binary16 d, 7 of
+//    |q| <= 127), so it is exactly hi + lo with hi = fp16(d * q) and
+//    lo = fma(d, q, -hi) (the difference is representable, so the fused result is
+//    exact).  hi and lo become two columns of the fp16 operand: column j < 8 holds
+//    token j's hi values, column j + 8 its lo values, and y[m] = S * (D[m] + D[m + 8]).
+//  * hi overflows once |d * q| reaches 65520.  A 32-value block whose d is 512 or
+//    more (|d * q| can then exceed the binary16 range) is left out of the main loop
+//    and done by a second pass, taken only by wavefronts that met such a block, with
+//    d / 256 (exact: a power of two, and d / 256 >= 2 stays normal) into a second
+//    accumulator that is multiplied by 256 at the end.  So every finite activation is
+//    handled exactly, and the main loop carries no extra work for it.
+//
+// One v_mfma_f32_16x16x32_f16 covers 16 weight rows x 32 k x 16 columns.  A wavefront's
+// 16 B weight load per chunk (lane l = 16 g + r: row r, k = 32 g .. 32 g + 31 of the
+// 128-k chunk) feeds four of them: MFMA t reads from lane l the codes k = 32 g + 8 t
+// .. + 7, which is the operand's "k group g" -- the reduction index is only permuted,
+// identically for both operands.  The activation operand of lane l (column l % 16, k
+// group g) is therefore the 32 codes q[m][128 c + 32 g .. + 31] and their one scale
+// d[m][4 c + g]: 34 bytes per lane and chunk, read straight from global memory (the
+// row is L2-resident) and expanded in registers.  The expansion (about 72 vector
+// instructions per chunk) is shared by the T tiles a block owns, so a wavefront
+// streams T KB of weights per chunk against one activation expansion.
+//
+// Block: W wavefronts, T consecutive 16-row tiles; wavefront v takes chunks
+// v, v + W, ... through D register slots of loads (software pipelined: while one chunk
+// is expanded and multiplied, the loads of the next D - 1 are in flight).  The W
+// partial tiles are summed through LDS at the end.
+#include "nvq_device.h"
+
+namespace nvq {
+
+template <int T, int W, int D>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                                const int8_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ d16, int M,
+                                                                float w_scale, float* __restrict__ y) {
+  constexpr int NT = 64 * W;
+  __shared__ floatx4 red[W * T * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const int nch = (K + 127) >> 7;
+  const int nb = K >> 5;
+  const int64_t ntiles = (N + 15) >> 4;
+  const int64_t tile0 = (int64_t)blockIdx.x * T;
+
+  const uint8_t* wt[T];
+  const uint8_t* st[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int64_t tile = tile0 + t < ntiles ? tile0 + t : ntiles - 1;
+    wt[t] = w + tile * nch * 1024 + 16 * lane;
+    st[t] = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
+  }
+  // this lane's activation column: token fr % 8 (columns of absent tokens repeat the
+  // last token and are never stored), part hi (fr < 8) or lo (fr >= 8)
+  const int m = min(fr & 7, M - 1);
+  const bool lo_lane = fr >= 8;
+  const int8_t* qm = q + (int64_t)m * K;
+  const uint16_t* dm = d16 + (int64_t)m * nb;
+
+  // D load slots, each one chunk ahead of the next: slot j holds chunk c + W j
+  u32x4 qa[D][2], bw[D][T];
+  uint32_t dv[D], bs[D][T];
+  auto issue = [&](int j, int c) {
+    // chunk index clamped (loads past the row's last chunk are never consumed); k
+    // groups past the row's end (a last chunk of 64) read the row's last 32 codes and
+    // get scale 0 when consumed, so they contribute nothing
+    c = min(c, nch - 1);
+    const int b = min(4 * c + fg, nb - 1);
+    qa[j][0] = *reinterpret_cast<const u32x4*>(qm + 32 * b);
+    qa[j][1] = *reinterpret_cast<const u32x4*>(qm + 32 * b + 16);
+    dv[j] = dm[b];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      bw[j][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt[t] + (int64_t)c * 1024));
+      bs[j][t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st[t] + (int64_t)c * 128));
+    }
+  };
+
+  floatx4 acc[T], accb[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    accb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // one chunk of slot j: the activation operands for scale dd (binary16 bits) into
+  // B[4], then the 4 x T MFMAs into a[]
+  auto chunk = [&](int j, uint32_t dd, floatx4* a) {
+    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)dd);
+    const half2_t d2 = {dh, dh};
+    const half2_t z2 = {(_Float16)0.0f, (_Float16)0.0f};
+    const half2_t dl2 = lo_lane ? d2 : z2;
+    half8_t B[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w0 = qa[j][u >> 1][2 * (u & 1)], w1 = qa[j][u >> 1][2 * (u & 1) + 1];
+      half2_t x0, x1, x2, x3;
+      i8x4_to_f16x4(w0, x0, x1);
+      i8x4_to_f16x4(w1, x2, x3);
+      // hi lanes: fma(q, d, -0) = fp16(d q); lo lanes: fma(q, d, -fp16(d q)) = lo
+      const half2_t b0 = __builtin_elementwise_fma(x0, d2, -(x0 * dl2));
+      const half2_t b1 = __builtin_elementwise_fma(x1, d2, -(x1 * dl2));
+      const half2_t b2 = __builtin_elementwise_fma(x2, d2, -(x2 * dl2));
+      const half2_t b3 = __builtin_elementwise_fma(x3, d2, -(x3 * dl2));
+      B[u] = half8_t{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const _Float16 s0 = (_Float16)ue4m3_to_f32<0>(bs[j][t]);
+      const _Float16 s1 = (_Float16)ue4m3_to_f32<1>(bs[j][t]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const half2_t s = u < 2 ? half2_t{s0, s0} : half2_t{s1, s1};
+        const uint32_t cw = bw[j][t][u];
+        const half2_t p0 = e2m1x2_to_f16<0>(cw) * s;
+        const half2_t p1 = e2m1x2_to_f16<1>(cw) * s;
+        const half2_t p2 = e2m1x2_to_f16<2>(cw) * s;
+        const half2_t p3 = e2m1x2_to_f16<3>(cw) * s;
+        const half8_t A = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[u], a[t], 0, 0, 0);
+      }
+    }
+  };
+
+  // scale of slot j's chunk c for this lane: 0 past the row's end; `big` marks
+  // |d| >= 512, whose blocks are left out here and done by the second pass below
+  auto scale = [&](int j, int c, bool& big) {
+    const uint32_t d = 4 * c + fg < nb ? dv[j] : 0u;
+    big = (d & 0x7FFFu) >= 0x6000u;
+    return d;
+  };
+
+  // software pipeline: slot j is consumed, then refilled with the chunk D slots later,
+  // so D chunks of loads stay in flight while one is computed
+  uint64_t any_big = 0;
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(j, wave + W * j);
+  for (int c = wave; c < nch; c += W * D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (c + W * j < nch) {
+        bool big;
+        const uint32_t d = scale(j, c + W * j, big);
+        any_big |= __builtin_amdgcn_ballot_w64(big);
+        chunk(j, big ? 0u : d, acc);
+      }
+      issue(j, c + W * (j + D));
+    }
+  }
+  // blocks with |d| >= 512 (only for activations near the binary16 range): one more
+  // pass over this wavefront's chunks with d / 256 (exponent field - 8; such a d is
+  // normal and d / 256 >= 2 stays normal) into the accumulator that is scaled by 256
+  if (any_big) {
+    for (int c = wave; c < nch; c += W) {
+      issue(0, c);
+      bool big;
+      const uint32_t d = scale(0, c, big);
+      chunk(0, big ? d - 0x2000u : 0u, accb);
+    }
+  }
+
+  // reduce the W wavefronts' partial tiles; column j < 8 + column j + 8 = token j
+#pragma unroll
+  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t] + 256.0f * accb[t];
+  __syncthreads();
+  const float* rf = reinterpret_cast<const float*>(red);
+  for (int o = tid; o < 8 * 16 * T; o += NT) {
+    const int mo = o / (16 * T), rr = o % (16 * T);
+    const int t = rr >> 4, r = rr & 15;
+    const int64_t row = (tile0 + t) * 16 + r;
+    if (mo >= M || row >= N) continue;
+    const int l_hi = mo + 16 * (r >> 2), l_lo = l_hi + 8, v = r & 3;
+    float s = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const int base = (ww * T + t) * 64;
+      s += rf[(base + l_hi) * 4 + v] + rf[(base + l_lo) * 4 + v];
+    }
+    y[(int64_t)mo * N + row] = s * w_scale;
+  }
+}
+
+template <int T, int W, int D>
+static hipError_t launch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int M,
+                             int64_t N, int64_t K, float* y, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const unsigned blocks = (unsigned)((ntiles + T - 1) / T);
+  hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D>), dim3(blocks), dim3(64 * W), 0, stream, w, N, (int)K, q,
+                     d16, M, w_scale, y);
+  return hipGetLastError();
+}
+
+// Tokens in groups of at most 8, one launch per group (each streams the weights once).
+// Launch shapes (measured on the layer shapes at M = 8): 4 tiles x 4 wavefronts x 2
+// slots when there are >= 2048 tiles (gate+up: 544 blocks, every wavefront resident
+// at once); otherwise 2 tiles x 8 wavefronts x 3 slots, which keeps more blocks and
+// more loads in flight on the smaller projections.
+hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
+                                       int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  for (int64_t m0 = 0; m0 < M; m0 += 8) {
+    const int mb = (int)(M - m0 < 8 ? M - m0 : 8);
+    const int8_t* qb = q + m0 * K;
+    const uint16_t* db = d16 + m0 * (K / 32);
+    float* yb = y + m0 * N;
+    const hipError_t e = ntiles >= 2048 ? launch_f16<4, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
+                                        : launch_f16<2, 8, 3>(w, w_scale, qb, db, mb, N, K, yb, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace nvq

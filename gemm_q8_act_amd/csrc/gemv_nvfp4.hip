@@ -1,4 +1,4 @@
-// gemv_nvfp4.hip -- batch-1 decode GEMV, NVFP4 weights x Q8_0 activations, gfx950.
+// gemv_nvfp4.hip -- single-token decode GEMV, NVFP4 weights x Q8_0 activations, gfx950.
 //
 // What is computed ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3,
 // Code map and bias-trick paragraph): for every 16-weight subblock an exact integer
@@ -35,7 +35,6 @@
 //    v_perm_b32 table lookups per four codes, summed inside v_dot4_i32_i8 (see
 //    nvq_device.h).  About 13 full-rate instructions per 8 weights: on MI355X this
 //    costs as much time as streaming the bytes, so it is the slower of the two.
-#include <algorithm>
 
 #include "nvq_device.h"
 #include "nvq_launch.h"
@@ -43,7 +42,6 @@
 namespace nvq {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Four activation codes -> the high parts h = q >> 4 as sign-magnitude E4M3 bytes
 // (|h| <= 8, value |h| * 2^-9 with the sign bit).
@@ -206,210 +204,6 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
     const int64_t r = tile * 16 + tid;
     if (r < N) y[r] = s * w_scale;
   }
-}
-
-// ---------------------------------------------------------------------------------
-// Batched decode, 2 <= M <= 8 tokens: the matrix-core loop of the M = 1 kernel, one
-// MFMA per token and tile-chunk, all tokens sharing each weight load.  The per-token
-// activation tables cover K in slices of SL chunks (LDS holds MT x SL x 256 B);
-// the weight chunks and activation codes of slice s+1 are loaded while slice s
-// computes.  Block: W wavefronts per 16-row tile, CPW = SL / W chunks per wavefront
-// and slice.
-// ---------------------------------------------------------------------------------
-template <int MT, int W>
-struct BatchCfg {
-  static constexpr int SL = 16;                 // chunks per slice
-  static constexpr int CPW = SL / W;            // chunks per wavefront and slice
-  static constexpr int NT = 64 * W;
-  static constexpr int QG = (MT * SL * 8 + NT - 1) / NT;  // 16-code activation groups per thread and slice
-  static constexpr int TAB = MT * SL * 256;     // table bytes
-  static constexpr int DTAB = MT * SL * 4 * 4;  // d table bytes
-  static constexpr int RED = W * MT * 64 * 4;   // partial sums
-  static constexpr int LDS = TAB + 16 + DTAB + RED;
-  static constexpr int DG = (MT * SL * 4 + NT - 1) / NT;  // activation scales per thread and slice
-  static_assert(CPW * W == SL, "batch shape");
-};
-
-template <int MT, int W>
-__global__ __launch_bounds__(64 * W) void gemv_nvfp4_batch_kernel(const uint8_t* __restrict__ w, int64_t N,
-                                                                  int K, const int8_t* __restrict__ q,
-                                                                  const uint16_t* __restrict__ d16, int M,
-                                                                  float w_scale, float* __restrict__ y) {
-  using C = BatchCfg<MT, W>;
-  constexpr int SL = C::SL, CPW = C::CPW, NT = C::NT, QG = C::QG, DG = C::DG;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* tab = smem;                                        // [MT][SL][256]
-  uint8_t* zero16 = smem + C::TAB;
-  float* dtab = reinterpret_cast<float*>(smem + C::TAB + 16);  // [MT][SL * 4]
-  float* red = reinterpret_cast<float*>(smem + C::TAB + 16 + C::DTAB);
-  const int nch = (K + 127) >> 7;
-  const int nslices = (nch + SL - 1) / SL;
-  const int nq16 = K >> 4, nd = K >> 5;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int64_t tile = blockIdx.x;
-  const int64_t ntiles = (N + 15) >> 4;
-  const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
-  const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
-  const u32x4* __restrict__ q16 = reinterpret_cast<const u32x4*>(q);
-
-  // per slice: this thread's activation groups (token t, 16-code group j of the slice)
-  // and weight chunks c = slice * SL + wave + W * i
-  struct Slice { u32x4 qa[QG]; uint32_t da[DG]; u32x4 bb[CPW]; uint32_t ss[CPW]; };
-  auto load = [&](int sl, Slice& x) {
-    const int s0 = sl * SL;
-#pragma unroll
-    for (int e = 0; e < QG; ++e) {
-      const int task = tid + e * NT, t = task / (SL * 8), j = task % (SL * 8);
-      const int tt = min(t, M - 1), jj = min(s0 * 8 + j, nq16 - 1);
-      x.qa[e] = q16[(int64_t)tt * nq16 + jj];
-    }
-#pragma unroll
-    for (int e = 0; e < DG; ++e) {
-      const int task = tid + e * NT, t = task / (SL * 4), b = task % (SL * 4);
-      x.da[e] = d16[(int64_t)min(t, M - 1) * nd + min(s0 * 4 + b, nd - 1)];
-    }
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = min(s0 + wave + W * i, nch - 1);
-      x.bb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt + (int64_t)c * 1024));
-      x.ss[i] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + (int64_t)c * 128));
-    }
-  };
-  auto build = [&](int sl, const Slice& x) {
-    const int s0 = sl * SL;
-#pragma unroll
-    for (int e = 0; e < QG; ++e) {
-      const int task = tid + e * NT, t = task / (SL * 8), j = task % (SL * 8);
-      if (t >= MT) break;  // (only when MT * SL * 8 is not a multiple of the block)
-      const int jg = s0 * 8 + j;  // global 16-code group
-      const bool ok = t < M && jg < nq16;
-      const u32x4 v = ok ? x.qa[e] : u32x4{0u, 0u, 0u, 0u};
-      const int c = j >> 3, o = 16 * (j & 7);
-      uint8_t* dst = tab + (t * SL + c) * 256 + o;
-      const u32x4 hi = {act_hi_e4m3(v[0]), act_hi_e4m3(v[1]), act_hi_e4m3(v[2]), act_hi_e4m3(v[3])};
-      const u32x4 lo = {v[0] & 0x0F0F0F0Fu, v[1] & 0x0F0F0F0Fu, v[2] & 0x0F0F0F0Fu, v[3] & 0x0F0F0F0Fu};
-      *reinterpret_cast<u32x4*>(dst) = hi;
-      *reinterpret_cast<u32x4*>(dst + 128) = lo;
-    }
-#pragma unroll
-    for (int e = 0; e < DG; ++e) {
-      const int task = tid + e * NT, t = task / (SL * 4), b = task % (SL * 4);
-      if (t < MT) dtab[t * SL * 4 + b] = (t < M && s0 * 4 + b < nd) ? f16_bits_to_f32((uint16_t)x.da[e]) : 0.0f;
-    }
-  };
-
-  float acc[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-  const int sbv = nl >> 1, part = nl & 1;
-  auto compute = [&](int sl, const Slice& x) {
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int c = sl * SL + wave + W * i;
-      if (c >= nch) continue;
-      const int cl = wave + W * i;  // chunk within the slice
-      const v8i bv = {(int)x.bb[i][0], (int)x.bb[i][1], (int)x.bb[i][2], (int)x.bb[i][3], 0, 0, 0, 0};
-      const float u0 = ue4m3_to_f32<0>(x.ss[i]), u1 = ue4m3_to_f32<1>(x.ss[i]);
-      // all MT tokens, branch-free (tokens >= M have zero tables), in three phases
-      // (operand reads, MFMAs, scaling) so that the MFMAs of different tokens are in
-      // flight together instead of each waiting for the previous token's result
-      floatx4 D[MT];
-      {
-        v8i av[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint8_t* base = tab + (t * SL + cl) * 256 + part * 128;
-          const uint8_t* pa = (sbv == g) ? base + 16 * g : zero16;
-          const uint8_t* pb = (sbv == g + 4) ? base + 64 + 16 * g : zero16;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(pb);
-          av[t] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-          D[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[t], bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
-                                                                  127 + 9, 0, 127);
-      }
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float i0 = fmaf(D[t][0], 16.0f, D[t][1]);
-        const float i1 = fmaf(D[t][2], 16.0f, D[t][3]);
-        acc[t] = fmaf(fmaf(i0, u0, i1 * u1), dtab[t * SL * 4 + 4 * cl + g], acc[t]);
-      }
-    }
-  };
-
-  Slice xa, xb;
-  load(0, xa);
-  if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
-  build(0, xa);
-  __syncthreads();
-  // two slices per iteration so the register sets alternate at compile time
-  for (int sl = 0; sl < nslices; sl += 2) {
-    load(min(sl + 1, nslices - 1), xb);
-    compute(sl, xa);
-    if (sl + 1 >= nslices) break;
-    __syncthreads();
-    build(sl + 1, xb);
-    __syncthreads();
-    load(min(sl + 2, nslices - 1), xa);
-    compute(sl + 1, xb);
-    if (sl + 2 >= nslices) break;
-    __syncthreads();
-    build(sl + 2, xa);
-    __syncthreads();
-  }
-
-  // reduce: per token, 4 lane groups x W wavefronts
-#pragma unroll
-  for (int t = 0; t < MT; ++t) red[(wave * MT + t) * 64 + lane] = acc[t];
-  __syncthreads();
-  if (tid < 16 * MT) {
-    const int t = tid >> 4, n = tid & 15;
-    float s = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) s += red[(ww * MT + t) * 64 + gg * 16 + n];
-    const int64_t r = tile * 16 + n;
-    if (t < M && r < N) y[(int64_t)t * N + r] = s * w_scale;
-  }
-}
-
-template <int MT, int W>
-static hipError_t launch_batch(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
-                               int M, int64_t N, int64_t K, float* y, hipStream_t stream) {
-  const int64_t ntiles = (N + 15) / 16;
-  constexpr int lds = BatchCfg<MT, W>::LDS;
-  auto fn = gemv_nvfp4_batch_kernel<MT, W>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles), dim3(64 * W), lds, stream, w, N, (int)K, q, d16, M,
-                     w_scale, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_nvfp4_batch(const uint8_t* w, float w_scale, const int8_t* q,
-                                   const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
-                                   hipStream_t stream) {
-  // tokens in groups of at most 8; each group streams the weights once
-  for (int64_t m0 = 0; m0 < M; m0 += 8) {
-    const int mb = (int)std::min<int64_t>(8, M - m0);
-    const int8_t* qb = q + m0 * K;
-    const uint16_t* db = d16 + m0 * (K / 32);
-    float* yb = y + m0 * N;
-    hipError_t e;
-    if (mb == 1) e = launch_gemv_nvfp4_m1(w, w_scale, qb, db, N, K, yb, nullptr, 0, stream);
-    else if (mb == 2) e = launch_batch<2, 8>(w, w_scale, qb, db, mb, N, K, yb, stream);
-    else if (mb <= 4) e = launch_batch<4, 8>(w, w_scale, qb, db, mb, N, K, yb, stream);
-    else e = launch_batch<8, 8>(w, w_scale, qb, db, mb, N, K, yb, stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }
 
 // Launch shape: 4 wavefronts x 5-chunk batches, or 8 x 3 for long rows over few tiles

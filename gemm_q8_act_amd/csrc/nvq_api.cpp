@@ -202,8 +202,8 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   if (M == 1 && gemv_fits_lds(K))
     return launched(nvq::launch_gemv_nvfp4_m1(wb, w_scale, q, d_f16, N, K, y, nullptr, 0, (hipStream_t)stream), "gemv_nvfp4");
-  if (M > 1 && gemv_fits_lds(K))
-    return launched(nvq::launch_gemv_nvfp4_batch(wb, w_scale, q, d_f16, M, N, K, y, (hipStream_t)stream), "gemv_nvfp4 (batched)");
+  if (M > 1)
+    return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, w_scale, q, d_f16, M, N, K, y, (hipStream_t)stream), "gemv_nvfp4 (batched)");
   return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
 }
 

@@ -17,11 +17,11 @@ hipError_t launch_act_quant(const float* x, int64_t M, int64_t K, int8_t* q, uin
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
                                 int32_t* isums, int mode, hipStream_t stream);
-// NVFP4, 2 <= M <= 15 tokens: the matrix-core decode loop over groups of up to 8
-// tokens (one launch per group, each streaming the weights once).
-hipError_t launch_gemv_nvfp4_batch(const uint8_t* w, float w_scale, const int8_t* q,
-                                   const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
-                                   hipStream_t stream);
+// NVFP4, 2 <= M <= 15 tokens: exact fp16 operands on the fp16 matrix core (groups of
+// up to 8 tokens, one launch per group).  No limit on K.
+hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q,
+                                       const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
+                                       hipStream_t stream);
 // LDS bytes the decode GEMV needs for a row length K.
 size_t gemv_lds_bytes(int64_t K);
 

@@ -123,6 +123,42 @@ def test_gemv_nvfp4_small_batch(oracle, M, N, K, kernel):
     check_y(host(y), yo, awa, f"gemv M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(2, 100, 640), (8, 100, 320), (5, 40, 128)])
+def test_gemv_batched_large_activations(oracle, M, N, K):
+    """Blocks whose binary16 scale d is >= 512 (|d * q| can pass the binary16 range)
+    take the batched kernel's second pass; blocks just below stay in the main loop."""
+    say(f"batched gemv large activations M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = NvCase(M, N, K, 900 + M, w_scale="uniform")
+    x = c.x.copy()
+    x[1, 40:44] = [3.0e5, -2.0e5, 1.0e5, 7.0]      # d ~ 2362: second pass
+    x[M - 1, 0:32] *= 6.0e4 / np.abs(x[M - 1, 0:32]).max()   # d ~ 472: main loop, |hi| near 60000
+    x[0, :] *= 1.0e5                                # every block of token 0: d >= 512
+    c.x = x
+    c.q, c.d, c.b = quantize_gpu(x)
+    c.qh, c.dh = host(c.q), host(c.d).view(np.uint16)
+    assert (c.dh[1] & 0x7FFF).max() >= 0x6000 and (c.dh[M - 1, 0] & 0x7FFF) < 0x6000
+    assert ((c.dh[0] & 0x7FFF) >= 0x6000).all()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    assert np.isfinite(host(y)).all()
+    check_y(host(y), yo, awa, f"large activations M={M} N={N} K={K}")
+
+
+def test_gemv_batched_ragged_tile_groups(oracle):
+    """More than 2048 tiles (blocks of 4 tiles) with a tile count that is not a
+    multiple of 4 and a ragged last tile."""
+    say("batched gemv M=3 N=32779 K=128")
+    torch = torch_dev()
+    M, N, K = 3, 32779, 128
+    c = NvCase(M, N, K, 4242)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, "M=3 N=32779 K=128")
+
+
 # M <= 64: per-block scaled tile kernel; M > 64: split-activation kernel, whose
 # small shapes always take the K-split + ordered-reduction route (fewer tiles than
 # compute units), except K = 64 (one stage: no split)
