@@ -202,21 +202,39 @@ static hipError_t launch_f16(const uint8_t* w, float w_scale, const int8_t* q, c
   return hipGetLastError();
 }
 
+// Tiles per block for many tiles.  The vector work of a block per chunk is about
+// 32 T + 72 instructions (weights of T tiles + one activation expansion), and a
+// compute unit runs ceil(blocks / 256) blocks' worth of it, so the launch takes the T
+// in {3, 4} that minimises ceil(ceil(tiles / T) / 256) * (32 T + 72) (measured at
+// M = 8: gate+up, 2176 tiles, 26.9 us with T = 4 and 23.3 us with T = 3).  T = 2
+// never wins this from 1024 tiles up, so only 3 and 4 are built.
+static int tiles_per_block(int64_t ntiles) {
+  int best = 4;
+  int64_t best_cost = -1;
+  for (int t = 4; t >= 3; --t) {
+    const int64_t per_cu = ((ntiles + t - 1) / t + 255) / 256;
+    const int64_t cost = per_cu * (32 * t + 72);
+    if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
+  }
+  return best;
+}
+
 // Tokens in groups of at most 8, one launch per group (each streams the weights once).
-// Launch shapes (measured on the layer shapes at M = 8): 4 tiles x 4 wavefronts x 2
-// slots when there are >= 2048 tiles (gate+up: 544 blocks, every wavefront resident
-// at once); otherwise 2 tiles x 8 wavefronts x 3 slots, which keeps more blocks and
-// more loads in flight on the smaller projections.
+// Fewer than 1024 tiles (QKV, O, down at hidden 5120): 2 tiles x 8 wavefronts x 3
+// slots, so the blocks keep enough loads in flight; more: T tiles x 4 wavefronts x 2
+// slots (every wavefront resident at once).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
                                        int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
+  const int T = ntiles < 1024 ? 0 : tiles_per_block(ntiles);
   for (int64_t m0 = 0; m0 < M; m0 += 8) {
     const int mb = (int)(M - m0 < 8 ? M - m0 : 8);
     const int8_t* qb = q + m0 * K;
     const uint16_t* db = d16 + m0 * (K / 32);
     float* yb = y + m0 * N;
-    const hipError_t e = ntiles >= 2048 ? launch_f16<4, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
-                                        : launch_f16<2, 8, 3>(w, w_scale, qb, db, mb, N, K, yb, stream);
+    const hipError_t e = T == 4   ? launch_f16<4, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
+                         : T == 3 ? launch_f16<3, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
+                                  : launch_f16<2, 8, 3>(w, w_scale, qb, db, mb, N, K, yb, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
