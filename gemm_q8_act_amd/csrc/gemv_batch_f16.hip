@@ -27,8 +27,9 @@
 // .. + 7, which is the operand's "k group g" -- the reduction index is only permuted,
 // identically for both operands.  The activation operand of lane l (column l % 16, k
 // group g) is therefore the 32 codes q[m][128 c + 32 g .. + 31] and their one scale
-// d[m][4 c + g]: 34 bytes per lane and chunk, read straight from global memory (the
-// row is L2-resident) and expanded in registers.  The expansion (about 72 vector
+// d[m][4 c + g], read straight from global memory (the row is L2-resident: 16 bytes
+// per lane, the other 16 from the partner lane of the same token) and expanded in
+// registers.  The expansion (about 72 vector
 // instructions per chunk) is shared by the T tiles a block owns, so a wavefront
 // streams T KB of weights per chunk against one activation expansion.
 //
@@ -54,23 +55,28 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
   const int64_t ntiles = (N + 15) >> 4;
   const int64_t tile0 = (int64_t)blockIdx.x * T;
 
+  // per-tile bases are wavefront-uniform; lane offsets are 32-bit, so the loads use
+  // scalar base + vector offset addressing
   const uint8_t* wt[T];
   const uint8_t* st[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int64_t tile = tile0 + t < ntiles ? tile0 + t : ntiles - 1;
-    wt[t] = w + tile * nch * 1024 + 16 * lane;
-    st[t] = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
+    wt[t] = w + tile * nch * 1024;
+    st[t] = w + ntiles * nch * 1024 + tile * nch * 128;
   }
+  const uint32_t wl = 16 * lane, sl = 2 * lane;
   // this lane's activation column: token fr % 8 (columns of absent tokens repeat the
   // last token and are never stored), part hi (fr < 8) or lo (fr >= 8)
   const int m = min(fr & 7, M - 1);
   const bool lo_lane = fr >= 8;
-  const int8_t* qm = q + (int64_t)m * K;
-  const uint16_t* dm = d16 + (int64_t)m * nb;
+  const uint32_t qoff = (uint32_t)m * (uint32_t)K, doff = (uint32_t)m * (uint32_t)nb;
 
-  // D load slots, each one chunk ahead of the next: slot j holds chunk c + W j
-  u32x4 qa[D][2], bw[D][T];
+  // D load slots, each one chunk ahead of the next: slot j holds chunk c + W j.  The
+  // hi and lo lanes of a token need the same 32 codes: each loads 16 of them (hi lanes
+  // the first half, lo lanes the second) and takes the other half from its partner
+  // lane (fr ^ 8) when the chunk is consumed.
+  u32x4 qa[D], bw[D][T];
   uint32_t dv[D], bs[D][T];
   auto issue = [&](int j, int c) {
     // chunk index clamped (loads past the row's last chunk are never consumed); k
@@ -78,34 +84,41 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
     // get scale 0 when consumed, so they contribute nothing
     c = min(c, nch - 1);
     const int b = min(4 * c + fg, nb - 1);
-    qa[j][0] = *reinterpret_cast<const u32x4*>(qm + 32 * b);
-    qa[j][1] = *reinterpret_cast<const u32x4*>(qm + 32 * b + 16);
-    dv[j] = dm[b];
+    qa[j] = *reinterpret_cast<const u32x4*>(q + (qoff + 32 * b + (lo_lane ? 16 : 0)));
+    dv[j] = d16[doff + b];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      bw[j][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt[t] + (int64_t)c * 1024));
-      bs[j][t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st[t] + (int64_t)c * 128));
+      bw[j][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt[t] + (int64_t)c * 1024 + wl));
+      bs[j][t] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st[t] + (int64_t)c * 128 + sl));
     }
   };
 
-  floatx4 acc[T], accb[T];
+  floatx4 acc[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    accb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int t = 0; t < T; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk of slot j: the activation operands for scale dd (binary16 bits) into
-  // B[4], then the 4 x T MFMAs into a[]
+  // one chunk of slot j with activation scale dd (binary16 bits): for each of the 4
+  // k groups, its activation operand, then the T weight operands and MFMAs into a[]
   auto chunk = [&](int j, uint32_t dd, floatx4* a) {
     const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)dd);
     const half2_t d2 = {dh, dh};
     const half2_t z2 = {(_Float16)0.0f, (_Float16)0.0f};
     const half2_t dl2 = lo_lane ? d2 : z2;
-    half8_t B[4];
+    _Float16 s[T][2];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      s[t][0] = (_Float16)ue4m3_to_f32<0>(bs[j][t]);
+      s[t][1] = (_Float16)ue4m3_to_f32<1>(bs[j][t]);
+    }
+    // the partner's 16 codes (row_ror:8 swaps lanes fr and fr ^ 8 of each row of 16)
+    u32x4 oth;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oth[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)qa[j][i], 0x128, 0xF, 0xF, false);
+    const u32x4 qlo = lo_lane ? oth : qa[j], qhi = lo_lane ? qa[j] : oth;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t w0 = qa[j][u >> 1][2 * (u & 1)], w1 = qa[j][u >> 1][2 * (u & 1) + 1];
+      const u32x4& qq = u < 2 ? qlo : qhi;
+      const uint32_t w0 = qq[2 * (u & 1)], w1 = qq[2 * (u & 1) + 1];
       half2_t x0, x1, x2, x3;
       i8x4_to_f16x4(w0, x0, x1);
       i8x4_to_f16x4(w1, x2, x3);
@@ -114,22 +127,17 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
       const half2_t b1 = __builtin_elementwise_fma(x1, d2, -(x1 * dl2));
       const half2_t b2 = __builtin_elementwise_fma(x2, d2, -(x2 * dl2));
       const half2_t b3 = __builtin_elementwise_fma(x3, d2, -(x3 * dl2));
-      B[u] = half8_t{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-    }
+      const half8_t B = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const _Float16 s0 = (_Float16)ue4m3_to_f32<0>(bs[j][t]);
-      const _Float16 s1 = (_Float16)ue4m3_to_f32<1>(bs[j][t]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const half2_t s = u < 2 ? half2_t{s0, s0} : half2_t{s1, s1};
+      for (int t = 0; t < T; ++t) {
+        const half2_t sc = {s[t][u >> 1], s[t][u >> 1]};
         const uint32_t cw = bw[j][t][u];
-        const half2_t p0 = e2m1x2_to_f16<0>(cw) * s;
-        const half2_t p1 = e2m1x2_to_f16<1>(cw) * s;
-        const half2_t p2 = e2m1x2_to_f16<2>(cw) * s;
-        const half2_t p3 = e2m1x2_to_f16<3>(cw) * s;
+        const half2_t p0 = e2m1x2_to_f16<0>(cw) * sc;
+        const half2_t p1 = e2m1x2_to_f16<1>(cw) * sc;
+        const half2_t p2 = e2m1x2_to_f16<2>(cw) * sc;
+        const half2_t p3 = e2m1x2_to_f16<3>(cw) * sc;
         const half8_t A = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[u], a[t], 0, 0, 0);
+        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, a[t], 0, 0, 0);
       }
     }
   };
@@ -163,17 +171,22 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
   // pass over this wavefront's chunks with d / 256 (exponent field - 8; such a d is
   // normal and d / 256 >= 2 stays normal) into the accumulator that is scaled by 256
   if (any_big) {
+    floatx4 accb[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) accb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int c = wave; c < nch; c += W) {
       issue(0, c);
       bool big;
       const uint32_t d = scale(0, c, big);
       chunk(0, big ? d - 0x2000u : 0u, accb);
     }
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] += 256.0f * accb[t];
   }
 
   // reduce the W wavefronts' partial tiles; column j < 8 + column j + 8 = token j
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t] + 256.0f * accb[t];
+  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t];
   __syncthreads();
   const float* rf = reinterpret_cast<const float*>(red);
   for (int o = tid; o < 8 * 16 * T; o += NT) {
