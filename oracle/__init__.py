@@ -72,6 +72,9 @@ class Oracle:
         lib.nvqo_matmul_nvfp4.restype = None
         lib.nvqo_matmul_nvfp4.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I64, _I64, _I64,
                                           _P, _I64, _P, _P]
+        lib.nvqo_matmul_nvfp4_routed.restype = None
+        lib.nvqo_matmul_nvfp4_routed.argtypes = [_P, _P, _P, _P, _I64, _I64, _P, _P, _I64, _I64, _I64,
+                                                 _P, _I64, _P, _P]
         lib.nvqo_matmul_q4_1.restype = None
         lib.nvqo_matmul_q4_1.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         self.lib = lib
@@ -125,6 +128,25 @@ class Oracle:
         awa = np.empty((M, nc), np.float64)
         self.lib.nvqo_matmul_nvfp4(_ptr(codes), _ptr(scales), float(np.float32(w_scale)), _ptr(q),
                                    _ptr(d16), M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
+        return y, awa
+
+    def matmul_nvfp4_routed(self, codes, scales, w_scales, ids, q, d16, cols=None):
+        """codes [E, N, K], scales [E, N, K/16], w_scales [E], ids int32 [M, A].
+        Returns (y float32 [M, A, ncols], abs_wa float64 [M, A, ncols])."""
+        codes = np.ascontiguousarray(codes, np.uint8)
+        scales = np.ascontiguousarray(scales, np.uint8)
+        w_scales = np.ascontiguousarray(w_scales, np.float32)
+        ids = np.ascontiguousarray(ids, np.int32)
+        q = np.ascontiguousarray(q, np.int8)
+        d16 = np.ascontiguousarray(d16, np.uint16)
+        E, N, K = codes.shape
+        M, A = ids.shape
+        c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+        nc = N if c is None else len(c)
+        y = np.empty((M, A, nc), np.float32)
+        awa = np.empty((M, A, nc), np.float64)
+        self.lib.nvqo_matmul_nvfp4_routed(_ptr(codes), _ptr(scales), _ptr(w_scales), _ptr(ids), E, A,
+                                          _ptr(q), _ptr(d16), M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
         return y, awa
 
     # -- Q4_1 --------------------------------------------------------------------

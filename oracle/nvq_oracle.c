@@ -223,6 +223,39 @@ void nvqo_matmul_nvfp4(const uint8_t* codes, const uint8_t* scales, float w_scal
     free(a);
 }
 
+/* Expert-routed product: the plain product above, once per (token, routing slot),
+ * with the expert the slot names.  Reading taken: the page gives only the shape of
+ * the routed step (K = 2048, 256 experts, 6 active per token); each expert is a
+ * complete NVFP4 matrix with its own per-tensor scale, and an expert index outside
+ * the table selects nothing (NaN marks the row). */
+void nvqo_matmul_nvfp4_routed(const uint8_t* codes, const uint8_t* scales, const float* w_scales,
+                              const int32_t* ids, int64_t E, int64_t A,
+                              const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K,
+                              const int64_t* cols, int64_t ncols,
+                              float* y, double* abs_wa)
+{
+    if (!cols)
+        ncols = N;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t a = 0; a < A; ++a) {
+            int64_t job = m * A + a;
+            int32_t e = ids[job];
+            float* yj = y + job * ncols;
+            double* aj = abs_wa ? abs_wa + job * ncols : NULL;
+            if (e < 0 || e >= E) {
+                for (int64_t j = 0; j < ncols; ++j) {
+                    yj[j] = NAN;
+                    if (aj)
+                        aj[j] = 0.0;
+                }
+                continue;
+            }
+            nvqo_matmul_nvfp4(codes + e * N * K, scales + e * N * (K / 16), w_scales[e],
+                              q + m * K, d16 + m * (K / 32), 1, N, K, cols, ncols, yj, aj);
+        }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Q4_1 x Q8_0                                                                */
 /* ------------------------------------------------------------------------- */

@@ -75,6 +75,20 @@ void nvqo_matmul_nvfp4(const uint8_t* codes, const uint8_t* scales, float w_scal
                        const int64_t* cols, int64_t ncols,
                        float* y, double* abs_wa);
 
+/* Expert-routed product (the "mul_mat_id" step that the NVFP4 handoff page's
+ * "Next steps" names for a mixture-of-experts shape): E expert matrices, and for
+ * every token m and routing slot a, the product of token m with expert ids[m][a].
+ * codes [E][N][K], scales [E][N][K/16], w_scales [E], ids [M][A] (int32),
+ * q [M][K], d16 [M][K/32].  y [M][A][ncols] and abs_wa (nullable) as for
+ * nvqo_matmul_nvfp4 per (m, a).  An id outside [0, E) selects no weights: its y row
+ * is NaN and its abs_wa row 0. */
+void nvqo_matmul_nvfp4_routed(const uint8_t* codes, const uint8_t* scales, const float* w_scales,
+                              const int32_t* ids, int64_t E, int64_t A,
+                              const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K,
+                              const int64_t* cols, int64_t ncols,
+                              float* y, double* abs_wa);
+
 /* ---- Q4_1 weights ---------------------------------------------------------- */
 
 /* qw [N][K] one byte per weight (0..15); dw, mw [N][K/32] fp16 bits; W = d*q + m.

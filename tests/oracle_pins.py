@@ -259,6 +259,40 @@ def battery(o) -> list[tuple[str, bool, str]]:
     ok13 &= (ysub[:, 0] == y1[:, 2]).all() and (ysub[:, 1] == y1[:, 0]).all()
     pin("matmul_nvfp4_special_cases", ok13, f"y={y[0]} closed={closed}")
 
+    # P16: expert-routed product against float64 dequantize-then-matmul per (token,
+    # slot); an out-of-range id gives a NaN row; relabelling the experts (storage order
+    # permuted, ids mapped) changes nothing
+    r = _rng(18)
+    E, A, M, N, K = 4, 3, 2, 5, 128
+    codes = r.integers(0, 16, (E, N, K), dtype=np.uint8)
+    ee = r.integers(-4, 5, (E, N, K // 16))
+    mm = r.integers(0, 8, (E, N, K // 16))
+    scales = (((ee + 7) << 3) | mm).astype(np.uint8)
+    wsc = r.uniform(0.5, 2.0, E).astype(np.float32)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    q, d16, _ = o.quantize_q8_0(x)
+    ids = np.array([[2, 0, 2], [3, 1, 7]], np.int32)       # a repeated expert; 7 is invalid
+    y, awa = o.matmul_nvfp4_routed(codes, scales, wsc, ids, q, d16)
+    Ad = np.repeat(f16_bits_to_f64(d16), 32, axis=1) * q.astype(np.float64)
+    Etab = np.array([e2m1_ref(c) for c in range(16)])
+    ok16 = True
+    for mi in range(M):
+        for a in range(A):
+            e = int(ids[mi, a])
+            if not 0 <= e < E:
+                ok16 &= bool(np.isnan(y[mi, a]).all()) and not awa[mi, a].any()
+                continue
+            Wd = np.float64(wsc[e]) * np.repeat(ue4m3_ref_table()[scales[e]], 16, axis=1) * Etab[codes[e]]
+            yref = Wd @ Ad[mi]
+            ok16 &= bool((np.abs(y[mi, a].astype(np.float64) - yref) <= np.spacing(np.abs(yref).astype(np.float32))).all())
+            ok16 &= bool(np.allclose(awa[mi, a], np.abs(Wd) @ np.abs(Ad[mi]), rtol=1e-12, atol=0))
+    perm = np.array([3, 0, 1, 2])                            # new slot i holds old expert perm[i]
+    inv = np.argsort(perm)
+    ids_p = np.where((ids >= 0) & (ids < E), inv[np.clip(ids, 0, E - 1)], ids).astype(np.int32)
+    y_p, _ = o.matmul_nvfp4_routed(codes[perm], scales[perm], wsc[perm], ids_p, q, d16)
+    ok16 &= bool(((y_p == y) | (np.isnan(y_p) & np.isnan(y))).all())
+    pin("matmul_nvfp4_routed_bruteforce_and_relabel", ok16)
+
     # P14/P15: Q4_1
     r = _rng(17)
     M, N, K = 3, 5, 128

@@ -21,10 +21,14 @@ MUTANTS = {
     "act_scale_index": ("a[k] = nvqo_f16_to_f64(d16[k / 32]) * (double)q[k];", "a[k] = nvqo_f16_to_f64(d16[k / 16 % (K / 32)]) * (double)q[k];"),
     "weight_scale_index": ("w[k] = (double)w_scale * nvqo_ue4m3(scales[k / 16]) * nvqo_e2m1(codes[k]);",
                            "w[k] = (double)w_scale * nvqo_ue4m3(scales[k / 32]) * nvqo_e2m1(codes[k]);"),
+    "routed_token_row": ("q + m * K, d16 + m * (K / 32), 1, N, K, cols, ncols, yj, aj);",
+                         "q, d16 + m * (K / 32), 1, N, K, cols, ncols, yj, aj);"),
+    "routed_expert_scale": ("scales + e * N * (K / 16), w_scales[e],", "scales + e * N * (K / 16), w_scales[a % E],"),
+    "routed_expert_codes": ("nvqo_matmul_nvfp4(codes + e * N * K,", "nvqo_matmul_nvfp4(codes + (E - 1 - e) * N * K,"),
     "q4_1_offset_dropped": ("w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k] + nvqo_f16_to_f64(mw[k / 32]);",
                             "w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k];"),
-    "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* ----",
-                           "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* ----"),
+    "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed",
+                           "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed"),
 }
 
 
