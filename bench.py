@@ -349,7 +349,50 @@ def time_extras():
             us = _event_time(lambda: nvq.nvq_gemm_q4_1(w, q, d, b, y), 20)
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
             out["q4_1_gemm_M512_N4096_K4096"] = dict(us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS)
+    out["moe_routed_gemv"] = time_moe()
     return out
+
+
+def time_moe(steps=400):
+    """Expert-routed decode step: 256 NVFP4 experts of N = K = 2048 (604 MB, more than
+    the 256 MB Infinity Cache), one token, 6 distinct experts per step drawn afresh
+    for every step (ids resident on the device before timing).  16 distinct experts
+    are generated and copied into the 256 expert slots (distinct HBM buffers)."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    wl = synth.WORKLOADS["moe"]
+    E, A, N, K = wl["experts"], wl["active"], wl["N"], wl["K"]
+    eb = nvfp4_bytes(N, K)
+    w = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+    wsc = np.empty(E, np.float32)
+    for e in range(16):
+        codes, scales, s = synth.nvfp4_weights(N, K, synth.seed_for("moe", "w", e), "uniform")
+        w[e * eb:(e + 1) * eb].copy_(dev_tensor(nvq.nvq_pack_nvfp4(codes, scales)))
+        wsc[e] = s
+    for e in range(16, E):
+        w[e * eb:(e + 1) * eb].copy_(w[(e % 16) * eb:(e % 16 + 1) * eb])
+        wsc[e] = wsc[e % 16]
+    wsc_d = torch.from_numpy(wsc).cuda()
+    ids = torch.from_numpy(synth.expert_ids(steps, A, E, synth.seed_for("moe", "ids"))).cuda()
+    x = dev_tensor(synth.activations(1, K, synth.seed_for("moe", "x")))
+    q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    d = torch.empty((1, K // 32), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, A, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_quantize_act_q8_0(x, q, d)
+    it = iter(range(10 ** 9))
+
+    def step():
+        s = next(it) % steps
+        nvq.nvq_gemv_nvfp4_routed(w, wsc_d, ids[s:s + 1], q, d, y)
+
+    us = _event_time(step, steps)
+    byts = A * eb + K * 17 // 16 + A * N * 4
+    return dict(us_avg=us, GBps=byts / (us * 1e-6) / 1e9, frac=byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                experts=E, active=A, N=N, K=K, weight_bytes_per_step=A * eb,
+                note="one launch per step (grid 128 tiles x 6 experts); each step's 6 experts drawn afresh")
 
 
 def _event_time(fn, reps):

@@ -30,7 +30,7 @@ NVQ_GEMV_MAX_M = 15
 EXPORTS = (
     "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_gemm_workspace_bytes",
     "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_dot4",
-    "nvq_gemm_nvfp4", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
+    "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
     "nvq_status_str", "nvq_last_error",
 )
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "nvq_quantize_act_q8_0": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_nvfp4_dot4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
+            "nvq_gemv_nvfp4_routed": (ctypes.c_int, [P, P, P, I64, I64, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_gemv_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
@@ -213,6 +214,23 @@ def nvq_gemv_nvfp4(w, w_scale: float, q, d_f16, y, stream=None) -> None:
     _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
     _check(lib().nvq_gemv_nvfp4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
                                 _stream(stream, y)), "nvq_gemv_nvfp4")
+
+
+def nvq_gemv_nvfp4_routed(w, w_scales, ids, q, d_f16, y, stream=None) -> None:
+    """w: uint8, n_experts packed [N][K] matrices back to back; w_scales float32
+    [n_experts]; ids int32 [M, n_active]; q, d_f16 [M, K]; y float32 [M, n_active, N]."""
+    import torch
+
+    M, K = _acts(q, d_f16)
+    E = w_scales.shape[0]
+    _need(w_scales, torch.float32, (E,), "w_scales")
+    A = ids.shape[1] if ids is not None and ids.dim() == 2 else -1
+    _need(ids, torch.int32, (M, A), "ids")
+    N = y.shape[2]
+    _need(y, torch.float32, (M, A, N), "y")
+    _weights(w, E * nvq_nvfp4_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_nvfp4_routed(_ptr(w), _ptr(w_scales), _ptr(ids), E, A, _ptr(q), _ptr(d_f16), M, N, K,
+                                       _ptr(y), _stream(stream, y)), "nvq_gemv_nvfp4_routed")
 
 
 def nvq_gemv_nvfp4_dot4(w, w_scale: float, q, d_f16, y, stream=None) -> None:

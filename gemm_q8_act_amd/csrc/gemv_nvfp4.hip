@@ -60,12 +60,12 @@ __host__ __device__ constexpr int64_t gemv_tab_bytes(int64_t nch) { return (nch 
 __host__ __device__ constexpr int64_t gemv_dtab_off(int64_t nch) { return gemv_tab_bytes(nch) + 16; }
 __host__ __device__ constexpr int64_t gemv_red_off(int64_t nch) { return gemv_dtab_off(nch) + (nch * 4 + 4) * 4; }
 
+// One 16-row tile of the product (the body of both kernels below).
 template <int MODE, bool DEBUG, int W, int P>
-__global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
-                                                            int K, const int8_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ d16,
-                                                            float w_scale, float* __restrict__ y,
-                                                            int32_t* __restrict__ isums) {
+__device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ w, int64_t N, int K,
+                                          const int8_t* __restrict__ q, const uint16_t* __restrict__ d16,
+                                          float w_scale, float* __restrict__ y, int32_t* __restrict__ isums,
+                                          int64_t tile) {
   constexpr int NT = 64 * W;
   extern __shared__ __align__(16) uint8_t smem[];
   const int nch = (K + 127) >> 7;
@@ -78,7 +78,6 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
   float* red = reinterpret_cast<float*>(smem + gemv_red_off(nch));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t tile = blockIdx.x;
   const int64_t ntiles = (N + 15) >> 4;
   const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
   const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
@@ -206,6 +205,43 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
   }
 }
 
+template <int MODE, bool DEBUG, int W, int P>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
+                                                            int K, const int8_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ d16,
+                                                            float w_scale, float* __restrict__ y,
+                                                            int32_t* __restrict__ isums) {
+  gemv_tile<MODE, DEBUG, W, P>(w, N, K, q, d16, w_scale, y, isums, blockIdx.x);
+}
+
+// Expert-routed form (the "mul_mat_id" step of a mixture-of-experts layer; "HANDOFF:
+// flint CPU optimization (Q4_1 + NVFP4)", section 7 "Open items / next steps", item 1):
+// grid.y enumerates the (token, routing slot) jobs, job = m * A + a.  The block reads
+// its expert id once (wavefront-uniform), and runs the same tile on that expert's
+// packed matrix, its per-tensor scale and token m's activations, into y[job][N].  An
+// id outside [0, E) reads no weights and writes NaN to its rows.
+template <int W, int P>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_routed_kernel(const uint8_t* __restrict__ w,
+                                                                   int64_t expert_bytes,
+                                                                   const float* __restrict__ w_scales,
+                                                                   const int32_t* __restrict__ ids, int E,
+                                                                   int A, int64_t N, int K,
+                                                                   const int8_t* __restrict__ q,
+                                                                   const uint16_t* __restrict__ d16,
+                                                                   float* __restrict__ y) {
+  const int job = blockIdx.y;
+  const int e = ids[job];
+  float* yj = y + (int64_t)job * N;
+  if (e < 0 || e >= E) {
+    const int64_t r = (int64_t)blockIdx.x * 16 + threadIdx.x;
+    if (threadIdx.x < 16 && r < N) yj[r] = __builtin_nanf("");
+    return;
+  }
+  const int64_t m = job / A;
+  gemv_tile<0, false, W, P>(w + (int64_t)e * expert_bytes, N, K, q + m * K, d16 + m * (K >> 5), w_scales[e], yj,
+                            nullptr, blockIdx.x);
+}
+
 // Launch shape: 4 wavefronts x 5-chunk batches, or 8 x 3 for long rows over few tiles
 // (the down projection: K = 17408 over 320 tiles), where more wavefronts per tile keep
 // more loads in flight per block.
@@ -244,6 +280,35 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
   if (mode != 0) return launch_gemv<1, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
   if (gemv_wide(ntiles, nch)) return launch_gemv<0, false, 8, 3>(w, w_scale, q, d16, N, K, y, isums, stream);
   return launch_gemv<0, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
+}
+
+template <int W, int P>
+static hipError_t launch_routed(const uint8_t* w, const float* w_scales, const int32_t* ids, int64_t E,
+                                int64_t A, int64_t M, const int8_t* q, const uint16_t* d16, int64_t N,
+                                int64_t K, float* y, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nch = (K + 127) / 128;
+  const size_t lds = (size_t)(gemv_red_off(nch) + W * 64 * 4);
+  const int64_t expert_bytes = ntiles * nch * (1024 + 128);
+  auto fn = gemv_nvfp4_routed_kernel<W, P>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles, (unsigned)(M * A)), dim3(64 * W), lds, stream, w, expert_bytes,
+                     w_scales, ids, (int)E, (int)A, N, (int)K, q, d16, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_nvfp4_routed(const uint8_t* w, const float* w_scales, const int32_t* ids, int64_t E,
+                                    int64_t A, int64_t M, const int8_t* q, const uint16_t* d16, int64_t N,
+                                    int64_t K, float* y, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nch = (K + 127) / 128;
+  if (gemv_wide(ntiles * M * A, nch))
+    return launch_routed<8, 3>(w, w_scales, ids, E, A, M, q, d16, N, K, y, stream);
+  return launch_routed<4, 5>(w, w_scales, ids, E, A, M, q, d16, N, K, y, stream);
 }
 
 }  // namespace nvq

@@ -207,6 +207,26 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
   return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
 }
 
+nvq_status nvq_gemv_nvfp4_routed(const void* w, const float* w_scales, const int32_t* ids, int64_t n_experts,
+                                 int64_t n_active, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N,
+                                 int64_t K, float* y, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_nvfp4_routed"));
+  if (!w_scales || !ids) return fail(NVQ_ERR_NULL, "nvq_gemv_nvfp4_routed: NULL pointer");
+  if (!aligned(w_scales, 4) || !aligned(ids, 4))
+    return fail(NVQ_ERR_ALIGN, "nvq_gemv_nvfp4_routed: w_scales and ids must be 4-byte aligned");
+  if (n_experts < 1 || n_experts >= kMaxDim || n_active < 1 || n_active > 65535)
+    return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4_routed: n_experts=%lld n_active=%lld out of range", (long long)n_experts,
+                (long long)n_active);
+  NVQ_TRY(check_dims(M, N, K, 64, 1, 65535 / n_active));
+  if (!gemv_fits_lds(K)) return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4_routed: K=%lld too large for the LDS activation table", (long long)K);
+  if ((int64_t)nvq_nvfp4_weight_bytes(N, K) > (int64_t)INT64_MAX / n_experts)
+    return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4_routed: expert table too large");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_nvfp4_routed(static_cast<const uint8_t*>(w), w_scales, ids, n_experts, n_active, M, q,
+                                                d_f16, N, K, y, (hipStream_t)stream),
+                  "gemv_nvfp4_routed");
+}
+
 nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                                int64_t M, int64_t N, int64_t K, float* y, void* stream) {
   NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_nvfp4_dot4"));

@@ -22,6 +22,11 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q,
                                        const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                                        hipStream_t stream);
+// NVFP4 expert-routed decode GEMV: E packed expert matrices back to back, ids [M][A]
+// (device int32), y [M][A][N]; one launch, grid.y = M * A jobs.
+hipError_t launch_gemv_nvfp4_routed(const uint8_t* w, const float* w_scales, const int32_t* ids, int64_t E,
+                                    int64_t A, int64_t M, const int8_t* q, const uint16_t* d16, int64_t N,
+                                    int64_t K, float* y, hipStream_t stream);
 // LDS bytes the decode GEMV needs for a row length K.
 size_t gemv_lds_bytes(int64_t K);
 

@@ -17,6 +17,11 @@ workloads this library targets):
 * Q4_1 weights: codes uniform 0..15, per 32 weights d ~ U[1e-3, 2e-2] and
   m ~ U[-0.1, 0], drawn in float32 and stored as binary16 (numpy's
   round-to-nearest-even conversion).
+* Expert routing (the mixture-of-experts decode step): 256 experts of shape
+  N = K = 2048 (the pages give K = 2048, 256 experts, 6 active; N is taken equal to
+  K), NVFP4 weights as above with a per-expert scale uniform in [0.5, 2]; each
+  token's 6 experts are distinct and uniform over the 256 (a top-6 router over
+  random logits).
 """
 from __future__ import annotations
 
@@ -31,6 +36,7 @@ WORKLOADS = {
     "prefill": dict(Ms=(256, 2048), N=17408, K=5120),
     "q4_1": dict(Ms=(1, 512), N=4096, K=4096),
     "stack": dict(Ms=(1, 8), layers=64, mats=LAYER),
+    "moe": dict(M=1, experts=256, active=6, N=2048, K=2048),
 }
 
 
@@ -75,9 +81,15 @@ def q4_1_weights(N: int, K: int, seed: int):
     return qw, d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)
 
 
+def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
+    """int32 [M, A]: for each token A distinct experts, uniform over E."""
+    r = rng(seed)
+    return np.stack([r.choice(E, size=A, replace=False) for _ in range(M)]).astype(np.int32)
+
+
 def seed_for(workload: str, tensor: str, index: int = 0) -> int:
     """Fixed, documented seed per (workload, tensor, index)."""
     base = {"gemv_small": 100, "layer": 200, "prefill": 300, "q4_1": 400, "stack": 500,
-            "test": 900}[workload]
+            "moe": 600, "test": 900}[workload]
     tag = sum((i + 1) * ord(ch) for i, ch in enumerate(tensor)) % 997
     return base * 1_000_003 + tag * 1009 + index

@@ -168,6 +168,25 @@ nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q,
                                const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
                                float* y, void* stream);
 
+/* Expert-routed decode GEMV: the "mul_mat_id" step of a mixture-of-experts layer
+ * ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 7 "Open items / next
+ * steps", item 1, which names the shape K = 2048, 256 experts, 6 active per token).
+ * w: n_experts packed NVFP4 [N][K] matrices back to back, expert e at byte offset
+ * e * nvq_nvfp4_weight_bytes(N, K) (device, 16-byte aligned); w_scales: float32
+ * [n_experts] per-tensor scales (device); ids: int32 [M][n_active] expert indices
+ * (device, e.g. written by a router kernel); q, d_f16: Q8_0 activations [M][K];
+ * y: float32 [M][n_active][N] (overwritten): y[m][a] = the nvq_gemv_nvfp4 result of
+ * token m against expert ids[m][a] (same kernel, same error bound).  An id outside
+ * [0, n_experts) is not an error the host can see: its y row is set to NaN and no
+ * weights are read for it.  1 <= n_active, M * n_active <= 65535, K % 64 == 0 and
+ * K within the decode GEMV's LDS limit (NVQ_ERR_SHAPE otherwise).  Each (token,
+ * slot) streams its expert's weights on its own; tokens that share an expert are
+ * not merged. */
+nvq_status nvq_gemv_nvfp4_routed(const void* w, const float* w_scales, const int32_t* ids,
+                                 int64_t n_experts, int64_t n_active, const int8_t* q,
+                                 const uint16_t* d_f16, int64_t M, int64_t N, int64_t K, float* y,
+                                 void* stream);
+
 /* Prefill GEMM (many tokens take the tiled form): M >= 16, N >= 1,
  * K % 64 == 0; arguments as for the GEMV plus a device workspace (16-byte aligned,
  * contents on entry irrelevant, overwritten) of at least

@@ -223,9 +223,10 @@ void nvqo_matmul_nvfp4(const uint8_t* codes, const uint8_t* scales, float w_scal
     free(a);
 }
 
-/* Expert-routed product: the plain product above, once per (token, routing slot),
- * with the expert the slot names.  Reading taken: the page gives only the shape of
- * the routed step (K = 2048, 256 experts, 6 active per token); each expert is a
+/* Expert-routed product ([HANDOFF] section 7 "Open items / next steps", item 1):
+ * the plain product above, once per (token, routing slot), with the expert the slot
+ * names.  Reading taken: the page gives only the shape of the routed step (K = 2048,
+ * 256 experts, 6 active per token); each expert is a
  * complete NVFP4 matrix with its own per-tensor scale, and an expert index outside
  * the table selects nothing (NaN marks the row). */
 void nvqo_matmul_nvfp4_routed(const uint8_t* codes, const uint8_t* scales, const float* w_scales,

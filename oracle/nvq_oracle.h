@@ -75,8 +75,8 @@ void nvqo_matmul_nvfp4(const uint8_t* codes, const uint8_t* scales, float w_scal
                        const int64_t* cols, int64_t ncols,
                        float* y, double* abs_wa);
 
-/* Expert-routed product (the "mul_mat_id" step that the NVFP4 handoff page's
- * "Next steps" names for a mixture-of-experts shape): E expert matrices, and for
+/* Expert-routed product (the "mul_mat_id" step of a mixture-of-experts layer,
+ * [HANDOFF] section 7 "Open items / next steps", item 1): E expert matrices, and for
  * every token m and routing slot a, the product of token m with expert ids[m][a].
  * codes [E][N][K], scales [E][N][K/16], w_scales [E], ids [M][A] (int32),
  * q [M][K], d16 [M][K/32].  y [M][A][ncols] and abs_wa (nullable) as for

@@ -182,6 +182,22 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_debug_isums(1, 0, A16, A16, 1, 8, 48, A16, None) == -2
 
 
+def test_routed_gemv_validation_without_gpu():
+    """Argument checks of the expert-routed GEMV return before any device call."""
+    L = nvq.lib()
+    f = L.nvq_gemv_nvfp4_routed
+    #   w    scales ids  E  A  q    d    M  N  K   y
+    assert f(A16, A16, A16, 0, 6, A16, A16, 1, 8, 64, A16, None) == -2       # no experts
+    assert f(A16, A16, A16, 4, 0, A16, A16, 1, 8, 64, A16, None) == -2       # no routing slot
+    assert f(A16, A16, A16, 4, 6, A16, A16, 1, 8, 48, A16, None) == -2       # K % 64
+    assert f(A16, A16, A16, 4, 6, A16, A16, 20000, 8, 64, A16, None) == -2   # M * n_active > 65535
+    assert f(A16, A16, A16, 4, 6, A16, A16, 1, 8, 98304, A16, None) == -2    # beyond the LDS table
+    assert f(A16, None, A16, 4, 6, A16, A16, 1, 8, 64, A16, None) == -1      # w_scales
+    assert f(A16, A16, None, 4, 6, A16, A16, 1, 8, 64, A16, None) == -1      # ids
+    assert f(A16, A16, A2, 4, 6, A16, A16, 1, 8, 64, A16, None) == -4        # ids alignment
+    assert f(A16, A16, A16, 4, 6, A16, A16, 1, 8, 64, MIS, None) == -4       # y alignment
+
+
 def test_status_strings():
     for s, name in [(0, "NVQ_OK"), (-1, "NVQ_ERR_NULL"), (-2, "NVQ_ERR_SHAPE"), (-3, "NVQ_ERR_RANGE"),
                     (-4, "NVQ_ERR_ALIGN"), (-5, "NVQ_ERR_DEVICE"), (-6, "NVQ_ERR_HIP"),

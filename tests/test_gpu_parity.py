@@ -343,6 +343,59 @@ def test_gemm_split_kernel_activation_range():
     assert (yh[rows] == yr[rows]).all()
 
 
+def _experts(E, N, K, seed):
+    """E seeded NVFP4 experts: logical codes/scales [E, N, K], per-expert scales, and
+    the packed table on the GPU (expert e at e * nvq_nvfp4_weight_bytes(N, K))."""
+    torch = torch_dev()
+    ws = [synth.nvfp4_weights(N, K, seed + e, "uniform") for e in range(E)]
+    codes = np.stack([c for c, _, _ in ws])
+    scales = np.stack([s for _, s, _ in ws])
+    wsc = np.array([v for _, _, v in ws], np.float32)
+    w = to_dev(np.concatenate([nvq.nvq_pack_nvfp4(c, s) for c, s, _ in ws]))
+    return codes, scales, wsc, w, torch.from_numpy(wsc).cuda()
+
+
+@pytest.mark.parametrize("E,A,M,N,K", [(5, 2, 3, 100, 320), (3, 4, 2, 33, 640), (8, 6, 1, 300, 2048),
+                                       (4, 3, 1, 40, 17408)])
+def test_gemv_routed(oracle, E, A, M, N, K):
+    """Expert-routed GEMV: every (token, slot) against the oracle's routed product,
+    with repeated experts; an out-of-range id gives a NaN row and leaves the others."""
+    say(f"routed gemv E={E} A={A} M={M} N={N} K={K}")
+    torch = torch_dev()
+    codes, scales, wsc, w, wsc_d = _experts(E, N, K, 700 + N)
+    ids = synth.rng(701 + N).integers(0, E, (M, A)).astype(np.int32)
+    ids[0, 0] = ids[0, A - 1] if A > 1 else ids[0, 0]       # one repeated expert
+    if M > 1:
+        ids[M - 1, A - 1] = E                                  # out of range
+    x = synth.activations(M, K, 702 + N)
+    q, d, _ = quantize_gpu(x)
+    y = torch.full((M, A, N), 7.0, dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4_routed(w, wsc_d, torch.from_numpy(ids).cuda(), q, d, y)
+    yo, awa = oracle.matmul_nvfp4_routed(codes, scales, wsc, ids, host(q), host(d).view(np.uint16))
+    yh = host(y)
+    bad = (ids < 0) | (ids >= E)
+    assert np.isnan(yh[bad]).all() and np.isnan(yo[bad]).all()
+    check_y(yh[~bad], yo[~bad], awa[~bad], f"routed E={E} A={A} M={M} N={N} K={K}")
+
+
+def test_gemv_routed_expert_shape(oracle):
+    """The routed step at the expert shape N = K = 2048, 6 active of 16 experts, two
+    tokens, sampled output columns."""
+    say("routed gemv at the expert shape")
+    torch = torch_dev()
+    E, A, M, N, K = 16, 6, 2, 2048, 2048
+    codes, scales, wsc, w, wsc_d = _experts(E, N, K, synth.seed_for("moe", "w"))
+    ids = synth.expert_ids(M, A, E, synth.seed_for("moe", "ids"))
+    x = synth.activations(M, K, synth.seed_for("moe", "x"))
+    q, d, _ = quantize_gpu(x)
+    y = torch.empty((M, A, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4_routed(w, wsc_d, torch.from_numpy(ids).cuda(), q, d, y)
+    cols = sample_cols(N, 40, 3)
+    yo, awa = oracle.matmul_nvfp4_routed(codes, scales, wsc, ids, host(q), host(d).view(np.uint16), cols=cols)
+    check_y(host(y)[:, :, cols].reshape(M * A, -1), yo.reshape(M * A, -1), awa.reshape(M * A, -1),
+            "routed expert shape")
+
+
 @pytest.mark.parametrize("K", [65536, 98304])
 def test_gemv_long_rows(oracle, K):
     """K = 65536 keeps the decode GEMV's activation table in LDS; K = 98304 does not
