@@ -55,6 +55,7 @@ def parse():
     p.add_argument("--stack", action="store_true", help="64-layer stack instead of one layer")
     p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
+    p.add_argument("--only-moe", action="store_true", help="time only the expert-routed decode step (profiling)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="for rocprofv3 --pmc runs: one 256 MiB device copy (calibration) and 4 gate+up "
                         "GEMV launches over distinct weight copies, then exit")
@@ -605,6 +606,9 @@ def main():
     if args.only_gemm:
         for M in (2048, 256):
             log(json.dumps(time_gemm(M)))
+        return
+    if args.only_moe:
+        log(json.dumps(time_moe()))
         return
 
     log("decode layer ...")
