@@ -444,7 +444,10 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   };
 
   // pipeline over stages t0 .. t1-1 (every global load index is clamped to the range,
-  // so no load is conditional and the in-order load counter stays exact)
+  // so no load is conditional and the in-order load counter stays exact).  The loop
+  // body has no branch: after the last stage the staging writes a clamped copy to the
+  // free buffer and the fragment read takes it, both unused; one basic block lets the
+  // scheduler spread the staging and the fragment reads between the MFMAs.
   Stage x;
   gload(t0, x);
   lstore(0, x);
@@ -455,11 +458,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   for (int t = t0; t < t1; ++t) {
     const int b = (t - t0) & 1;
     fread(b, 1, f1);
-    if (t + 1 < t1) lstore(b ^ 1, x);  // stage t+1, loaded one stage ago
+    lstore(b ^ 1, x);                  // stage t+1, loaded one stage ago
     mfmas(f0);
     gload(min(t + 2, t1 - 1), x);
     __syncthreads();                   // stage t+1 visible; stage t-1's buffer free
-    if (t + 1 < t1) fread(b ^ 1, 0, f0);
+    fread(b ^ 1, 0, f0);
     mfmas(f1);
   }
 
