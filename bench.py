@@ -252,9 +252,10 @@ def sleep_cycles_per_ms():
     return _SLEEP_RATE[0]
 
 
-def hbm_ceiling():
-    """Measured ceilings (the roofline-by-measurement method): device-to-device copy
-    of 1 GiB (read + write bytes) and a read-only reduction over 1 GiB."""
+def torch_reference_rates():
+    """Context, not ceilings: torch's own device-to-device copy of 1 GiB (read + write
+    bytes) and float32 sum over 1 GiB (read bytes).  A tuned streaming read reaches
+    more than either on this chip (about 7 TB/s with 16-byte non-temporal loads)."""
     import torch
 
     n = 1 << 30
@@ -277,8 +278,9 @@ def hbm_ceiling():
     torch.cuda.synchronize()
     copy_s = e0.elapsed_time(e1) / 5 * 1e-3
     read_s = e1.elapsed_time(e2) / 5 * 1e-3
-    return dict(copy_GBps=2 * n / copy_s / 1e9, read_GBps=n / read_s / 1e9,
-                note="1 GiB device copy (read+write bytes) and float32 sum reduction (read bytes), torch kernels")
+    return dict(copy_GBps=2 * n / copy_s / 1e9, sum_read_GBps=n / read_s / 1e9,
+                note="torch kernels on 1 GiB: device copy (read+write bytes), float32 sum (read bytes); "
+                     "not a ceiling")
 
 
 def time_gemm(M, N=17408, K=5120, reps=10, warm=3):
@@ -629,7 +631,7 @@ def main():
                             graph=not args.eager),
                 roofline=roofline, per_kernel=per)
     if not args.no_extras:
-        line["hbm_ceiling"] = hbm_ceiling()
+        line["torch_reference_rates"] = torch_reference_rates()
     if not args.no_gemm:
         log("prefill gemm ...")
         g = {f"M{M}": time_gemm(M) for M in (2048, 256)}
