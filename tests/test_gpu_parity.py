@@ -297,6 +297,67 @@ def test_determinism_and_guard_bands(oracle):
     assert (host(y2) == 4.0 * host(y1)).all()
 
 
+def test_side_stream_and_graph_replay():
+    """Every compute entry on a non-default stream, then the same sequence captured in a
+    HIP graph and replayed three times, with eager work on the inputs between replays:
+    each replay equals the eager run bit for bit (no memset nodes are involved)."""
+    say("side stream + graph replay")
+    torch = torch_dev()
+    N, K = 300, 640
+    codes, scales, ws = synth.nvfp4_weights(N, K, 61, "uniform")
+    w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    experts = [synth.nvfp4_weights(N, K, 62 + e, "uniform") for e in range(3)]
+    wr = to_dev(np.concatenate([nvq.nvq_pack_nvfp4(c, s) for c, s, _ in experts]))
+    wsc = torch.from_numpy(np.array([v for _, _, v in experts], np.float32)).cuda()
+    ids = torch.from_numpy(np.array([[2, 0]], np.int32)).cuda()
+    xs = {M: to_dev(synth.activations(M, K, 70 + M, outliers=True)) for M in (1, 8, 80)}
+    qd = {M: (torch.empty((M, K), dtype=torch.int8, device="cuda"),
+              torch.empty((M, K // 32), dtype=torch.int16, device="cuda")) for M in xs}
+    ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
+    yr = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
+    wsp = torch.empty(max(nvq.lib().nvq_gemm_workspace_bytes(0, 80, N, K), 16), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+
+    def seq():
+        for M, x in xs.items():
+            q, d = qd[M]
+            nvq.nvq_quantize_act_q8_0(x, q, d)
+            if M < 16:
+                nvq.nvq_gemv_nvfp4(w, ws, q, d, ys[M])
+            else:
+                nvq.nvq_gemm_nvfp4(w, ws, q, d, ys[M], workspace=wsp)
+        nvq.nvq_gemv_nvfp4_routed(wr, wsc, ids, qd[1][0], qd[1][1], yr)
+
+    def snapshot():
+        return [host(ys[M]).copy() for M in xs] + [host(yr).copy()]
+
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        seq()
+    s.synchronize()
+    eager = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            seq()
+    s.synchronize()
+    saved = {M: x.clone() for M, x in xs.items()}
+    for rep in range(3):
+        for M in xs:                      # eager work between replays, then inputs restored
+            xs[M].mul_(-1.0)
+        seq()
+        torch.cuda.synchronize()
+        for M in xs:
+            xs[M].copy_(saved[M])
+        for y in list(ys.values()) + [yr]:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snapshot(), eager):
+            assert (a.view(np.uint32) == b.view(np.uint32)).all(), f"replay {rep}"
+
+
 def test_gemm_split_kernel_determinism_and_guard_bands(oracle):
     """M > 64 with K-split parts: bitwise-identical repeats, nothing written outside y."""
     say("gemm (M > 64, K-split) determinism + guard bands")
