@@ -349,9 +349,13 @@ def time_extras():
             out["q4_1_gemv_N4096_K4096"] = dict(us_avg=us, GBps=byts / (us * 1e-6) / 1e9,
                                                 note="10.5 MB of weights: Infinity-Cache resident across repeats")
         else:
-            us = _event_time(lambda: nvq.nvq_gemm_q4_1(w, q, d, b, y), 20)
+            need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_1, M, N, K)
+            wsq = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            us = _event_time(lambda: nvq.nvq_gemm_q4_1(w, q, d, b, y, workspace=wsq), 20)
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            out["q4_1_gemm_M512_N4096_K4096"] = dict(us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS)
+            out["q4_1_gemm_M512_N4096_K4096"] = dict(
+                us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
+                note="fp16 MFMA, three passes per product (weight and activation each split in two terms)")
     out["moe_routed_gemv"] = time_moe()
     return out
 

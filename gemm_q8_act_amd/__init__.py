@@ -280,6 +280,10 @@ def nvq_gemm_q4_1(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
     _need(y, torch.float32, (M, N), "y")
     _need(bsum16, torch.int16, (M, K // 16), "bsum16")
     _weights(w, nvq_q4_1_weight_bytes(N, K), "w")
+    if workspace is None:
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_Q4_1, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvq_gemm_q4_1(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
                                _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q4_1")

@@ -112,10 +112,10 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K) {
 }
 
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  // NVFP4 with M > 64: fp32 partial tiles of the K-split work items that fill the
-  // last round over the compute units.  Q4_1 keeps all partial sums on chip.
-  if (fmt != NVQ_FMT_NVFP4 || M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
-  return nvq::gemm_nvfp4_workspace(M, N, K);
+  // M > 64: fp32 partial tiles of the K-split work items that fill the last round
+  // over the compute units.
+  if ((fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1) || M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
+  return fmt == NVQ_FMT_NVFP4 ? nvq::gemm_nvfp4_workspace(M, N, K) : nvq::gemm_q4_1_workspace(M, N, K);
 }
 
 nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3, int64_t N, int64_t K,
@@ -266,10 +266,8 @@ nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
   if (!aligned(bsum16, 2)) return fail(NVQ_ERR_ALIGN, "nvq_gemv_q4_1: bsum16 must be 2-byte aligned");
   NVQ_TRY(check_dims(M, N, K, 32, 1, NVQ_GEMV_MAX_M));
   NVQ_TRY(check_device());
-  const uint8_t* wb = static_cast<const uint8_t*>(w);
-  if (M == 1)
-    return launched(nvq::launch_gemv_q4_1_m1(wb, q, d_f16, bsum16, N, K, y, nullptr, (hipStream_t)stream), "gemv_q4_1");
-  return launched(nvq::launch_gemm_q4_1(wb, q, d_f16, bsum16, M, N, K, y, nullptr, (hipStream_t)stream), "gemv_q4_1 (tiled)");
+  return launched(nvq::launch_gemv_q4_1(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        (hipStream_t)stream), "gemv_q4_1");
 }
 
 nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
@@ -281,8 +279,10 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
   NVQ_TRY(check_dims(M, N, K, 32, 16, kMaxM));
   const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_Q4_1, M, N, K);
   if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_q4_1: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q4_1: workspace must be 16-byte aligned");
   NVQ_TRY(check_device());
-  return launched(nvq::launch_gemm_q4_1(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr, (hipStream_t)stream), "gemm_q4_1");
+  return launched(nvq::launch_gemm_q4_1(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q4_1");
 }
 
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,
@@ -299,16 +299,15 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   hipStream_t st = (hipStream_t)stream;
   if (path == NVQ_PATH_GEMM) {
     if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_nvfp4");
-    return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemm_q4_1");
+    return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_1");
   }
+  if (fmt == NVQ_FMT_Q4_1) return launched(nvq::launch_gemv_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_1");
   const int64_t per_m = N * (K / 16);
-  if (fmt == NVQ_FMT_NVFP4 && !gemv_fits_lds(K))
+  if (!gemv_fits_lds(K))
     return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the decode GEMV kernels", (long long)K);
   for (int64_t m = 0; m < M; ++m) {
-    hipError_t e = (fmt == NVQ_FMT_NVFP4)
-        ? nvq::launch_gemv_nvfp4_m1(wb, 1.0f, q + m * K, nullptr, N, K, nullptr, isums + m * per_m,
-                                    path == NVQ_PATH_GEMV_DOT4 ? 1 : 0, st)
-        : nvq::launch_gemv_q4_1_m1(wb, q + m * K, nullptr, nullptr, N, K, nullptr, isums + m * per_m, st);
+    hipError_t e = nvq::launch_gemv_nvfp4_m1(wb, 1.0f, q + m * K, nullptr, N, K, nullptr, isums + m * per_m,
+                                             path == NVQ_PATH_GEMV_DOT4 ? 1 : 0, st);
     if (e != hipSuccess) return fail(NVQ_ERR_HIP, "debug gemv launch: %s", hipGetErrorString(e));
   }
   g_err[0] = '\0';

@@ -38,14 +38,18 @@ hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              int32_t* isums, float* workspace, hipStream_t stream);
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
 
-// Q4_1, M == 1, integer-dot path.
-hipError_t launch_gemv_q4_1_m1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
-                               const int16_t* bsum16, int64_t N, int64_t K, float* y,
-                               int32_t* isums, hipStream_t stream);
-
-// Q4_1, MFMA tiled path (any M >= 1).
-hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+// Q4_1 GEMV (any M; the API uses it for M <= 15), integer-dot path; with isums the
+// debug sums [M][N][K/16].
+hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, hipStream_t stream);
+
+// Q4_1, MFMA paths (any M >= 1): the tiled kernel for M <= 64 or K % 64 != 0, the
+// two-term fp16 kernel otherwise, which needs gemm_q4_1_workspace(M, N, K) bytes of
+// device workspace (may be 0).
+hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, float* workspace, hipStream_t stream);
+size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K);
 
 }  // namespace nvq

@@ -7,13 +7,20 @@
 //     sum_k w*a = da * (d * sum_k c*q + m * sum_k q),
 // the second sum being the block's activation code sum (two bsum16 values).
 //
-// GEMV (M == 1): same lane mapping as the NVFP4 GEMV -- a unit is one 32-weight
+// GEMV (M <= 15): same lane mapping as the NVFP4 GEMV -- a unit is one 32-weight
 // block (16 B of codes + one 4-byte (d, m) pair), the codes are unsigned nibbles
-// used directly as int8 by v_dot4_i32_i8.
+// used directly as int8 by v_dot4_i32_i8.  A wavefront holds its rows' weights in
+// registers and walks the tokens, reading each token's activations (cache-resident)
+// once per row group.
 //
-// GEMM: like the NVFP4 tiled kernel with a 32-k stage; codes become exact
-// integer-valued fp16, P = sum c*q over the block is an exact fp32 integer
-// (|P| <= 32*15*127 = 60960), and per element acc += da*(d*P + m*bsum32).
+// GEMM, M <= 64 (and K % 64 != 0): like the NVFP4 tiled kernel with a 32-k stage;
+// codes become exact integer-valued fp16, P = sum c*q over the block is an exact fp32
+// integer (|P| <= 32*15*127 = 60960), and per element acc += da*(d*P + m*bsum32).
+//
+// GEMM, M > 64 and K % 64 == 0: both operands as two binary16 terms, so the matrix
+// core accumulates whole rows (see gemm_q4_1_big_kernel below).
+#include <algorithm>
+
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
@@ -21,6 +28,8 @@ namespace nvq {
 
 constexpr int kQ41MaxUPL = 10;
 __host__ __device__ constexpr int q41_rg(int upl) { return upl >= 7 ? 1 : (upl >= 4 ? 2 : 4); }
+// tokens whose activations a GEMV wavefront holds at once (8 UPL registers each)
+__host__ __device__ constexpr int q41_tb(int upl) { return upl <= 2 ? 4 : (upl <= 4 ? 2 : 1); }
 
 // 8 unsigned 4-bit codes (byte i: code 2i low nibble, 2i+1 high) dotted with the
 // matching even / odd activation codes.
@@ -30,14 +39,14 @@ __device__ __forceinline__ int dot8_u4(uint32_t c, uint32_t qe, uint32_t qo, int
   return acc;
 }
 
-template <int LPR, int UPL, bool DEBUG>
+template <int LPR, int UPL, bool MULTI, bool DEBUG>
 __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __restrict__ w,
                                                            int64_t N, int K,
                                                            const int8_t* __restrict__ q,
                                                            const uint16_t* __restrict__ d16,
                                                            const int16_t* __restrict__ bsum16,
                                                            float* __restrict__ y,
-                                                           int32_t* __restrict__ isums) {
+                                                           int32_t* __restrict__ isums, int M) {
   constexpr int RG = q41_rg(UPL);
   constexpr int RPG = 64 / LPR;
   constexpr int RPW = RPG * RG;
@@ -69,54 +78,71 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
     }
   }
 
-  uint32_t qe[UPL][4], qo[UPL][4];
-  float da[UPL], bs[UPL];
+  // tokens in groups of TB: the activation loads of a group are issued together,
+  // so a group costs one cache round trip; tokens past M load token M-1 and store
+  // nothing
+  constexpr int TB = MULTI ? q41_tb(UPL) : 1;
+  if (!MULTI && !DEBUG) M = 1;  // the single-token production instance
+  for (int m0 = 0; m0 < M; m0 += TB) {
+    uint32_t qe[TB][UPL][4], qo[TB][UPL][4];
+    float da[TB][UPL], bs[TB][UPL];
 #pragma unroll
-  for (int j = 0; j < UPL; ++j) {
-    const int u = sub + LPR * j;
-    if (u < units) {
-      const uint4 a = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u);
-      const uint4 b = *reinterpret_cast<const uint4*>(q + 32 * (int64_t)u + 16);
-      split_even_odd(a.x, a.y, qe[j][0], qo[j][0]);
-      split_even_odd(a.z, a.w, qe[j][1], qo[j][1]);
-      split_even_odd(b.x, b.y, qe[j][2], qo[j][2]);
-      split_even_odd(b.z, b.w, qe[j][3], qo[j][3]);
-      if (!DEBUG) {
-        da[j] = f16_bits_to_f32(d16[u]);
-        bs[j] = (float)((int)bsum16[2 * u] + (int)bsum16[2 * u + 1]);
-      } else {
-        da[j] = bs[j] = 0.0f;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t m = min(m0 + tb, M - 1);
+      const int8_t* __restrict__ qm = q + m * K;
+#pragma unroll
+      for (int j = 0; j < UPL; ++j) {
+        const int u = sub + LPR * j;
+        if (u < units) {
+          const uint4 a = *reinterpret_cast<const uint4*>(qm + 32 * (int64_t)u);
+          const uint4 b = *reinterpret_cast<const uint4*>(qm + 32 * (int64_t)u + 16);
+          split_even_odd(a.x, a.y, qe[tb][j][0], qo[tb][j][0]);
+          split_even_odd(a.z, a.w, qe[tb][j][1], qo[tb][j][1]);
+          split_even_odd(b.x, b.y, qe[tb][j][2], qo[tb][j][2]);
+          split_even_odd(b.z, b.w, qe[tb][j][3], qo[tb][j][3]);
+          if (!DEBUG) {
+            da[tb][j] = f16_bits_to_f32(d16[m * nb + u]);
+            bs[tb][j] = (float)((int)bsum16[m * 2 * nb + 2 * u] + (int)bsum16[m * 2 * nb + 2 * u + 1]);
+          } else {
+            da[tb][j] = bs[tb][j] = 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qe[tb][j][i] = qo[tb][j][i] = 0u;
+          da[tb][j] = bs[tb][j] = 0.0f;
+        }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) qe[j][i] = qo[j][i] = 0u;
-      da[j] = bs[j] = 0.0f;
     }
-  }
 
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int64_t row = row0 + r * RPG + slot;
-    float acc = 0.0f;
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t m = m0 + tb;
+      if (TB > 1 && m >= M) break;
 #pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-      const int i0 = dot8_u4(cw[r][j].y, qe[j][1], qo[j][1], dot8_u4(cw[r][j].x, qe[j][0], qo[j][0], 0));
-      const int i1 = dot8_u4(cw[r][j].w, qe[j][3], qo[j][3], dot8_u4(cw[r][j].z, qe[j][2], qo[j][2], 0));
-      if (DEBUG) {
-        const int u = sub + LPR * j;
-        if (row < N && u < units) {
-          isums[row * (K >> 4) + 2 * u] = i0;
-          isums[row * (K >> 4) + 2 * u + 1] = i1;
+      for (int r = 0; r < RG; ++r) {
+        const int64_t row = row0 + r * RPG + slot;
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < UPL; ++j) {
+          const int i0 = dot8_u4(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], dot8_u4(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0));
+          const int i1 = dot8_u4(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], dot8_u4(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0));
+          if (DEBUG) {
+            const int u = sub + LPR * j;
+            if (row < N && u < units) {
+              isums[(m * N + row) * (K >> 4) + 2 * u] = i0;
+              isums[(m * N + row) * (K >> 4) + 2 * u + 1] = i1;
+            }
+          } else {
+            const float dw = f16_bits_to_f32((uint16_t)(pw[r][j] & 0xFFFFu));
+            const float mw = f16_bits_to_f32((uint16_t)(pw[r][j] >> 16));
+            acc = fmaf(da[tb][j], fmaf(dw, (float)(i0 + i1), mw * bs[tb][j]), acc);
+          }
         }
-      } else {
-        const float dw = f16_bits_to_f32((uint16_t)(pw[r][j] & 0xFFFFu));
-        const float mw = f16_bits_to_f32((uint16_t)(pw[r][j] >> 16));
-        acc = fmaf(da[j], fmaf(dw, (float)(i0 + i1), mw * bs[j]), acc);
+        if (!DEBUG) {
+          acc = group_sum<LPR>(acc);
+          if (sub == 0 && row < N) y[m * N + row] = acc;
+        }
       }
-    }
-    if (!DEBUG) {
-      acc = group_sum<LPR>(acc);
-      if (sub == 0 && row < N) y[row] = acc;
     }
   }
 }
@@ -327,22 +353,28 @@ __global__ __launch_bounds__(256) void gemm_q4_1_kernel(const uint8_t* __restric
 
 namespace {
 typedef void (*gemv_q41_fn)(const uint8_t*, int64_t, int, const int8_t*, const uint16_t*,
-                            const int16_t*, float*, int32_t*);
-template <int LPR, bool DEBUG>
+                            const int16_t*, float*, int32_t*, int);
+template <int LPR, bool MULTI, bool DEBUG>
 gemv_q41_fn pick_q41(int upl) {
   switch (upl) {
-    case 1: return gemv_q4_1_m1_kernel<LPR, 1, DEBUG>;
-    case 2: return gemv_q4_1_m1_kernel<LPR, 2, DEBUG>;
-    case 3: return gemv_q4_1_m1_kernel<LPR, 3, DEBUG>;
-    case 4: return gemv_q4_1_m1_kernel<LPR, 4, DEBUG>;
-    case 5: return gemv_q4_1_m1_kernel<LPR, 5, DEBUG>;
-    case 6: return gemv_q4_1_m1_kernel<LPR, 6, DEBUG>;
-    case 7: return gemv_q4_1_m1_kernel<LPR, 7, DEBUG>;
-    case 8: return gemv_q4_1_m1_kernel<LPR, 8, DEBUG>;
-    case 9: return gemv_q4_1_m1_kernel<LPR, 9, DEBUG>;
-    case 10: return gemv_q4_1_m1_kernel<LPR, 10, DEBUG>;
+    case 1: return gemv_q4_1_m1_kernel<LPR, 1, MULTI, DEBUG>;
+    case 2: return gemv_q4_1_m1_kernel<LPR, 2, MULTI, DEBUG>;
+    case 3: return gemv_q4_1_m1_kernel<LPR, 3, MULTI, DEBUG>;
+    case 4: return gemv_q4_1_m1_kernel<LPR, 4, MULTI, DEBUG>;
+    case 5: return gemv_q4_1_m1_kernel<LPR, 5, MULTI, DEBUG>;
+    case 6: return gemv_q4_1_m1_kernel<LPR, 6, MULTI, DEBUG>;
+    case 7: return gemv_q4_1_m1_kernel<LPR, 7, MULTI, DEBUG>;
+    case 8: return gemv_q4_1_m1_kernel<LPR, 8, MULTI, DEBUG>;
+    case 9: return gemv_q4_1_m1_kernel<LPR, 9, MULTI, DEBUG>;
+    case 10: return gemv_q4_1_m1_kernel<LPR, 10, MULTI, DEBUG>;
     default: return nullptr;
   }
+}
+// one token (or the debug sums) at a time, or TB tokens per pass
+template <int LPR>
+gemv_q41_fn pick_q41_for(int upl, bool multi, bool debug) {
+  if (debug) return pick_q41<LPR, false, true>(upl);
+  return multi ? pick_q41<LPR, true, false>(upl) : pick_q41<LPR, false, false>(upl);
 }
 template <int BM, int BN, bool DEBUG>
 hipError_t launch_q41_tile(const uint8_t* w, const int8_t* q, const uint16_t* d16,
@@ -352,6 +384,13 @@ hipError_t launch_q41_tile(const uint8_t* w, const int8_t* q, const uint16_t* d1
   hipLaunchKernelGGL((gemm_q4_1_kernel<BM, BN, DEBUG>), grid, dim3(256), 0, stream, w, N, (int)K,
                      q, d16, bsum16, M, y, isums);
   return hipGetLastError();
+}
+hipError_t launch_q41_tiled(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream) {
+  if (isums) return launch_q41_tile<16, 64, true>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  if (M <= 16) return launch_q41_tile<16, 128, false>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  return launch_q41_tile<64, 128, false>(w, q, d16, bsum16, M, N, K, y, isums, stream);
 }
 }  // namespace
 
@@ -377,34 +416,438 @@ static void gemv_m1_config(int64_t K, int* lpr_out, int* upl_out) {
   *upl_out = best_upl;
 }
 
-hipError_t launch_gemv_q4_1_m1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
-                               const int16_t* bsum16, int64_t N, int64_t K, float* y,
-                               int32_t* isums, hipStream_t stream) {
+hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream) {
   const bool debug = isums != nullptr;
   int lpr = 0, upl = 0;
   gemv_m1_config(K, &lpr, &upl);
   if (lpr == 0) {
     // very long rows: the tiled kernel handles any K
-    return launch_gemm_q4_1(w, q, d16, bsum16, 1, N, K, y, isums, stream);
+    return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
   }
   gemv_q41_fn fn = nullptr;
-  if (lpr == 64) fn = debug ? pick_q41<64, true>(upl) : pick_q41<64, false>(upl);
-  if (lpr == 32) fn = debug ? pick_q41<32, true>(upl) : pick_q41<32, false>(upl);
-  if (lpr == 16) fn = debug ? pick_q41<16, true>(upl) : pick_q41<16, false>(upl);
+  const bool multi = M > 1;
+  if (lpr == 64) fn = pick_q41_for<64>(upl, multi, debug);
+  if (lpr == 32) fn = pick_q41_for<32>(upl, multi, debug);
+  if (lpr == 16) fn = pick_q41_for<16>(upl, multi, debug);
   if (!fn) return hipErrorInvalidValue;
   const int64_t rows_per_block = 4 * (64 / lpr) * q41_rg(upl);
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, stream, w, N, (int)K, q, d16, bsum16,
-                     y, isums);
+                     y, isums, (int)M);
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Two-term fp16 Q4_1 kernel (K % 64 == 0).  The weight w = d*c + m (binary16 d, m;
+// c in 0..15) is formed in fp32 as w' = 2^s * w (one rounding) and split into
+// hi = fp16(w') and lo = fp16(w' - hi).  The power of two 2^s is chosen per weight row
+// (over the k range of the work item) from the bound |m| + 15|d| of its blocks so
+// that |w'| < 2^15: hi never overflows and lo is a normal binary16 number unless
+// |w'| < 2^-3, so hi + lo = w' to 2^-23 |w'|, or to 2^-25 absolute, i.e. 2^-39 of the
+// row's largest weight.  The activation is split exactly as in the NVFP4 large-M
+// kernel (d*q = hi + lo).  The matrix core then accumulates whole rows of
+//     W'.A = Wh.Ah + Wh.Al + Wl.Ah (+ Wl.Al, dropped: at most 2^-22 |W.A|),
+// three MFMA passes, with no per-block vector work; the offset term m * sum(a) is
+// inside W, and the result is multiplied by 2^-s (exact).  Error per output: a few
+// 2^-22 of sum |w*a| plus float32 accumulation, far inside the 1e-5 bound.
+//
+// Block: 512 threads, WN x WM wavefronts, each a (32 TN) x (32 TM) tile of
+// v_mfma_f32_32x32x16_f16 products; block tile BN = 32 WN TN weight rows by
+// BM = 32 WM TM tokens.  LDS holds two 64-k stages: the two weight planes (fp16 hi,
+// lo), raw int8 activation codes and their binary16 scales; each wavefront splits its
+// activation fragments in registers.  Work items and the ordered K-split reduction
+// follow the NVFP4 large-M kernel.
+// ---------------------------------------------------------------------------------
+namespace {
+constexpr int kQThreads = 512, kQSlots = 256, kQMaxSplit = 16;
+constexpr int kQLRW = 72;  // halves per LDS weight row (64 k + 8 pad)
+constexpr int kQLRA = 72;  // bytes per LDS activation row (64 codes + 8 pad)
+
+template <int WN_, int WM_, int TN_, int TM_>
+struct Q41Cfg {
+  static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_;
+  static constexpr int BN = 32 * WN * TN, BM = 32 * WM * TM;
+  static constexpr int kAcc = 16 * TN * TM;  // fp32 accumulators per thread
+  static constexpr int kStageW = BN * kQLRW * 2, kStageA = BM * kQLRA, kStageD = BM * 4;
+  static constexpr int kStage = 2 * kStageW + kStageA + kStageD;
+  static constexpr int kLds = 2 * kStage + BN * 4;  // + 2^-s of each weight row
+  static constexpr int CPT = BN * 64 / kQThreads;   // weight codes staged per thread
+  static constexpr int TPR = 64 / CPT;              // threads per weight row
+  static constexpr int ABT = BM * 64 / kQThreads;   // activation bytes staged per thread
+  static constexpr int APR = 64 / ABT;              // threads per activation row
+  static_assert(WN * WM * 64 == kQThreads, "8 wavefronts");
+  static_assert(CPT == 16 || CPT == 32, "one 32-block per thread and stage");
+  static_assert(ABT == 8 || ABT == 16 || ABT == 32, "activation staging width");
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+using Q41Big = Q41Cfg<2, 4, 2, 2>;  // 128 weight rows x 256 tokens
+using Q41Mid = Q41Cfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
+
+struct Q41Plan {
+  int64_t tiles_n, tiles, full, split_tiles;
+  int split;
+  int stages;
+};
+
+template <class C>
+Q41Plan q41_plan(int64_t M, int64_t N, int64_t K) {
+  Q41Plan p;
+  p.tiles_n = (N + C::BN - 1) / C::BN;
+  p.tiles = p.tiles_n * ((M + C::BM - 1) / C::BM);
+  p.stages = (int)(K / 64);
+  const int64_t r = p.tiles % kQSlots;
+  p.split = 1;
+  if (r != 0) p.split = (int)std::min<int64_t>({kQSlots / r, (int64_t)kQMaxSplit, (int64_t)p.stages});
+  if (p.split < 2) p.split = 1;
+  p.split_tiles = p.split > 1 ? r : 0;
+  p.full = p.tiles - p.split_tiles;
+  return p;
+}
+
+// which kernel runs a Q4_1 GEMM of this shape (the GEMV kernel falls back to the
+// tiled one for rows longer than 20480)
+constexpr int kQ41GemvMaxM = 16;
+enum Q41Path { kQ41Gemv, kQ41Tiled, kQ41Mid, kQ41Big };
+Q41Path q41_path(int64_t M, int64_t K) {
+  if (M <= kQ41GemvMaxM) return kQ41Gemv;
+  if (K % 64 != 0) return kQ41Tiled;
+  return M <= 64 ? kQ41Mid : kQ41Big;
+}
+
+template <int NW>
+struct Words {
+  uint32_t v[NW];
+};
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words(const void* p) {
+  Words<NW> r;
+  if constexpr (NW == 2) {
+    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+    r.v[0] = t[0];
+    r.v[1] = t[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h) {
+      const u32x4 t = reinterpret_cast<const u32x4*>(p)[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.v[4 * h + e] = t[e];
+    }
+  }
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ void store_words(void* p, const Words<NW>& w) {
+  if constexpr (NW == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{w.v[0], w.v[1]};
+  } else {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h)
+      reinterpret_cast<u32x4*>(p)[h] = u32x4{w.v[4 * h], w.v[4 * h + 1], w.v[4 * h + 2], w.v[4 * h + 3]};
+  }
+}
+}  // namespace
+
+size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K) {
+  const Q41Path path = q41_path(M, K);
+  if (path != kQ41Mid && path != kQ41Big) return 0;
+  const Q41Plan p = path == kQ41Big ? q41_plan<Q41Big>(M, N, K) : q41_plan<Q41Mid>(M, N, K);
+  const int acc = path == kQ41Big ? Q41Big::kAcc : Q41Mid::kAcc;
+  return (size_t)(p.split_tiles * p.split) * kQThreads * acc * sizeof(float);
+}
+
+template <class C>
+__global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                                 const int8_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ d16, int64_t M,
+                                                                 float* __restrict__ y, float* __restrict__ part_ws,
+                                                                 Q41Plan plan) {
+  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
+  constexpr int LRW = kQLRW, LRA = kQLRA, CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+  const int64_t item = blockIdx.x;
+  int64_t tile, part = -1;
+  int t0 = 0, t1 = plan.stages;
+  if (item < plan.full) {
+    tile = item;
+  } else {
+    const int64_t it = item - plan.full;
+    tile = plan.full + it / plan.split;
+    part = it % plan.split;
+    t0 = (int)(part * plan.stages / plan.split);
+    t1 = (int)((part + 1) * plan.stages / plan.split);
+  }
+  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
+  const int64_t crow = K >> 1;  // code bytes per weight row
+  const int nb32 = K >> 5;
+  const uint32_t* __restrict__ dmw = reinterpret_cast<const uint32_t*>(w + N * crow);
+
+  // staging task of this thread: CPT weight codes of row wrow at k-offset CPT wq of
+  // the stage, all in one 32-block, with that block's (d, m); ABT activation codes of
+  // row arow; for tid < 2 BM one activation scale.  Rows beyond N / M are clamped to
+  // valid memory and their results never stored.
+  const int wrow = tid / TPR, wq = tid % TPR;
+  const int64_t wr = min(n0 + wrow, N - 1);
+  const uint8_t* __restrict__ wbase = w + wr * crow + (CPT / 2) * wq;
+  const uint32_t* __restrict__ dmbase = dmw + wr * nb32 + (CPT * wq) / 32;
+  const int arow = tid / APR, aoff = ABT * (tid % APR);
+  const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
+  const bool dtask = tid < 2 * BM;
+  const int drow = tid % BM, dblk = (tid / BM) & 1;
+  const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm, dr; };
+
+  // row scale 2^s: the largest bound |m| + 15|d| of this row's blocks in [t0, t1),
+  // taken by the TPR threads that stage the row, placed in [2^14, 2^15).  A zero row
+  // takes s = 0; a non-finite d or m gives a non-finite row anyway.
+  float bmax = 0.0f;
+  const uint32_t* __restrict__ dmrow = dmw + wr * nb32;
+#pragma unroll 4
+  for (int b = 2 * t0 + wq; b < 2 * t1; b += TPR) {
+    const uint32_t v = dmrow[b];
+    bmax = fmaxf(bmax, fabsf(f16_bits_to_f32((uint16_t)(v >> 16))) + 15.0f * fabsf(f16_bits_to_f32((uint16_t)(v & 0xFFFFu))));
+  }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
+  if constexpr (TPR == 4) bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
+  // a nonzero bound is at least 2^-24 (binary16's least magnitude), so it is a
+  // normal float: bmax in [2^(E-127), 2^(E-126)) with E its biased exponent
+  int rexp = 0;
+  if (bmax > 0.0f && bmax <= 3.0e38f) rexp = 15 - ((int)((__float_as_uint(bmax) >> 23) & 0xFF) - 126);
+  const float rscale = ldexpf(1.0f, rexp);
+  if (wq == 0) reinterpret_cast<float*>(smem + 2 * C::kStage)[wrow] = ldexpf(1.0f, -rexp);
+
+  auto gload = [&](int t, Stage& x) {
+    x.wc = load_words<CPT / 8>(wbase + (int64_t)t * 32);
+    x.dm = dmbase[2 * t];
+    x.a = load_words<ABT / 4>(abase + 64 * t);
+    x.dr = dtask ? dbase[2 * t] : 0u;
+  };
+  auto lstore = [&](int b, const Stage& x) {
+    uint8_t* st = smem + b * C::kStage;
+    _Float16* lh = reinterpret_cast<_Float16*>(st);
+    _Float16* ll = reinterpret_cast<_Float16*>(st + C::kStageW);
+    uint8_t* la = st + 2 * C::kStageW;
+    uint16_t* ld = reinterpret_cast<uint16_t*>(st + 2 * C::kStageW + C::kStageA);
+    const float dw = rscale * f16_bits_to_f32((uint16_t)(x.dm & 0xFFFFu));
+    const float mw = rscale * f16_bits_to_f32((uint16_t)(x.dm >> 16));
+#pragma unroll
+    for (int h = 0; h < CPT / 8; ++h) {
+      const uint32_t cw = x.wc.v[h];
+      half8_t vh, vl;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float c = (float)((cw >> (4 * j)) & 0xFu);  // byte j/2: code 2i low nibble, 2i+1 high
+        const float wf = fmaf(dw, c, mw);
+        const _Float16 hi = (_Float16)wf;
+        vh[j] = hi;
+        vl[j] = (_Float16)(wf - (float)hi);
+      }
+      *reinterpret_cast<half8_t*>(lh + wrow * LRW + CPT * wq + 8 * h) = vh;
+      *reinterpret_cast<half8_t*>(ll + wrow * LRW + CPT * wq + 8 * h) = vl;
+    }
+    store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
+    if (dtask) ld[2 * drow + dblk] = (uint16_t)x.dr;
+  };
+
+  floatx16 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = floatx16{};
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  struct Frag { half8_t ah[2][TN], al[2][TN]; uint2 raw[2][TM]; uint32_t dd[TM]; };
+  auto fread = [&](int b, int u, Frag& f) {
+    const uint8_t* st = smem + b * C::kStage;
+    const _Float16* lh = reinterpret_cast<const _Float16*>(st);
+    const _Float16* ll = reinterpret_cast<const _Float16*>(st + C::kStageW);
+    const uint8_t* la = st + 2 * C::kStageW;
+    const uint16_t* ld = reinterpret_cast<const uint16_t*>(st + 2 * C::kStageW + C::kStageA);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const int off = (wn * (32 * TN) + 32 * i + fr) * LRW + 32 * u + 16 * h + fk;
+        f.ah[h][i] = *reinterpret_cast<const half8_t*>(lh + off);
+        f.al[h][i] = *reinterpret_cast<const half8_t*>(ll + off);
+      }
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int r = wm * (32 * TM) + 32 * j + fr;
+      f.dd[j] = ld[2 * r + u];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
+    }
+  };
+  auto mfmas = [&](const Frag& f) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      half8_t bh[TM], bl[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)f.dd[j]);
+        const half2_t d2 = {dh, dh};
+        half2_t a0, a1, c0, c1;
+        i8x4_to_f16x4(f.raw[h][j].x, a0, a1);
+        i8x4_to_f16x4(f.raw[h][j].y, c0, c1);
+        const half2_t h0 = a0 * d2, h1 = a1 * d2, h2 = c0 * d2, h3 = c1 * d2;
+        const half2_t l0 = __builtin_elementwise_fma(a0, d2, -h0);
+        const half2_t l1 = __builtin_elementwise_fma(a1, d2, -h1);
+        const half2_t l2 = __builtin_elementwise_fma(c0, d2, -h2);
+        const half2_t l3 = __builtin_elementwise_fma(c1, d2, -h3);
+        bh[j] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+        bl[j] = half8_t{l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bl[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[h][i], bh[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  };
+
+  // pipeline over stages t0 .. t1-1; loads clamped, loop body branch-free (after the
+  // last stage the staging writes a clamped copy nobody reads)
+  Stage x;
+  gload(t0, x);
+  lstore(0, x);
+  gload(min(t0 + 1, t1 - 1), x);
+  __syncthreads();
+  Frag f0, f1;
+  fread(0, 0, f0);
+  for (int t = t0; t < t1; ++t) {
+    const int b = (t - t0) & 1;
+    fread(b, 1, f1);
+    lstore(b ^ 1, x);
+    mfmas(f0);
+    gload(min(t + 2, t1 - 1), x);
+    __syncthreads();
+    fread(b ^ 1, 0, f0);
+    mfmas(f1);
+  }
+
+  // undo the row scales (the first barrier of the pipeline ordered their stores)
+  const float* rinv = reinterpret_cast<const float*>(smem + 2 * C::kStage);
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const floatx4 r = *reinterpret_cast<const floatx4*>(rinv + wn * (32 * TN) + 32 * i + 8 * e4 + 4 * (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[i][j][4 * e4 + rr] *= r[rr];
+    }
+  if (part >= 0) {
+    float* dst = part_ws + ((item - plan.full) * C::kAcc) * kQThreads + tid;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dst[((i * TM + j) * 16 + e) * kQThreads] = acc[i][j][e];
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = m0 + wm * (32 * TM) + 32 * j + fr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * e4 + 4 * (lane >> 5);
+        const floatx4 v = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2], acc[i][j][4 * e4 + 3]};
+        if ((N & 3) == 0 && n + 3 < N) {
+          *reinterpret_cast<floatx4*>(y + m * N + n) = v;
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (n + rr < N) y[m * N + n + rr] = v[rr];
+        }
+      }
+  }
+}
+
+// Sums the K parts of every split tile in part order (p = 0, 1, ...) and stores the
+// tile; block (split tile, group of 8 accumulator slots), as for the NVFP4 kernel.
+template <class C>
+__global__ __launch_bounds__(512) void gemm_q4_1_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
+                                                               int64_t M, float* __restrict__ y, Q41Plan plan) {
+  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM, kGroups = C::kAcc / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave / WM, wm = wave % WM;
+  const int64_t st = blockIdx.x / kGroups;
+  const int grp = blockIdx.x % kGroups;
+  const int ij = grp >> 1, i = ij / TM, j = ij % TM, e0 = 8 * grp;
+  const int64_t tile = plan.full + st;
+  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
+  const float* src = part_ws + (st * plan.split * C::kAcc + e0) * kQThreads + tid;
+  float v[8][kQMaxSplit];
+#pragma unroll
+  for (int p = 0; p < kQMaxSplit; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e][p] = p < plan.split ? src[((int64_t)p * C::kAcc + e) * kQThreads] : 0.0f;
+  const int64_t m = m0 + wm * (32 * TM) + 32 * j + (lane & 31);
+  if (m >= M) return;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float o[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      float s = v[4 * h + rr][0];
+#pragma unroll
+      for (int p = 1; p < kQMaxSplit; ++p)
+        if (p < plan.split) s += v[4 * h + rr][p];
+      o[rr] = s;
+    }
+    const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
+    if ((N & 3) == 0 && n + 3 < N) {
+      *reinterpret_cast<floatx4*>(y + m * N + n) = floatx4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (n + rr < N) y[m * N + n + rr] = o[rr];
+    }
+  }
+}
+
+namespace {
+template <class C>
+hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
+                            int64_t K, float* y, float* workspace, hipStream_t stream) {
+  const Q41Plan plan = q41_plan<C>(M, N, K);
+  if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (ea != hipSuccess) return ea;
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  hipLaunchKernelGGL(gemm_q4_1_f16x2_kernel<C>, dim3((unsigned)items), dim3(kQThreads), C::kLds, stream, w, N,
+                     (int)K, q, d16, M, y, workspace, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.split_tiles == 0) return e;
+  hipLaunchKernelGGL(gemm_q4_1_reduce_kernel<C>, dim3((unsigned)(plan.split_tiles * (C::kAcc / 8))),
+                     dim3(kQThreads), 0, stream, workspace, N, M, y, plan);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
-                            int32_t* isums, hipStream_t stream) {
-  if (isums) return launch_q41_tile<16, 64, true>(w, q, d16, bsum16, M, N, K, y, isums, stream);
-  if (M <= 16) return launch_q41_tile<16, 128, false>(w, q, d16, bsum16, M, N, K, y, isums, stream);
-  return launch_q41_tile<64, 128, false>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+                            int32_t* isums, float* workspace, hipStream_t stream) {
+  if (isums) return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  switch (q41_path(M, K)) {
+    case kQ41Gemv: return launch_gemv_q4_1(w, q, d16, bsum16, M, N, K, y, nullptr, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big>(w, q, d16, M, N, K, y, workspace, stream);
+    case kQ41Mid: return launch_q41_f16x2<Q41Mid>(w, q, d16, M, N, K, y, workspace, stream);
+    default: return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  }
 }
 
 }  // namespace nvq

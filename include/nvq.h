@@ -115,10 +115,10 @@ size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
 
 /* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt
- * is NVQ_FMT_*): for NVFP4 with M > 64, the fp32 partial tiles of the K-split work
- * items that even out the last round of 256 x 256 tiles over the chip's 256
- * compute units (at most 64 MiB); otherwise 0.  Pure function.  When it is 0 the
- * workspace pointer may be NULL. */
+ * is NVQ_FMT_*): with M > 64 and K % 64 == 0, the fp32 partial tiles of the K-split
+ * work items that even out the last round of tiles (NVFP4 256 x 256, Q4_1 128 x 256)
+ * over the chip's 256 compute units (at most 64 MiB); otherwise 0.  Pure function.
+ * When it is 0 the workspace pointer may be NULL. */
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ---- packers (host memory in, host memory out) ------------------------------ */

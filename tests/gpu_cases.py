@@ -76,10 +76,12 @@ class NvCase:
 
 
 class Q41Case:
-    def __init__(self, M, N, K, seed):
+    """Seeded Q4_1 case; ``weights`` = (qw, dw, mw) and ``x`` replace the seeded ones."""
+
+    def __init__(self, M, N, K, seed, weights=None, x=None):
         self.M, self.N, self.K = M, N, K
-        self.qw, self.dw, self.mw = synth.q4_1_weights(N, K, seed)
-        self.x = synth.activations(M, K, seed + 1)
+        self.qw, self.dw, self.mw = weights if weights is not None else synth.q4_1_weights(N, K, seed)
+        self.x = x if x is not None else synth.activations(M, K, seed + 1)
         self.w = to_dev(nvq.nvq_pack_q4_1(self.qw, self.dw, self.mw))
         self.q, self.d, self.b = quantize_gpu(self.x)
         self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)

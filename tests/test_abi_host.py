@@ -65,7 +65,17 @@ def test_sizes():
     assert ws(nvq.NVQ_FMT_NVFP4, 65, 33, 64) == 0                               # one stage: no split
     assert ws(nvq.NVQ_FMT_NVFP4, 4096, 4096, 1024) == 0                         # 256 tiles: full rounds
     assert ws(nvq.NVQ_FMT_NVFP4, 64, 17408, 5120) == 0                          # M <= 64: tile kernel
-    assert ws(nvq.NVQ_FMT_Q4_1, 2048, 4096, 4096) == 0
+    # Q4_1, split up to 16 ways: M > 64 in 128 x 256 tiles with 64 accumulators per
+    # thread, 16 < M <= 64 in 256 x 64 tiles with 32
+    q41_tile, q41_mid = 512 * 64 * 4, 512 * 32 * 4
+    assert ws(nvq.NVQ_FMT_Q4_1, 2048, 4096, 4096) == 0                          # 256 tiles: full rounds
+    assert ws(nvq.NVQ_FMT_Q4_1, 512, 4096, 4096) == 64 * 4 * q41_tile           # 64 tiles, 256 // 64 = 4
+    assert ws(nvq.NVQ_FMT_Q4_1, 300, 19200, 256) == 44 * 4 * q41_tile           # 300 tiles: 44 left, 4 stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 100, 8, 640) == 1 * 10 * q41_tile               # split <= stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 64, 4096, 4096) == 16 * 16 * q41_mid            # 16 tiles of 256 rows
+    assert ws(nvq.NVQ_FMT_Q4_1, 17, 8, 64) == 0                                 # one stage: no split
+    assert ws(nvq.NVQ_FMT_Q4_1, 16, 4096, 4096) == 0                            # M <= 16: tiled kernel
+    assert ws(nvq.NVQ_FMT_Q4_1, 100, 8, 96) == 0                                # K % 64 != 0: tiled kernel
     assert ws(nvq.NVQ_FMT_NVFP4, 2048, 17408, 96) == 0                          # invalid K
 
 
@@ -172,6 +182,8 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, None, 0, None) == -7
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, A16, 16, None) == -7   # too small
     assert L.nvq_gemm_q4_1(A16, A16, A16, A2, 8, 8, 32, A16, None, 0, None) == -2
+    assert L.nvq_gemm_q4_1(A16, A16, A16, A2, 100, 8, 640, A16, None, 0, None) == -7   # K-split parts
+    assert L.nvq_gemm_q4_1(A16, A16, A16, A2, 100, 8, 640, A16, MIS, 1 << 21, None) == -4  # ws alignment
     assert L.nvq_quantize_act_q8_0(A16, 1, 48, A16, A16, None, None) == -2
     assert L.nvq_quantize_act_q8_0(MIS, 1, 64, A16, A16, None, None) == -4
     assert L.nvq_quantize_act_q8_0(None, 1, 64, A16, A16, None, None) == -1

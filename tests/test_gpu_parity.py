@@ -234,7 +234,8 @@ def test_batched_decode_m8_full_size(oracle):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 33, 96), (4, 70, 160), (16, 64, 32),
-                                   (33, 100, 320)])
+                                   (33, 100, 320), (8, 300, 4096), (15, 129, 640), (3, 33, 20480),
+                                   (2, 50, 24576), (1, 40, 24576)])
 def test_q4_1_small(oracle, M, N, K):
     say(f"q4_1 M={M} N={N} K={K}")
     torch = torch_dev()
@@ -257,6 +258,113 @@ def test_q4_1_gemm_full_size(oracle):
     cols = sample_cols(4096, 48, 3)
     yo, awa = c.oracle_y(oracle, cols=cols)
     check_y(host(y)[:, cols], yo, awa, "q4_1 M=512")
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 128, 64), (100, 300, 640), (257, 77, 192), (300, 130, 1024),
+                                   (96, 64, 96), (128, 40, 4096), (17, 300, 640), (40, 77, 192),
+                                   (64, 520, 1024), (50, 64, 96)])
+def test_q4_1_gemm_large_m(oracle, M, N, K):
+    """M > 16: the two-term fp16 kernels (256 x 64 tiles up to M = 64, 128 x 256 above;
+    K % 64 == 0; K-split parts on small grids, ragged N and M tiles, N % 4 != 0) and the
+    tiled kernel (K = 96)."""
+    say(f"q4_1 gemm M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = Q41Case(M, N, K, 53 + M + N)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q4_1 M={M} N={N} K={K}")
+
+
+def test_q4_1_gemm_full_and_split_tiles(oracle):
+    """300 weight tiles: 256 whole-K work items plus 44 tiles split along K."""
+    say("q4_1 gemm M=300 N=19200 K=256")
+    torch = torch_dev()
+    M, N, K = 300, 19200, 256
+    c = Q41Case(M, N, K, 8181)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+    cols = sample_cols(N, 64, 5)
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(host(y)[:, cols], yo, awa, "q4_1 M=300 N=19200")
+
+
+def _q41_extreme_rows(N, K, seed):
+    """Q4_1 weights whose rows span the binary16 range: tiny (subnormal d, m), huge
+    (|d * 15 + m| near 1e6), all-zero, mixed-sign offsets, and ordinary rows."""
+    qw, dw, mw = synth.q4_1_weights(N, K, seed)
+    d = dw.view(np.float16).astype(np.float32)
+    m = mw.view(np.float16).astype(np.float32)
+    d[0], m[0] = 3e-7, -2e-6          # binary16 subnormals
+    d[1], m[1] = 65504.0, -65504.0    # largest finite d and m
+    d[2], m[2] = 0.0, 0.0             # zero row
+    d[3], m[3] = 1e-3, 7.0            # offset far above the code range
+    d[4, ::2], m[4, ::2] = 4000.0, 1e-4  # blocks of very different size in one row
+    d[5], m[5] = 6e-8, 0.0            # least binary16 magnitude
+    return qw, d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(80, 70, 640), (40, 70, 640), (8, 70, 640)])
+def test_q4_1_extreme_weight_rows(oracle, M, N, K):
+    """Per-row weight magnitudes from 6e-8 to 1e6 in one matrix, through both two-term
+    GEMM kernels (M = 80, 40) and the GEMV (M = 8)."""
+    say(f"q4_1 extreme weight rows M={M}")
+    torch = torch_dev()
+    c = Q41Case(M, N, K, 0, weights=_q41_extreme_rows(N, K, 919), x=synth.activations(M, K, 920))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemm_q4_1 if M > nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemv_q4_1)(c.w, c.q, c.d, c.b, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q4_1 extreme rows M={M}")
+    assert (host(y)[:, 2] == 0.0).all()
+
+
+@pytest.mark.parametrize("M", [300, 48])
+def test_q4_1_gemm_split_determinism_and_guard_bands(oracle, M):
+    """Two-term Q4_1 kernels with K-split parts: junk workspace on entry,
+    bitwise-identical repeats, nothing written outside y."""
+    say(f"q4_1 gemm (M={M}, K-split) determinism + guard bands")
+    torch = torch_dev()
+    N, K = 260, 1024
+    c = Q41Case(M, N, K, 4343)
+    need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_1, M, N, K)
+    assert need > 0
+    guard = 4096
+    outs = []
+    for rep in range(2):
+        buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+        y = buf[guard:guard + M * N].view(M, N)
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+        nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y, workspace=ws)
+        torch.cuda.synchronize()
+        b = host(buf)
+        assert (b[:guard] == 12345.0).all() and (b[guard + M * N:] == 12345.0).all()
+        outs.append(b[guard:guard + M * N].copy())
+    assert (outs[0].view(np.uint32) == outs[1].view(np.uint32)).all()
+    yo, awa = c.oracle_y(oracle, cols=np.arange(0, N, 5))
+    check_y(outs[0].reshape(M, N)[:, ::5], yo, awa, "q4_1 split determinism case")
+
+
+@pytest.mark.parametrize("M", [96, 24])
+def test_q4_1_gemm_activation_range(M):
+    """As for NVFP4: rows of the two-term kernels (M > 16) whose scaled activations
+    exceed the binary16 range come out non-finite; every other row is unaffected."""
+    say(f"q4_1 gemm (M={M}) activation range contract")
+    torch = torch_dev()
+    N, K = 64, 128
+    c = Q41Case(M, N, K, 79)
+    x = synth.activations(M, K, 80)
+    x[5, 3] = 1.0e6
+    x2 = x.copy()
+    x2[5] = 0.0
+    ys = []
+    for xx in (x, x2):
+        q, d, b = quantize_gpu(xx)
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        nvq.nvq_gemm_q4_1(c.w, q, d, b, y)
+        ys.append(host(y))
+    assert not np.isfinite(ys[0][5]).all()
+    rows = [r for r in range(M) if r != 5]
+    assert (ys[0][rows] == ys[1][rows]).all()
 
 
 @pytest.mark.parametrize("path", [nvq.NVQ_PATH_GEMV, nvq.NVQ_PATH_GEMM])
