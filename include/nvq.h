@@ -205,7 +205,14 @@ nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const u
 
 /* Q4_1 GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 32 == 0.
  * bsum16 [M][K/16] (from nvq_quantize_act_q8_0) is required: the offset m of each
- * 32-block multiplies the sum of that block's activation codes. */
+ * 32-block multiplies the sum of that block's activation codes.  Same error bound
+ * as the NVFP4 entries.  The GEMM takes a device workspace as nvq_gemm_nvfp4 does,
+ * of nvq_gemm_workspace_bytes(NVQ_FMT_Q4_1, M, N, K) bytes (NULL when that is 0).
+ * For M > 16 with K % 64 == 0 the GEMM forms each weight in two binary16 terms
+ * (after a per-row power-of-two scaling, so any finite d, m are fine) and folds
+ * each activation scale into an exact pair of binary16 values, which holds for
+ * |d * q| < 65520; a token row with larger activations yields non-finite outputs in
+ * that row, as for nvq_gemm_nvfp4.  The GEMV has no such limit. */
 nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
                          const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                          void* stream);
