@@ -56,6 +56,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
     p.add_argument("--only-moe", action="store_true", help="time only the expert-routed decode step (profiling)")
+    p.add_argument("--only-q4-1", action="store_true", help="time only the Q4_1 GEMV and GEMM (profiling)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="for rocprofv3 --pmc runs: one 256 MiB device copy (calibration) and 4 gate+up "
                         "GEMV launches over distinct weight copies, then exit")
@@ -332,7 +333,19 @@ def time_extras():
     nvq.nvq_quantize_act_q8_0(x, q, d, b)
     us = _event_time(lambda: nvq.nvq_gemv_nvfp4(w, ws, q, d, y), 200)
     out["gemv_small_N4864_K896"] = dict(us_avg=us, GBps=gemv_alg_bytes(1, N, K) / (us * 1e-6) / 1e9)
-    # Q4_1 N = K = 4096: GEMV M=1 and GEMM M=512
+    out.update(time_q4_1())
+    out["moe_routed_gemv"] = time_moe()
+    return out
+
+
+def time_q4_1():
+    """Q4_1 N = K = 4096: the GEMV at M = 1 and the GEMM at M = 512."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    out = {}
     N = K = 4096
     qw, dw, mw = synth.q4_1_weights(N, K, synth.seed_for("q4_1", "w"))
     w = dev_tensor(nvq.nvq_pack_q4_1(qw, dw, mw))
@@ -356,7 +369,6 @@ def time_extras():
             out["q4_1_gemm_M512_N4096_K4096"] = dict(
                 us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
                 note="fp16 MFMA, three passes per product (weight and activation each split in two terms)")
-    out["moe_routed_gemv"] = time_moe()
     return out
 
 
@@ -615,6 +627,9 @@ def main():
         return
     if args.only_moe:
         log(json.dumps(time_moe()))
+        return
+    if args.only_q4_1:
+        log(json.dumps(time_q4_1()))
         return
 
     log("decode layer ...")
