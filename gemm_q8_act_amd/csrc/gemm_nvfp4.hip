@@ -8,17 +8,18 @@
 // [2^-10, 2688], so it is exact in fp16; activation codes q (|q| <= 127) are exact
 // in fp16 too.  Two kernels:
 //
-//   * gemm_nvfp4_tile_kernel (M <= 64, the GEMV entry for 2 <= M <= 15, and the
-//     debug sums).  Per 32-k chunk (one Q8_0 block) one v_mfma_f32_16x16x32_f16
+//   * gemm_nvfp4_tile_kernel (the debug sums, and M = 1 rows too long for the decode
+//     kernels' activation table).  Per 32-k chunk (one Q8_0 block) one v_mfma_f32_16x16x32_f16
 //     with a zero accumulator gives P[n][m] = sum_k w16 * q, exact in fp32; the
 //     chunk's activation scale is applied on the vector unit,
 //     acc[n][m] += d[m][chunk] * P[n][m].  Weights are the MFMA A operand (rows n)
 //     and activations B (columns m), so one d value per lane scales all of that
 //     lane's accumulators.  A 256-thread block computes BN weight rows x BM tokens
 //     per 128-k step from double-buffered LDS.
-//   * gemm_nvfp4_kernel (M > 64), below: the activation scale is folded into an
+//   * gemm_nvfp4_kernel (M > 16), below: the activation scale is folded into an
 //     exact two-term fp16 split of the activations so the matrix core accumulates
 //     the whole row by itself.
+// A GEMM of 2 <= M <= 16 tokens runs the batched decode kernel (gemv_batch_f16.hip).
 #include <algorithm>
 
 #include "nvq_device.h"
@@ -244,7 +245,7 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 }  // namespace
 
 // ---------------------------------------------------------------------------------
-// Large-M kernel: exact two-term split of the scaled activations.
+// Two-term kernel (M > 16): exact two-term split of the scaled activations.
 //
 // The per-32 activation scale d is folded into the activation operand instead of
 // being applied to partial products on the vector unit: d * q has at most 18
@@ -257,14 +258,14 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 // as |d * q| stays below 65520 (|x| < 65504); beyond that hi is infinite and the
 // affected outputs become non-finite rather than silently wrong.
 //
-// Block: 512 threads (8 wavefronts, 2 along n x 4 along m), tile 256 weight rows x
-// 256 tokens, wavefront tile 128 x 64 (4 x 2 v_mfma_f32_32x32x16_f16 tiles).
-// LDS holds two 64-k stages (double buffered): weights expanded to fp16 (E2M1 *
-// UE4M3, exact), raw int8 activation codes and their binary16 scales.  Each
-// wavefront splits its own activation fragments into (hi, lo) in registers.
-// Fragments of the next 32-k substep are read while the MFMAs of the current one
-// issue; global loads run two stages ahead; staging of stage t+1 overlaps the
-// MFMAs of stage t.
+// Block: 512 threads, WN x WM wavefronts, each a (32 TN) x (32 TM) tile of
+// v_mfma_f32_32x32x16_f16 products; the block tile is 256 weight rows by
+// BM = 32 WM TM tokens (64 for 16 < M <= 64, 128 up to M = 128, 256 above).  LDS holds two 64-k
+// stages (double buffered): weights expanded to fp16 (E2M1 * UE4M3, exact), raw
+// int8 activation codes and their binary16 scales.  Each wavefront splits its own
+// activation fragments into (hi, lo) in registers.  Fragments of the next 32-k
+// substep are read while the MFMAs of the current one issue; global loads run two
+// stages ahead; staging of stage t+1 overlaps the MFMAs of stage t.
 //
 // Work items: full tiles, then -- for the tiles of an incomplete last round over
 // the 256 compute units -- K-split parts whose fp32 partial tiles go to the
@@ -272,16 +273,31 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 // (deterministic: no atomics).
 // ---------------------------------------------------------------------------------
 namespace {
-constexpr int kBigBN = 256, kBigBM = 256, kBigThreads = 512;
+constexpr int kBigThreads = 512;
 constexpr int kBigLRW = 72;   // halves per LDS weight row (64 k + 8 pad)
 constexpr int kBigLRA = 72;   // bytes per LDS activation row (64 codes + 8 pad: 18 dwords, so the
                               // 8-byte fragment reads of 16 consecutive rows hit distinct banks)
-constexpr int kBigStageW = kBigBN * kBigLRW * 2, kBigStageA = kBigBM * kBigLRA, kBigStageD = kBigBM * 4;
-constexpr int kBigStage = kBigStageW + kBigStageA + kBigStageD;
-constexpr int kBigLds = 2 * kBigStage;
-constexpr int kBigAcc = 128;  // fp32 accumulators per thread (4 x 2 tiles x 16)
 constexpr int kSlots = 256;   // compute units of the chip: work items of the last round
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 16;
+
+template <int WN_, int WM_, int TN_, int TM_>
+struct NvCfg {
+  static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_;
+  static constexpr int BN = 32 * WN * TN, BM = 32 * WM * TM;
+  static constexpr int kAcc = 16 * TN * TM;  // fp32 accumulators per thread
+  static constexpr int kStageW = BN * kBigLRW * 2, kStageA = BM * kBigLRA, kStageD = BM * 4;
+  static constexpr int kStage = kStageW + kStageA + kStageD;
+  static constexpr int kLds = 2 * kStage;
+  static constexpr int ABT = BM * 64 / kBigThreads;  // activation bytes staged per thread
+  static constexpr int APR = 64 / ABT;               // threads per activation row
+  static_assert(WN * WM * 64 == kBigThreads, "8 wavefronts");
+  static_assert(BN == 256, "weight staging: 32 codes (one packed lane slot) per thread and stage");
+  static_assert(ABT == 8 || ABT == 16 || ABT == 32, "activation staging width");
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+using NvBig = NvCfg<2, 4, 4, 2>;  // 256 weight rows x 256 tokens
+using NvM128 = NvCfg<4, 2, 2, 2>; // 256 weight rows x 128 tokens
+using NvMid = NvCfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
 
 struct BigPlan {
   int64_t tiles_n, tiles, full, split_tiles;
@@ -289,10 +305,11 @@ struct BigPlan {
   int stages;
 };
 
+template <class C>
 BigPlan big_plan(int64_t M, int64_t N, int64_t K) {
   BigPlan p;
-  p.tiles_n = (N + kBigBN - 1) / kBigBN;
-  p.tiles = p.tiles_n * ((M + kBigBM - 1) / kBigBM);
+  p.tiles_n = (N + C::BN - 1) / C::BN;
+  p.tiles = p.tiles_n * ((M + C::BM - 1) / C::BM);
   p.stages = (int)(K / 64);
   const int64_t r = p.tiles % kSlots;
   p.split = 1;
@@ -302,21 +319,44 @@ BigPlan big_plan(int64_t M, int64_t N, int64_t K) {
   p.full = p.tiles - p.split_tiles;
   return p;
 }
+
+// which kernel runs an NVFP4 GEMM of M tokens: M = 1 only for rows too long for the
+// decode kernels' activation table
+enum NvPath { kNvTiled, kNvBatched, kNvMid, kNvM128, kNvBig };
+NvPath nv_path(int64_t M) {
+  if (M == 1) return kNvTiled;
+  if (M <= 16) return kNvBatched;
+  if (M <= 64) return kNvMid;
+  return M <= 128 ? kNvM128 : kNvBig;
+}
+
+}  // namespace
+
+namespace {
+template <class C>
+size_t two_term_workspace(int64_t M, int64_t N, int64_t K) {
+  const BigPlan p = big_plan<C>(M, N, K);
+  return (size_t)(p.split_tiles * p.split) * kBigThreads * C::kAcc * sizeof(float);
+}
 }  // namespace
 
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
-  if (M <= 64) return 0;
-  const BigPlan p = big_plan(M, N, K);
-  return (size_t)(p.split_tiles * p.split) * kBigThreads * kBigAcc * sizeof(float);
+  switch (nv_path(M)) {
+    case kNvMid: return two_term_workspace<NvMid>(M, N, K);
+    case kNvM128: return two_term_workspace<NvM128>(M, N, K);
+    case kNvBig: return two_term_workspace<NvBig>(M, N, K);
+    default: return 0;
+  }
 }
 
+template <class C>
 __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
                                                             int K, const int8_t* __restrict__ q,
                                                             const uint16_t* __restrict__ d16, int64_t M,
                                                             float w_scale, float* __restrict__ y,
                                                             float* __restrict__ part_ws, BigPlan plan) {
-  constexpr int BN = kBigBN, BM = kBigBM, WM = 4, TN = 4, TM = 2;
-  constexpr int LRW = kBigLRW, LRA = kBigLRA;
+  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
+  constexpr int LRW = kBigLRW, LRA = kBigLRA, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave / WM, wm = wave % WM;
@@ -340,48 +380,46 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   const int nb32 = K >> 5;
 
   // staging task of this thread: 32 weight codes (one 16 B lane slot) of row wrow and
-  // k-quarter (2 (t & 1) + whh) of chunk t >> 1; 32 activation codes of row arow;
-  // one activation scale.  Rows beyond N / M are clamped to valid memory: their
-  // results are never stored.
+  // k-quarter (2 (t & 1) + whh) of chunk t >> 1; ABT activation codes of row arow; for
+  // tid < 2 BM one activation scale.  Rows beyond N / M are clamped to valid memory:
+  // their results are never stored.
   const int wrow = tid >> 1, whh = tid & 1;
   const int64_t wtile = min(n0 / 16 + (wrow >> 4), ntiles - 1);
   const uint8_t* __restrict__ wbase = w + wtile * nch * 1024 + 16 * (wrow & 15);
   const uint8_t* __restrict__ sbase = sc + wtile * nch * 128 + 2 * (wrow & 15);
-  const int arow = tid >> 1, ahh = tid & 1;
-  const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + 32 * ahh;
-  const int drow = tid & 255, dblk = tid >> 8;
+  const int arow = tid / APR, aoff = ABT * (tid % APR);
+  const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
+  const bool dtask = 2 * BM >= kBigThreads || tid < 2 * BM;
+  const int drow = tid % BM, dblk = (tid / BM) & 1;
   const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
-  struct Stage { uint4 wr; uint32_t sr; uint4 a0, a1; uint32_t dr; };
+  struct Stage { Words<ABT / 4> a; u32x4 wr; uint32_t sr, dr; };
   auto gload = [&](int t, Stage& x) {
     const int c = t >> 1, g = 2 * (t & 1) + whh;
-    x.wr = *reinterpret_cast<const uint4*>(wbase + (int64_t)c * 1024 + 256 * g);
+    x.wr = *reinterpret_cast<const u32x4*>(wbase + (int64_t)c * 1024 + 256 * g);
     x.sr = *reinterpret_cast<const uint16_t*>(sbase + (int64_t)c * 128 + 32 * g);
-    const uint4* ap = reinterpret_cast<const uint4*>(abase + 64 * t);
-    x.a0 = ap[0];
-    x.a1 = ap[1];
-    x.dr = dbase[2 * t];
+    x.a = load_words<ABT / 4>(abase + 64 * t);
+    x.dr = dtask ? dbase[2 * t] : 0u;
   };
   auto lstore = [&](int b, const Stage& x) {
-    uint8_t* st = smem + b * kBigStage;
+    uint8_t* st = smem + b * C::kStage;
     _Float16* lw = reinterpret_cast<_Float16*>(st);
-    uint8_t* la = st + kBigStageW;
-    uint16_t* ld = reinterpret_cast<uint16_t*>(st + kBigStageW + kBigStageA);
+    uint8_t* la = st + C::kStageW;
+    uint16_t* ld = reinterpret_cast<uint16_t*>(st + C::kStageW + C::kStageA);
     const _Float16 u0 = (_Float16)ue4m3_to_f32<0>(x.sr), u1 = (_Float16)ue4m3_to_f32<1>(x.sr);
     const half2_t s0 = {u0, u0}, s1 = {u1, u1};
-    const uint32_t cc[4] = {x.wr.x, x.wr.y, x.wr.z, x.wr.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const half2_t s = d < 2 ? s0 : s1;
-      const half2_t p0 = e2m1x2_to_f16<0>(cc[d]) * s;
-      const half2_t p1 = e2m1x2_to_f16<1>(cc[d]) * s;
-      const half2_t p2 = e2m1x2_to_f16<2>(cc[d]) * s;
-      const half2_t p3 = e2m1x2_to_f16<3>(cc[d]) * s;
+      const uint32_t cw = x.wr[d];
+      const half2_t p0 = e2m1x2_to_f16<0>(cw) * s;
+      const half2_t p1 = e2m1x2_to_f16<1>(cw) * s;
+      const half2_t p2 = e2m1x2_to_f16<2>(cw) * s;
+      const half2_t p3 = e2m1x2_to_f16<3>(cw) * s;
       const half8_t v = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       *reinterpret_cast<half8_t*>(lw + wrow * LRW + 32 * whh + 8 * d) = v;
     }
-    *reinterpret_cast<uint4*>(la + arow * LRA + 32 * ahh) = x.a0;
-    *reinterpret_cast<uint4*>(la + arow * LRA + 32 * ahh + 16) = x.a1;
-    ld[2 * drow + dblk] = (uint16_t)x.dr;
+    store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
+    if (dtask) ld[2 * drow + dblk] = (uint16_t)x.dr;
   };
 
   floatx16 acc[TN][TM];
@@ -394,18 +432,18 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   // activation codes, activation scales
   struct Frag { half8_t af[2][TN]; uint2 raw[2][TM]; uint32_t dd[TM]; };
   auto fread = [&](int b, int u, Frag& f) {
-    const uint8_t* st = smem + b * kBigStage;
+    const uint8_t* st = smem + b * C::kStage;
     const _Float16* lw = reinterpret_cast<const _Float16*>(st);
-    const uint8_t* la = st + kBigStageW;
-    const uint16_t* ld = reinterpret_cast<const uint16_t*>(st + kBigStageW + kBigStageA);
+    const uint8_t* la = st + C::kStageW;
+    const uint16_t* ld = reinterpret_cast<const uint16_t*>(st + C::kStageW + C::kStageA);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < TN; ++i)
-        f.af[h][i] = *reinterpret_cast<const half8_t*>(lw + (wn * (BN / 2) + 32 * i + fr) * LRW + 32 * u + 16 * h + fk);
+        f.af[h][i] = *reinterpret_cast<const half8_t*>(lw + (wn * (32 * TN) + 32 * i + fr) * LRW + 32 * u + 16 * h + fk);
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
-      const int r = wm * (BM / WM) + 32 * j + fr;
+      const int r = wm * (32 * TM) + 32 * j + fr;
       f.dd[j] = ld[2 * r + u];
 #pragma unroll
       for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
@@ -468,7 +506,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
 
   if (part >= 0) {
     // partial tile: thread-private accumulators to the workspace, element-major
-    float* dst = part_ws + ((item - plan.full) * kBigAcc) * kBigThreads + tid;
+    float* dst = part_ws + ((item - plan.full) * C::kAcc) * kBigThreads + tid;
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -479,13 +517,13 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   }
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wm * (BM / WM) + 32 * j + fr;
+    const int64_t m = m0 + wm * (32 * TM) + 32 * j + fr;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < TN; ++i)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const int64_t n = n0 + wn * (BN / 2) + 32 * i + 8 * e4 + 4 * (lane >> 5);
+        const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * e4 + 4 * (lane >> 5);
         const floatx4 v = {acc[i][j][4 * e4] * w_scale, acc[i][j][4 * e4 + 1] * w_scale,
                            acc[i][j][4 * e4 + 2] * w_scale, acc[i][j][4 * e4 + 3] * w_scale};
         if ((N & 3) == 0 && n + 3 < N) {
@@ -503,27 +541,26 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
 // the tile.  Block (split tile, group of 8 accumulator slots): each thread reduces the
 // same 8 slots of one producer thread, so every load of a part is one coalesced 2 KB
 // row of the element-major workspace.
-constexpr int kReduceGroups = kBigAcc / 8;
-
+template <class C>
 __global__ __launch_bounds__(512) void gemm_nvfp4_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
                                                                 int64_t M, float w_scale,
                                                                 float* __restrict__ y, BigPlan plan) {
-  constexpr int BN = kBigBN, BM = kBigBM, WM = 4, TM = 2;
+  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM, kGroups = C::kAcc / 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave / WM, wm = wave % WM;
-  const int64_t st = blockIdx.x / kReduceGroups;  // split tile index
-  const int grp = blockIdx.x % kReduceGroups;     // accumulator slots 8 grp .. 8 grp + 7
+  const int64_t st = blockIdx.x / kGroups;  // split tile index
+  const int grp = blockIdx.x % kGroups;     // accumulator slots 8 grp .. 8 grp + 7
   const int ij = grp >> 1, i = ij / TM, j = ij % TM, e0 = 8 * grp;
   const int64_t tile = plan.full + st;
   const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
-  const float* src = part_ws + (st * plan.split * kBigAcc + e0) * kBigThreads + tid;
+  const float* src = part_ws + (st * plan.split * C::kAcc + e0) * kBigThreads + tid;
   float v[8][kMaxSplit];
 #pragma unroll
   for (int p = 0; p < kMaxSplit; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      v[e][p] = p < plan.split ? src[((int64_t)p * kBigAcc + e) * kBigThreads] : 0.0f;
-  const int64_t m = m0 + wm * (BM / WM) + 32 * j + (lane & 31);
+      v[e][p] = p < plan.split ? src[((int64_t)p * C::kAcc + e) * kBigThreads] : 0.0f;
+  const int64_t m = m0 + wm * (32 * TM) + 32 * j + (lane & 31);
   if (m >= M) return;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -537,7 +574,7 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_reduce_kernel(const float* __r
       o[rr] = s * w_scale;
     }
     // slot e0 + 4 h + rr of thread tid holds row 8 ((e0 % 16) / 4 + h) + 4 (lane >> 5) + rr
-    const int64_t n = n0 + wn * (BN / 2) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
+    const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
     if ((N & 3) == 0 && n + 3 < N) {
       *reinterpret_cast<floatx4*>(y + m * N + n) = floatx4{o[0], o[1], o[2], o[3]};
     } else {
@@ -548,24 +585,37 @@ __global__ __launch_bounds__(512) void gemm_nvfp4_reduce_kernel(const float* __r
   }
 }
 
+namespace {
+template <class C>
+hipError_t launch_two_term(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int64_t M,
+                           int64_t N, int64_t K, float* y, float* workspace, hipStream_t stream) {
+  const BigPlan plan = big_plan<C>(M, N, K);
+  if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel<C>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (ea != hipSuccess) return ea;
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  hipLaunchKernelGGL(gemm_nvfp4_kernel<C>, dim3((unsigned)items), dim3(kBigThreads), C::kLds, stream, w, N,
+                     (int)K, q, d16, M, w_scale, y, workspace, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.split_tiles == 0) return e;
+  hipLaunchKernelGGL(gemm_nvfp4_reduce_kernel<C>, dim3((unsigned)(plan.split_tiles * (C::kAcc / 8))),
+                     dim3(kBigThreads), 0, stream, workspace, N, M, w_scale, y, plan);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream) {
   if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
-  if (M <= 16) return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
-  if (M <= 64) return launch_tile<64, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
-  const BigPlan plan = big_plan(M, N, K);
-  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, kBigLds);
-  if (ea != hipSuccess) return ea;
-  const int64_t items = plan.full + plan.split_tiles * plan.split;
-  hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)items), dim3(kBigThreads), kBigLds, stream, w, N,
-                     (int)K, q, d16, M, w_scale, y, workspace, plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.split_tiles == 0) return e;
-  hipLaunchKernelGGL(gemm_nvfp4_reduce_kernel, dim3((unsigned)(plan.split_tiles * kReduceGroups)),
-                     dim3(kBigThreads), 0, stream, workspace, N, M, w_scale, y, plan);
-  return hipGetLastError();
+  switch (nv_path(M)) {
+    case kNvBatched: return launch_gemv_nvfp4_batch_f16(w, w_scale, q, d16, M, N, K, y, stream);
+    case kNvMid: return launch_two_term<NvMid>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
+    case kNvM128: return launch_two_term<NvM128>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
+    case kNvBig: return launch_two_term<NvBig>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
+    default: return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+  }
 }
 
 }  // namespace nvq

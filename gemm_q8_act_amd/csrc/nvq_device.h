@@ -17,6 +17,41 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// NW 32-bit words moved as one 8-byte (NW = 2) or 16-byte vector access per 4 words;
+// p must be aligned to the access size.  A plain array of scalars, so the compiler
+// keeps it in registers.
+template <int NW>
+struct Words {
+  uint32_t v[NW];
+};
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words(const void* p) {
+  Words<NW> r;
+  if constexpr (NW == 2) {
+    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
+    r.v[0] = t[0];
+    r.v[1] = t[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h) {
+      const u32x4 t = reinterpret_cast<const u32x4*>(p)[h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.v[4 * h + e] = t[e];
+    }
+  }
+  return r;
+}
+template <int NW>
+__device__ __forceinline__ void store_words(void* p, const Words<NW>& w) {
+  if constexpr (NW == 2) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{w.v[0], w.v[1]};
+  } else {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h)
+      reinterpret_cast<u32x4*>(p)[h] = u32x4{w.v[4 * h], w.v[4 * h + 1], w.v[4 * h + 2], w.v[4 * h + 3]};
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Byte permute and integer dot product.
 // v_perm_b32(s0, s1, sel): result byte i = pool[sel_i] where pool bytes 0..3 come

@@ -455,7 +455,8 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 //
 // Block: 512 threads, WN x WM wavefronts, each a (32 TN) x (32 TM) tile of
 // v_mfma_f32_32x32x16_f16 products; block tile BN = 32 WN TN weight rows by
-// BM = 32 WM TM tokens.  LDS holds two 64-k stages: the two weight planes (fp16 hi,
+// BM = 32 WM TM tokens (256 x 64 for 16 < M <= 64, 128 x 128 up to M = 128,
+// 128 x 256 above).  LDS holds two 64-k stages: the two weight planes (fp16 hi,
 // lo), raw int8 activation codes and their binary16 scales; each wavefront splits its
 // activation fragments in registers.  Work items and the ordered K-split reduction
 // follow the NVFP4 large-M kernel.
@@ -482,8 +483,9 @@ struct Q41Cfg {
   static_assert(ABT == 8 || ABT == 16 || ABT == 32, "activation staging width");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
-using Q41Big = Q41Cfg<2, 4, 2, 2>;  // 128 weight rows x 256 tokens
-using Q41Mid = Q41Cfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
+using Q41Big = Q41Cfg<2, 4, 2, 2>;   // 128 weight rows x 256 tokens
+using Q41M128 = Q41Cfg<2, 4, 2, 1>;  // 128 weight rows x 128 tokens
+using Q41Mid = Q41Cfg<4, 2, 2, 1>;   // 256 weight rows x 64 tokens
 
 struct Q41Plan {
   int64_t tiles_n, tiles, full, split_tiles;
@@ -509,52 +511,31 @@ Q41Plan q41_plan(int64_t M, int64_t N, int64_t K) {
 // which kernel runs a Q4_1 GEMM of this shape (the GEMV kernel falls back to the
 // tiled one for rows longer than 20480)
 constexpr int kQ41GemvMaxM = 16;
-enum Q41Path { kQ41Gemv, kQ41Tiled, kQ41Mid, kQ41Big };
+enum Q41Path { kQ41Gemv, kQ41Tiled, kQ41Mid, kQ41M128, kQ41Big };
 Q41Path q41_path(int64_t M, int64_t K) {
   if (M <= kQ41GemvMaxM) return kQ41Gemv;
   if (K % 64 != 0) return kQ41Tiled;
-  return M <= 64 ? kQ41Mid : kQ41Big;
+  if (M <= 64) return kQ41Mid;
+  return M <= 128 ? kQ41M128 : kQ41Big;
 }
 
-template <int NW>
-struct Words {
-  uint32_t v[NW];
-};
-template <int NW>
-__device__ __forceinline__ Words<NW> load_words(const void* p) {
-  Words<NW> r;
-  if constexpr (NW == 2) {
-    const u32x2 t = *reinterpret_cast<const u32x2*>(p);
-    r.v[0] = t[0];
-    r.v[1] = t[1];
-  } else {
-#pragma unroll
-    for (int h = 0; h < NW / 4; ++h) {
-      const u32x4 t = reinterpret_cast<const u32x4*>(p)[h];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) r.v[4 * h + e] = t[e];
-    }
-  }
-  return r;
-}
-template <int NW>
-__device__ __forceinline__ void store_words(void* p, const Words<NW>& w) {
-  if constexpr (NW == 2) {
-    *reinterpret_cast<u32x2*>(p) = u32x2{w.v[0], w.v[1]};
-  } else {
-#pragma unroll
-    for (int h = 0; h < NW / 4; ++h)
-      reinterpret_cast<u32x4*>(p)[h] = u32x4{w.v[4 * h], w.v[4 * h + 1], w.v[4 * h + 2], w.v[4 * h + 3]};
-  }
+}  // namespace
+
+namespace {
+template <class C>
+size_t q41_workspace(int64_t M, int64_t N, int64_t K) {
+  const Q41Plan p = q41_plan<C>(M, N, K);
+  return (size_t)(p.split_tiles * p.split) * kQThreads * C::kAcc * sizeof(float);
 }
 }  // namespace
 
 size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K) {
-  const Q41Path path = q41_path(M, K);
-  if (path != kQ41Mid && path != kQ41Big) return 0;
-  const Q41Plan p = path == kQ41Big ? q41_plan<Q41Big>(M, N, K) : q41_plan<Q41Mid>(M, N, K);
-  const int acc = path == kQ41Big ? Q41Big::kAcc : Q41Mid::kAcc;
-  return (size_t)(p.split_tiles * p.split) * kQThreads * acc * sizeof(float);
+  switch (q41_path(M, K)) {
+    case kQ41Mid: return q41_workspace<Q41Mid>(M, N, K);
+    case kQ41M128: return q41_workspace<Q41M128>(M, N, K);
+    case kQ41Big: return q41_workspace<Q41Big>(M, N, K);
+    default: return 0;
+  }
 }
 
 template <class C>
@@ -595,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const uint32_t* __restrict__ dmbase = dmw + wr * nb32 + (CPT * wq) / 32;
   const int arow = tid / APR, aoff = ABT * (tid % APR);
   const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
-  const bool dtask = tid < 2 * BM;
+  const bool dtask = 2 * BM >= kQThreads || tid < 2 * BM;
   const int drow = tid % BM, dblk = (tid / BM) & 1;
   const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
   struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm, dr; };
@@ -846,6 +827,7 @@ hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
     case kQ41Gemv: return launch_gemv_q4_1(w, q, d16, bsum16, M, N, K, y, nullptr, stream);
     case kQ41Big: return launch_q41_f16x2<Q41Big>(w, q, d16, M, N, K, y, workspace, stream);
     case kQ41Mid: return launch_q41_f16x2<Q41Mid>(w, q, d16, M, N, K, y, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128>(w, q, d16, M, N, K, y, workspace, stream);
     default: return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
   }
 }

@@ -115,9 +115,9 @@ size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
 
 /* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt
- * is NVQ_FMT_*): with M > 64 and K % 64 == 0, the fp32 partial tiles of the K-split
- * work items that even out the last round of tiles (NVFP4 256 x 256, Q4_1 128 x 256)
- * over the chip's 256 compute units (at most 64 MiB); otherwise 0.  Pure function.
+ * is NVQ_FMT_*): with M > 16 and K % 64 == 0, the fp32 partial tiles of the K-split
+ * work items that even out the last round of tiles over the chip's 256 compute units
+ * (at most 32 MiB); otherwise 0.  Pure function.
  * When it is 0 the workspace pointer may be NULL. */
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
@@ -192,11 +192,11 @@ nvq_status nvq_gemv_nvfp4_routed(const void* w, const float* w_scales, const int
  * contents on entry irrelevant, overwritten) of at least
  * nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K) bytes; NULL is accepted when
  * that size is 0.  Calls that share a workspace must not overlap in time.
- * For M > 64 the kernel folds each activation scale into an exact pair of binary16
+ * For M > 16 the kernel folds each activation scale into an exact pair of binary16
  * values (hi + lo = d * q); this is exact for |d * q| < 65520, i.e. activations
  * below the binary16 range limit.  A row with larger activations yields
- * non-finite outputs in that row (never silently wrong values); the GEMV entry
- * points have no such limit. */
+ * non-finite outputs in that row (never silently wrong values); M = 16 and the
+ * GEMV entry points have no such limit. */
 nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y,
                           void* workspace, size_t ws_bytes, void* stream);

@@ -53,25 +53,32 @@ def test_sizes():
     assert nvq.nvq_q4_1_weight_bytes(4096, 4096) == 4096 * 4096 * 5 // 8
     assert nvq.nvq_q4_1_weight_bytes(3, 32) == 3 * 20
     assert nvq.nvq_q4_1_weight_bytes(3, 48) == 0
-    # K-split workspace of the M > 64 GEMM: fp32 partial tiles of 256 x 256 (one per
-    # 512-thread work item x 128 accumulators), for the tiles of an incomplete last
-    # round over 256 compute units, split up to 8 ways (at most one per 64-k stage)
-    tile_bytes = 512 * 128 * 4
+    # K-split workspace of the two-term GEMM (M > 16): fp32 partial tiles (one per
+    # 512-thread work item: 256 x 256 tiles with 128 accumulators per thread for
+    # M > 128, 256 x 128 with 64 for M <= 128, 256 x 64 with 32 for M <= 64), for the
+    # tiles of an incomplete last round over 256 compute units, split up to 16 ways (at
+    # most one per 64-k stage)
+    tile_bytes, m128_bytes, mid_bytes = 512 * 128 * 4, 512 * 64 * 4, 512 * 32 * 4
     ws = nvq.nvq_gemm_workspace_bytes
     assert ws(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) == 32 * 8 * tile_bytes      # 544 tiles: 32 left over
     assert ws(nvq.NVQ_FMT_NVFP4, 256, 17408, 5120) == 68 * 3 * tile_bytes       # 68 tiles, 256 // 68 = 3
-    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 640) == 1 * 8 * tile_bytes             # 1 tile, 10 stages
-    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 192) == 1 * 3 * tile_bytes             # split <= stages
+    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 640) == 1 * 10 * m128_bytes            # 1 tile, 10 stages
+    assert ws(nvq.NVQ_FMT_NVFP4, 100, 8, 192) == 1 * 3 * m128_bytes             # split <= stages
+    assert ws(nvq.NVQ_FMT_NVFP4, 200, 8, 640) == 1 * 10 * tile_bytes
+    assert ws(nvq.NVQ_FMT_NVFP4, 256, 4096, 4096) == 16 * 16 * tile_bytes       # 16 tiles: split 16 ways
     assert ws(nvq.NVQ_FMT_NVFP4, 65, 33, 64) == 0                               # one stage: no split
     assert ws(nvq.NVQ_FMT_NVFP4, 4096, 4096, 1024) == 0                         # 256 tiles: full rounds
-    assert ws(nvq.NVQ_FMT_NVFP4, 64, 17408, 5120) == 0                          # M <= 64: tile kernel
-    # Q4_1, split up to 16 ways: M > 64 in 128 x 256 tiles with 64 accumulators per
-    # thread, 16 < M <= 64 in 256 x 64 tiles with 32
+    assert ws(nvq.NVQ_FMT_NVFP4, 64, 17408, 5120) == 68 * 3 * mid_bytes         # 256 x 64 tiles
+    assert ws(nvq.NVQ_FMT_NVFP4, 17, 300, 640) == 2 * 10 * mid_bytes
+    assert ws(nvq.NVQ_FMT_NVFP4, 16, 17408, 5120) == 0                          # M <= 16: batched GEMV
+    # Q4_1, split up to 16 ways: M > 128 in 128 x 256 tiles with 64 accumulators per
+    # thread, 64 < M <= 128 in 128 x 128 tiles and 16 < M <= 64 in 256 x 64 tiles with 32
     q41_tile, q41_mid = 512 * 64 * 4, 512 * 32 * 4
     assert ws(nvq.NVQ_FMT_Q4_1, 2048, 4096, 4096) == 0                          # 256 tiles: full rounds
     assert ws(nvq.NVQ_FMT_Q4_1, 512, 4096, 4096) == 64 * 4 * q41_tile           # 64 tiles, 256 // 64 = 4
     assert ws(nvq.NVQ_FMT_Q4_1, 300, 19200, 256) == 44 * 4 * q41_tile           # 300 tiles: 44 left, 4 stages
-    assert ws(nvq.NVQ_FMT_Q4_1, 100, 8, 640) == 1 * 10 * q41_tile               # split <= stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 100, 8, 640) == 1 * 10 * q41_mid                # split <= stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 200, 8, 640) == 1 * 10 * q41_tile
     assert ws(nvq.NVQ_FMT_Q4_1, 64, 4096, 4096) == 16 * 16 * q41_mid            # 16 tiles of 256 rows
     assert ws(nvq.NVQ_FMT_Q4_1, 17, 8, 64) == 0                                 # one stage: no split
     assert ws(nvq.NVQ_FMT_Q4_1, 16, 4096, 4096) == 0                            # M <= 16: tiled kernel

@@ -160,12 +160,14 @@ def test_gemv_batched_ragged_tile_groups(oracle, N):
     check_y(host(y), yo, awa, f"M=3 N={N} K=128")
 
 
-# M <= 64: per-block scaled tile kernel; M > 64: split-activation kernel, whose
-# small shapes always take the K-split + ordered-reduction route (fewer tiles than
-# compute units), except K = 64 (one stage: no split)
+# M = 16: batched decode kernel (two token groups); 16 < M <= 64 and M > 64: the
+# split-activation kernel in 256 x 64 and 256 x 256 tiles, whose small shapes always
+# take the K-split + ordered-reduction route (fewer tiles than compute units), except
+# K = 64 (one stage: no split)
 @pytest.mark.parametrize("M,N,K", [(16, 64, 64), (17, 77, 192), (100, 300, 640), (64, 128, 2048),
                                    (129, 257, 1024), (40, 70, 320), (300, 600, 384), (65, 33, 64),
-                                   (257, 1000, 448), (520, 129, 128)])
+                                   (257, 1000, 448), (520, 129, 128), (16, 300, 5120), (33, 520, 64),
+                                   (64, 2000, 1024)])
 def test_gemm_nvfp4(oracle, M, N, K):
     say(f"gemm_nvfp4 M={M} N={N} K={K}")
     torch = torch_dev()
@@ -264,9 +266,9 @@ def test_q4_1_gemm_full_size(oracle):
                                    (96, 64, 96), (128, 40, 4096), (17, 300, 640), (40, 77, 192),
                                    (64, 520, 1024), (50, 64, 96)])
 def test_q4_1_gemm_large_m(oracle, M, N, K):
-    """M > 16: the two-term fp16 kernels (256 x 64 tiles up to M = 64, 128 x 256 above;
-    K % 64 == 0; K-split parts on small grids, ragged N and M tiles, N % 4 != 0) and the
-    tiled kernel (K = 96)."""
+    """M > 16: the two-term fp16 kernels (256 x 64 tiles up to M = 64, 128 x 128 up to
+    M = 128, 128 x 256 above; K % 64 == 0; K-split parts on small grids, ragged N and M
+    tiles, N % 4 != 0) and the tiled kernel (K = 96)."""
     say(f"q4_1 gemm M={M} N={N} K={K}")
     torch = torch_dev()
     c = Q41Case(M, N, K, 53 + M + N)
@@ -304,10 +306,10 @@ def _q41_extreme_rows(N, K, seed):
     return qw, d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("M,N,K", [(80, 70, 640), (40, 70, 640), (8, 70, 640)])
+@pytest.mark.parametrize("M,N,K", [(200, 70, 640), (80, 70, 640), (40, 70, 640), (8, 70, 640)])
 def test_q4_1_extreme_weight_rows(oracle, M, N, K):
-    """Per-row weight magnitudes from 6e-8 to 1e6 in one matrix, through both two-term
-    GEMM kernels (M = 80, 40) and the GEMV (M = 8)."""
+    """Per-row weight magnitudes from 6e-8 to 1e6 in one matrix, through the three
+    two-term GEMM tile shapes (M = 200, 80, 40) and the GEMV (M = 8)."""
     say(f"q4_1 extreme weight rows M={M}")
     torch = torch_dev()
     c = Q41Case(M, N, K, 0, weights=_q41_extreme_rows(N, K, 919), x=synth.activations(M, K, 920))
@@ -318,7 +320,7 @@ def test_q4_1_extreme_weight_rows(oracle, M, N, K):
     assert (host(y)[:, 2] == 0.0).all()
 
 
-@pytest.mark.parametrize("M", [300, 48])
+@pytest.mark.parametrize("M", [300, 100, 48])
 def test_q4_1_gemm_split_determinism_and_guard_bands(oracle, M):
     """Two-term Q4_1 kernels with K-split parts: junk workspace on entry,
     bitwise-identical repeats, nothing written outside y."""
@@ -344,7 +346,7 @@ def test_q4_1_gemm_split_determinism_and_guard_bands(oracle, M):
     check_y(outs[0].reshape(M, N)[:, ::5], yo, awa, "q4_1 split determinism case")
 
 
-@pytest.mark.parametrize("M", [96, 24])
+@pytest.mark.parametrize("M", [200, 96, 24])
 def test_q4_1_gemm_activation_range(M):
     """As for NVFP4: rows of the two-term kernels (M > 16) whose scaled activations
     exceed the binary16 range come out non-finite; every other row is unaffected."""
@@ -466,11 +468,13 @@ def test_side_stream_and_graph_replay():
             assert (a.view(np.uint32) == b.view(np.uint32)).all(), f"replay {rep}"
 
 
-def test_gemm_split_kernel_determinism_and_guard_bands(oracle):
-    """M > 64 with K-split parts: bitwise-identical repeats, nothing written outside y."""
-    say("gemm (M > 64, K-split) determinism + guard bands")
+@pytest.mark.parametrize("M", [300, 100, 40])
+def test_gemm_split_kernel_determinism_and_guard_bands(oracle, M):
+    """Two-term GEMM (all three token-tile heights) with K-split parts:
+    bitwise-identical repeats, nothing written outside y."""
+    say(f"gemm (M={M}, K-split) determinism + guard bands")
     torch = torch_dev()
-    M, N, K = 300, 520, 1024
+    N, K = 520, 1024
     c = NvCase(M, N, K, 4242, w_scale=1.25, outliers=True)
     guard = 4096
     outs = []
@@ -489,12 +493,13 @@ def test_gemm_split_kernel_determinism_and_guard_bands(oracle):
     check_y(outs[0].reshape(M, N)[:, ::7], yo, awa, "gemm split determinism case")
 
 
-def test_gemm_split_kernel_activation_range():
+@pytest.mark.parametrize("M", [200, 96, 24])
+def test_gemm_split_kernel_activation_range(M):
     """Rows whose scaled activations exceed the binary16 range come out non-finite
-    (documented contract of the M > 64 GEMM); every other row is unaffected."""
-    say("gemm (M > 64) activation range contract")
+    (documented contract of the M > 16 GEMM); every other row is unaffected."""
+    say(f"gemm (M={M}) activation range contract")
     torch = torch_dev()
-    M, N, K = 96, 64, 128
+    N, K = 64, 128
     c = NvCase(M, N, K, 77)
     x = synth.activations(M, K, 78)
     x[5, 3] = 1.0e6  # |d * q| far above 65504 in row 5
