@@ -333,8 +333,30 @@ def time_extras():
     nvq.nvq_quantize_act_q8_0(x, q, d, b)
     us = _event_time(lambda: nvq.nvq_gemv_nvfp4(w, ws, q, d, y), 200)
     out["gemv_small_N4864_K896"] = dict(us_avg=us, GBps=gemv_alg_bytes(1, N, K) / (us * 1e-6) / 1e9)
+    out.update(time_act_quant())
     out.update(time_q4_1())
     out["moe_routed_gemv"] = time_moe()
+    return out
+
+
+def time_act_quant():
+    """Q8_0 activation quantization with bsum16: the prefill input (M = 2048, K = 5120,
+    0.1 % outliers) against HBM, and one decode row (M = 1), which is launch-bound."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    out = {}
+    for M, K in ((2048, 5120), (1, 5120)):
+        x = dev_tensor(synth.activations(M, K, synth.seed_for("prefill", "x") + M, outliers=True))
+        q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
+        b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
+        us = _event_time(lambda: nvq.nvq_quantize_act_q8_0(x, q, d, b), 100)
+        byts = M * K * 4 + M * K + M * (K // 32) * 2 + M * (K // 16) * 2  # x in; q, d16, bsum16 out
+        gbps = byts / (us * 1e-6) / 1e9
+        out[f"act_quant_M{M}_K{K}"] = dict(us_avg=us, GBps=gbps, frac=gbps / HBM_PEAK_GBS, bytes=byts)
     return out
 
 
