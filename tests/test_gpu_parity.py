@@ -60,6 +60,52 @@ def test_act_quant_edge_blocks(oracle, K):
     assert do[2].max() < 0x0400 and do[2].max() > 0      # the subnormal-scale row is exercised
 
 
+def _near_tie_rows(rows, K, seed):
+    """Blocks whose quotients x / d32 sit on or within a few ulps of half-integers: the
+    block's first value is amax (it fixes d32 = float32(amax / 127)), the others are
+    float32((k + 0.5) * d32) moved by -3 .. +3 ulps, for random amax and k."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    x = np.zeros((rows, K), np.float32)
+    for i in range(rows):
+        for b in range(K // 32):
+            amax = np.float32(r.choice([1.0, 127.0, 3.0e4, 1e-3]) * r.uniform(0.5, 2.0))
+            d32 = np.float32(amax / np.float32(127.0))
+            k = r.integers(-127, 127, 31).astype(np.float32)
+            base = ((k + np.float32(0.5)) * d32).astype(np.float32)
+            steps = r.integers(-3, 4, 31)
+            v = base.copy()
+            for j in range(31):
+                for _ in range(abs(int(steps[j]))):
+                    v[j] = np.nextafter(v[j], np.float32(np.inf) if steps[j] > 0 else np.float32(-np.inf))
+            v = np.clip(v, -amax, amax)
+            x[i, 32 * b] = amax if r.integers(0, 2) else -amax
+            x[i, 32 * b + 1: 32 * b + 32] = v
+    return x
+
+
+def test_act_quant_near_ties(oracle):
+    """Quotients on and next to rounding ties decide the same codes as the oracle's
+    correctly rounded division."""
+    say("act_quant near-tie blocks")
+    x = _near_tie_rows(48, 1024, 4711)
+    q, d, b = quantize_gpu(x)
+    qo, do, bo = oracle.quantize_q8_0(x)
+    assert (host(q) == qo).all()
+    assert (host(d).view(np.uint16) == do).all()
+    assert (host(b) == bo).all()
+
+
+def test_act_quant_large(oracle):
+    """The prefill input shape (two blocks per thread), outliers included."""
+    say("act_quant M=512 K=5120")
+    x = synth.activations(512, 5120, synth.seed_for("test", "act_large"), outliers=True)
+    q, d, b = quantize_gpu(x)
+    qo, do, bo = oracle.quantize_q8_0(x)
+    assert (host(q) == qo).all()
+    assert (host(d).view(np.uint16) == do).all()
+    assert (host(b) == bo).all()
+
+
 def test_act_quant_without_bsum(oracle):
     torch = torch_dev()
     x = synth.activations(4, 256, 5)
