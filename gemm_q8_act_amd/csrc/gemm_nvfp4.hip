@@ -22,6 +22,7 @@
 // A GEMM of 2 <= M <= 16 tokens runs the batched decode kernel (gemv_batch_f16.hip).
 #include <algorithm>
 
+#include "ksplit.h"
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
@@ -269,16 +270,14 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 //
 // Work items: full tiles, then -- for the tiles of an incomplete last round over
 // the 256 compute units -- K-split parts whose fp32 partial tiles go to the
-// workspace and are summed in part order by gemm_nvfp4_reduce_kernel
-// (deterministic: no atomics).
+// workspace and are summed in part order by ksplit_reduce_kernel (ksplit.h;
+// deterministic: no atomics).
 // ---------------------------------------------------------------------------------
 namespace {
 constexpr int kBigThreads = 512;
 constexpr int kBigLRW = 72;   // halves per LDS weight row (64 k + 8 pad)
 constexpr int kBigLRA = 72;   // bytes per LDS activation row (64 codes + 8 pad: 18 dwords, so the
                               // 8-byte fragment reads of 16 consecutive rows hit distinct banks)
-constexpr int kSlots = 256;   // compute units of the chip: work items of the last round
-constexpr int kMaxSplit = 16;
 
 template <int WN_, int WM_, int TN_, int TM_>
 struct NvCfg {
@@ -299,27 +298,6 @@ using NvBig = NvCfg<2, 4, 4, 2>;  // 256 weight rows x 256 tokens
 using NvM128 = NvCfg<4, 2, 2, 2>; // 256 weight rows x 128 tokens
 using NvMid = NvCfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
 
-struct BigPlan {
-  int64_t tiles_n, tiles, full, split_tiles;
-  int split;  // K parts per split tile (1: no split)
-  int stages;
-};
-
-template <class C>
-BigPlan big_plan(int64_t M, int64_t N, int64_t K) {
-  BigPlan p;
-  p.tiles_n = (N + C::BN - 1) / C::BN;
-  p.tiles = p.tiles_n * ((M + C::BM - 1) / C::BM);
-  p.stages = (int)(K / 64);
-  const int64_t r = p.tiles % kSlots;
-  p.split = 1;
-  if (r != 0) p.split = (int)std::min<int64_t>({kSlots / r, (int64_t)kMaxSplit, (int64_t)p.stages});
-  if (p.split < 2) p.split = 1;
-  p.split_tiles = p.split > 1 ? r : 0;
-  p.full = p.tiles - p.split_tiles;
-  return p;
-}
-
 // which kernel runs an NVFP4 GEMM of M tokens: M = 1 only for rows too long for the
 // decode kernels' activation table
 enum NvPath { kNvTiled, kNvBatched, kNvMid, kNvM128, kNvBig };
@@ -332,19 +310,11 @@ NvPath nv_path(int64_t M) {
 
 }  // namespace
 
-namespace {
-template <class C>
-size_t two_term_workspace(int64_t M, int64_t N, int64_t K) {
-  const BigPlan p = big_plan<C>(M, N, K);
-  return (size_t)(p.split_tiles * p.split) * kBigThreads * C::kAcc * sizeof(float);
-}
-}  // namespace
-
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
   switch (nv_path(M)) {
-    case kNvMid: return two_term_workspace<NvMid>(M, N, K);
-    case kNvM128: return two_term_workspace<NvM128>(M, N, K);
-    case kNvBig: return two_term_workspace<NvBig>(M, N, K);
+    case kNvMid: return ksplit_workspace<NvMid>(M, N, K);
+    case kNvM128: return ksplit_workspace<NvM128>(M, N, K);
+    case kNvBig: return ksplit_workspace<NvBig>(M, N, K);
     default: return 0;
   }
 }
@@ -354,7 +324,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
                                                             int K, const int8_t* __restrict__ q,
                                                             const uint16_t* __restrict__ d16, int64_t M,
                                                             float w_scale, float* __restrict__ y,
-                                                            float* __restrict__ part_ws, BigPlan plan) {
+                                                            float* __restrict__ part_ws, KSplitPlan plan) {
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kBigLRW, LRA = kBigLRA, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -537,59 +507,11 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   }
 }
 
-// Sums the K parts of every split tile in part order (fp32, p = 0, 1, ...) and stores
-// the tile.  Block (split tile, group of 8 accumulator slots): each thread reduces the
-// same 8 slots of one producer thread, so every load of a part is one coalesced 2 KB
-// row of the element-major workspace.
-template <class C>
-__global__ __launch_bounds__(512) void gemm_nvfp4_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
-                                                                int64_t M, float w_scale,
-                                                                float* __restrict__ y, BigPlan plan) {
-  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM, kGroups = C::kAcc / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave / WM, wm = wave % WM;
-  const int64_t st = blockIdx.x / kGroups;  // split tile index
-  const int grp = blockIdx.x % kGroups;     // accumulator slots 8 grp .. 8 grp + 7
-  const int ij = grp >> 1, i = ij / TM, j = ij % TM, e0 = 8 * grp;
-  const int64_t tile = plan.full + st;
-  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
-  const float* src = part_ws + (st * plan.split * C::kAcc + e0) * kBigThreads + tid;
-  float v[8][kMaxSplit];
-#pragma unroll
-  for (int p = 0; p < kMaxSplit; ++p)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v[e][p] = p < plan.split ? src[((int64_t)p * C::kAcc + e) * kBigThreads] : 0.0f;
-  const int64_t m = m0 + wm * (32 * TM) + 32 * j + (lane & 31);
-  if (m >= M) return;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float o[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float s = v[4 * h + rr][0];
-#pragma unroll
-      for (int p = 1; p < kMaxSplit; ++p)
-        if (p < plan.split) s += v[4 * h + rr][p];
-      o[rr] = s * w_scale;
-    }
-    // slot e0 + 4 h + rr of thread tid holds row 8 ((e0 % 16) / 4 + h) + 4 (lane >> 5) + rr
-    const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
-    if ((N & 3) == 0 && n + 3 < N) {
-      *reinterpret_cast<floatx4*>(y + m * N + n) = floatx4{o[0], o[1], o[2], o[3]};
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (n + rr < N) y[m * N + n + rr] = o[rr];
-    }
-  }
-}
-
 namespace {
 template <class C>
 hipError_t launch_two_term(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int64_t M,
                            int64_t N, int64_t K, float* y, float* workspace, hipStream_t stream) {
-  const BigPlan plan = big_plan<C>(M, N, K);
+  const KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
   hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel<C>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -599,9 +521,7 @@ hipError_t launch_two_term(const uint8_t* w, float w_scale, const int8_t* q, con
                      (int)K, q, d16, M, w_scale, y, workspace, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
-  hipLaunchKernelGGL(gemm_nvfp4_reduce_kernel<C>, dim3((unsigned)(plan.split_tiles * (C::kAcc / 8))),
-                     dim3(kBigThreads), 0, stream, workspace, N, M, w_scale, y, plan);
-  return hipGetLastError();
+  return launch_ksplit_reduce<C>(workspace, N, M, w_scale, y, plan, stream);
 }
 }  // namespace
 

@@ -21,6 +21,7 @@
 // core accumulates whole rows (see gemm_q4_1_big_kernel below).
 #include <algorithm>
 
+#include "ksplit.h"
 #include "nvq_device.h"
 #include "nvq_launch.h"
 
@@ -462,7 +463,7 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 // follow the NVFP4 large-M kernel.
 // ---------------------------------------------------------------------------------
 namespace {
-constexpr int kQThreads = 512, kQSlots = 256, kQMaxSplit = 16;
+constexpr int kQThreads = 512;
 constexpr int kQLRW = 72;  // halves per LDS weight row (64 k + 8 pad)
 constexpr int kQLRA = 72;  // bytes per LDS activation row (64 codes + 8 pad)
 
@@ -487,27 +488,6 @@ using Q41Big = Q41Cfg<2, 4, 2, 2>;   // 128 weight rows x 256 tokens
 using Q41M128 = Q41Cfg<2, 4, 2, 1>;  // 128 weight rows x 128 tokens
 using Q41Mid = Q41Cfg<4, 2, 2, 1>;   // 256 weight rows x 64 tokens
 
-struct Q41Plan {
-  int64_t tiles_n, tiles, full, split_tiles;
-  int split;
-  int stages;
-};
-
-template <class C>
-Q41Plan q41_plan(int64_t M, int64_t N, int64_t K) {
-  Q41Plan p;
-  p.tiles_n = (N + C::BN - 1) / C::BN;
-  p.tiles = p.tiles_n * ((M + C::BM - 1) / C::BM);
-  p.stages = (int)(K / 64);
-  const int64_t r = p.tiles % kQSlots;
-  p.split = 1;
-  if (r != 0) p.split = (int)std::min<int64_t>({kQSlots / r, (int64_t)kQMaxSplit, (int64_t)p.stages});
-  if (p.split < 2) p.split = 1;
-  p.split_tiles = p.split > 1 ? r : 0;
-  p.full = p.tiles - p.split_tiles;
-  return p;
-}
-
 // which kernel runs a Q4_1 GEMM of this shape (the GEMV kernel falls back to the
 // tiled one for rows longer than 20480)
 constexpr int kQ41GemvMaxM = 16;
@@ -521,19 +501,11 @@ Q41Path q41_path(int64_t M, int64_t K) {
 
 }  // namespace
 
-namespace {
-template <class C>
-size_t q41_workspace(int64_t M, int64_t N, int64_t K) {
-  const Q41Plan p = q41_plan<C>(M, N, K);
-  return (size_t)(p.split_tiles * p.split) * kQThreads * C::kAcc * sizeof(float);
-}
-}  // namespace
-
 size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K) {
   switch (q41_path(M, K)) {
-    case kQ41Mid: return q41_workspace<Q41Mid>(M, N, K);
-    case kQ41M128: return q41_workspace<Q41M128>(M, N, K);
-    case kQ41Big: return q41_workspace<Q41Big>(M, N, K);
+    case kQ41Mid: return ksplit_workspace<Q41Mid>(M, N, K);
+    case kQ41M128: return ksplit_workspace<Q41M128>(M, N, K);
+    case kQ41Big: return ksplit_workspace<Q41Big>(M, N, K);
     default: return 0;
   }
 }
@@ -543,7 +515,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
                                                                  const int8_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ d16, int64_t M,
                                                                  float* __restrict__ y, float* __restrict__ part_ws,
-                                                                 Q41Plan plan) {
+                                                                 KSplitPlan plan) {
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kQLRW, LRA = kQLRA, CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -755,55 +727,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   }
 }
 
-// Sums the K parts of every split tile in part order (p = 0, 1, ...) and stores the
-// tile; block (split tile, group of 8 accumulator slots), as for the NVFP4 kernel.
-template <class C>
-__global__ __launch_bounds__(512) void gemm_q4_1_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
-                                                               int64_t M, float* __restrict__ y, Q41Plan plan) {
-  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM, kGroups = C::kAcc / 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave / WM, wm = wave % WM;
-  const int64_t st = blockIdx.x / kGroups;
-  const int grp = blockIdx.x % kGroups;
-  const int ij = grp >> 1, i = ij / TM, j = ij % TM, e0 = 8 * grp;
-  const int64_t tile = plan.full + st;
-  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
-  const float* src = part_ws + (st * plan.split * C::kAcc + e0) * kQThreads + tid;
-  float v[8][kQMaxSplit];
-#pragma unroll
-  for (int p = 0; p < kQMaxSplit; ++p)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      v[e][p] = p < plan.split ? src[((int64_t)p * C::kAcc + e) * kQThreads] : 0.0f;
-  const int64_t m = m0 + wm * (32 * TM) + 32 * j + (lane & 31);
-  if (m >= M) return;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float o[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      float s = v[4 * h + rr][0];
-#pragma unroll
-      for (int p = 1; p < kQMaxSplit; ++p)
-        if (p < plan.split) s += v[4 * h + rr][p];
-      o[rr] = s;
-    }
-    const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5);
-    if ((N & 3) == 0 && n + 3 < N) {
-      *reinterpret_cast<floatx4*>(y + m * N + n) = floatx4{o[0], o[1], o[2], o[3]};
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (n + rr < N) y[m * N + n + rr] = o[rr];
-    }
-  }
-}
-
 namespace {
 template <class C>
 hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
                             int64_t K, float* y, float* workspace, hipStream_t stream) {
-  const Q41Plan plan = q41_plan<C>(M, N, K);
+  const KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
   hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
@@ -813,9 +741,7 @@ hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d
                      (int)K, q, d16, M, y, workspace, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
-  hipLaunchKernelGGL(gemm_q4_1_reduce_kernel<C>, dim3((unsigned)(plan.split_tiles * (C::kAcc / 8))),
-                     dim3(kQThreads), 0, stream, workspace, N, M, y, plan);
-  return hipGetLastError();
+  return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
 }
 }  // namespace
 
