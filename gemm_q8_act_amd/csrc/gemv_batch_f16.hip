@@ -1,4 +1,4 @@
-// gemv_batch_f16.hip -- batched decode GEMV (2 <= M <= 8 tokens per launch), NVFP4
+// gemv_batch_f16.hip -- batched decode GEMV (2 <= M <= 16 tokens per launch), NVFP4
 // weights x Q8_0 activations, on gfx950's fp16 matrix cores.
 //
 // What is computed ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3):
@@ -41,13 +41,13 @@
 
 namespace nvq {
 
-template <int T, int W, int D>
+template <int T, int W, int D, int G>
 __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
                                                                 const int8_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ d16, int M,
                                                                 float w_scale, float* __restrict__ y) {
   constexpr int NT = 64 * W;
-  __shared__ floatx4 red[W * T * 64];
+  __shared__ floatx4 red[W * T * G * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fg = lane >> 4;
   const int nch = (K + 127) >> 7;
@@ -66,26 +66,35 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
     st[t] = w + ntiles * nch * 1024 + tile * nch * 128;
   }
   const uint32_t wl = 16 * lane, sl = 2 * lane;
-  // this lane's activation column: token fr % 8 (columns of absent tokens repeat the
-  // last token and are never stored), part hi (fr < 8) or lo (fr >= 8)
-  const int m = min(fr & 7, M - 1);
+  // this lane's activation column in token group gi: token 8 gi + fr % 8 (columns of
+  // absent tokens repeat the last token and are never stored), part hi (fr < 8) or
+  // lo (fr >= 8)
   const bool lo_lane = fr >= 8;
-  const uint32_t qoff = (uint32_t)m * (uint32_t)K, doff = (uint32_t)m * (uint32_t)nb;
+  uint32_t qoff[G], doff[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int m = min(8 * gi + (fr & 7), M - 1);
+    qoff[gi] = (uint32_t)m * (uint32_t)K;
+    doff[gi] = (uint32_t)m * (uint32_t)nb;
+  }
 
   // D load slots, each one chunk ahead of the next: slot j holds chunk c + W j.  The
   // hi and lo lanes of a token need the same 32 codes: each loads 16 of them (hi lanes
   // the first half, lo lanes the second) and takes the other half from its partner
   // lane (fr ^ 8) when the chunk is consumed.
-  u32x4 qa[D], bw[D][T];
-  uint32_t dv[D], bs[D][T];
+  u32x4 qa[G][D], bw[D][T];
+  uint32_t dv[G][D], bs[D][T];
   auto issue = [&](int j, int c) {
     // chunk index clamped (loads past the row's last chunk are never consumed); k
     // groups past the row's end (a last chunk of 64) read the row's last 32 codes and
     // get scale 0 when consumed, so they contribute nothing
     c = min(c, nch - 1);
     const int b = min(4 * c + fg, nb - 1);
-    qa[j] = *reinterpret_cast<const u32x4*>(q + (qoff + 32 * b + (lo_lane ? 16 : 0)));
-    dv[j] = d16[doff + b];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      qa[gi][j] = *reinterpret_cast<const u32x4*>(q + (qoff[gi] + 32 * b + (lo_lane ? 16 : 0)));
+      dv[gi][j] = d16[doff[gi] + b];
+    }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       bw[j][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt[t] + (int64_t)c * 1024 + wl));
@@ -93,41 +102,54 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
     }
   };
 
-  floatx4 acc[T];
+  floatx4 acc[G][T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[gi][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk of slot j with activation scale dd (binary16 bits): for each of the 4
-  // k groups, its activation operand, then the T weight operands and MFMAs into a[]
-  auto chunk = [&](int j, uint32_t dd, floatx4* a) {
-    const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)dd);
-    const half2_t d2 = {dh, dh};
+  // one chunk of slot j with the token groups' activation scales dd[] (binary16 bits):
+  // for each of the 4 k groups, the activation operand of every token group, then the
+  // T weight operands (expanded once for all groups) and MFMAs into a[][]
+  auto chunk = [&](int j, const uint32_t* dd, floatx4 (*a)[T]) {
     const half2_t z2 = {(_Float16)0.0f, (_Float16)0.0f};
-    const half2_t dl2 = lo_lane ? d2 : z2;
+    half2_t d2[G], dl2[G];
+    u32x4 qlo[G], qhi[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)dd[gi]);
+      d2[gi] = half2_t{dh, dh};
+      dl2[gi] = lo_lane ? d2[gi] : z2;
+      // the partner's 16 codes (row_ror:8 swaps lanes fr and fr ^ 8 of each row of 16)
+      u32x4 oth;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oth[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)qa[gi][j][i], 0x128, 0xF, 0xF, false);
+      qlo[gi] = lo_lane ? oth : qa[gi][j];
+      qhi[gi] = lo_lane ? qa[gi][j] : oth;
+    }
     _Float16 s[T][2];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       s[t][0] = (_Float16)ue4m3_to_f32<0>(bs[j][t]);
       s[t][1] = (_Float16)ue4m3_to_f32<1>(bs[j][t]);
     }
-    // the partner's 16 codes (row_ror:8 swaps lanes fr and fr ^ 8 of each row of 16)
-    u32x4 oth;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oth[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)qa[j][i], 0x128, 0xF, 0xF, false);
-    const u32x4 qlo = lo_lane ? oth : qa[j], qhi = lo_lane ? qa[j] : oth;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const u32x4& qq = u < 2 ? qlo : qhi;
-      const uint32_t w0 = qq[2 * (u & 1)], w1 = qq[2 * (u & 1) + 1];
-      half2_t x0, x1, x2, x3;
-      i8x4_to_f16x4(w0, x0, x1);
-      i8x4_to_f16x4(w1, x2, x3);
-      // hi lanes: fma(q, d, -0) = fp16(d q); lo lanes: fma(q, d, -fp16(d q)) = lo
-      const half2_t b0 = __builtin_elementwise_fma(x0, d2, -(x0 * dl2));
-      const half2_t b1 = __builtin_elementwise_fma(x1, d2, -(x1 * dl2));
-      const half2_t b2 = __builtin_elementwise_fma(x2, d2, -(x2 * dl2));
-      const half2_t b3 = __builtin_elementwise_fma(x3, d2, -(x3 * dl2));
-      const half8_t B = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+      half8_t B[G];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const u32x4& qq = u < 2 ? qlo[gi] : qhi[gi];
+        const uint32_t w0 = qq[2 * (u & 1)], w1 = qq[2 * (u & 1) + 1];
+        half2_t x0, x1, x2, x3;
+        i8x4_to_f16x4(w0, x0, x1);
+        i8x4_to_f16x4(w1, x2, x3);
+        // hi lanes: fma(q, d, -0) = fp16(d q); lo lanes: fma(q, d, -fp16(d q)) = lo
+        const half2_t b0 = __builtin_elementwise_fma(x0, d2[gi], -(x0 * dl2[gi]));
+        const half2_t b1 = __builtin_elementwise_fma(x1, d2[gi], -(x1 * dl2[gi]));
+        const half2_t b2 = __builtin_elementwise_fma(x2, d2[gi], -(x2 * dl2[gi]));
+        const half2_t b3 = __builtin_elementwise_fma(x3, d2[gi], -(x3 * dl2[gi]));
+        B[gi] = half8_t{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+      }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const half2_t sc = {s[t][u >> 1], s[t][u >> 1]};
@@ -137,17 +159,26 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
         const half2_t p2 = e2m1x2_to_f16<2>(cw) * sc;
         const half2_t p3 = e2m1x2_to_f16<3>(cw) * sc;
         const half8_t A = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        a[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, a[t], 0, 0, 0);
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) a[gi][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[gi], a[gi][t], 0, 0, 0);
       }
     }
   };
 
-  // scale of slot j's chunk c for this lane: 0 past the row's end; `big` marks
-  // |d| >= 512, whose blocks are left out here and done by the second pass below
-  auto scale = [&](int j, int c, bool& big) {
-    const uint32_t d = 4 * c + fg < nb ? dv[j] : 0u;
-    big = (d & 0x7FFFu) >= 0x6000u;
-    return d;
+  // scales of slot j's chunk c for this lane (one per token group): 0 past the row's
+  // end; `big` marks |d| >= 512, whose blocks are left out here (scale 0) and done by
+  // the second pass below, which takes d / 256 for them (exponent field - 8; such a d
+  // is normal and d / 256 >= 2 stays normal) and 0 for the others
+  auto scales = [&](int j, int c, bool second, uint32_t* dd) {
+    bool any = false;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const uint32_t d = 4 * c + fg < nb ? dv[gi][j] : 0u;
+      const bool big = (d & 0x7FFFu) >= 0x6000u;
+      any |= big;
+      dd[gi] = second ? (big ? d - 0x2000u : 0u) : (big ? 0u : d);
+    }
+    return any;
   };
 
   // software pipeline: slot j is consumed, then refilled with the chunk D slots later,
@@ -159,60 +190,73 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       if (c + W * j < nch) {
-        bool big;
-        const uint32_t d = scale(j, c + W * j, big);
-        any_big |= __builtin_amdgcn_ballot_w64(big);
-        chunk(j, big ? 0u : d, acc);
+        uint32_t dd[G];
+        any_big |= __builtin_amdgcn_ballot_w64(scales(j, c + W * j, false, dd));
+        chunk(j, dd, acc);
       }
       issue(j, c + W * (j + D));
     }
   }
   // blocks with |d| >= 512 (only for activations near the binary16 range): one more
-  // pass over this wavefront's chunks with d / 256 (exponent field - 8; such a d is
-  // normal and d / 256 >= 2 stays normal) into the accumulator that is scaled by 256
+  // pass over this wavefront's chunks into the accumulator that is scaled by 256
   if (any_big) {
-    floatx4 accb[T];
+    floatx4 accb[G][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) accb[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int t = 0; t < T; ++t) accb[gi][t] = floatx4{0.f, 0.f, 0.f, 0.f};
     for (int c = wave; c < nch; c += W) {
       issue(0, c);
-      bool big;
-      const uint32_t d = scale(0, c, big);
-      chunk(0, big ? d - 0x2000u : 0u, accb);
+      uint32_t dd[G];
+      (void)scales(0, c, true, dd);
+      chunk(0, dd, accb);
     }
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] += 256.0f * accb[t];
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[gi][t] += 256.0f * accb[gi][t];
   }
 
-  // reduce the W wavefronts' partial tiles; column j < 8 + column j + 8 = token j
+  // reduce the W wavefronts' partial tiles; in token group gi, column j < 8 +
+  // column j + 8 = token 8 gi + j
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[t];
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[((wave * G + gi) * T + t) * 64 + lane] = acc[gi][t];
   __syncthreads();
   const float* rf = reinterpret_cast<const float*>(red);
-  for (int o = tid; o < 8 * 16 * T; o += NT) {
+  for (int o = tid; o < 8 * G * 16 * T; o += NT) {
     const int mo = o / (16 * T), rr = o % (16 * T);
-    const int t = rr >> 4, r = rr & 15;
+    const int t = rr >> 4, r = rr & 15, gi = mo >> 3;
     const int64_t row = (tile0 + t) * 16 + r;
     if (mo >= M || row >= N) continue;
-    const int l_hi = mo + 16 * (r >> 2), l_lo = l_hi + 8, v = r & 3;
+    const int l_hi = (mo & 7) + 16 * (r >> 2), l_lo = l_hi + 8, v = r & 3;
     float s = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
-      const int base = (ww * T + t) * 64;
+      const int base = ((ww * G + gi) * T + t) * 64;
       s += rf[(base + l_hi) * 4 + v] + rf[(base + l_lo) * 4 + v];
     }
     y[(int64_t)mo * N + row] = s * w_scale;
   }
 }
 
-template <int T, int W, int D>
+template <int T, int W, int D, int G>
 static hipError_t launch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int M,
                              int64_t N, int64_t K, float* y, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   const unsigned blocks = (unsigned)((ntiles + T - 1) / T);
-  hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D>), dim3(blocks), dim3(64 * W), 0, stream, w, N, (int)K, q,
+  hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D, G>), dim3(blocks), dim3(64 * W), 0, stream, w, N, (int)K, q,
                      d16, M, w_scale, y);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
+                                   int M, int64_t N, int64_t K, float* y, hipStream_t stream) {
+  return T == 4   ? launch_f16<4, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream)
+         : T == 3 ? launch_f16<3, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream)
+                  : launch_f16<2, 8, 3, G>(w, w_scale, q, d16, M, N, K, y, stream);
 }
 
 // Tiles per block for many tiles.  The vector work of a block per chunk is about
@@ -232,22 +276,22 @@ static int tiles_per_block(int64_t ntiles) {
   return best;
 }
 
-// Tokens in groups of at most 8, one launch per group (each streams the weights once).
-// Fewer than 1024 tiles (QKV, O, down at hidden 5120): 2 tiles x 8 wavefronts x 3
-// slots, so the blocks keep enough loads in flight; more: T tiles x 4 wavefronts x 2
-// slots (every wavefront resident at once).
+// Tokens in launches of at most 16, each streaming the weights once: up to 8 tokens
+// as one group of MFMA columns, 9 to 16 as two groups that share every weight
+// expansion.  Fewer than 1024 tiles (QKV, O, down at hidden 5120): 2 tiles x 8
+// wavefronts x 3 slots, so the blocks keep enough loads in flight; more: T tiles x 4
+// wavefronts x 2 slots (every wavefront resident at once).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
                                        int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   const int T = ntiles < 1024 ? 0 : tiles_per_block(ntiles);
-  for (int64_t m0 = 0; m0 < M; m0 += 8) {
-    const int mb = (int)(M - m0 < 8 ? M - m0 : 8);
+  for (int64_t m0 = 0; m0 < M; m0 += 16) {
+    const int mb = (int)(M - m0 < 16 ? M - m0 : 16);
     const int8_t* qb = q + m0 * K;
     const uint16_t* db = d16 + m0 * (K / 32);
     float* yb = y + m0 * N;
-    const hipError_t e = T == 4   ? launch_f16<4, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
-                         : T == 3 ? launch_f16<3, 4, 2>(w, w_scale, qb, db, mb, N, K, yb, stream)
-                                  : launch_f16<2, 8, 3>(w, w_scale, qb, db, mb, N, K, yb, stream);
+    const hipError_t e = mb > 8 ? launch_f16_group<2>(T, w, w_scale, qb, db, mb, N, K, yb, stream)
+                                : launch_f16_group<1>(T, w, w_scale, qb, db, mb, N, K, yb, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
