@@ -681,8 +681,8 @@ def main():
                             value=g2["TFLOPs"], unit="TFLOP/s",
                             roofline=dict(bound="mfma", achieved=g2["TFLOPs"], peak=FP16_PEAK_TFLOPS,
                                           unit="TFLOP/s", frac=g2["frac"], traffic=None,
-                                          kernel="gemm_nvfp4_kernel + gemm_nvfp4_reduce_kernel (fp16 MFMA "
-                                                 "32x32x16 on the exact hi/lo activation split)",
+                                          kernel="gemm_nvfp4_kernel<NvCfg<2,4,4,2>> + ksplit_reduce_kernel (fp16 "
+                                                 "MFMA 32x32x16 on the exact hi/lo activation split)",
                                           mfma_issued_frac=2.0 * g2["frac"],
                                           note="algorithmic flops 2*M*N*K; the hi/lo split issues twice "
                                                "that on the matrix cores"),

@@ -112,7 +112,7 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K) {
 }
 
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  // M > 64: fp32 partial tiles of the K-split work items that fill the last round
+  // M > 16: fp32 partial tiles of the K-split work items that fill the last round
   // over the compute units.
   if ((fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1) || M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
   return fmt == NVQ_FMT_NVFP4 ? nvq::gemm_nvfp4_workspace(M, N, K) : nvq::gemm_q4_1_workspace(M, N, K);

@@ -17,8 +17,8 @@ hipError_t launch_act_quant(const float* x, int64_t M, int64_t K, int8_t* q, uin
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
                                 int32_t* isums, int mode, hipStream_t stream);
-// NVFP4, 2 <= M <= 15 tokens: exact fp16 operands on the fp16 matrix core (groups of
-// up to 8 tokens, one launch per group).  No limit on K.
+// NVFP4, 2 <= M <= 16 tokens: exact fp16 operands on the fp16 matrix core, one launch
+// (one weight stream) per 16 tokens.  No limit on K.
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q,
                                        const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                                        hipStream_t stream);
@@ -30,23 +30,24 @@ hipError_t launch_gemv_nvfp4_routed(const uint8_t* w, const float* w_scales, con
 // LDS bytes the decode GEMV needs for a row length K.
 size_t gemv_lds_bytes(int64_t K);
 
-// NVFP4, MFMA tiled paths (any M >= 1; used for M >= 2).  isums != nullptr selects
-// the debug variant.  M > 64 uses the split-activation kernel, whose K-split parts
-// need gemm_nvfp4_workspace(M, N, K) bytes of device workspace (may be 0).
+// NVFP4 GEMM paths (any M >= 1): M = 1 the tiled kernel (rows too long for the decode
+// kernels), 2 <= M <= 16 the batched decode kernel, M > 16 the split-activation
+// kernel, whose K-split parts need gemm_nvfp4_workspace(M, N, K) bytes of device
+// workspace (may be 0).  isums != nullptr selects the tiled debug variant.
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream);
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
 
-// Q4_1 GEMV (any M; the API uses it for M <= 15), integer-dot path; with isums the
+// Q4_1 GEMV (any M; used for M <= 16), integer-dot path; with isums the
 // debug sums [M][N][K/16].
 hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, hipStream_t stream);
 
-// Q4_1, MFMA paths (any M >= 1): the tiled kernel for M <= 64 or K % 64 != 0, the
-// two-term fp16 kernel otherwise, which needs gemm_q4_1_workspace(M, N, K) bytes of
-// device workspace (may be 0).
+// Q4_1 GEMM paths (any M >= 1): M <= 16 the GEMV kernel, M > 16 the two-term fp16
+// kernel when K % 64 == 0 (it needs gemm_q4_1_workspace(M, N, K) bytes of device
+// workspace, may be 0), else the tiled kernel, which also gives the debug sums.
 hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, float* workspace, hipStream_t stream);

@@ -7,18 +7,19 @@
 //     sum_k w*a = da * (d * sum_k c*q + m * sum_k q),
 // the second sum being the block's activation code sum (two bsum16 values).
 //
-// GEMV (M <= 15): same lane mapping as the NVFP4 GEMV -- a unit is one 32-weight
+// GEMV (M <= 16): same lane mapping as the NVFP4 GEMV -- a unit is one 32-weight
 // block (16 B of codes + one 4-byte (d, m) pair), the codes are unsigned nibbles
 // used directly as int8 by v_dot4_i32_i8.  A wavefront holds its rows' weights in
 // registers and walks the tokens, reading each token's activations (cache-resident)
 // once per row group.
 //
-// GEMM, M <= 64 (and K % 64 != 0): like the NVFP4 tiled kernel with a 32-k stage;
-// codes become exact integer-valued fp16, P = sum c*q over the block is an exact fp32
-// integer (|P| <= 32*15*127 = 60960), and per element acc += da*(d*P + m*bsum32).
+// GEMM, tiled (K % 64 != 0, and the debug sums): like the NVFP4 tiled kernel with a
+// 32-k stage; codes become exact integer-valued fp16, P = sum c*q over the block is an
+// exact fp32 integer (|P| <= 32*15*127 = 60960), and per element
+// acc += da*(d*P + m*bsum32).
 //
-// GEMM, M > 64 and K % 64 == 0: both operands as two binary16 terms, so the matrix
-// core accumulates whole rows (see gemm_q4_1_big_kernel below).
+// GEMM, M > 16 and K % 64 == 0: both operands as two binary16 terms, so the matrix
+// core accumulates whole rows (see gemm_q4_1_f16x2_kernel below).
 #include <algorithm>
 
 #include "ksplit.h"

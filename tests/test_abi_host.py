@@ -184,7 +184,7 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 15, 8, 64, A16, None, 0, None) == -2   # M < 16
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 32, A16, None, 0, None) == -2   # K % 64
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 16, 8, 64, MIS, None, 0, None) == -4   # y alignment
-    # M > 64 with K-split parts needs a workspace: missing -> NVQ_ERR_WORKSPACE before any device call
+    # M > 16 with K-split parts needs a workspace: missing -> NVQ_ERR_WORKSPACE before any device call
     assert L.nvq_gemm_workspace_bytes(0, 100, 8, 640) > 0
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, None, 0, None) == -7
     assert L.nvq_gemm_nvfp4(A16, 1.0, A16, A16, 100, 8, 640, A16, A16, 16, None) == -7   # too small
