@@ -466,26 +466,36 @@ def test_side_stream_and_graph_replay():
     wr = to_dev(np.concatenate([nvq.nvq_pack_nvfp4(c, s) for c, s, _ in experts]))
     wsc = torch.from_numpy(np.array([v for _, _, v in experts], np.float32)).cuda()
     ids = torch.from_numpy(np.array([[2, 0]], np.int32)).cuda()
-    xs = {M: to_dev(synth.activations(M, K, 70 + M, outliers=True)) for M in (1, 8, 80)}
+    qw, dw, mw = synth.q4_1_weights(N, K, 63)
+    w41 = to_dev(nvq.nvq_pack_q4_1(qw, dw, mw))
+    # every dispatch: decode, batched (one and two column groups), the three GEMM tile
+    # heights with K-split parts; Q4_1 GEMV (one and several tokens) and GEMM
+    Ms = (1, 8, 12, 40, 80, 200)
+    xs = {M: to_dev(synth.activations(M, K, 70 + M, outliers=True)) for M in Ms}
     qd = {M: (torch.empty((M, K), dtype=torch.int8, device="cuda"),
-              torch.empty((M, K // 32), dtype=torch.int16, device="cuda")) for M in xs}
+              torch.empty((M, K // 32), dtype=torch.int16, device="cuda"),
+              torch.empty((M, K // 16), dtype=torch.int16, device="cuda")) for M in xs}
     ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
+    ys41 = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
     yr = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
-    wsp = torch.empty(max(nvq.lib().nvq_gemm_workspace_bytes(0, 80, N, K), 16), dtype=torch.uint8, device="cuda")
+    need = max(nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms)
+    wsp = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
 
     def seq():
         for M, x in xs.items():
-            q, d = qd[M]
-            nvq.nvq_quantize_act_q8_0(x, q, d)
+            q, d, b = qd[M]
+            nvq.nvq_quantize_act_q8_0(x, q, d, b)
             if M < 16:
                 nvq.nvq_gemv_nvfp4(w, ws, q, d, ys[M])
+                nvq.nvq_gemv_q4_1(w41, q, d, b, ys41[M])
             else:
                 nvq.nvq_gemm_nvfp4(w, ws, q, d, ys[M], workspace=wsp)
+                nvq.nvq_gemm_q4_1(w41, q, d, b, ys41[M], workspace=wsp)
         nvq.nvq_gemv_nvfp4_routed(wr, wsc, ids, qd[1][0], qd[1][1], yr)
 
     def snapshot():
-        return [host(ys[M]).copy() for M in xs] + [host(yr).copy()]
+        return [host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -505,7 +515,7 @@ def test_side_stream_and_graph_replay():
         torch.cuda.synchronize()
         for M in xs:
             xs[M].copy_(saved[M])
-        for y in list(ys.values()) + [yr]:
+        for y in list(ys.values()) + list(ys41.values()) + [yr]:
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
