@@ -415,6 +415,25 @@ def test_q4_1_gemm_activation_range(M):
     assert (ys[0][rows] == ys[1][rows]).all()
 
 
+@pytest.mark.parametrize("M", [3, 12, 16, 20, 100, 300])
+def test_single_output_row(oracle, M):
+    """N = 1 (one weight row, every tile ragged) through each NVFP4 and Q4_1 dispatch,
+    at the shortest and a long K."""
+    say(f"N = 1, M={M}")
+    torch = torch_dev()
+    for K in (64, 5120):
+        c = NvCase(M, 1, K, 5000 + M + K)
+        y = torch.empty((M, 1), dtype=torch.float32, device="cuda")
+        (nvq.nvq_gemv_nvfp4 if M <= nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemm_nvfp4)(c.w, c.ws, c.q, c.d, y)
+        yo, awa = c.oracle_y(oracle)
+        check_y(host(y), yo, awa, f"nvfp4 N=1 M={M} K={K}")
+        c4 = Q41Case(M, 1, K, 6000 + M + K)
+        y4 = torch.empty((M, 1), dtype=torch.float32, device="cuda")
+        (nvq.nvq_gemv_q4_1 if M <= nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemm_q4_1)(c4.w, c4.q, c4.d, c4.b, y4)
+        yo4, awa4 = c4.oracle_y(oracle)
+        check_y(host(y4), yo4, awa4, f"q4_1 N=1 M={M} K={K}")
+
+
 @pytest.mark.parametrize("path", [nvq.NVQ_PATH_GEMV, nvq.NVQ_PATH_GEMM])
 def test_q4_1_isums_bit_exact(oracle, path):
     say(f"q4_1 isums path={path}")
