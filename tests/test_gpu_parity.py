@@ -415,6 +415,32 @@ def test_q4_1_gemm_activation_range(M):
     assert (ys[0][rows] == ys[1][rows]).all()
 
 
+@pytest.mark.parametrize("fmt,M,N", [("nvfp4", 300, 2560), ("nvfp4", 100, 5120), ("nvfp4", 40, 5120),
+                                      ("q4_1", 300, 2560), ("q4_1", 100, 2560), ("q4_1", 40, 5120)])
+def test_gemm_ksplit_many_parts(oracle, fmt, M, N):
+    """20 (or 40) tiles of 20 stages in the last round, each split into 12 (or 6) K
+    parts summed in order; repeat calls bitwise identical.  One shape per token-tile
+    height and format."""
+    say(f"{fmt} gemm K-split parts M={M} N={N}")
+    torch = torch_dev()
+    K = 1280
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    cols = sample_cols(N, 96, M + N)
+    if fmt == "nvfp4":
+        c = NvCase(M, N, K, 7100 + M, w_scale=0.75)
+        nvq.nvq_gemm_nvfp4(c.w, c.ws, c.q, c.d, y)
+        first = host(y).copy()
+        nvq.nvq_gemm_nvfp4(c.w, c.ws, c.q, c.d, y)
+    else:
+        c = Q41Case(M, N, K, 7200 + M)
+        nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+        first = host(y).copy()
+        nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+    assert (host(y).view(np.uint32) == first.view(np.uint32)).all()
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(first[:, cols], yo, awa, f"{fmt} tail crossing M={M} N={N}")
+
+
 @pytest.mark.parametrize("M", [3, 12, 16, 20, 100, 300])
 def test_single_output_row(oracle, M):
     """N = 1 (one weight row, every tile ragged) through each NVFP4 and Q4_1 dispatch,
