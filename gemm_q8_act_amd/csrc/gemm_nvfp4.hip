@@ -299,11 +299,11 @@ using NvM128 = NvCfg<4, 2, 2, 2>; // 256 weight rows x 128 tokens
 using NvMid = NvCfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
 
 // which kernel runs an NVFP4 GEMM of M tokens: M = 1 only for rows too long for the
-// decode kernels' activation table
+// decode kernels' activation table; the batched kernel indexes activations in 32 bits
 enum NvPath { kNvTiled, kNvBatched, kNvMid, kNvM128, kNvBig };
-NvPath nv_path(int64_t M) {
+NvPath nv_path(int64_t M, int64_t K) {
   if (M == 1) return kNvTiled;
-  if (M <= 16) return kNvBatched;
+  if (M <= 16 && M * K < (int64_t(1) << 32)) return kNvBatched;
   if (M <= 64) return kNvMid;
   return M <= 128 ? kNvM128 : kNvBig;
 }
@@ -311,7 +311,7 @@ NvPath nv_path(int64_t M) {
 }  // namespace
 
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
-  switch (nv_path(M)) {
+  switch (nv_path(M, K)) {
     case kNvMid: return ksplit_workspace<NvMid>(M, N, K);
     case kNvM128: return ksplit_workspace<NvM128>(M, N, K);
     case kNvBig: return ksplit_workspace<NvBig>(M, N, K);
@@ -529,7 +529,7 @@ hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream) {
   if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
-  switch (nv_path(M)) {
+  switch (nv_path(M, K)) {
     case kNvBatched: return launch_gemv_nvfp4_batch_f16(w, w_scale, q, d16, M, N, K, y, stream);
     case kNvMid: return launch_two_term<NvMid>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
     case kNvM128: return launch_two_term<NvM128>(w, w_scale, q, d16, M, N, K, y, workspace, stream);

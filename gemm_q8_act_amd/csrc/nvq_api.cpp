@@ -198,6 +198,8 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
                           int64_t M, int64_t N, int64_t K, float* y, void* stream) {
   NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_nvfp4"));
   NVQ_TRY(check_dims(M, N, K, 64, 1, NVQ_GEMV_MAX_M));
+  if (M > 1 && M * K >= (int64_t(1) << 32))  // the batched kernel indexes activations in 32 bits
+    return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4: M*K=%lld too large for the batched kernel (< 2^32)", (long long)(M * K));
   NVQ_TRY(check_device());
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   if (M == 1 && gemv_fits_lds(K))

@@ -18,7 +18,8 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
                                 int32_t* isums, int mode, hipStream_t stream);
 // NVFP4, 2 <= M <= 16 tokens: exact fp16 operands on the fp16 matrix core, one launch
-// (one weight stream) per 16 tokens.  No limit on K.
+// (one weight stream) per 16 tokens.  Any K with M * K < 2^32 (32-bit activation
+// offsets; the callers check).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q,
                                        const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                                        hipStream_t stream);

@@ -152,8 +152,8 @@ nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
  * y [M][N] float32 (overwritten).  M == 1 runs the decode kernel whose per-16
  * integer sums come from the matrix cores reading the FP4 codes directly (K up to
  * what its on-chip activation table holds, about 70000; longer rows run the tiled
- * kernel).  2 <= M runs the batched kernel, all tokens in one launch streaming the
- * weights once: exact binary16 operands (E2M1 * UE4M3 weights;
+ * kernel).  2 <= M runs the batched kernel (M * K < 2^32, NVQ_ERR_SHAPE otherwise),
+ * all tokens in one launch streaming the weights once: exact binary16 operands (E2M1 * UE4M3 weights;
  * d * q split exactly into two binary16 terms) on the fp16 matrix cores, any K.
  * Per output the error against the exact product is at most 1e-5 * sum_k |W*A|
  * + 1e-6 (float32 accumulation of exact terms). */

@@ -176,6 +176,7 @@ def test_gemv_validation_without_gpu():
     assert L.nvq_gemv_nvfp4(MIS, 1.0, A16, A16, 1, 8, 64, A16, st) == -4     # w alignment
     assert L.nvq_gemv_nvfp4(A16, 1.0, A16, ctypes.c_void_p(0x20001), 1, 8, 64, A16, st) == -4
     assert L.nvq_gemv_q4_1(A16, A16, A16, None, 1, 8, 32, A16, st) == -1     # bsum16 required
+    assert L.nvq_gemv_nvfp4(A16, 1.0, A16, A16, 3, 8, (1 << 31) - 64, A16, st) == -2  # batched: M*K < 2^32
     assert L.nvq_gemv_q4_1(A16, A16, A16, A2, 1, 8, 48, A16, st) == -2       # K % 32
 
 
