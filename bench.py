@@ -17,6 +17,12 @@ stack (M = 1 or 8) of the same layer shapes.
 Roofline: per-kernel durations come from HIP events recorded on the stream the
 kernels are launched on (torch's current stream).  Peaks: HBM 8000 GB/s, dense
 fp16 MFMA 2500 TFLOP/s (the GEMM computes in fp16 x fp16 -> fp32).
+
+Every timed region starts at the GPU's steady clock: the W warm-up steps of the
+layer (default 2000, about 0.1 s, before K = 2000 timed steps) and, for every other
+measurement, about 0.25 s of untimed repeats of the same work run right before it.  An idle MI355X needs tens of
+milliseconds to raise its engine clock; a GEMM timed during that ramp reads ~20 %
+slow, an HBM-bound GEMV about 1 %.
 """
 from __future__ import annotations
 
@@ -44,9 +50,12 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--copies", type=int, default=8, help="distinct HBM copies of the layer weights")
+    p.add_argument("--spin-up", type=float, default=0.25,
+                   help="seconds of untimed repeats before each timed measurement other than the layer step "
+                        "(shorter values keep profiler traces small)")
     p.add_argument("--eager", action="store_true",
                    help="launch every kernel from Python instead of replaying a captured HIP graph")
     p.add_argument("--no-gemm", action="store_true")
@@ -155,8 +164,8 @@ def time_layer(args):
     M = 1
     layer = Layer(M, args.copies)
     torch.cuda.synchronize()
-    for s in range(args.warmup):
-        layer.step(s % args.copies)
+    for c in range(args.copies):  # one eager pass over every weight copy before capture
+        layer.step(c)
     torch.cuda.synchronize()
 
     graph = None
@@ -171,10 +180,15 @@ def time_layer(args):
                     layer.step(c)
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
-        for _ in range(2):
-            graph.replay()
-        torch.cuda.synchronize()
 
+    # the W untimed warm-up steps run right before the timed region: an idle GPU takes
+    # tens of milliseconds to raise its engine clock
+    if graph is not None:
+        for _ in range(max(1, -(-args.warmup // args.copies))):
+            graph.replay()
+    else:
+        for s in range(args.warmup):
+            layer.step(s % args.copies)
     steps = args.steps
     if graph is not None:
         reps = max(1, steps // args.copies)
@@ -203,8 +217,8 @@ def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
     """Average launch duration of one GEMV: HIP events (on the launch stream) around a
     batch of back-to-back launches that rotate through at least ``min_bytes`` of
     distinct weight copies, so no launch finds its weights in the 256 MB Infinity
-    Cache.  A sleep kernel queued before each batch lets the host enqueue the whole
-    batch before the GPU reaches it, so the batch runs at the GPU's pace."""
+    Cache.  A backlog queued before each batch (see ``backlog``) lets the host enqueue
+    the whole batch before the GPU reaches it, so the batch runs at the GPU's pace."""
     import torch
 
     import gemm_q8_act_amd as nvq
@@ -213,14 +227,12 @@ def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
     wbytes = nvfp4_bytes(m["N"], m["K"])
     extra = max(0, -(-min_bytes // wbytes) - len(m["w"]))
     ws = list(m["w"]) + [m["w"][i % len(m["w"])].clone() for i in range(extra)]
-    for w in ws:
-        fn(w, m["ws"], m["q"], m["d"], m["y"])
-    torch.cuda.synchronize()
-    cyc = int(sleep_cycles_per_ms() * 3.0)  # 3 ms backlog
+    it = iter(range(10 ** 9))
+    host_s, call_s = spin_up(lambda: fn(ws[next(it) % len(ws)], m["ws"], m["q"], m["d"], m["y"]))
     ms = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(cyc)
+        backlog(host_s, call_s, len(ws))
         e0.record()
         for w in ws:
             fn(w, m["ws"], m["q"], m["d"], m["y"])
@@ -236,6 +248,41 @@ def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
 
 
 _SLEEP_RATE = []
+SPIN_UP_S = 0.25
+
+
+def spin_up(fn, seconds=None):
+    """Untimed repeats of ``fn`` for about ``seconds`` (default ``--spin-up``) of wall
+    time before a timed region: an idle MI355X takes tens of milliseconds to bring its
+    engine clock up, and a matrix-core-bound kernel timed during that ramp reads up to
+    ~20 % slow."""
+    import torch
+
+    seconds = SPIN_UP_S if seconds is None else seconds
+    t0 = time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        for _ in range(8):
+            fn()
+        b = time.perf_counter()
+        torch.cuda.synchronize()
+        c = time.perf_counter()
+        if c - t0 >= seconds:
+            return (b - a) / 8, (c - a) / 8  # host enqueue time per call, wall time per call
+
+
+def backlog(host_s, call_s, n):
+    """Queue work ahead of a timed batch of ``n`` calls so that the GPU never waits for
+    the host: nothing when a call keeps the GPU busy for at least twice the host's
+    enqueue time (the host stays ahead by itself), else a sleep kernel that lasts about
+    as long as the host needs to enqueue the batch.  The sleep is kept that short
+    because the engine clock sinks while it runs: a 5 ms sleep before a prefill GEMM
+    costs it ~12 %."""
+    import torch
+
+    if call_s >= 2.0 * host_s:
+        return
+    torch.cuda._sleep(int(sleep_cycles_per_ms() * (1e3 * 1.5 * n * host_s + 0.2)))
 
 
 def sleep_cycles_per_ms():
@@ -284,7 +331,41 @@ def torch_reference_rates():
                      "not a ceiling")
 
 
-def time_gemm(M, N=17408, K=5120, reps=10, warm=3):
+def torch_fp16_gemm_rate(M=2048, N=17408, K=5120, reps=20):
+    """Context, not a ceiling of this kernel: torch.matmul (the vendor library's plain
+    fp16 GEMM, no quantization) of the prefill shape, y[M][N] = x[M][K] . W[N][K]^T,
+    timed like the GEMM below, on random N(0, 1) operands and on constant ones.  The
+    gap between the two is the chip's power limit: random operands toggle more bits,
+    and the engine clock drops to stay within the board power."""
+    import torch
+
+    out = dict(M=M, N=N, K=K)
+    for kind in ("random", "constant"):
+        if kind == "random":
+            g = torch.Generator(device="cuda")
+            g.manual_seed(1)
+            a = torch.randn((M, K), dtype=torch.float16, device="cuda", generator=g)
+            b = torch.randn((N, K), dtype=torch.float16, device="cuda", generator=g)
+        else:
+            a = torch.ones((M, K), dtype=torch.float16, device="cuda")
+            b = torch.ones((N, K), dtype=torch.float16, device="cuda")
+        bt = b.t()
+        spin_up(lambda: torch.matmul(a, bt))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, bt)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out[kind] = dict(us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS)
+        del a, b, bt
+    out["note"] = "torch.matmul fp16 x fp16 -> fp16 (vendor GEMM), context only"
+    return out
+
+
+def time_gemm(M, N=17408, K=5120, reps=20):
     import torch
 
     import gemm_q8_act_amd as nvq
@@ -298,13 +379,13 @@ def time_gemm(M, N=17408, K=5120, reps=10, warm=3):
     b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     nvq.nvq_quantize_act_q8_0(x, q, d, b)
-    for _ in range(warm):
-        nvq.nvq_gemm_nvfp4(w, ws, q, d, y)
-    torch.cuda.synchronize()
+    need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, M, N, K)
+    wsp = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    spin_up(lambda: nvq.nvq_gemm_nvfp4(w, ws, q, d, y, workspace=wsp))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for e0, e1 in ev:
         e0.record()
-        nvq.nvq_gemm_nvfp4(w, ws, q, d, y)
+        nvq.nvq_gemm_nvfp4(w, ws, q, d, y, workspace=wsp)
         e1.record()
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
@@ -439,11 +520,9 @@ def time_moe(steps=400):
 def _event_time(fn, reps):
     import torch
 
-    for _ in range(5):
-        fn()
-    torch.cuda.synchronize()
+    host_s, call_s = spin_up(fn)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(sleep_cycles_per_ms() * 5.0))  # backlog: launches queue behind it
+    backlog(host_s, call_s, reps)
     e0.record()
     for _ in range(reps):
         fn()
@@ -510,8 +589,18 @@ def run_stack(args):
                     l.step(0)
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
-        graph.replay()
+    # untimed warm-up steps for about SPIN_UP_S seconds right before the timed region
+    # (the engine clock of an idle GPU takes tens of milliseconds to come up)
+    warm = 0
+    t0 = time.perf_counter()
+    while warm < 2 or time.perf_counter() - t0 < SPIN_UP_S:
+        if graph is not None:
+            graph.replay()
+        else:
+            for l in layers:
+                l.step(0)
         torch.cuda.synchronize()
+        warm += 1
     steps = max(2, args.steps // 20)
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -523,7 +612,7 @@ def run_stack(args):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gbps = wbytes * steps / el / 1e9
-    line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=2,
+    line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=warm,
                 ms_per_step=1e3 * el / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="int8/fp32", data="synthetic",
                 config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408",
@@ -616,14 +705,42 @@ def summarize_trace(path):
     print("\n".join(out))
 
 
+def summarize_clock(run_dir):
+    """Engine clock per (kernel, grid) from a ``rocprofv3 --pmc GRBM_COUNT`` run:
+    GRBM_COUNT (GPU clocks, summed over the XCDs) / XCD count / dispatch time.  The
+    counting window is a few microseconds longer than the dispatch, so kernels shorter
+    than ~0.2 ms read high; long ones read the clock they ran at."""
+    import collections
+    import csv
+
+    xcc = next(int(r["Num_Xcc"]) for r in csv.DictReader(open(os.path.join(run_dir, "run_agent_info.csv")))
+               if r.get("Name", "").startswith("gfx"))
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(os.path.join(run_dir, "run_counter_collection.csv"))):
+        if r["Counter_Name"] != "GRBM_COUNT":
+            continue
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg[(r["Kernel_Name"].split("(")[0], r["Grid_Size"])].append((us, float(r["Counter_Value"]) / xcc / us))
+    for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(u for u, _ in kv[1])):
+        us = np.array([u for u, _ in v])
+        mhz = np.array([f for _, f in v])
+        print(f"{name[:60]:60s} grid={grid:>9s} n={len(v):5d} avg_us={us.mean():9.2f} "
+              f"clock_MHz p50={np.median(mhz):6.0f} min={mhz.min():6.0f} max={mhz.max():6.0f}")
+
+
 def main():
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2])
+        return
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-clock":
+        summarize_clock(sys.argv[2])
         return
     if len(sys.argv) == 4 and sys.argv[1] == "--summarize-pmc":
         summarize_pmc(sys.argv[2], sys.argv[3])
         return
     args = parse()
+    global SPIN_UP_S
+    SPIN_UP_S = args.spin_up
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -686,7 +803,7 @@ def main():
                                           mfma_issued_frac=2.0 * g2["frac"],
                                           note="algorithmic flops 2*M*N*K; the hi/lo split issues twice "
                                                "that on the matrix cores"),
-                            runs=g)
+                            runs=g, vendor_fp16_gemm=torch_fp16_gemm_rate())
     if not args.no_extras:
         log("extras ...")
         line["extras"] = time_extras()
