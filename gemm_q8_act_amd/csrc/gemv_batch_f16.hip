@@ -254,23 +254,34 @@ static hipError_t launch_f16(const uint8_t* w, float w_scale, const int8_t* q, c
 template <int G>
 static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
                                    int M, int64_t N, int64_t K, float* y, hipStream_t stream) {
-  return T == 4   ? launch_f16<4, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream)
-         : T == 3 ? launch_f16<3, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream)
-                  : launch_f16<2, 8, 3, G>(w, w_scale, q, d16, M, N, K, y, stream);
+  switch (T) {
+    case 4: return launch_f16<4, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 5: return launch_f16<5, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 6: return launch_f16<6, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 7: return launch_f16<7, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 8: return launch_f16<8, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 9:
+      if constexpr (G == 1) return launch_f16<9, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+      return hipErrorInvalidValue;  // not chosen for two token groups (the LDS reduction would not fit)
+    default: return launch_f16<2, 8, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+  }
 }
 
 // Tiles per block for many tiles.  The vector work of a block per chunk is about
-// 32 T + 72 instructions (weights of T tiles + one activation expansion), and a
-// compute unit runs ceil(blocks / 256) blocks' worth of it, so the launch takes the T
-// in {3, 4} that minimises ceil(ceil(tiles / T) / 256) * (32 T + 72) (measured at
-// M = 8: gate+up, 2176 tiles, 26.9 us with T = 4 and 23.3 us with T = 3).  T = 2
-// never wins this from 1024 tiles up, so only 3 and 4 are built.
-static int tiles_per_block(int64_t ntiles) {
+// 32 T + 72 G instructions (weights of T tiles + one activation expansion per token
+// group), and a compute unit runs ceil(blocks / 256) blocks' worth of it, so the launch
+// takes the T in 4 .. 9 (4 .. 8 for two groups) that minimises
+// ceil(ceil(tiles / T) / 256) * (32 T + 72 G).  Measured at M = 8: gate+up (2176
+// tiles) 24.2 us with T = 3, 22.4 with T = 5 and 20.8-21.3 with T = 9 (one block per
+// compute unit); N = 17408 (1088 tiles) 16.2 us with T = 3 and 12.8 with T = 5.  T = 3
+// never wins this from 1024 tiles up (it did under the former choice between 3 and 4
+// only), so it is not built.
+static int tiles_per_block(int64_t ntiles, int G) {
   int best = 4;
   int64_t best_cost = -1;
-  for (int t = 4; t >= 3; --t) {
+  for (int t = 4; t <= (G == 1 ? 9 : 8); ++t) {
     const int64_t per_cu = ((ntiles + t - 1) / t + 255) / 256;
-    const int64_t cost = per_cu * (32 * t + 72);
+    const int64_t cost = per_cu * (32 * t + 72 * G);
     if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;
   }
   return best;
@@ -279,18 +290,20 @@ static int tiles_per_block(int64_t ntiles) {
 // Tokens in launches of at most 16, each streaming the weights once: up to 8 tokens
 // as one group of MFMA columns, 9 to 16 as two groups that share every weight
 // expansion.  Fewer than 1024 tiles (QKV, O, down at hidden 5120): 2 tiles x 8
-// wavefronts x 3 slots, so the blocks keep enough loads in flight; more: T tiles x 4
-// wavefronts x 2 slots (every wavefront resident at once).
+// wavefronts x 2 slots, so the blocks keep enough loads in flight (3 slots measured
+// 4-8 % slower); more: T tiles x 4 wavefronts x 2 slots (every wavefront resident at
+// once).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
                                        int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
-  const int T = ntiles < 1024 ? 0 : tiles_per_block(ntiles);
   for (int64_t m0 = 0; m0 < M; m0 += 16) {
     const int mb = (int)(M - m0 < 16 ? M - m0 : 16);
+    const int G = mb > 8 ? 2 : 1;
+    const int T = ntiles < 1024 ? 0 : tiles_per_block(ntiles, G);
     const int8_t* qb = q + m0 * K;
     const uint16_t* db = d16 + m0 * (K / 32);
     float* yb = y + m0 * N;
-    const hipError_t e = mb > 8 ? launch_f16_group<2>(T, w, w_scale, qb, db, mb, N, K, yb, stream)
+    const hipError_t e = G == 2 ? launch_f16_group<2>(T, w, w_scale, qb, db, mb, N, K, yb, stream)
                                 : launch_f16_group<1>(T, w, w_scale, qb, db, mb, N, K, yb, stream);
     if (e != hipSuccess) return e;
   }

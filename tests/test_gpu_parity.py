@@ -192,18 +192,32 @@ def test_gemv_batched_large_activations(oracle, M, N, K):
     check_y(host(y), yo, awa, f"large activations M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("N", [32749, 16395])
-def test_gemv_batched_ragged_tile_groups(oracle, N):
-    """Blocks of 4 tiles (2047 tiles) and of 3 tiles (1025 tiles): a last block that is
-    only partly filled, and a ragged last tile."""
-    say(f"batched gemv M=3 N={N} K=128")
+# Batched decode from 1024 tiles up: T tiles per block with T chosen by tile count.
+# (M, N): tiles -> T, blocks, tiles in the last block; every N leaves a ragged last tile.
+@pytest.mark.parametrize("M,N", [
+    (3, 16379),   # 1024 tiles -> T 4, 256 blocks, last full
+    (3, 17627),   # 1102 -> T 5, 221 blocks, last 2
+    (3, 22395),   # 1400 -> T 6, 234, last 2
+    (3, 25595),   # 1600 -> T 7, 229, last 4
+    (3, 28843),   # 1803 -> T 8, 226, last 3
+    (3, 33595),   # 2100 -> T 9, 234, last 3
+    (12, 17627),  # two token groups: 1102 -> T 5
+    (12, 22395),  # 1400 -> T 6
+    (12, 25595),  # 1600 -> T 7
+    (12, 28843),  # 1803 -> T 8
+    (12, 34811),  # 2176 -> T 5, 436 blocks, last 1
+])
+def test_gemv_batched_ragged_tile_groups(oracle, M, N):
+    """Every tiles-per-block choice of the batched decode kernel, each with a last block
+    that is only partly filled (or exactly full) and a ragged last tile."""
+    say(f"batched gemv M={M} N={N} K=128")
     torch = torch_dev()
-    M, K = 3, 128
-    c = NvCase(M, N, K, 4242)
+    K = 128
+    c = NvCase(M, N, K, 4242 + M)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
     yo, awa = c.oracle_y(oracle)
-    check_y(host(y), yo, awa, f"M=3 N={N} K=128")
+    check_y(host(y), yo, awa, f"M={M} N={N} K=128")
 
 
 # M = 16: batched decode kernel (two token groups); 16 < M <= 64 and M > 64: the
