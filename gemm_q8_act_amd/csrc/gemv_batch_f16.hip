@@ -48,7 +48,9 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
                                                                 float w_scale, float* __restrict__ y) {
   constexpr int NT = 64 * W;
   __shared__ floatx4 red[W * T * G * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wavefront index is uniform (readfirstlane tells the compiler so, which keeps
+  // the chunk loop's indices in scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fg = lane >> 4;
   const int nch = (K + 127) >> 7;
   const int nb = K >> 5;
@@ -127,12 +129,9 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
       qlo[gi] = lo_lane ? oth : qa[gi][j];
       qhi[gi] = lo_lane ? qa[gi][j] : oth;
     }
-    _Float16 s[T][2];
+    half2_t s[T];  // the lane's two UE4M3 scales (low word of its 16-bit load), exact in fp16
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      s[t][0] = (_Float16)ue4m3_to_f32<0>(bs[j][t]);
-      s[t][1] = (_Float16)ue4m3_to_f32<1>(bs[j][t]);
-    }
+    for (int t = 0; t < T; ++t) s[t] = ue4m3x2_to_f16(bs[j][t]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       half8_t B[G];
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const half2_t sc = {s[t][u >> 1], s[t][u >> 1]};
+        const half2_t sc = {s[t][u >> 1], s[t][u >> 1]};  // subblock 2g + (u >> 1)
         const uint32_t cw = bw[j][t][u];
         const half2_t p0 = e2m1x2_to_f16<0>(cw) * sc;
         const half2_t p1 = e2m1x2_to_f16<1>(cw) * sc;

@@ -119,6 +119,13 @@ __device__ __forceinline__ float ue4m3_to_f32(uint32_t v) {
   return __builtin_amdgcn_cvt_f32_fp8((int)v, SEL);
 }
 
+// The two UE4M3 bytes of the low 16 bits of v -> two fp16 values (byte 0 first).
+// Every UE4M3 value (2^-9 .. 448, subnormals included) is exact in fp16; the
+// instruction's scale operand only contributes its exponent, here 2^0.
+__device__ __forceinline__ half2_t ue4m3x2_to_f16(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+}
+
 // ---------------------------------------------------------------------------
 // Two E2M1 codes of byte SEL of v -> two fp16 values (low nibble first).  The
 // instruction's scale operand only contributes its power-of-two exponent, so it

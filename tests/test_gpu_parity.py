@@ -733,6 +733,27 @@ def test_subnormal_ue4m3_scales(oracle, M):
     check_y(host(y), yo, awa, f"subnormal scales M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 5, 12, 40, 300])
+def test_every_ue4m3_byte(oracle, M):
+    """Row n of the weights uses the single UE4M3 byte n (0x00 .. 0x7E, every valid byte,
+    subnormals included) for all its scales, so a wrong decode of any byte in any path
+    shows in that row alone."""
+    say(f"every UE4M3 byte M={M}")
+    torch = torch_dev()
+    N, K = 127, 256
+    codes, _, ws = synth.nvfp4_weights(N, K, 21)
+    scales = np.repeat(np.arange(N, dtype=np.uint8)[:, None], K // 16, axis=1)
+    c = NvCase(M, N, K, 22)
+    c.codes, c.scales, c.ws = codes, scales, ws
+    c.w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemv_nvfp4 if M <= 15 else nvq.nvq_gemm_nvfp4)(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    yh = host(y)
+    assert (yh[:, 0] == 0.0).all()  # byte 0x00: scale 0
+    check_y(yh, yo, awa, f"every UE4M3 byte M={M}")
+
+
 def test_validation_leaves_output_untouched():
     torch = torch_dev()
     y = torch.full((16, 64), 7.0, dtype=torch.float32, device="cuda")
