@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void gemm_q4_1_kernel(const uint8_t* __restric
   __shared__ __align__(16) float ldm[2][BN * 2];   // (d, m) per weight row
   __shared__ __align__(16) float lab[2][BM * 2];   // (da, bsum32) per token
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
   const int64_t crow = K >> 1, nb = K >> 5, ns = K >> 4;
   const int nks = K / BK;
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kQLRW, LRA = kQLRA, CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave / WM, wm = wave % WM;
   const int64_t item = blockIdx.x;
   int64_t tile, part = -1;
