@@ -273,14 +273,15 @@ def spin_up(fn, seconds=None):
 
 def backlog(host_s, call_s, n):
     """Queue work ahead of a timed batch of ``n`` calls so that the GPU never waits for
-    the host: nothing when a call keeps the GPU busy for at least twice the host's
-    enqueue time (the host stays ahead by itself), else a sleep kernel that lasts about
-    as long as the host needs to enqueue the batch.  The sleep is kept that short
+    the host: nothing when a call keeps the GPU busy for at least four times the host's
+    enqueue time (the host stays well ahead by itself), else a sleep kernel that lasts
+    about as long as the host needs to enqueue the batch.  The sleep is kept that short
     because the engine clock sinks while it runs: a 5 ms sleep before a prefill GEMM
-    costs it ~12 %."""
+    costs it ~12 %.  With only a 2x margin, back-to-back 17 us GEMV launches read ~4 %
+    slow against their traced durations: the queue stays one launch deep."""
     import torch
 
-    if call_s >= 2.0 * host_s:
+    if call_s >= 4.0 * host_s:
         return
     torch.cuda._sleep(int(sleep_cycles_per_ms() * (1e3 * 1.5 * n * host_s + 0.2)))
 
@@ -798,7 +799,7 @@ def main():
                             value=g2["TFLOPs"], unit="TFLOP/s",
                             roofline=dict(bound="mfma", achieved=g2["TFLOPs"], peak=FP16_PEAK_TFLOPS,
                                           unit="TFLOP/s", frac=g2["frac"], traffic=None,
-                                          kernel="gemm_nvfp4_kernel<NvCfg<2,4,4,2>> + ksplit_reduce_kernel (fp16 "
+                                          kernel="gemm_nvfp4_kernel<NvCfg<1,8,8,1>> + ksplit_reduce_kernel (fp16 "
                                                  "MFMA 32x32x16 on the exact hi/lo activation split)",
                                           mfma_issued_frac=2.0 * g2["frac"],
                                           note="algorithmic flops 2*M*N*K; the hi/lo split issues twice "

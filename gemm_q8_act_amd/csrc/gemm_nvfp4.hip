@@ -294,7 +294,9 @@ struct NvCfg {
   static_assert(ABT == 8 || ABT == 16 || ABT == 32, "activation staging width");
   static_assert(kLds <= 160 * 1024, "LDS");
 };
-using NvBig = NvCfg<2, 4, 4, 2>;  // 256 weight rows x 256 tokens
+using NvBig = NvCfg<1, 8, 8, 1>;  // 256 weight rows x 256 tokens: each wavefront all 256 rows x 32
+                                  // tokens, so every token's activation split is done once
+                                  // per block (2 x 4 wavefronts of 128 x 64: 3 % slower)
 using NvM128 = NvCfg<4, 2, 2, 2>; // 256 weight rows x 128 tokens
 using NvMid = NvCfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
 
