@@ -297,7 +297,7 @@ struct NvCfg {
 using NvBig = NvCfg<1, 8, 8, 1>;  // 256 weight rows x 256 tokens: each wavefront all 256 rows x 32
                                   // tokens, so every token's activation split is done once
                                   // per block (2 x 4 wavefronts of 128 x 64: 3 % slower)
-using NvM128 = NvCfg<4, 2, 2, 2>; // 256 weight rows x 128 tokens
+using NvM128 = NvCfg<2, 4, 4, 1>; // 256 weight rows x 128 tokens (4 x 2 wavefronts of 64 x 64: 2-6 % slower)
 using NvMid = NvCfg<4, 2, 2, 1>;  // 256 weight rows x 64 tokens
 
 // which kernel runs an NVFP4 GEMM of M tokens: M = 1 only for rows too long for the
