@@ -291,6 +291,21 @@ def test_batched_decode_m8_full_size(oracle):
     check_y(host(y)[:, cols], yo, awa, "M=8 gate_up")
 
 
+@pytest.mark.parametrize("M", [12, 16])
+def test_batched_decode_two_groups_full_size(oracle, M):
+    """Two token groups over many tiles and chunks: N = 17408 (1088 tiles, 5 per block),
+    K = 5120 (40 chunks); M = 16 through the GEMM entry (which sends it here)."""
+    say(f"batched decode M={M} N=17408 K=5120")
+    torch = torch_dev()
+    N, K = 17408, 5120
+    c = NvCase(M, N, K, 4100 + M, w_scale="uniform")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemv_nvfp4 if M <= nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemm_nvfp4)(c.w, c.ws, c.q, c.d, y)
+    cols = sample_cols(N, 48, 9)
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(host(y)[:, cols], yo, awa, f"M={M} N=17408")
+
+
 # ---------------------------------------------------------------------------
 # Q4_1
 # ---------------------------------------------------------------------------
