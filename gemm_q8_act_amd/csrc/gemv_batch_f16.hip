@@ -47,7 +47,7 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
                                                                 const uint16_t* __restrict__ d16, int M,
                                                                 float w_scale, float* __restrict__ y) {
   constexpr int NT = 64 * W;
-  __shared__ floatx4 red[W * T * G * 64];
+  __shared__ floatx4 red[W * T * 64];
   // the wavefront index is uniform (readfirstlane tells the compiler so, which keeps
   // the chunk loop's indices in scalar registers)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,27 +216,30 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
       for (int t = 0; t < T; ++t) acc[gi][t] += 256.0f * accb[gi][t];
   }
 
-  // reduce the W wavefronts' partial tiles; in token group gi, column j < 8 +
-  // column j + 8 = token 8 gi + j
-#pragma unroll
-  for (int gi = 0; gi < G; ++gi)
-#pragma unroll
-    for (int t = 0; t < T; ++t) red[((wave * G + gi) * T + t) * 64 + lane] = acc[gi][t];
-  __syncthreads();
+  // reduce the W wavefronts' partial tiles, one token group at a time (so the LDS
+  // buffer holds one group: T = 9 fits for two groups too); in token group gi, column
+  // j < 8 + column j + 8 = token 8 gi + j
   const float* rf = reinterpret_cast<const float*>(red);
-  for (int o = tid; o < 8 * G * 16 * T; o += NT) {
-    const int mo = o / (16 * T), rr = o % (16 * T);
-    const int t = rr >> 4, r = rr & 15, gi = mo >> 3;
-    const int64_t row = (tile0 + t) * 16 + r;
-    if (mo >= M || row >= N) continue;
-    const int l_hi = (mo & 7) + 16 * (r >> 2), l_lo = l_hi + 8, v = r & 3;
-    float s = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const int base = ((ww * G + gi) * T + t) * 64;
-      s += rf[(base + l_hi) * 4 + v] + rf[(base + l_lo) * 4 + v];
+  for (int gi = 0; gi < G; ++gi) {
+    if (gi > 0) __syncthreads();  // the previous group's sums are read
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[(wave * T + t) * 64 + lane] = acc[gi][t];
+    __syncthreads();
+    for (int o = tid; o < 8 * 16 * T; o += NT) {
+      const int j = o / (16 * T), rr = o % (16 * T);
+      const int t = rr >> 4, r = rr & 15, mo = 8 * gi + j;
+      const int64_t row = (tile0 + t) * 16 + r;
+      if (mo >= M || row >= N) continue;
+      const int l_hi = j + 16 * (r >> 2), l_lo = l_hi + 8, v = r & 3;
+      float s = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) {
+        const int base = (ww * T + t) * 64;
+        s += rf[(base + l_hi) * 4 + v] + rf[(base + l_lo) * 4 + v];
+      }
+      y[(int64_t)mo * N + row] = s * w_scale;
     }
-    y[(int64_t)mo * N + row] = s * w_scale;
   }
 }
 
@@ -259,9 +262,7 @@ static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const
     case 6: return launch_f16<6, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
     case 7: return launch_f16<7, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
     case 8: return launch_f16<8, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 9:
-      if constexpr (G == 1) return launch_f16<9, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-      return hipErrorInvalidValue;  // not chosen for two token groups (the LDS reduction would not fit)
+    case 9: return launch_f16<9, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
     default: return launch_f16<2, 8, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
   }
 }
@@ -269,7 +270,7 @@ static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const
 // Tiles per block for many tiles.  The vector work of a block per chunk is about
 // 32 T + 72 G instructions (weights of T tiles + one activation expansion per token
 // group), and a compute unit runs ceil(blocks / 256) blocks' worth of it, so the launch
-// takes the T in 4 .. 9 (4 .. 8 for two groups) that minimises
+// takes the T in 4 .. 9 that minimises
 // ceil(ceil(tiles / T) / 256) * (32 T + 72 G).  Measured at M = 8: gate+up (2176
 // tiles) 24.2 us with T = 3, 22.4 with T = 5 and 20.8-21.3 with T = 9 (one block per
 // compute unit); N = 17408 (1088 tiles) 16.2 us with T = 3 and 12.8 with T = 5.  T = 3
@@ -278,7 +279,7 @@ static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const
 static int tiles_per_block(int64_t ntiles, int G) {
   int best = 4;
   int64_t best_cost = -1;
-  for (int t = 4; t <= (G == 1 ? 9 : 8); ++t) {
+  for (int t = 4; t <= 9; ++t) {
     const int64_t per_cu = ((ntiles + t - 1) / t + 255) / 256;
     const int64_t cost = per_cu * (32 * t + 72 * G);
     if (best_cost < 0 || cost < best_cost) best = t, best_cost = cost;

@@ -205,7 +205,7 @@ def test_gemv_batched_large_activations(oracle, M, N, K):
     (12, 22395),  # 1400 -> T 6
     (12, 25595),  # 1600 -> T 7
     (12, 28843),  # 1803 -> T 8
-    (12, 34811),  # 2176 -> T 5, 436 blocks, last 1
+    (12, 34811),  # 2176 -> T 9, 242 blocks, last 7
 ])
 def test_gemv_batched_ragged_tile_groups(oracle, M, N):
     """Every tiles-per-block choice of the batched decode kernel, each with a last block
