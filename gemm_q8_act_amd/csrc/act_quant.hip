@@ -31,10 +31,12 @@ __device__ __forceinline__ void quant_block(float4 v, int64_t g, int p, bool val
   a = fmaxf(a, __shfl_xor(a, 4, 64));
 
   // d32 = amax / 127 and q = rint(x / d32): IEEE float32 division (this file is
-  // compiled without fast-math, so '/' is correctly rounded), ties to even.
+  // compiled without fast-math, so '/' is correctly rounded), ties to even.  A
+  // block whose d32 is 0 (all zero, or float32 subnormals below 127 * 2^-150)
+  // keeps q = 0: x / 0 names no code, and d * q is 0 either way.
   const float d = a / 127.0f;
   int qi[4] = {0, 0, 0, 0};
-  if (a != 0.0f) {
+  if (d != 0.0f) {
     const float xs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -29,7 +29,8 @@
  *     amax = max |x|; d32 = amax / 127 (IEEE float32 division);
  *     d = binary16(d32) rounded to nearest even (stored);
  *     q = clamp(rint(x / d32), -127, 127) with IEEE float32 division by the
- *         unrounded d32 and ties to even; amax == 0 gives d = 0, q = 0.
+ *         unrounded d32 and ties to even; a block whose d32 is 0 (amax == 0,
+ *         or float32 subnormals below 127 * 2^-150) gives d = 0, q = 0.
  *     A[m][k] = d[m][k/32] * q[m][k].  bsum16[m][j] = sum of the 16 codes
  *     q[m][16j .. 16j+15] (int16).
  *

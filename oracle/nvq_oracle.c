@@ -102,7 +102,9 @@ uint16_t nvqo_f32_to_f16(float f)
  * section 3, block_q8_0 activations and their per-16 code sums "bsums").
  * Readings: d32 = amax / 127 in fp32; the stored scale is fp16(d32) rounded to
  * nearest even; the codes are rint(x / d32) (IEEE fp32 division by the unrounded
- * d32, ties to even) clamped to +-127; an all-zero block stores d = 0 and q = 0. */
+ * d32, ties to even) clamped to +-127; an all-zero block stores d = 0 and q = 0,
+ * and so does a block of float32 subnormals so small that d32 rounds to 0 (x / 0
+ * names no integer code; the block's dequantized values d * q are 0 either way). */
 void nvqo_quantize_q8_0(const float* x, int64_t M, int64_t K,
                         int8_t* q, uint16_t* d16, int16_t* bsum16)
 {
@@ -121,7 +123,7 @@ void nvqo_quantize_q8_0(const float* x, int64_t M, int64_t K,
             d16[m * nb + b] = nvqo_f32_to_f16(d);
             for (int j = 0; j < 32; ++j) {
                 int v = 0;
-                if (amax != 0.0f) {
+                if (d != 0.0f) {
                     float t = xb[j] / d;
                     float r = rintf(t);
                     if (r > 127.0f) r = 127.0f;

@@ -172,6 +172,22 @@ def battery(o) -> list[tuple[str, bool, str]]:
     ok7 &= list(q4[0]) == [-v for v in exp_q]
     pin("q8_0_constructed_ties", ok7, f"q={list(q[0][:10])} d={hex(int(d16[0,0]))}")
 
+    # P7b: float32 subnormal blocks.  amax = 50 * 2^-149 gives d32 = amax / 127 below
+    # half the least subnormal, so d32 rounds to 0: the block stores d = 0 and q = 0
+    # like an all-zero block.  amax = 127 * 2^-149 gives d32 = 2^-149 exactly, a
+    # non-zero divisor, so the codes are the integers x / 2^-149 themselves.
+    tiny = np.float32(2.0 ** -149)
+    blk5 = np.zeros(64, np.float32)
+    blk5[:4] = [50 * tiny, -50 * tiny, 7 * tiny, -tiny]
+    blk5[32:36] = [127 * tiny, -5 * tiny, 64 * tiny, 0.0]
+    d32a = np.float32(blk5[0] / np.float32(127.0))
+    d32b = np.float32(blk5[32] / np.float32(127.0))
+    q5, d5, b5 = o.quantize_q8_0(blk5[None, :])
+    ok7b = d32a == 0.0 and d32b == tiny
+    ok7b &= not q5[0, :32].any() and int(d5[0, 0]) == 0 and int(b5[0, 0]) == 0 and int(b5[0, 1]) == 0
+    ok7b &= list(q5[0, 32:36]) == [127, -5, 64, 0] and int(d5[0, 1]) == 0
+    pin("q8_0_underflowing_scale", ok7b, f"q={list(q5[0, :4])} {list(q5[0, 32:36])} d={list(d5[0])}")
+
     # P8: Q8_0 on random rows: properties + numpy float32 / float16 cross-check
     x = _rng(12).standard_normal((5, 96)).astype(np.float32) * np.float32(3.0)
     x[1, 40] = 0.0

@@ -33,6 +33,10 @@ def _edge_rows(K):
     one = np.zeros(K, np.float32)
     one[K // 2] = -1.0                                         # single non-zero per row
     rows.append(one)
+    sub = (r.integers(-60, 61, K) * np.float32(2.0 ** -149)).astype(np.float32)
+    sub[32:64] *= 2                                            # float32 subnormals: d32 rounds to 0 where
+    sub[32] = 127 * np.float32(2.0 ** -149)                    # amax < 63.5 * 2^-149, else d32 = 2^-149
+    rows.append(sub)
     return np.stack(rows)
 
 
@@ -58,6 +62,7 @@ def test_act_quant_edge_blocks(oracle, K):
     assert (host(d).view(np.uint16) == do).all()
     assert (host(b) == bo).all()
     assert do[2].max() < 0x0400 and do[2].max() > 0      # the subnormal-scale row is exercised
+    assert not qo[6, :32].any() and qo[6, 32] == 127 and qo[6, 33:64].any()  # d32 = 0 and d32 = 2^-149 blocks
 
 
 def _near_tie_rows(rows, K, seed):

@@ -16,6 +16,7 @@ MUTANTS = {
     "f16_subnormal_shift": ("int shift = 14 - e;", "int shift = 13 - e;"),
     "q8_round_half_away": ("float r = rintf(t);", "float r = roundf(t);"),
     "q8_divide_by_f16": ("float t = xb[j] / d;", "float t = xb[j] / (float)nvqo_f16_to_f64(nvqo_f32_to_f16(d));"),
+    "q8_zero_scale_guard": ("if (d != 0.0f) {", "if (amax != 0.0f) {"),
     "q8_bsum_offset": ("bsum16[m * (K / 16) + 2 * b + h] = (int16_t)s;", "bsum16[m * (K / 16) + 2 * b + (1 - h)] = (int16_t)s;"),
     "isums_index": ("acc += l * (int32_t)q[m * K + k];", "acc += l * (int32_t)q[m * K + (k ^ 1)];"),
     "act_scale_index": ("a[k] = nvqo_f16_to_f64(d16[k / 32]) * (double)q[k];", "a[k] = nvqo_f16_to_f64(d16[k / 16 % (K / 32)]) * (double)q[k];"),
