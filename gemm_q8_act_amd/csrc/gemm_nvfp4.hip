@@ -255,9 +255,12 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 // and lo = fma(d, q, -hi) (one v_pk_fma_f16; the exact difference is representable,
 // so the fused result is exact).  Then y = S * (W16 . hi + W16 . lo) with the
 // matrix core accumulating across the whole row: twice the MFMA work of a single
-// pass, but no per-block vector FMA and no partial-product registers.  Exact as long
-// as |d * q| stays below 65520 (|x| < 65504); beyond that hi is infinite and the
-// affected outputs become non-finite rather than silently wrong.
+// pass, but no per-block vector FMA and no partial-product registers.  hi stays
+// finite while |d * q| < 65520; a 32-value block whose d is 512 or more (where
+// |d * q| can pass that) is left out of the main pass (d -> 0) and done by a second
+// pass, taken only by blocks that met such a d, with d / 256 into the same
+// accumulators scaled by 2^-8 before and 2^8 after (both exact): every finite
+// activation is handled exactly, and the main pass carries no extra MFMA work.
 //
 // Block: 512 threads, WN x WM wavefronts, each a (32 TN) x (32 TM) tile of
 // v_mfma_f32_32x32x16_f16 products; the block tile is 256 weight rows by
@@ -272,6 +275,13 @@ hipError_t launch_tile(const uint8_t* w, float w_scale, const int8_t* q, const u
 // the 256 compute units -- K-split parts whose fp32 partial tiles go to the
 // workspace and are summed in part order by ksplit_reduce_kernel (ksplit.h;
 // deterministic: no atomics).
+//
+// DEBUG instance (the integer per-16 sums of this kernel's data path): the same
+// staging, fp16 weight expansion, activation split and MFMAs with unit scales
+// (UE4M3 = 1, d = 1, so hi = q and lo = 0); each 16-k half of a 32-k substep is one
+// subblock, so two MFMAs (hi, lo) with a zero accumulator give 32 x 32 per-subblock
+// sums sum E2M1 * q, exact in fp32 (|2 sum| <= 24384), written as L = 2 E2M1 sums.
+// Each work item (K-split parts included) writes the subblocks of its own k range.
 // ---------------------------------------------------------------------------------
 namespace {
 constexpr int kBigThreads = 512;
@@ -321,12 +331,13 @@ size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K) {
   }
 }
 
-template <class C>
+template <class C, bool DEBUG>
 __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
                                                             int K, const int8_t* __restrict__ q,
                                                             const uint16_t* __restrict__ d16, int64_t M,
                                                             float w_scale, float* __restrict__ y,
-                                                            float* __restrict__ part_ws, KSplitPlan plan) {
+                                                            float* __restrict__ part_ws,
+                                                            int32_t* __restrict__ isums, KSplitPlan plan) {
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kBigLRW, LRA = kBigLRA, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -363,21 +374,26 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
   const bool dtask = 2 * BM >= kBigThreads || tid < 2 * BM;
   const int drow = tid % BM, dblk = (tid / BM) & 1;
-  const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  const uint16_t* __restrict__ dbase = DEBUG ? nullptr : d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  bool anybig = false;  // this thread staged an activation scale d >= 512
   struct Stage { Words<ABT / 4> a; u32x4 wr; uint32_t sr, dr; };
   auto gload = [&](int t, Stage& x) {
     const int c = t >> 1, g = 2 * (t & 1) + whh;
     x.wr = *reinterpret_cast<const u32x4*>(wbase + (int64_t)c * 1024 + 256 * g);
     x.sr = *reinterpret_cast<const uint16_t*>(sbase + (int64_t)c * 128 + 32 * g);
     x.a = load_words<ABT / 4>(abase + 64 * t);
-    x.dr = dtask ? dbase[2 * t] : 0u;
+    if constexpr (DEBUG) x.dr = 0x3C00u;  // d = 1
+    else x.dr = dtask ? dbase[2 * t] : 0u;
   };
-  auto lstore = [&](int b, const Stage& x) {
+  // pass 0: the main pass (blocks with d >= 512 get d = 0); pass 1: those blocks only,
+  // with d / 256
+  auto lstore = [&](int b, const Stage& x, int pass) {
     uint8_t* st = smem + b * C::kStage;
     _Float16* lw = reinterpret_cast<_Float16*>(st);
     uint8_t* la = st + C::kStageW;
     uint16_t* ld = reinterpret_cast<uint16_t*>(st + C::kStageW + C::kStageA);
-    const _Float16 u0 = (_Float16)ue4m3_to_f32<0>(x.sr), u1 = (_Float16)ue4m3_to_f32<1>(x.sr);
+    const _Float16 u0 = DEBUG ? (_Float16)1.0f : (_Float16)ue4m3_to_f32<0>(x.sr);
+    const _Float16 u1 = DEBUG ? (_Float16)1.0f : (_Float16)ue4m3_to_f32<1>(x.sr);
     const half2_t s0 = {u0, u0}, s1 = {u1, u1};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -391,7 +407,14 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
       *reinterpret_cast<half8_t*>(lw + wrow * LRW + 32 * whh + 8 * d) = v;
     }
     store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
-    if (dtask) ld[2 * drow + dblk] = (uint16_t)x.dr;
+    if (dtask) {
+      uint32_t dr = x.dr;
+      if constexpr (!DEBUG) {
+        anybig |= act_scale_big(dr);
+        dr = act_scale_for_pass(dr, pass);
+      }
+      ld[2 * drow + dblk] = (uint16_t)dr;
+    }
   };
 
   floatx16 acc[TN][TM];
@@ -421,7 +444,8 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
       for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
     }
   };
-  auto mfmas = [&](const Frag& f) {
+  // the MFMAs of substep u of stage t (t, u only locate the subblocks of the DEBUG sums)
+  auto mfmas = [&](const Frag& f, int t, int u) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       half8_t bh[TM], bl[TM];
@@ -440,16 +464,35 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
         bh[j] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
         bl[j] = half8_t{l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
       }
+      if constexpr (DEBUG) {
+        // subblock 4 t + 2 u + h: its sums for 32 weight rows x 32 tokens per (i, j)
+        const int64_t sb = 4 * (int64_t)t + 2 * u + h, nsb = K >> 4;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bh[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TM; ++j) {
+            floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bh[j], floatx16{}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bl[j], p, 0, 0, 0);
+            const int64_t m = m0 + wm * (32 * TM) + 32 * j + fr;
+            if (m >= M) continue;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+            for (int e = 0; e < 16; ++e) {
+              const int64_t n = n0 + wn * (32 * TN) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              if (n < N) isums[(m * N + n) * nsb + sb] = (int32_t)(2.0f * p[e]);
+            }
+          }
+      } else {
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bl[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bh[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.af[h][i], bl[j], acc[i][j], 0, 0, 0);
+      }
     }
   };
 
@@ -460,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   // scheduler spread the staging and the fragment reads between the MFMAs.
   Stage x;
   gload(t0, x);
-  lstore(0, x);
+  lstore(0, x, 0);
   gload(min(t0 + 1, t1 - 1), x);
   __syncthreads();
   Frag f0, f1;
@@ -468,12 +511,37 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
   for (int t = t0; t < t1; ++t) {
     const int b = (t - t0) & 1;
     fread(b, 1, f1);
-    lstore(b ^ 1, x);                  // stage t+1, loaded one stage ago
-    mfmas(f0);
+    lstore(b ^ 1, x, 0);               // stage t+1, loaded one stage ago
+    mfmas(f0, t, 0);
     gload(min(t + 2, t1 - 1), x);
     __syncthreads();                   // stage t+1 visible; stage t-1's buffer free
     fread(b ^ 1, 0, f0);
-    mfmas(f1);
+    mfmas(f1, t, 1);
+  }
+  if constexpr (DEBUG) return;
+
+  // second pass over the stages for blocks with d >= 512 (activations near the
+  // binary16 range; not taken otherwise): plain staging through buffer 0, into the
+  // accumulators scaled by 2^-8 (exact) and restored by 2^8 afterwards
+  if (__syncthreads_or(anybig)) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] *= 0.00390625f;
+    for (int t = t0; t < t1; ++t) {
+      gload(t, x);
+      __syncthreads();                 // every read of buffer 0 done
+      lstore(0, x, 1);
+      __syncthreads();
+      fread(0, 0, f0);
+      mfmas(f0, t, 0);
+      fread(0, 1, f1);
+      mfmas(f1, t, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] *= 256.0f;
   }
 
   if (part >= 0) {
@@ -510,17 +578,26 @@ __global__ __launch_bounds__(512, 1) void gemm_nvfp4_kernel(const uint8_t* __res
 }
 
 namespace {
+// isums != nullptr: the DEBUG instance (per-16 sums, no workspace, no reduction)
 template <class C>
 hipError_t launch_two_term(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int64_t M,
-                           int64_t N, int64_t K, float* y, float* workspace, hipStream_t stream) {
+                           int64_t N, int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream) {
   const KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  if (isums) {
+    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel<C, true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<C, true>), dim3((unsigned)items), dim3(kBigThreads), C::kLds, stream, w,
+                       N, (int)K, q, d16, M, 1.0f, y, nullptr, isums, plan);
+    return hipGetLastError();
+  }
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
-  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel<C>),
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nvfp4_kernel<C, false>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (ea != hipSuccess) return ea;
-  const int64_t items = plan.full + plan.split_tiles * plan.split;
-  hipLaunchKernelGGL(gemm_nvfp4_kernel<C>, dim3((unsigned)items), dim3(kBigThreads), C::kLds, stream, w, N,
-                     (int)K, q, d16, M, w_scale, y, workspace, plan);
+  hipLaunchKernelGGL((gemm_nvfp4_kernel<C, false>), dim3((unsigned)items), dim3(kBigThreads), C::kLds, stream, w,
+                     N, (int)K, q, d16, M, w_scale, y, workspace, nullptr, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
   return launch_ksplit_reduce<C>(workspace, N, M, w_scale, y, plan, stream);
@@ -530,13 +607,14 @@ hipError_t launch_two_term(const uint8_t* w, float w_scale, const int8_t* q, con
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream) {
-  if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
   switch (nv_path(M, K)) {
-    case kNvBatched: return launch_gemv_nvfp4_batch_f16(w, w_scale, q, d16, M, N, K, y, stream);
-    case kNvMid: return launch_two_term<NvMid>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
-    case kNvM128: return launch_two_term<NvM128>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
-    case kNvBig: return launch_two_term<NvBig>(w, w_scale, q, d16, M, N, K, y, workspace, stream);
-    default: return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case kNvBatched: return launch_gemv_nvfp4_batch_f16(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case kNvMid: return launch_two_term<NvMid>(w, w_scale, q, d16, M, N, K, y, isums, workspace, stream);
+    case kNvM128: return launch_two_term<NvM128>(w, w_scale, q, d16, M, N, K, y, isums, workspace, stream);
+    case kNvBig: return launch_two_term<NvBig>(w, w_scale, q, d16, M, N, K, y, isums, workspace, stream);
+    default:
+      if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+      return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
   }
 }
 

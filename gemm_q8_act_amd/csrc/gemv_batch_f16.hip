@@ -37,15 +37,25 @@
 // v, v + W, ... through D register slots of loads (software pipelined: while one chunk
 // is expanded and multiplied, the loads of the next D - 1 are in flight).  The W
 // partial tiles are summed through LDS at the end.
+//
+// DEBUG instance (the integer per-16 sums of this kernel's data path): the same
+// loads, expansions and fp16 MFMAs with unit scales (UE4M3 = 1, d = 1, so the hi
+// column of a token is q and its lo column 0).  MFMA u of a chunk holds, in k group g,
+// the 8 codes k = 32 g + 8 u .. + 7, i.e. part of subblock 2 g + (u >> 1); so per k
+// group g and subblock half the activation operand is masked to group g and two
+// MFMAs (u = 2 half, 2 half + 1) sum the 16 codes of subblock 2 g + half, exact in
+// fp32.  A token's sum is its hi column plus its lo column (lanes l and l ^ 8),
+// written as L = 2 E2M1 sums.  Each chunk is written by the one wavefront that owns it.
 #include "nvq_device.h"
 
 namespace nvq {
 
-template <int T, int W, int D, int G>
+template <int T, int W, int D, int G, bool DEBUG>
 __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
                                                                 const int8_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ d16, int M,
-                                                                float w_scale, float* __restrict__ y) {
+                                                                float w_scale, float* __restrict__ y,
+                                                                int32_t* __restrict__ isums) {
   constexpr int NT = 64 * W;
   __shared__ floatx4 red[W * T * 64];
   // the wavefront index is uniform (readfirstlane tells the compiler so, which keeps
@@ -95,7 +105,7 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       qa[gi][j] = *reinterpret_cast<const u32x4*>(q + (qoff[gi] + 32 * b + (lo_lane ? 16 : 0)));
-      dv[gi][j] = d16[doff[gi] + b];
+      dv[gi][j] = DEBUG ? 0x3C00u : (uint32_t)d16[doff[gi] + b];  // DEBUG: d = 1
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
     }
     half2_t s[T];  // the lane's two UE4M3 scales (low word of its 16-bit load), exact in fp16
 #pragma unroll
-    for (int t = 0; t < T; ++t) s[t] = ue4m3x2_to_f16(bs[j][t]);
+    for (int t = 0; t < T; ++t) s[t] = DEBUG ? half2_t{(_Float16)1.0f, (_Float16)1.0f} : ue4m3x2_to_f16(bs[j][t]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       half8_t B[G];
@@ -164,18 +174,78 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
     }
   };
 
+  // DEBUG: the per-16 sums of slot j's chunk c (unit scales), written to isums
+  auto chunk_sums = [&](int j, int c) {
+    const int64_t nsb = K >> 4;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // operands of MFMAs u = 2 half and 2 half + 1, as in chunk() with d = 1, UE4M3 = 1
+      half8_t A[2][T], B[2][G];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * half + uu;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          u32x4 oth;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oth[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)qa[gi][j][i], 0x128, 0xF, 0xF, false);
+          const u32x4 qq = (u < 2) == lo_lane ? oth : qa[gi][j];  // hi lanes hold the first 16 codes
+          half2_t x0, x1, x2, x3;
+          i8x4_to_f16x4(qq[2 * (u & 1)], x0, x1);
+          i8x4_to_f16x4(qq[2 * (u & 1) + 1], x2, x3);
+          const half2_t one = {(_Float16)1.0f, (_Float16)1.0f}, z2 = {(_Float16)0.0f, (_Float16)0.0f};
+          const half2_t dl = lo_lane ? one : z2;
+          const half2_t b0 = __builtin_elementwise_fma(x0, one, -(x0 * dl));
+          const half2_t b1 = __builtin_elementwise_fma(x1, one, -(x1 * dl));
+          const half2_t b2 = __builtin_elementwise_fma(x2, one, -(x2 * dl));
+          const half2_t b3 = __builtin_elementwise_fma(x3, one, -(x3 * dl));
+          B[uu][gi] = half8_t{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const uint32_t cw = bw[j][t][u];
+          const half2_t p0 = e2m1x2_to_f16<0>(cw), p1 = e2m1x2_to_f16<1>(cw);
+          const half2_t p2 = e2m1x2_to_f16<2>(cw), p3 = e2m1x2_to_f16<3>(cw);
+          A[uu][t] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t sb = 8 * (int64_t)c + 2 * g + half;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            floatx4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+              const half8_t bm = fg == g ? B[uu][gi] : half8_t{};
+              p = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[uu][t], bm, p, 0, 0, 0);
+            }
+            // column fr: token 8 gi + fr % 8, hi (fr < 8) or lo part; rows 4 fg + rr
+            const int m = 8 * gi + fr;
+            const int64_t row0 = (tile0 + t) * 16 + 4 * fg;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const float v = p[rr] + __shfl_xor(p[rr], 8);
+              if (fr < 8 && m < M && row0 + rr < N && sb < nsb)
+                isums[((int64_t)m * N + row0 + rr) * nsb + sb] = (int32_t)(2.0f * v);
+            }
+          }
+      }
+    }
+  };
+
   // scales of slot j's chunk c for this lane (one per token group): 0 past the row's
-  // end; `big` marks |d| >= 512, whose blocks are left out here (scale 0) and done by
-  // the second pass below, which takes d / 256 for them (exponent field - 8; such a d
-  // is normal and d / 256 >= 2 stays normal) and 0 for the others
+  // end; blocks with d >= 512 are left out here (scale 0) and done by the second pass
+  // below, which takes d / 256 for them and 0 for the others (act_scale_for_pass)
   auto scales = [&](int j, int c, bool second, uint32_t* dd) {
     bool any = false;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) {
       const uint32_t d = 4 * c + fg < nb ? dv[gi][j] : 0u;
-      const bool big = (d & 0x7FFFu) >= 0x6000u;
-      any |= big;
-      dd[gi] = second ? (big ? d - 0x2000u : 0u) : (big ? 0u : d);
+      any |= act_scale_big(d);
+      dd[gi] = act_scale_for_pass(d, second ? 1 : 0);
     }
     return any;
   };
@@ -189,13 +259,18 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       if (c + W * j < nch) {
-        uint32_t dd[G];
-        any_big |= __builtin_amdgcn_ballot_w64(scales(j, c + W * j, false, dd));
-        chunk(j, dd, acc);
+        if constexpr (DEBUG) {
+          chunk_sums(j, c + W * j);
+        } else {
+          uint32_t dd[G];
+          any_big |= __builtin_amdgcn_ballot_w64(scales(j, c + W * j, false, dd));
+          chunk(j, dd, acc);
+        }
       }
       issue(j, c + W * (j + D));
     }
   }
+  if constexpr (DEBUG) return;
   // blocks with |d| >= 512 (only for activations near the binary16 range): one more
   // pass over this wavefront's chunks into the accumulator that is scaled by 256
   if (any_big) {
@@ -245,25 +320,29 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_f16_kernel(const uint8_t* _
 
 template <int T, int W, int D, int G>
 static hipError_t launch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16, int M,
-                             int64_t N, int64_t K, float* y, hipStream_t stream) {
+                             int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   const unsigned blocks = (unsigned)((ntiles + T - 1) / T);
-  hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D, G>), dim3(blocks), dim3(64 * W), 0, stream, w, N, (int)K, q,
-                     d16, M, w_scale, y);
+  if (isums)
+    hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D, G, true>), dim3(blocks), dim3(64 * W), 0, stream, w, N,
+                       (int)K, q, d16, M, w_scale, y, isums);
+  else
+    hipLaunchKernelGGL((gemv_nvfp4_f16_kernel<T, W, D, G, false>), dim3(blocks), dim3(64 * W), 0, stream, w, N,
+                       (int)K, q, d16, M, w_scale, y, nullptr);
   return hipGetLastError();
 }
 
 template <int G>
 static hipError_t launch_f16_group(int T, const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
-                                   int M, int64_t N, int64_t K, float* y, hipStream_t stream) {
+                                   int M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
   switch (T) {
-    case 4: return launch_f16<4, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 5: return launch_f16<5, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 6: return launch_f16<6, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 7: return launch_f16<7, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 8: return launch_f16<8, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    case 9: return launch_f16<9, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
-    default: return launch_f16<2, 8, 2, G>(w, w_scale, q, d16, M, N, K, y, stream);
+    case 4: return launch_f16<4, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case 5: return launch_f16<5, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case 6: return launch_f16<6, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case 7: return launch_f16<7, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case 8: return launch_f16<8, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    case 9: return launch_f16<9, 4, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
+    default: return launch_f16<2, 8, 2, G>(w, w_scale, q, d16, M, N, K, y, isums, stream);
   }
 }
 
@@ -294,17 +373,19 @@ static int tiles_per_block(int64_t ntiles, int G) {
 // 4-8 % slower); more: T tiles x 4 wavefronts x 2 slots (every wavefront resident at
 // once).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
-                                       int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
+                                       int64_t M, int64_t N, int64_t K, float* y, int32_t* isums,
+                                       hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   for (int64_t m0 = 0; m0 < M; m0 += 16) {
     const int mb = (int)(M - m0 < 16 ? M - m0 : 16);
     const int G = mb > 8 ? 2 : 1;
     const int T = ntiles < 1024 ? 0 : tiles_per_block(ntiles, G);
     const int8_t* qb = q + m0 * K;
-    const uint16_t* db = d16 + m0 * (K / 32);
-    float* yb = y + m0 * N;
-    const hipError_t e = G == 2 ? launch_f16_group<2>(T, w, w_scale, qb, db, mb, N, K, yb, stream)
-                                : launch_f16_group<1>(T, w, w_scale, qb, db, mb, N, K, yb, stream);
+    const uint16_t* db = isums ? nullptr : d16 + m0 * (K / 32);
+    float* yb = isums ? nullptr : y + m0 * N;
+    int32_t* ib = isums ? isums + m0 * N * (K / 16) : nullptr;
+    const hipError_t e = G == 2 ? launch_f16_group<2>(T, w, w_scale, qb, db, mb, N, K, yb, ib, stream)
+                                : launch_f16_group<1>(T, w, w_scale, qb, db, mb, N, K, yb, ib, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

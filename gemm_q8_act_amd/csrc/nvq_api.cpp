@@ -205,7 +205,7 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
   if (M == 1 && gemv_fits_lds(K))
     return launched(nvq::launch_gemv_nvfp4_m1(wb, w_scale, q, d_f16, N, K, y, nullptr, 0, (hipStream_t)stream), "gemv_nvfp4");
   if (M > 1)
-    return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, w_scale, q, d_f16, M, N, K, y, (hipStream_t)stream), "gemv_nvfp4 (batched)");
+    return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, w_scale, q, d_f16, M, N, K, y, nullptr, (hipStream_t)stream), "gemv_nvfp4 (batched)");
   return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
 }
 
@@ -296,17 +296,27 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(isums, 4)) return fail(NVQ_ERR_ALIGN, "nvq_debug_isums: w and q must be 16-byte aligned, isums 4-byte");
   NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : 32, 1, kMaxM));
   if (M > kMaxElems / (N * (K / 16))) return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: output too large");
+  if (fmt == NVQ_FMT_NVFP4 && path == NVQ_PATH_GEMV && M > 1 && (M < 16 ? M : 16) * K >= (int64_t(1) << 32))
+    return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the batched kernel (16 * K < 2^32)", (long long)K);
+  if (path == NVQ_PATH_GEMV_DOT4 && !gemv_fits_lds(K))
+    return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the v_dot4 decode kernel", (long long)K);
   NVQ_TRY(check_device());
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   hipStream_t st = (hipStream_t)stream;
+  // The sums come from the kernel the product entry would run for this shape: the GEMM
+  // dispatch (tiled at M = 1, batched up to 16, two-term above) or the GEMV dispatch
+  // (the M = 1 decode kernel, or the tiled one for rows past its LDS table; the
+  // batched kernel for M >= 2, 16 tokens per launch).
   if (path == NVQ_PATH_GEMM) {
     if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_nvfp4");
     return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_1");
   }
   if (fmt == NVQ_FMT_Q4_1) return launched(nvq::launch_gemv_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_1");
+  if (path == NVQ_PATH_GEMV) {
+    if (M > 1) return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, st), "debug gemv_nvfp4 (batched)");
+    if (!gemv_fits_lds(K)) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemv_nvfp4 (tiled)");
+  }
   const int64_t per_m = N * (K / 16);
-  if (!gemv_fits_lds(K))
-    return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the decode GEMV kernels", (long long)K);
   for (int64_t m = 0; m < M; ++m) {
     hipError_t e = nvq::launch_gemv_nvfp4_m1(wb, 1.0f, q + m * K, nullptr, N, K, nullptr, isums + m * per_m,
                                              path == NVQ_PATH_GEMV_DOT4 ? 1 : 0, st);

@@ -136,6 +136,19 @@ __device__ __forceinline__ half2_t e2m1x2_to_f16(uint32_t v) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, SEL);
 }
 
+// Activation scales d >= 512 (binary16 bits in [0x6000, 0x7C00): finite, exponent
+// field >= 24), for which |d * q| can pass the binary16 range.  The kernels that fold
+// d into binary16 operands leave such blocks out of their main pass (d -> 0) and
+// take them in a second pass with d / 256 (exponent field - 8: exact, and still a
+// normal number), whose accumulator is multiplied by 256 at the end.  Infinite or
+// NaN d stay in the main pass, so they still give non-finite outputs.
+__device__ __forceinline__ bool act_scale_big(uint32_t d) { return ((d & 0x7FFFu) - 0x6000u) < 0x1C00u; }
+// the binary16 bits a block's d takes in pass 0 (main) or pass 1 (d >= 512 only)
+__device__ __forceinline__ uint32_t act_scale_for_pass(uint32_t d, int pass) {
+  const bool big = act_scale_big(d);
+  return pass == 0 ? (big ? 0u : d) : (big ? d - 0x2000u : 0u);
+}
+
 // binary16 bits -> float (exact)
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);

@@ -19,10 +19,11 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
                                 int32_t* isums, int mode, hipStream_t stream);
 // NVFP4, 2 <= M <= 16 tokens: exact fp16 operands on the fp16 matrix core, one launch
 // (one weight stream) per 16 tokens.  Any K with M * K < 2^32 (32-bit activation
-// offsets; the callers check).
+// offsets; the callers check).  isums != nullptr selects the debug variant (per-16
+// integer sums [M][N][K/16] of the same data path; d16 and y unused).
 hipError_t launch_gemv_nvfp4_batch_f16(const uint8_t* w, float w_scale, const int8_t* q,
                                        const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
-                                       hipStream_t stream);
+                                       int32_t* isums, hipStream_t stream);
 // NVFP4 expert-routed decode GEMV: E packed expert matrices back to back, ids [M][A]
 // (device int32), y [M][A][N]; one launch, grid.y = M * A jobs.
 hipError_t launch_gemv_nvfp4_routed(const uint8_t* w, const float* w_scales, const int32_t* ids, int64_t E,
@@ -34,7 +35,8 @@ size_t gemv_lds_bytes(int64_t K);
 // NVFP4 GEMM paths (any M >= 1): M = 1 the tiled kernel (rows too long for the decode
 // kernels), 2 <= M <= 16 the batched decode kernel, M > 16 the split-activation
 // kernel, whose K-split parts need gemm_nvfp4_workspace(M, N, K) bytes of device
-// workspace (may be 0).  isums != nullptr selects the tiled debug variant.
+// workspace (may be 0).  isums != nullptr selects the debug variant of the kernel the
+// shape dispatches to (per-16 integer sums, no workspace).
 hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream);
@@ -48,7 +50,8 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 
 // Q4_1 GEMM paths (any M >= 1): M <= 16 the GEMV kernel, M > 16 the two-term fp16
 // kernel when K % 64 == 0 (it needs gemm_q4_1_workspace(M, N, K) bytes of device
-// workspace, may be 0), else the tiled kernel, which also gives the debug sums.
+// workspace, may be 0), else the tiled kernel.  isums != nullptr selects the debug
+// variant of the kernel the shape dispatches to.
 hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, float* workspace, hipStream_t stream);

@@ -449,7 +449,8 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 // that |w'| < 2^15: hi never overflows and lo is a normal binary16 number unless
 // |w'| < 2^-3, so hi + lo = w' to 2^-23 |w'|, or to 2^-25 absolute, i.e. 2^-39 of the
 // row's largest weight.  The activation is split exactly as in the NVFP4 large-M
-// kernel (d*q = hi + lo).  The matrix core then accumulates whole rows of
+// kernel (d*q = hi + lo; blocks with d >= 512 go through the same second pass with
+// d / 256).  The matrix core then accumulates whole rows of
 //     W'.A = Wh.Ah + Wh.Al + Wl.Ah (+ Wl.Al, dropped: at most 2^-22 |W.A|),
 // three MFMA passes, with no per-block vector work; the offset term m * sum(a) is
 // inside W, and the result is multiplied by 2^-s (exact).  Error per output: a few
@@ -462,6 +463,13 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 // lo), raw int8 activation codes and their binary16 scales; each wavefront splits its
 // activation fragments in registers.  Work items and the ordered K-split reduction
 // follow the NVFP4 large-M kernel.
+//
+// DEBUG instance (the integer per-16 sums sum c * q of this kernel's data path): the
+// same staging and MFMAs with d = 1 and m = 0 for every weight block and d = 1 for
+// every activation block.  The row bound is then 15, so w' = 2^11 c (exact in
+// binary16, lo = 0) and the activation split is hi = q, lo = 0; the three MFMAs of a
+// 16-k half with a zero accumulator give 2^11 sum c * q, exact in fp32 (every partial
+// sum is a multiple of 2^11 below 2^26), and the row factor 2^-11 makes it an integer.
 // ---------------------------------------------------------------------------------
 namespace {
 constexpr int kQThreads = 512;
@@ -511,12 +519,12 @@ size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K) {
   }
 }
 
-template <class C>
+template <class C, bool DEBUG>
 __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
                                                                  const int8_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ d16, int64_t M,
                                                                  float* __restrict__ y, float* __restrict__ part_ws,
-                                                                 KSplitPlan plan) {
+                                                                 int32_t* __restrict__ isums, KSplitPlan plan) {
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kQLRW, LRA = kQLRA, CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -551,7 +559,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
   const bool dtask = 2 * BM >= kQThreads || tid < 2 * BM;
   const int drow = tid % BM, dblk = (tid / BM) & 1;
-  const uint16_t* __restrict__ dbase = d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  const uint16_t* __restrict__ dbase = DEBUG ? nullptr : d16 + min(m0 + drow, M - 1) * nb32 + dblk;
+  bool anybig = false;  // this thread staged an activation scale d >= 512
+  constexpr uint32_t kUnitDM = 0x00003C00u;  // DEBUG weight block: d = 1, m = 0
   struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm, dr; };
 
   // row scale 2^s: the largest bound |m| + 15|d| of this row's blocks in [t0, t1),
@@ -561,7 +571,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const uint32_t* __restrict__ dmrow = dmw + wr * nb32;
 #pragma unroll 4
   for (int b = 2 * t0 + wq; b < 2 * t1; b += TPR) {
-    const uint32_t v = dmrow[b];
+    const uint32_t v = DEBUG ? kUnitDM : dmrow[b];
     bmax = fmaxf(bmax, fabsf(f16_bits_to_f32((uint16_t)(v >> 16))) + 15.0f * fabsf(f16_bits_to_f32((uint16_t)(v & 0xFFFFu))));
   }
   bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
@@ -575,11 +585,14 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 
   auto gload = [&](int t, Stage& x) {
     x.wc = load_words<CPT / 8>(wbase + (int64_t)t * 32);
-    x.dm = dmbase[2 * t];
+    x.dm = DEBUG ? kUnitDM : dmbase[2 * t];
     x.a = load_words<ABT / 4>(abase + 64 * t);
-    x.dr = dtask ? dbase[2 * t] : 0u;
+    if constexpr (DEBUG) x.dr = 0x3C00u;  // d = 1
+    else x.dr = dtask ? dbase[2 * t] : 0u;
   };
-  auto lstore = [&](int b, const Stage& x) {
+  // pass 0: the main pass (activation blocks with d >= 512 get d = 0); pass 1: those
+  // blocks only, with d / 256
+  auto lstore = [&](int b, const Stage& x, int pass) {
     uint8_t* st = smem + b * C::kStage;
     _Float16* lh = reinterpret_cast<_Float16*>(st);
     _Float16* ll = reinterpret_cast<_Float16*>(st + C::kStageW);
@@ -603,7 +616,14 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
       *reinterpret_cast<half8_t*>(ll + wrow * LRW + CPT * wq + 8 * h) = vl;
     }
     store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
-    if (dtask) ld[2 * drow + dblk] = (uint16_t)x.dr;
+    if (dtask) {
+      uint32_t dr = x.dr;
+      if constexpr (!DEBUG) {
+        anybig |= act_scale_big(dr);
+        dr = act_scale_for_pass(dr, pass);
+      }
+      ld[2 * drow + dblk] = (uint16_t)dr;
+    }
   };
 
   floatx16 acc[TN][TM];
@@ -635,7 +655,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
       for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
     }
   };
-  auto mfmas = [&](const Frag& f) {
+  const float* rinv = reinterpret_cast<const float*>(smem + 2 * C::kStage);
+  // the MFMAs of substep u of stage t (t, u only locate the subblocks of the DEBUG sums)
+  auto mfmas = [&](const Frag& f, int t, int u) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       half8_t bh[TM], bl[TM];
@@ -654,14 +676,34 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
         bh[j] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
         bl[j] = half8_t{l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
       }
+      if constexpr (DEBUG) {
+        // subblock 4 t + 2 u + h: 2^11 sum c * q for 32 weight rows x 32 tokens per (i, j)
+        const int64_t sb = 4 * (int64_t)t + 2 * u + h, nsb = K >> 4;
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+        for (int i = 0; i < TN; ++i)
 #pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bh[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bl[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[h][i], bh[j], acc[i][j], 0, 0, 0);
-        }
+          for (int j = 0; j < TM; ++j) {
+            floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bh[j], floatx16{}, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bl[j], p, 0, 0, 0);
+            p = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[h][i], bh[j], p, 0, 0, 0);
+            const int64_t m = m0 + wm * (32 * TM) + 32 * j + fr;
+            if (m >= M) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int r = wn * (32 * TN) + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              if (n0 + r < N) isums[(m * N + n0 + r) * nsb + sb] = (int32_t)(p[e] * rinv[r]);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bh[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[h][i], bl[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[h][i], bh[j], acc[i][j], 0, 0, 0);
+          }
+      }
     }
   };
 
@@ -669,7 +711,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   // last stage the staging writes a clamped copy nobody reads)
   Stage x;
   gload(t0, x);
-  lstore(0, x);
+  lstore(0, x, 0);
   gload(min(t0 + 1, t1 - 1), x);
   __syncthreads();
   Frag f0, f1;
@@ -677,16 +719,40 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   for (int t = t0; t < t1; ++t) {
     const int b = (t - t0) & 1;
     fread(b, 1, f1);
-    lstore(b ^ 1, x);
-    mfmas(f0);
+    lstore(b ^ 1, x, 0);
+    mfmas(f0, t, 0);
     gload(min(t + 2, t1 - 1), x);
     __syncthreads();
     fread(b ^ 1, 0, f0);
-    mfmas(f1);
+    mfmas(f1, t, 1);
+  }
+  if constexpr (DEBUG) return;
+
+  // second pass for activation blocks with d >= 512 (not taken otherwise): plain
+  // staging through buffer 0, into the accumulators scaled by 2^-8 and restored by
+  // 2^8 afterwards (both exact)
+  if (__syncthreads_or(anybig)) {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] *= 0.00390625f;
+    for (int t = t0; t < t1; ++t) {
+      gload(t, x);
+      __syncthreads();  // every read of buffer 0 done
+      lstore(0, x, 1);
+      __syncthreads();
+      fread(0, 0, f0);
+      mfmas(f0, t, 0);
+      fread(0, 1, f1);
+      mfmas(f1, t, 1);
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) acc[i][j] *= 256.0f;
   }
 
   // undo the row scales (the first barrier of the pipeline ordered their stores)
-  const float* rinv = reinterpret_cast<const float*>(smem + 2 * C::kStage);
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -729,17 +795,26 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 }
 
 namespace {
+// isums != nullptr: the DEBUG instance (per-16 sums, no workspace, no reduction)
 template <class C>
 hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
-                            int64_t K, float* y, float* workspace, hipStream_t stream) {
+                            int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream) {
   const KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  if (isums) {
+    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, true>), dim3((unsigned)items), dim3(kQThreads), C::kLds, stream,
+                       w, N, (int)K, q, d16, M, y, nullptr, isums, plan);
+    return hipGetLastError();
+  }
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
-  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C>),
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, false>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (ea != hipSuccess) return ea;
-  const int64_t items = plan.full + plan.split_tiles * plan.split;
-  hipLaunchKernelGGL(gemm_q4_1_f16x2_kernel<C>, dim3((unsigned)items), dim3(kQThreads), C::kLds, stream, w, N,
-                     (int)K, q, d16, M, y, workspace, plan);
+  hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, false>), dim3((unsigned)items), dim3(kQThreads), C::kLds, stream,
+                     w, N, (int)K, q, d16, M, y, workspace, nullptr, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
   return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
@@ -749,12 +824,11 @@ hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d
 hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, float* workspace, hipStream_t stream) {
-  if (isums) return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
   switch (q41_path(M, K)) {
-    case kQ41Gemv: return launch_gemv_q4_1(w, q, d16, bsum16, M, N, K, y, nullptr, stream);
-    case kQ41Big: return launch_q41_f16x2<Q41Big>(w, q, d16, M, N, K, y, workspace, stream);
-    case kQ41Mid: return launch_q41_f16x2<Q41Mid>(w, q, d16, M, N, K, y, workspace, stream);
-    case kQ41M128: return launch_q41_f16x2<Q41M128>(w, q, d16, M, N, K, y, workspace, stream);
+    case kQ41Gemv: return launch_gemv_q4_1(w, q, d16, bsum16, M, N, K, y, isums, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41Mid: return launch_q41_f16x2<Q41Mid>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128>(w, q, d16, M, N, K, y, isums, workspace, stream);
     default: return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
   }
 }

@@ -146,15 +146,30 @@ def test_gemv_nvfp4_m1(oracle, N, K, kernel):
 @pytest.mark.parametrize("M", [1, 3])
 @pytest.mark.parametrize("path", [nvq.NVQ_PATH_GEMV, nvq.NVQ_PATH_GEMV_DOT4])
 def test_gemv_isums_bit_exact(oracle, M, path):
+    """GEMV dispatch: M = 1 the decode kernel (matrix-core or v_dot4 inner loop),
+    M = 3 the batched kernel (GEMV path) or one v_dot4 launch per token."""
     say(f"debug isums GEMV path={path} M={M}")
     torch = torch_dev()
     for N, K in [(37, 128), (33, 320), (70, 5120), (9, 20544)]:
         c = NvCase(M, N, K, 1234 + N)
-        isums = torch.empty((M, N, K // 16), dtype=torch.int32, device="cuda")
+        isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
         nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, path, c.w, c.q, N, isums)
         ref = oracle.isums_nvfp4(c.codes, c.qh)
         assert (host(isums) == ref).all(), (N, K)
         assert np.abs(ref).max() > 0
+
+
+# Batched decode kernel, every token-group count and both launch shapes (fewer than
+# 1024 tiles: 2 tiles x 8 wavefronts; from 1024 tiles up: T tiles x 4 wavefronts).
+@pytest.mark.parametrize("M,N,K", [(2, 300, 640), (8, 129, 1024), (12, 77, 320), (15, 64, 5120),
+                                   (8, 16379, 128), (12, 17627, 192), (5, 40, 64)])
+def test_batched_isums_bit_exact(oracle, M, N, K):
+    say(f"debug isums batched GEMV M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = NvCase(M, N, K, 4400 + M + N)
+    isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
+    nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, nvq.NVQ_PATH_GEMV, c.w, c.q, N, isums)
+    assert (host(isums) == oracle.isums_nvfp4(c.codes, c.qh)).all()
 
 
 # ---------------------------------------------------------------------------
@@ -243,11 +258,31 @@ def test_gemm_nvfp4(oracle, M, N, K):
     check_y(host(y), yo, awa, f"gemm M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 70, 128), (17, 33, 192), (5, 64, 1024), (3, 20, 320)])
+# GEMM dispatch: M = 1 the tiled kernel; 2 <= M <= 16 the batched kernel; the
+# two-term kernel's three token-tile heights above (64: M <= 64, 128: M <= 128,
+# 256), small grids split along K (up to 16 parts per tile), ragged N and M tiles.
+@pytest.mark.parametrize("M,N,K", [(1, 70, 128), (2, 33, 192), (8, 64, 1024), (12, 20, 320), (15, 77, 640),
+                                   (16, 100, 5120), (17, 33, 192), (40, 300, 1024), (64, 257, 640),
+                                   (65, 70, 448), (100, 300, 1024), (128, 64, 2048), (129, 33, 320),
+                                   (300, 300, 1024), (257, 520, 64)])
 def test_gemm_isums_bit_exact(oracle, M, N, K):
     say(f"debug isums GEMM path M={M} N={N} K={K}")
     torch = torch_dev()
     c = NvCase(M, N, K, 55 + M)
+    isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
+    nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, nvq.NVQ_PATH_GEMM, c.w, c.q, N, isums)
+    ref = oracle.isums_nvfp4(c.codes, c.qh)
+    assert (host(isums) == ref).all()
+    assert np.abs(ref).max() > 0
+
+
+def test_gemm_isums_prefill_depth(oracle):
+    """The two-term kernel's sums over the full prefill depth K = 5120 (80 stages, 256 x
+    256 tiles, every tile split along K on this small grid), 256 tokens."""
+    say("debug isums GEMM path M=256 N=512 K=5120")
+    torch = torch_dev()
+    M, N, K = 256, 512, 5120
+    c = NvCase(M, N, K, 5151, outliers=True)
     isums = torch.empty((M, N, K // 16), dtype=torch.int32, device="cuda")
     nvq.nvq_debug_isums(nvq.NVQ_FMT_NVFP4, nvq.NVQ_PATH_GEMM, c.w, c.q, N, isums)
     assert (host(isums) == oracle.isums_nvfp4(c.codes, c.qh)).all()
@@ -284,16 +319,32 @@ def test_prefill_gemm_full_size(oracle, M):
     check_y(host(y)[:, cols], yo, awa, f"prefill M={M}")
 
 
-def test_batched_decode_m8_full_size(oracle):
-    say("batched decode M=8 gate_up N=34816 K=5120")
+@pytest.mark.parametrize("name,N,K", list(synth.LAYER))
+def test_batched_decode_m8_full_size(oracle, name, N, K):
+    """The layer set at M = 8 (batched decode of the 64-layer stack): gate+up takes the
+    many-tile launch (T tiles per block), QKV, O and down the fewer-than-1024-tile one;
+    down runs 136 chunks per row."""
+    say(f"batched decode M=8 {name} N={N} K={K}")
     torch = torch_dev()
-    N, K = 34816, 5120
-    c = NvCase(8, N, K, synth.seed_for("stack", "gate_up"), w_scale="uniform")
+    c = NvCase(8, N, K, synth.seed_for("stack", name), w_scale="uniform")
     y = torch.empty((8, N), dtype=torch.float32, device="cuda")
     nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
     cols = sample_cols(N, 48, 8)
     yo, awa = c.oracle_y(oracle, cols=cols)
-    check_y(host(y)[:, cols], yo, awa, "M=8 gate_up")
+    check_y(host(y)[:, cols], yo, awa, f"M=8 {name}")
+
+
+def test_batched_decode_m12_down(oracle):
+    """Two token groups at the down projection's shape (N = 5120, K = 17408)."""
+    say("batched decode M=12 down N=5120 K=17408")
+    torch = torch_dev()
+    N, K = 5120, 17408
+    c = NvCase(12, N, K, synth.seed_for("stack", "down12"), w_scale="uniform")
+    y = torch.empty((12, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_nvfp4(c.w, c.ws, c.q, c.d, y)
+    cols = sample_cols(N, 48, 12)
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(host(y)[:, cols], yo, awa, "M=12 down")
 
 
 @pytest.mark.parametrize("M", [12, 16])
@@ -426,27 +477,33 @@ def test_q4_1_gemm_split_determinism_and_guard_bands(oracle, M):
     check_y(outs[0].reshape(M, N)[:, ::5], yo, awa, "q4_1 split determinism case")
 
 
+def _large_activations(M, K, seed):
+    """Activations that reach past the binary16 range once scaled: blocks with d >= 512
+    (the two-term kernels' second pass), one token with every block that large, one
+    block just below the threshold (|d * q| near 60000, main pass), the rest N(0, 1)."""
+    x = synth.activations(M, K, seed)
+    x[5, 3] = 1.0e6                                        # d ~ 7874
+    x[1, 40:44] = [3.0e5, -2.0e5, 1.0e5, 7.0]              # d ~ 2362
+    x[M - 1, 0:32] *= 6.0e4 / np.abs(x[M - 1, 0:32]).max()  # d ~ 472
+    x[2, :] *= 1.0e5                                       # every block of token 2
+    x[M // 2, K - 32:] = 8.0e6                             # d ~ 63000, the last block of a row
+    return x
+
+
 @pytest.mark.parametrize("M", [200, 96, 24])
-def test_q4_1_gemm_activation_range(M):
-    """As for NVFP4: rows of the two-term kernels (M > 16) whose scaled activations
-    exceed the binary16 range come out non-finite; every other row is unaffected."""
-    say(f"q4_1 gemm (M={M}) activation range contract")
+def test_q4_1_gemm_activation_range(oracle, M):
+    """Q4_1 two-term kernels (M > 16): activations whose scaled values pass the binary16
+    range (blocks with d >= 512) are exact through the second pass, every tile height
+    and K-split parts included."""
+    say(f"q4_1 gemm (M={M}) large activations")
     torch = torch_dev()
-    N, K = 64, 128
-    c = Q41Case(M, N, K, 79)
-    x = synth.activations(M, K, 80)
-    x[5, 3] = 1.0e6
-    x2 = x.copy()
-    x2[5] = 0.0
-    ys = []
-    for xx in (x, x2):
-        q, d, b = quantize_gpu(xx)
-        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        nvq.nvq_gemm_q4_1(c.w, q, d, b, y)
-        ys.append(host(y))
-    assert not np.isfinite(ys[0][5]).all()
-    rows = [r for r in range(M) if r != 5]
-    assert (ys[0][rows] == ys[1][rows]).all()
+    N, K = 300, 640
+    c = Q41Case(M, N, K, 79, x=_large_activations(M, K, 80))
+    assert ((c.dh[2] & 0x7FFF) >= 0x6000).all() and (c.dh[M - 1, 0] & 0x7FFF) < 0x6000
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q4_1 large activations M={M}")
 
 
 @pytest.mark.parametrize("fmt,M,N", [("nvfp4", 300, 2560), ("nvfp4", 100, 5120), ("nvfp4", 40, 5120),
@@ -500,9 +557,24 @@ def test_q4_1_isums_bit_exact(oracle, path):
     torch = torch_dev()
     for M, N, K in [(1, 37, 96), (3, 70, 256)]:
         c = Q41Case(M, N, K, 71 + N)
-        isums = torch.empty((M, N, K // 16), dtype=torch.int32, device="cuda")
+        isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
         nvq.nvq_debug_isums(nvq.NVQ_FMT_Q4_1, path, c.w, c.q, N, isums)
         assert (host(isums) == oracle.isums_q4_1(c.qw, c.qh)).all(), (M, N, K)
+
+
+# Q4_1 GEMM dispatch for M > 16: the two-term kernel (K % 64 == 0; its three tile
+# shapes, K-split parts on small grids) or the tiled kernel (K = 96).
+@pytest.mark.parametrize("M,N,K", [(17, 300, 640), (40, 77, 192), (64, 520, 1024), (100, 130, 1024),
+                                   (128, 40, 4096), (200, 70, 640), (512, 256, 4096), (20, 33, 96)])
+def test_q4_1_gemm_isums_bit_exact(oracle, M, N, K):
+    say(f"q4_1 isums GEMM path M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = Q41Case(M, N, K, 83 + M + N)
+    isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
+    nvq.nvq_debug_isums(nvq.NVQ_FMT_Q4_1, nvq.NVQ_PATH_GEMM, c.w, c.q, N, isums)
+    ref = oracle.isums_q4_1(c.qw, c.qh)
+    assert (host(isums) == ref).all()
+    assert np.abs(ref).max() > 0
 
 
 # ---------------------------------------------------------------------------
@@ -628,28 +700,46 @@ def test_gemm_split_kernel_determinism_and_guard_bands(oracle, M):
     check_y(outs[0].reshape(M, N)[:, ::7], yo, awa, "gemm split determinism case")
 
 
-@pytest.mark.parametrize("M", [200, 96, 24])
-def test_gemm_split_kernel_activation_range(M):
-    """Rows whose scaled activations exceed the binary16 range come out non-finite
-    (documented contract of the M > 16 GEMM); every other row is unaffected."""
-    say(f"gemm (M={M}) activation range contract")
+@pytest.mark.parametrize("M,N", [(200, 300), (96, 300), (24, 300), (16, 300), (12, 300), (12, 17627),
+                                 (16, 16379)])
+def test_gemm_split_kernel_activation_range(oracle, M, N):
+    """NVFP4 GEMM entry: activations whose scaled values pass the binary16 range
+    (blocks with d >= 512) are exact through the second pass of the two-term kernel
+    (M > 16: every tile height, K-split parts on this small grid) and of the batched
+    kernel (M = 16 through the GEMM entry, M = 12 through the GEMV entry; both launch
+    shapes: 2 tiles per block below 1024 tiles, 4 or 5 from 1024 up)."""
+    say(f"gemm (M={M}) large activations N={N}")
     torch = torch_dev()
-    N, K = 64, 128
-    c = NvCase(M, N, K, 77)
-    x = synth.activations(M, K, 78)
-    x[5, 3] = 1.0e6  # |d * q| far above 65504 in row 5
-    q, d, _ = quantize_gpu(x)
+    K = 640
+    c = NvCase(M, N, K, 77, w_scale=1.5)
+    c.x = _large_activations(M, K, 78)
+    c.q, c.d, c.b = quantize_gpu(c.x)
+    c.qh, c.dh = host(c.q), host(c.d).view(np.uint16)
+    assert ((c.dh[2] & 0x7FFF) >= 0x6000).all() and (c.dh[M - 1, 0] & 0x7FFF) < 0x6000
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    nvq.nvq_gemm_nvfp4(c.w, c.ws, q, d, y)
-    y_ref = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    x2 = x.copy()
-    x2[5] = 0.0
-    q2, d2, _ = quantize_gpu(x2)
-    nvq.nvq_gemm_nvfp4(c.w, c.ws, q2, d2, y_ref)
-    yh, yr = host(y), host(y_ref)
-    assert not np.isfinite(yh[5]).all()
-    rows = [r for r in range(M) if r != 5]
-    assert (yh[rows] == yr[rows]).all()
+    (nvq.nvq_gemv_nvfp4 if M <= nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemm_nvfp4)(c.w, c.ws, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"large activations M={M}")
+
+
+def test_gemm_large_activations_prefill_shape(oracle):
+    """The prefill shape (M = 2048, N = 17408, K = 5120: whole tiles and split tiles) with
+    a few large-activation tokens, sampled output columns."""
+    say("prefill gemm M=2048 with large activations")
+    torch = torch_dev()
+    M, N, K = 2048, 17408, 5120
+    c = NvCase(M, N, K, synth.seed_for("prefill", "big"), outliers=True)
+    x = c.x
+    x[7, 100] = 2.0e6                    # m-tile 0
+    x[1500, :64] *= 3.0e4                # m-tile 5, two blocks
+    x[2047, 5000:5090] = -9.0e5          # last token, blocks near the end of K
+    c.q, c.d, c.b = quantize_gpu(x)
+    c.qh, c.dh = host(c.q), host(c.d).view(np.uint16)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_nvfp4(c.w, c.ws, c.q, c.d, y)
+    cols = sample_cols(N, 24, 77)
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(host(y)[:, cols], yo, awa, "prefill with large activations")
 
 
 def _experts(E, N, K, seed):
