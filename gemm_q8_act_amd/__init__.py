@@ -30,7 +30,7 @@ NVQ_GEMV_MAX_M = 15
 EXPORTS = (
     "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_gemm_workspace_bytes",
     "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_dot4",
-    "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
+    "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
     "nvq_status_str", "nvq_last_error",
 )
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
             "nvq_gemv_nvfp4_dot4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_nvfp4_routed": (ctypes.c_int, [P, P, P, I64, I64, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P, SZ, P]),
+            "nvq_gemm_nvfp4_noalloc": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_debug_isums": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P, P, I64, I64, I64, P, P]),
@@ -258,6 +259,19 @@ def nvq_gemm_nvfp4(w, w_scale: float, q, d_f16, y, workspace=None, stream=None) 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvq_gemm_nvfp4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
                                 _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_nvfp4")
+
+
+def nvq_gemm_nvfp4_noalloc(w, w_scale: float, q, d_f16, y, stream=None) -> None:
+    """nvq_gemm_nvfp4 with its K-split partials in the library's static per-GPU scratch
+    (nothing allocated; calls on one GPU must not overlap in time)."""
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemm_nvfp4_noalloc(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
+                                        _stream(stream, y)), "nvq_gemm_nvfp4_noalloc")
 
 
 def nvq_gemv_q4_1(w, q, d_f16, bsum16, y, stream=None) -> None:

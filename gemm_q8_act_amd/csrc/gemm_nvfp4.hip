@@ -21,6 +21,7 @@
 //     the whole row by itself.
 // A GEMM of 2 <= M <= 16 tokens runs the batched decode kernel (gemv_batch_f16.hip).
 #include <algorithm>
+#include <mutex>
 
 #include "ksplit.h"
 #include "nvq_device.h"
@@ -616,6 +617,51 @@ hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
       if (isums) return launch_tile<16, 64, true>(w, w_scale, q, d16, M, N, K, y, isums, stream);
       return launch_tile<16, 128, false>(w, w_scale, q, d16, M, N, K, y, isums, stream);
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (nvq_gemm_nvfp4_noalloc): the
+// K-split partial tiles go to this file-scope device array instead of a workspace
+// argument.  Every GPU the library runs on holds its own copy until the process ends.
+// No shape needs more: at most 256 K-split work items (one round over the compute
+// units), each one 512-thread partial tile of at most 128 float accumulators per
+// thread.  Its contents need no clearing: every part writes its whole partial tile
+// before the reduction reads it.  Calls that overlap in time on one GPU share it and
+// race.  In host code `scratch` only names the host-side stand-in of the symbol;
+// its device address on each GPU comes from hipGetSymbolAddress, taken once per
+// device on that device's first call and kept in g_scratch_dev.
+// ---------------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static_assert(kNoAllocScratchBytes == (size_t)kKSplitSlots * kKSplitThreads * 128 * sizeof(float),
+              "largest K-split plan: 256 items x 512 threads x 128 accumulators");
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];  // device address of `scratch` per device index
+}  // namespace
+
+size_t gemm_nvfp4_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t launch_gemm_nvfp4_noalloc(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
+                                     int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_dev[dev] = p;
+    }
+    ptr = g_scratch_dev[dev];
+  }
+  if (gemm_nvfp4_workspace(M, N, K) > kNoAllocScratchBytes) return hipErrorInvalidValue;  // callers check first
+  return launch_gemm_nvfp4(w, w_scale, q, d16, M, N, K, y, nullptr, static_cast<float*>(ptr), stream);
 }
 
 }  // namespace nvq

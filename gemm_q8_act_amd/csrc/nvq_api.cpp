@@ -245,19 +245,37 @@ nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q, co
   return NVQ_OK;
 }
 
+static nvq_status check_gemm_nvfp4(const void* w, const int8_t* q, const uint16_t* d_f16, const void* y, int64_t M,
+                                    int64_t N, int64_t K, const char* who) {
+  NVQ_TRY(check_common(w, q, d_f16, y, who));
+  NVQ_TRY(check_dims(M, N, K, 64, 16, kMaxM));
+  if ((M + 255) / 256 > (int64_t)1 << 31 || (N + 255) / 256 > (((int64_t)1 << 31) - 1) / ((M + 255) / 256))
+    return fail(NVQ_ERR_SHAPE, "%s: M=%lld x N=%lld has too many 256 x 256 tiles for one launch", who, (long long)M, (long long)N);
+  return NVQ_OK;
+}
+
 nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y, void* workspace,
                           size_t ws_bytes, void* stream) {
-  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_nvfp4"));
-  NVQ_TRY(check_dims(M, N, K, 64, 16, kMaxM));
-  if ((M + 255) / 256 > (int64_t)1 << 31 || (N + 255) / 256 > (((int64_t)1 << 31) - 1) / ((M + 255) / 256))
-    return fail(NVQ_ERR_SHAPE, "nvq_gemm_nvfp4: M=%lld x N=%lld has too many 256 x 256 tiles for one launch", (long long)M, (long long)N);
+  NVQ_TRY(check_gemm_nvfp4(w, q, d_f16, y, M, N, K, "nvq_gemm_nvfp4"));
   const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K);
   if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_nvfp4: workspace of %zu bytes required", need);
   if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_nvfp4: workspace must be 16-byte aligned");
   NVQ_TRY(check_device());
   return launched(nvq::launch_gemm_nvfp4(static_cast<const uint8_t*>(w), w_scale, q, d_f16, M, N, K, y, nullptr,
                                          static_cast<float*>(workspace), (hipStream_t)stream), "gemm_nvfp4");
+}
+
+nvq_status nvq_gemm_nvfp4_noalloc(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
+                                  int64_t M, int64_t N, int64_t K, float* y, void* stream) {
+  NVQ_TRY(check_gemm_nvfp4(w, q, d_f16, y, M, N, K, "nvq_gemm_nvfp4_noalloc"));
+  const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K);
+  if (need > nvq::gemm_nvfp4_noalloc_scratch_bytes() || need > NVQ_NOALLOC_SCRATCH_BYTES)
+    return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_nvfp4_noalloc: shape needs %zu bytes of scratch, more than the static %zu",
+                need, (size_t)NVQ_NOALLOC_SCRATCH_BYTES);
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemm_nvfp4_noalloc(static_cast<const uint8_t*>(w), w_scale, q, d_f16, M, N, K, y,
+                                                 (hipStream_t)stream), "gemm_nvfp4_noalloc");
 }
 
 nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,

@@ -41,6 +41,12 @@ hipError_t launch_gemm_nvfp4(const uint8_t* w, float w_scale, const int8_t* q,
                              const uint16_t* d16, int64_t M, int64_t N, int64_t K, float* y,
                              int32_t* isums, float* workspace, hipStream_t stream);
 size_t gemm_nvfp4_workspace(int64_t M, int64_t N, int64_t K);
+// The same NVFP4 GEMM dispatch with the K-split partials in the library's static
+// per-device scratch array (no allocation; calls on one GPU must not overlap), and
+// that array's size.
+hipError_t launch_gemm_nvfp4_noalloc(const uint8_t* w, float w_scale, const int8_t* q, const uint16_t* d16,
+                                     int64_t M, int64_t N, int64_t K, float* y, hipStream_t stream);
+size_t gemm_nvfp4_noalloc_scratch_bytes();
 
 // Q4_1 GEMV (any M; used for M <= 16), integer-dot path; with isums the
 // debug sums [M][N][K/16].

@@ -202,6 +202,19 @@ nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const u
                           int64_t M, int64_t N, int64_t K, float* y,
                           void* workspace, size_t ws_bytes, void* stream);
 
+/* The same prefill GEMM for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the K-split partial tiles go to a static scratch array inside
+ * the library, NVQ_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU it runs on, held until the
+ * process ends.  Every valid shape fits (the largest K-split plan needs exactly that
+ * much); a shape that needed more would be rejected with NVQ_ERR_WORKSPACE.  The call
+ * allocates nothing and needs no cleared memory.  Calls on one GPU share its scratch:
+ * calls that overlap in time on one GPU (different streams, or different host threads)
+ * race and give wrong results; serialise them.  Results equal nvq_gemm_nvfp4's. */
+#define NVQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+nvq_status nvq_gemm_nvfp4_noalloc(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
+                                  int64_t M, int64_t N, int64_t K, float* y, void* stream);
+
 /* ---- Q4_1 products ------------------------------------------------------------ */
 
 /* Q4_1 GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 32 == 0.
