@@ -108,18 +108,22 @@ typedef int nvq_status;
 
 /* Bytes of a packed NVFP4 weight buffer [N][K]: Np*Kp*9/16 with Np = N rounded up
  * to 16 and Kp = K rounded up to 128.  0 if N < 1 or K is not a positive multiple
- * of 64. */
+ * of 64.  Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3
+ * (NVFP4 blocks of 64 weights: 4-bit codes plus one UE4M3 byte per 16, i.e. 4.5 bits
+ * per weight); the tile-interleaved order is this library's own. */
 size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
 
 /* Bytes of a packed Q4_1 weight buffer [N][K]: N*K*5/8.  0 if N < 1 or K is not a
- * positive multiple of 32. */
+ * positive multiple of 32.  Follows: the llama.cpp 2-bit GGUF tutorial, GGML type
+ * table (Q4_1: 32 weights per block, 4-bit codes plus a binary16 scale and offset). */
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
 
 /* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt
  * is NVQ_FMT_*): with M > 16 and K % 64 == 0, the fp32 partial tiles of the K-split
  * work items that even out the last round of tiles over the chip's 256 compute units
- * (at most 32 MiB); otherwise 0.  Pure function.
- * When it is 0 the workspace pointer may be NULL. */
+ * (at most 64 MiB: 256 work items x 512 threads x 128 floats); otherwise 0.  Pure
+ * function.  When it is 0 the workspace pointer may be NULL.  (A scheduling detail
+ * of this library; the pages have no counterpart.) */
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
 /* ---- packers (host memory in, host memory out) ------------------------------ */
@@ -127,22 +131,29 @@ size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 /* codes: [N][K] bytes, one E2M1 code (0..15) per byte; ue4m3: [N][K/16] bytes.
  * Writes nvq_nvfp4_weight_bytes(N, K) bytes to dst_host.  K % 64 == 0.
  * NVQ_ERR_RANGE if a code exceeds 15 or a scale byte has bit 7 set or equals 0x7F
- * (dst_host is then left unspecified). */
+ * (dst_host is then left unspecified).  Host memory only, caller-owned.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3 (E2M1 codes,
+ * one UE4M3 scale per 16 weights). */
 nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3,
                           int64_t N, int64_t K, void* dst_host);
 
 /* q: [N][K] bytes (0..15); d_f16, m_f16: [N][K/32] binary16 bit patterns.
  * Writes nvq_q4_1_weight_bytes(N, K) bytes to dst_host.  K % 32 == 0.
- * NVQ_ERR_RANGE if a code exceeds 15. */
+ * NVQ_ERR_RANGE if a code exceeds 15.  Host memory only, caller-owned.
+ * Follows: the llama.cpp 2-bit GGUF tutorial, GGML type table (Q4_1), and "HANDOFF:
+ * flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_1 weights in the same work). */
 nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t* m_f16,
                          int64_t N, int64_t K, void* dst_host);
 
 /* ---- activation quantization ------------------------------------------------ */
 
 /* Q8_0 quantization of x [M][K] float32 into q [M][K] int8, d_f16 [M][K/32]
- * (binary16 bits) and, if bsum16 is not NULL, bsum16 [M][K/16] int16.  M >= 1,
- * K % 32 == 0.  Bit-exact with the definition above.  Non-finite x, or
- * amax > 65504 * 127, are outside the contract. */
+ * (binary16 bits) and, if bsum16 is not NULL, bsum16 [M][K/16] int16 (all device).
+ * M >= 1, K % 32 == 0.  Bit-exact with the definition above.  Non-finite x, or
+ * amax > 65504 * 127, are outside the contract.
+ * Follows: the llama.cpp 2-bit GGUF tutorial, GGML type table (Q8_0: 32 int8 codes
+ * and one binary16 d per block); "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)",
+ * section 3, bias-trick paragraph (the per-16 sums of the activation codes). */
 nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
                                  int8_t* q, uint16_t* d_f16, int16_t* bsum16, void* stream);
 
@@ -154,17 +165,23 @@ nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
  * integer sums come from the matrix cores reading the FP4 codes directly (K up to
  * what its on-chip activation table holds, about 70000; longer rows run the tiled
  * kernel).  2 <= M runs the batched kernel (M * K < 2^32, NVQ_ERR_SHAPE otherwise),
- * all tokens in one launch streaming the weights once: exact binary16 operands (E2M1 * UE4M3 weights;
- * d * q split exactly into two binary16 terms) on the fp16 matrix cores, any K.
+ * all tokens in one launch streaming the weights once: exact binary16 operands
+ * (E2M1 * UE4M3 weights; d * q split exactly into two binary16 terms, activation
+ * blocks with d >= 512 in a second pass at d / 256) on the fp16 matrix cores, any K.
  * Per output the error against the exact product is at most 1e-5 * sum_k |W*A|
- * + 1e-6 (float32 accumulation of exact terms). */
+ * + 1e-6 (float32 accumulation of exact terms).
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
+ * (the batch-1 vector dot: one integer sum per 16-subblock, scaled once by the
+ * subblock's UE4M3 and the block's activation scale). */
 nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y, void* stream);
 
 /* The same decode GEMV with the per-16 integer sums computed on the vector unit:
  * E2M1 -> int8 by v_perm_b32 table lookups and v_dot4_i32_i8 (one launch per
  * token).  Same arguments, results within the same bound.  K is limited to what
- * the on-chip activation table holds (NVQ_ERR_SHAPE beyond, about 70000). */
+ * the on-chip activation table holds (NVQ_ERR_SHAPE beyond, about 70000).
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map and
+ * bias-trick paragraph (integer LUT of the codes, int8 dot products per 16). */
 nvq_status nvq_gemv_nvfp4_dot4(const void* w, float w_scale, const int8_t* q,
                                const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
                                float* y, void* stream);
@@ -194,10 +211,12 @@ nvq_status nvq_gemv_nvfp4_routed(const void* w, const float* w_scales, const int
  * nvq_gemm_workspace_bytes(NVQ_FMT_NVFP4, M, N, K) bytes; NULL is accepted when
  * that size is 0.  Calls that share a workspace must not overlap in time.
  * For M > 16 the kernel folds each activation scale into an exact pair of binary16
- * values (hi + lo = d * q); this is exact for |d * q| < 65520, i.e. activations
- * below the binary16 range limit.  A row with larger activations yields
- * non-finite outputs in that row (never silently wrong values); M = 16 and the
- * GEMV entry points have no such limit. */
+ * values (hi + lo = d * q); activation blocks with d >= 512, whose d * q can pass
+ * the binary16 range, are summed in a second pass at d / 256, so every finite
+ * activation in the contract is exact.  Same error bound as the GEMV.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
+ * (batches larger than one take a tiled matmul that unpacks weight and activation
+ * tiles and applies the per-16 weight scale beside them). */
 nvq_status nvq_gemm_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y,
                           void* workspace, size_t ws_bytes, void* stream);
@@ -224,9 +243,12 @@ nvq_status nvq_gemm_nvfp4_noalloc(const void* w, float w_scale, const int8_t* q,
  * of nvq_gemm_workspace_bytes(NVQ_FMT_Q4_1, M, N, K) bytes (NULL when that is 0).
  * For M > 16 with K % 64 == 0 the GEMM forms each weight in two binary16 terms
  * (after a per-row power-of-two scaling, so any finite d, m are fine) and folds
- * each activation scale into an exact pair of binary16 values, which holds for
- * |d * q| < 65520; a token row with larger activations yields non-finite outputs in
- * that row, as for nvq_gemm_nvfp4.  The GEMV has no such limit. */
+ * each activation scale into an exact pair of binary16 values, with the same
+ * second pass as nvq_gemm_nvfp4 for blocks with d >= 512.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_1 vec_dot
+ * and tiled kernels beside the NVFP4 ones) and section 3, bias-trick paragraph (the
+ * activation code sums that the offset term needs); the llama.cpp 2-bit GGUF
+ * tutorial, GGML type table (Q4_1 block). */
 nvq_status nvq_gemv_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
                          const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                          void* stream);
@@ -236,18 +258,36 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
 
 /* ---- debug: integer per-16 partial sums --------------------------------------- */
 
-/* isums [M][N][K/16] int32 = for each 16-subblock, sum_j L(code) * q (NVFP4, with
- * L(c) = 2*E2M1(c), an integer in -12..12) or sum_j code * q (Q4_1, unsigned codes).
- * fmt: NVQ_FMT_*; path: NVQ_PATH_GEMV, NVQ_PATH_GEMM or (NVFP4 only)
- * NVQ_PATH_GEMV_DOT4 selects which production kernel's data path (weight load,
- * code expansion, integer / matrix-core contraction) produces the sums, run with
- * unit scales.  Any M >= 1 is accepted for every path; K % 64 == 0 (NVFP4) or
- * K % 32 == 0 (Q4_1). */
+/* isums [M][N][K/16] int32 (device, overwritten) = for each 16-subblock,
+ * sum_j L(code) * q (NVFP4, with L(c) = 2*E2M1(c), an integer in -12..12) or
+ * sum_j code * q (Q4_1, unsigned codes).  fmt: NVQ_FMT_*.  path picks the product
+ * entry whose kernel computes the sums, run with unit scales (UE4M3 = 1, d = 1; Q4_1
+ * d = 1, m = 0) through its own weight loads, code expansion and integer or
+ * matrix-core contraction -- the kernel that entry dispatches for this M:
+ *   NVQ_PATH_GEMV      nvq_gemv_nvfp4 / nvq_gemv_q4_1: NVFP4 M = 1 the matrix-core
+ *                      decode kernel (the tiled kernel past its LDS table), M >= 2 the
+ *                      batched kernel (16 tokens per launch); Q4_1 the GEMV kernel;
+ *   NVQ_PATH_GEMM      nvq_gemm_nvfp4 / nvq_gemm_q4_1 (any M >= 1): NVFP4 M = 1 the
+ *                      tiled kernel, 2 <= M <= 16 the batched kernel, M > 16 the
+ *                      two-term kernel of M's tile height with its K-split work items;
+ *                      Q4_1 M <= 16 the GEMV kernel, M > 16 the two-term kernel
+ *                      (K % 64 == 0) or the tiled kernel;
+ *   NVQ_PATH_GEMV_DOT4 nvq_gemv_nvfp4_dot4 (NVFP4 only): the v_dot4 decode kernel,
+ *                      one launch per token.
+ * K % 64 == 0 (NVFP4) or K % 32 == 0 (Q4_1).
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
+ * (one int32 sum per 16-subblock, lane k of the sum = subblock k/2) and bias-trick
+ * paragraph; the integer sums are unique, so they are checked bit for bit. */
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q,
                            int64_t M, int64_t N, int64_t K, int32_t* isums, void* stream);
 
 /* ---- errors ------------------------------------------------------------------- */
 
+/* Name of a status code, and the calling thread's last error message (static
+ * strings owned by the library).  The pages print no error API; "HANDOFF: flint CPU
+ * optimization (Q4_1 + NVFP4)", section 3 (kernel tests pass silently on zeroed
+ * decode tables unless the library is initialised) and its VNNI-only dispatch guard
+ * are why this library has no silent init and no silent fallback path. */
 const char* nvq_status_str(nvq_status s);
 const char* nvq_last_error(void);
 
