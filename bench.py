@@ -9,20 +9,24 @@ s % copies, so consecutive steps never find their weights in the 256 MB
 Infinity Cache.  Inputs are resident in HBM before the timed region.
 
 Also measured in the same run (reported as sub-objects of the JSON line): the
-prefill GEMM TFLOP/s at M = 2048 (and 256), N = 17408, K = 5120; the small
-GEMV (N = 4864, K = 896) and the Q4_1 GEMV / GEMM (N = K = 4096); the oracle's
-CPU throughput on the same layer.  ``--stack`` instead measures the 64-layer
-stack (M = 1 or 8) of the same layer shapes.
+64-layer stack of the same layer shapes at M = 1 and M = 8 (11.9 GB of weights per
+step); the prefill GEMM TFLOP/s at M = 2048 (and 256), N = 17408, K = 5120; the
+small GEMV (N = 4864, K = 896) and the Q4_1 GEMV (HBM-cold, rotating over >= 1 GB of
+weight copies) / GEMM (N = K = 4096); the oracle's CPU throughput on the same layer.
+``--stack`` measures only the stack (M = ``--tokens``).
 
 Roofline: per-kernel durations come from HIP events recorded on the stream the
 kernels are launched on (torch's current stream).  Peaks: HBM 8000 GB/s, dense
 fp16 MFMA 2500 TFLOP/s (the GEMM computes in fp16 x fp16 -> fp32).
 
-Every timed region starts at the GPU's steady clock: the W warm-up steps of the
-layer (default 2000, about 0.1 s, before K = 2000 timed steps) and, for every other
-measurement, about 0.25 s of untimed repeats of the same work run right before it.  An idle MI355X needs tens of
-milliseconds to raise its engine clock; a GEMM timed during that ramp reads ~20 %
-slow, an HBM-bound GEMV about 1 %.
+Every timed region starts at the GPU's steady clock: the layer runs its W warm-up
+steps and then at least ``--spin-up`` seconds (default 0.25) of further untimed steps
+right before the K timed ones, and every other measurement is preceded by the same
+spin-up of its own work.  An idle MI355X needs tens of milliseconds to raise its
+engine clock; a GEMM timed during that ramp reads ~20 % slow, an HBM-bound GEMV
+about 1 %.  Exactly K layer steps are timed: captured HIP graphs of one to
+``--copies`` consecutive steps (one per weight copy) are replayed so that step s uses
+copy s % copies.
 """
 from __future__ import annotations
 
@@ -61,6 +65,7 @@ def parse():
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-stack", action="store_true", help="skip the 64-layer stack sub-objects")
     p.add_argument("--stack", action="store_true", help="64-layer stack instead of one layer")
     p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
@@ -93,9 +98,11 @@ def gemv_alg_bytes(M, N, K):
 
 
 class Layer:
-    """Device-resident decode layer: packed weights (``copies`` replicas), activations."""
+    """Device-resident decode layer: packed weights (``copies`` replicas), activations.
+    ``share_from``: take that layer's packed weights (cloned into ``copies`` new
+    buffers, or used as they are with ``clone=False``) instead of generating them."""
 
-    def __init__(self, M, copies, seed_base=0, share_from=None):
+    def __init__(self, M, copies, seed_base=0, share_from=None, clone=True):
         import torch
 
         import gemm_q8_act_amd as nvq
@@ -111,8 +118,10 @@ class Layer:
                 packed, ws = share_from.mats[i]["w"][0], share_from.mats[i]["ws"]
             if share_from is None:
                 ws_list = [packed] + [packed.clone() for _ in range(copies - 1)]
-            else:
+            elif clone:
                 ws_list = [packed.clone() for _ in range(copies)]
+            else:
+                ws_list = list(share_from.mats[i]["w"])
             x = dev_tensor(synth.activations(M, K, synth.seed_for("layer", "x_" + name, seed_base)))
             self.mats.append(dict(
                 name=name, N=N, K=K, w=ws_list, ws=float(ws), x=x,
@@ -168,41 +177,51 @@ def time_layer(args):
         layer.step(c)
     torch.cuda.synchronize()
 
-    graph = None
+    graphs = {}
     if not args.eager:
-        # one graph holds `copies` consecutive steps (one per weight copy)
+        # graphs[r] holds r consecutive layer steps over weight copies 0 .. r-1: a run of
+        # n steps replays graphs[copies] n // copies times, then graphs[n % copies], so
+        # step s always uses copy s % copies and any number of steps is exact.  (One
+        # replay per step would add the graph launch's own ~6 us to every 47 us step.)
         s_cap = torch.cuda.Stream()
         s_cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s_cap):
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=s_cap):
-                for c in range(args.copies):
-                    layer.step(c)
+            for r in range(1, args.copies + 1):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s_cap):
+                    for c in range(r):
+                        layer.step(c)
+                graphs[r] = g
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
 
-    # the W untimed warm-up steps run right before the timed region: an idle GPU takes
-    # tens of milliseconds to raise its engine clock
-    if graph is not None:
-        for _ in range(max(1, -(-args.warmup // args.copies))):
-            graph.replay()
-    else:
-        for s in range(args.warmup):
-            layer.step(s % args.copies)
+    def run_steps(n):
+        if graphs:
+            for _ in range(n // args.copies):
+                graphs[args.copies].replay()
+            if n % args.copies:
+                graphs[n % args.copies].replay()
+        else:
+            for s in range(n):
+                layer.step(s % args.copies)
+
+    # the W untimed warm-up steps, then untimed steps for at least --spin-up seconds,
+    # right before the timed region: an idle GPU takes tens of milliseconds to raise
+    # its engine clock, and a few warm-up steps do not span that
+    run_steps(args.warmup)
+    spin = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SPIN_UP_S:
+        run_steps(64)
+        spin += 64
+        torch.cuda.synchronize()
     steps = args.steps
-    if graph is not None:
-        reps = max(1, steps // args.copies)
-        steps = reps * args.copies
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graph is not None:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        for s in range(steps):
-            layer.step(s % args.copies)
+    run_steps(steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    layer.spin_up_steps = spin
 
     # per-kernel durations: HIP events on the launch stream around batches of
     # back-to-back launches of one GEMV over >= 1 GB of weight copies
@@ -461,10 +480,20 @@ def time_q4_1():
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         nvq.nvq_quantize_act_q8_0(x, q, d, b)
         if M == 1:
-            us = _event_time(lambda: nvq.nvq_gemv_q4_1(w, q, d, b, y), 200)
             byts = N * K * 5 // 8 + K * 17 // 16 + K // 8 + 4 * N
-            out["q4_1_gemv_N4096_K4096"] = dict(us_avg=us, GBps=byts / (us * 1e-6) / 1e9,
-                                                note="10.5 MB of weights: Infinity-Cache resident across repeats")
+            us_hot = _event_time(lambda: nvq.nvq_gemv_q4_1(w, q, d, b, y), 200)
+            # HBM-cold: back-to-back launches rotating over >= 1 GB of distinct copies
+            copies = [w] + [w.clone() for _ in range(-(-(1 << 30) // (N * K * 5 // 8)) - 1)]
+            us = rotated_time(lambda wi: nvq.nvq_gemv_q4_1(wi, q, d, b, y), copies)
+            gbps = byts / (us * 1e-6) / 1e9
+            out["q4_1_gemv_N4096_K4096"] = dict(
+                us_avg=us, GBps=gbps, alg_bytes=byts, copies=len(copies),
+                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbps / HBM_PEAK_GBS,
+                              traffic=None, kernel="gemv_q4_1_m1_kernel (v_dot4 on unsigned codes)"),
+                us_cache_resident=us_hot,
+                note=f"HBM-cold: back-to-back launches over {len(copies)} distinct weight copies (>= 1 GB); "
+                     f"us_cache_resident repeats one 10.5 MB copy (Infinity-Cache resident)")
+            del copies
         else:
             need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_1, M, N, K)
             wsq = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
@@ -518,6 +547,27 @@ def time_moe(steps=400):
                 note="one launch per step (grid 128 tiles x 6 experts); each step's 6 experts drawn afresh")
 
 
+def rotated_time(fn, copies, reps=6):
+    """Average duration of ``fn(copy)`` over back-to-back launches that rotate through
+    ``copies`` (distinct HBM buffers, >= 1 GB in all, so no launch finds its weights in
+    the 256 MB Infinity Cache): HIP events on the launch stream around each batch."""
+    import torch
+
+    it = iter(range(10 ** 9))
+    host_s, call_s = spin_up(lambda: fn(copies[next(it) % len(copies)]))
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        backlog(host_s, call_s, len(copies))
+        e0.record()
+        for c in copies:
+            fn(c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / len(copies))
+    return 1e3 * float(np.mean(ms))
+
+
 def _event_time(fn, reps):
     import torch
 
@@ -532,55 +582,86 @@ def _event_time(fn, reps):
     return 1e3 * e0.elapsed_time(e1) / reps
 
 
+def host_cpu():
+    """Host CPU description: model name, logical CPUs, CPUs this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return dict(cpu_model=model, logical_cpus=os.cpu_count(), cpus_allowed=allowed)
+
+
 def cpu_baseline():
     """The oracle (plain scalar C, untouched) on the same decode layer: Q8_0
     quantization of the four inputs + all output rows of the four GEMVs, split over
-    host threads by output rows."""
+    host threads by output rows (about 10 s), then one pass on a single thread."""
     import oracle
     from gemm_q8_act_amd import synth
 
     o = oracle.load()
-    threads = min(16, os.cpu_count() or 1)
+    hc = host_cpu()
+    threads = max(1, min(16, hc["cpus_allowed"]))
     mats = []
     for name, N, K in synth.LAYER:
         codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name, 0), "uniform")
         x = synth.activations(1, K, synth.seed_for("layer", "x_" + name, 0))
         mats.append((N, K, codes, scales, ws, x))
-    t0 = time.perf_counter()
-    wbytes = 0
-    passes = 0
-    while True:  # whole-layer passes until about 10 s of wall time have gone by
-        for N, K, codes, scales, ws, x in mats:
-            q, d, _ = o.quantize_q8_0(x)
-            o.matmul_threads("nvfp4", (codes, scales, ws), q, d, np.arange(N), threads)
-            wbytes += nvfp4_bytes(N, K)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= 10.0:
-            break
-    return dict(value=wbytes / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{passes} passes over the full decode layer (Q8_0 of the 4 inputs + all 52224 output "
-                       f"rows of the QKV/O/gate+up/down GEMVs), M=1; {el:.2f} s wall on {threads} host threads")
+
+    def passes(nthreads, seconds):
+        t0 = time.perf_counter()
+        wbytes = n = 0
+        while True:  # whole-layer passes until `seconds` of wall time have gone by
+            for N, K, codes, scales, ws, x in mats:
+                q, d, _ = o.quantize_q8_0(x)
+                o.matmul_threads("nvfp4", (codes, scales, ws), q, d, np.arange(N), nthreads)
+                wbytes += nvfp4_bytes(N, K)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return wbytes / el / 1e9, n, el
+
+    gbps, n, el = passes(threads, 10.0)
+    gbps1, n1, el1 = passes(1, 0.0)  # one pass
+    return dict(value=gbps, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n} passes over the full decode layer (Q8_0 of the 4 inputs + all 52224 output rows of "
+                       f"the QKV/O/gate+up/down GEMVs, 185.8 MB of NVFP4 weights), M=1; {el:.2f} s wall on "
+                       f"{threads} host threads; then {n1} pass on 1 thread in {el1:.2f} s",
+                single_thread_GBps=gbps1, host=hc)
 
 
-def run_stack(args):
-    """64-layer stack of the layer shapes, one token step = 256 GEMVs (+ their
-    input quantization) back to back on one stream."""
+def stack_layers(M, weights_from=None):
+    """64 device-resident layers: layer 0's packed weights cloned into 63 more distinct
+    HBM buffers (11.9 GB in all), or the weights of ``weights_from`` (another stack)
+    used as they are; activations differ per layer."""
+    if weights_from is None:
+        layers = [Layer(M, 1)]
+        layers += [Layer(M, 1, seed_base=i, share_from=layers[0]) for i in range(1, 64)]
+    else:
+        layers = [Layer(M, 1, seed_base=i, share_from=weights_from[i], clone=False) for i in range(64)]
+    return layers
+
+
+def time_stack(layers, steps, eager=False):
+    """One token step over the 64-layer stack = 256 GEMVs (+ their input
+    quantization) back to back on one stream, one captured graph per step."""
     import torch
 
-    M = args.tokens
-    # layer 0's packed weights are cloned into 63 more distinct HBM buffers
-    # (11.9 GB in all); activations differ per layer
-    layers = [Layer(M, 1)]
-    layers += [Layer(M, 1, seed_base=i, share_from=layers[0]) for i in range(1, 64)]
+    M = layers[0].M
     torch.cuda.synchronize()
     wbytes = sum(l.weight_bytes() for l in layers)
+    alg = sum(gemv_alg_bytes(M, m["N"], m["K"]) for l in layers for m in l.mats)
     for _ in range(2):
         for l in layers:
             l.step(0)
     torch.cuda.synchronize()
     graph = None
-    if not args.eager:  # one stack step (256 quantizations + 256 GEMVs) per graph replay
+    if not eager:  # one stack step (256 quantizations + 256 GEMVs) per graph replay
         s_cap = torch.cuda.Stream()
         s_cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s_cap):
@@ -602,7 +683,6 @@ def run_stack(args):
                 l.step(0)
         torch.cuda.synchronize()
         warm += 1
-    steps = max(2, args.steps // 20)
     t0 = time.perf_counter()
     for _ in range(steps):
         if graph is not None:
@@ -613,13 +693,26 @@ def run_stack(args):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gbps = wbytes * steps / el / 1e9
-    line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=warm,
-                ms_per_step=1e3 * el / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
-                dtype="int8/fp32", data="synthetic",
+    del graph
+    return dict(M=M, steps=steps, warmup_steps=warm, ms_per_step=1e3 * el / steps, weight_GBps=gbps,
+                weight_bytes_per_step=wbytes, alg_bytes_per_step=alg,
+                roofline=dict(bound="hbm", achieved=alg * steps / el / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=alg * steps / el / 1e9 / HBM_PEAK_GBS, traffic=None,
+                              scope="whole stack step: 256 Q8_0 launches + 256 GEMVs; algorithmic bytes = "
+                                    "weights + Q8_0 activations + fp32 outputs"),
+                graph=not eager)
+
+
+def run_stack(args):
+    """--stack: the 64-layer stack alone at M = --tokens, as the one JSON line."""
+    M = args.tokens
+    r = time_stack(stack_layers(M), max(2, min(args.steps, 50)), args.eager)
+    line = dict(metric=METRIC, value=r["weight_GBps"], unit="GB/s", n_gpus=1, steps=r["steps"],
+                warmup=r["warmup_steps"], ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="int8/fp32", data="synthetic",
                 config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408",
-                            weight_bytes=wbytes, graph=not args.eager),
-                roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBS, unit="GB/s",
-                              frac=gbps / HBM_PEAK_GBS, traffic=None))
+                            weight_bytes=r["weight_bytes_per_step"], graph=r["graph"]),
+                roofline=r["roofline"])
     print(json.dumps(line), flush=True)
 
 
@@ -781,14 +874,29 @@ def main():
     roofline = dict(bound="hbm", achieved=gu["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=gu["GBps"] / HBM_PEAK_GBS, traffic=load_traffic("gemv_nvfp4_gate_up"),
                     kernel="gemv_nvfp4_kernel<0,false,4,5> (matrix-core decode GEMV), gate+up N=34816 K=5120",
+                    scope="the dominant kernel alone (the gate+up GEMV, 54 % of the step's weight bytes); "
+                          "`value` is the whole layer step (4 Q8_0 launches + 4 GEMVs)",
                     us_per_launch=gu["us_avg"], alg_bytes_per_launch=gu["alg_bytes"])
     line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=args.warmup,
                 ms_per_step=1e3 * elapsed / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="int8/fp32", data="synthetic",
                 config=dict(workload="decode layer hidden=5120 ffn=17408, M=1: Q8_0 + QKV/O/gate_up/down GEMVs",
                             weight_bytes_per_step=wbytes, weight_copies=args.copies,
-                            graph=not args.eager),
+                            graph=not args.eager, spin_up_steps=layer.spin_up_steps),
                 roofline=roofline, per_kernel=per)
+    del layer
+    if not args.no_stack:
+        log("64-layer stack, M = 1 and 8 ...")
+        nst = max(5, min(args.steps, 40))
+        st1 = stack_layers(1)
+        s1 = time_stack(st1, nst, args.eager)
+        st8 = stack_layers(8, weights_from=st1)
+        s8 = time_stack(st8, nst, args.eager)
+        line["stack"] = {"M1": s1, "M8": s8,
+                         "workload": "64 layers of the layer set (QKV/O/gate_up/down), 11.9 GB of NVFP4 weights "
+                                     "resident, one graph replay per token step; M=8 is batched decode"}
+        del st1, st8
+        torch.cuda.empty_cache()
     if not args.no_extras:
         line["torch_reference_rates"] = torch_reference_rates()
     if not args.no_gemm:
