@@ -3,7 +3,10 @@
 Headline (``value``): decode weight-streaming throughput, GB/s of NVFP4 weight
 bytes, for one transformer layer at hidden 5120 / ffn 17408 with M = 1 token:
 one step = Q8_0 quantization of the four GEMV inputs + the QKV [7168x5120],
-O [5120x5120], gate+up [34816x5120] and down [5120x17408] GEMVs.  The layer's
+O [5120x5120], gate+up [34816x5120] and down [5120x17408] GEMVs, run as the library
+runs a single token: four nvq_gemv_nvfp4_fused launches (the quantization inside
+each GEMV).  The same step as eight launches (nvq_quantize_act_q8_0 +
+nvq_gemv_nvfp4 per matrix) is timed beside it (``layer_two_launch``).  The layer's
 185.8 MB of weights are replicated ``--copies`` times in HBM and step s uses copy
 s % copies, so consecutive steps never find their weights in the 256 MB
 Infinity Cache.  Inputs are resident in HBM before the timed region.
@@ -97,6 +100,12 @@ def gemv_alg_bytes(M, N, K):
     return nvfp4_bytes(N, K) + M * K * 17 // 16 + 4 * M * N
 
 
+def fused_alg_bytes(N, K):
+    """Bytes the fused quantization + GEMV of one token must move: packed weights +
+    the float32 activation row + float32 outputs."""
+    return nvfp4_bytes(N, K) + 4 * K + 4 * N
+
+
 class Layer:
     """Device-resident decode layer: packed weights (``copies`` replicas), activations.
     ``share_from``: take that layer's packed weights (cloned into ``copies`` new
@@ -133,11 +142,19 @@ class Layer:
         return sum(nvfp4_bytes(m["N"], m["K"]) for m in self.mats)
 
     def step(self, copy):
+        """Quantization launch + GEMV launch per matrix."""
         import gemm_q8_act_amd as nvq
 
         for m in self.mats:
             nvq.nvq_quantize_act_q8_0(m["x"], m["q"], m["d"])
             nvq.nvq_gemv_nvfp4(m["w"][copy], m["ws"], m["q"], m["d"], m["y"])
+
+    def step_fused(self, copy):
+        """One launch per matrix: the quantization fused into the GEMV (M = 1 only)."""
+        import gemm_q8_act_amd as nvq
+
+        for m in self.mats:
+            nvq.nvq_gemv_nvfp4_fused(m["w"][copy], m["ws"], m["x"], m["y"])
 
 
 def kernel_src_hash():
@@ -167,14 +184,18 @@ def load_traffic(kernel_key):
 # measurements
 # ---------------------------------------------------------------------------
 
-def time_layer(args):
+def time_layer(args, fused=True, layer=None):
+    """Exactly --steps layer steps (after --warmup steps and the spin-up), fused
+    (one launch per matrix) or as quantization + GEMV launches."""
     import torch
 
     M = 1
-    layer = Layer(M, args.copies)
+    if layer is None:
+        layer = Layer(M, args.copies)
+    step = layer.step_fused if fused else layer.step
     torch.cuda.synchronize()
     for c in range(args.copies):  # one eager pass over every weight copy before capture
-        layer.step(c)
+        step(c)
     torch.cuda.synchronize()
 
     graphs = {}
@@ -190,7 +211,7 @@ def time_layer(args):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=s_cap):
                     for c in range(r):
-                        layer.step(c)
+                        step(c)
                 graphs[r] = g
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
@@ -203,7 +224,7 @@ def time_layer(args):
                 graphs[n % args.copies].replay()
         else:
             for s in range(n):
-                layer.step(s % args.copies)
+                step(s % args.copies)
 
     # the W untimed warm-up steps, then untimed steps for at least --spin-up seconds,
     # right before the timed region: an idle GPU takes tens of milliseconds to raise
@@ -221,18 +242,28 @@ def time_layer(args):
     run_steps(steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    layer.spin_up_steps = spin
+    del graphs
+    return layer, steps, elapsed, spin
 
-    # per-kernel durations: HIP events on the launch stream around batches of
-    # back-to-back launches of one GEMV over >= 1 GB of weight copies
+
+def layer_kernel_times(layer):
+    """Per-kernel durations: HIP events on the launch stream around batches of
+    back-to-back launches of one GEMV over >= 1 GB of weight copies; the plain GEMV
+    (its Q8_0 input already made), the fused one (from the float32 row), the v_dot4
+    variant, and one quantization launch."""
     per = {}
     for m in layer.mats:
         per[m["name"]] = gemv_batch_time(layer, m)
+        f = gemv_batch_time(layer, m, fused=True)
+        per[m["name"]].update(fused_us=f["us_avg"], fused_us_p50=f["us_p50"], fused_GBps=f["GBps"],
+                              fused_alg_bytes=f["alg_bytes"])
         per[m["name"]]["dot4_us"] = gemv_batch_time(layer, m, dot4=True)["us_avg"]
-    return layer, steps, elapsed, per
+        per[m["name"]]["quant_us"] = _event_time(lambda: __import__("gemm_q8_act_amd").nvq_quantize_act_q8_0(
+            m["x"], m["q"], m["d"]), 200)
+    return per
 
 
-def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
+def gemv_batch_time(layer, m, dot4=False, fused=False, min_bytes=1 << 30, reps=6):
     """Average launch duration of one GEMV: HIP events (on the launch stream) around a
     batch of back-to-back launches that rotate through at least ``min_bytes`` of
     distinct weight copies, so no launch finds its weights in the 256 MB Infinity
@@ -242,26 +273,33 @@ def gemv_batch_time(layer, m, dot4=False, min_bytes=1 << 30, reps=6):
 
     import gemm_q8_act_amd as nvq
 
-    fn = nvq.nvq_gemv_nvfp4_dot4 if dot4 else nvq.nvq_gemv_nvfp4
+    if fused:
+        def fn(w):
+            nvq.nvq_gemv_nvfp4_fused(w, m["ws"], m["x"], m["y"])
+    else:
+        g = nvq.nvq_gemv_nvfp4_dot4 if dot4 else nvq.nvq_gemv_nvfp4
+
+        def fn(w):
+            g(w, m["ws"], m["q"], m["d"], m["y"])
     wbytes = nvfp4_bytes(m["N"], m["K"])
     extra = max(0, -(-min_bytes // wbytes) - len(m["w"]))
     ws = list(m["w"]) + [m["w"][i % len(m["w"])].clone() for i in range(extra)]
     it = iter(range(10 ** 9))
-    host_s, call_s = spin_up(lambda: fn(ws[next(it) % len(ws)], m["ws"], m["q"], m["d"], m["y"]))
+    host_s, call_s = spin_up(lambda: fn(ws[next(it) % len(ws)]))
     ms = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         backlog(host_s, call_s, len(ws))
         e0.record()
         for w in ws:
-            fn(w, m["ws"], m["q"], m["d"], m["y"])
+            fn(w)
         e1.record()
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1) / len(ws))
     nlaunch = len(ws)
     del ws
     us = 1e3 * float(np.mean(ms))
-    ab = gemv_alg_bytes(layer.M, m["N"], m["K"])
+    ab = fused_alg_bytes(m["N"], m["K"]) if fused else gemv_alg_bytes(layer.M, m["N"], m["K"])
     return dict(N=m["N"], K=m["K"], us_avg=us, us_p50=1e3 * float(np.median(ms)), alg_bytes=ab,
                 GBps=ab / (us * 1e-6) / 1e9, launches_per_batch=nlaunch)
 
@@ -433,7 +471,17 @@ def time_extras():
     y = torch.empty((1, N), dtype=torch.float32, device="cuda")
     nvq.nvq_quantize_act_q8_0(x, q, d, b)
     us = _event_time(lambda: nvq.nvq_gemv_nvfp4(w, ws, q, d, y), 200)
-    out["gemv_small_N4864_K896"] = dict(us_avg=us, GBps=gemv_alg_bytes(1, N, K) / (us * 1e-6) / 1e9)
+
+    def two():
+        nvq.nvq_quantize_act_q8_0(x, q, d)
+        nvq.nvq_gemv_nvfp4(w, ws, q, d, y)
+
+    us2 = _event_time(two, 200)
+    usf = _event_time(lambda: nvq.nvq_gemv_nvfp4_fused(w, ws, x, y), 200)
+    out["gemv_small_N4864_K896"] = dict(us_avg=us, GBps=gemv_alg_bytes(1, N, K) / (us * 1e-6) / 1e9,
+                                        quant_plus_gemv_us=us2, fused_us=usf,
+                                        note="L2-resident; us_avg is the GEMV on ready Q8_0 input, fused_us the one "
+                                             "launch from float32 input, quant_plus_gemv_us the two launches")
     out.update(time_act_quant())
     out.update(time_q4_1())
     out["moe_routed_gemv"] = time_moe()
@@ -742,7 +790,11 @@ def traffic_probe():
     for w in wl:
         nvq.nvq_gemv_nvfp4(w, float(ws), q, d, y)
     torch.cuda.synchronize()
-    log(f"traffic probe: copy {n} B; 4 x gate+up GEMV N={N} K={K}, {nvfp4_bytes(N, K)} weight bytes each")
+    for w in wl:
+        nvq.nvq_gemv_nvfp4_fused(w, float(ws), x, y)
+    torch.cuda.synchronize()
+    log(f"traffic probe: copy {n} B; 4 x gate+up GEMV and 4 x fused gate+up N={N} K={K}, "
+        f"{nvfp4_bytes(N, K)} weight bytes each")
 
 
 def summarize_pmc(fetch_csv, write_csv):
@@ -769,14 +821,15 @@ def summarize_pmc(fetch_csv, write_csv):
     cw = max(v for k, g, v in wr if "copyBuffer" in k)
     ff, fw = (n / 1024) / cf, (n / 1024) / cw
     res = dict(calibration=dict(copy_bytes=n, fetch_kib=cf, write_kib=cw, fetch_factor=ff, write_factor=fw))
-    gf = [(k, g, v) for k, g, v in f if "gemv_nvfp4_kernel" in k]
-    gw = [v for k, g, v in wr if "gemv_nvfp4_kernel" in k]
-    if gf:
-        vf, vw = float(np.mean([v for _, _, v in gf])), float(np.mean(gw)) if gw else 0.0
-        res["gemv_nvfp4_gate_up"] = dict(
-            kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
-            bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=gemv_alg_bytes(1, 34816, 5120),
-            src_hash=kernel_src_hash())
+    for key, name, alg in (("gemv_nvfp4_gate_up", "gemv_nvfp4_kernel", gemv_alg_bytes(1, 34816, 5120)),
+                           ("gemv_nvfp4_fused_gate_up", "gemv_nvfp4_fused_kernel", fused_alg_bytes(34816, 5120))):
+        gf = [(k, g, v) for k, g, v in f if name in k]
+        gw = [v for k, g, v in wr if name in k]
+        if gf:
+            vf, vw = float(np.mean([v for _, _, v in gf])), float(np.mean(gw)) if gw else 0.0
+            res[key] = dict(
+                kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
+                bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=alg, src_hash=kernel_src_hash())
     print(json.dumps(res, indent=1))
 
 
@@ -866,24 +919,38 @@ def main():
         return
 
     log("decode layer ...")
-    layer, steps, elapsed, per = time_layer(args)
+    layer, steps, elapsed, spin = time_layer(args, fused=True)
+    _, steps2, elapsed2, spin2 = time_layer(args, fused=False, layer=layer)
+    per = layer_kernel_times(layer)
     wbytes = layer.weight_bytes()
     gbps = wbytes * steps / elapsed / 1e9
-    # dominant kernel: the gate+up GEMV (54 % of the step's weight bytes)
+    # dominant kernel: the gate+up GEMV (54 % of the step's weight bytes), here fused
     gu = per["gate_up"]
-    roofline = dict(bound="hbm", achieved=gu["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=gu["GBps"] / HBM_PEAK_GBS, traffic=load_traffic("gemv_nvfp4_gate_up"),
-                    kernel="gemv_nvfp4_kernel<0,false,4,5> (matrix-core decode GEMV), gate+up N=34816 K=5120",
-                    scope="the dominant kernel alone (the gate+up GEMV, 54 % of the step's weight bytes); "
-                          "`value` is the whole layer step (4 Q8_0 launches + 4 GEMVs)",
-                    us_per_launch=gu["us_avg"], alg_bytes_per_launch=gu["alg_bytes"])
+    gf = gu["fused_GBps"]
+    roofline = dict(bound="hbm", achieved=gf, peak=HBM_PEAK_GBS, unit="GB/s", frac=gf / HBM_PEAK_GBS,
+                    traffic=load_traffic("gemv_nvfp4_fused_gate_up"),
+                    kernel="gemv_nvfp4_fused_kernel<4,5,5> (Q8_0 quantization + matrix-core decode GEMV, one "
+                           "launch), gate+up N=34816 K=5120",
+                    scope="the dominant kernel of the step alone (the fused gate+up GEMV, 54 % of the step's "
+                          "weight bytes); `value` is the whole layer step (4 fused launches)",
+                    us_per_launch=gu["fused_us"], alg_bytes_per_launch=gu["fused_alg_bytes"])
+    roofline_gemv = dict(bound="hbm", achieved=gu["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=gu["GBps"] / HBM_PEAK_GBS, traffic=load_traffic("gemv_nvfp4_gate_up"),
+                         kernel="gemv_nvfp4_kernel<0,false,4,5> (matrix-core decode GEMV on Q8_0 input), gate+up",
+                         us_per_launch=gu["us_avg"], alg_bytes_per_launch=gu["alg_bytes"])
     line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=args.warmup,
                 ms_per_step=1e3 * elapsed / steps, higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="int8/fp32", data="synthetic",
-                config=dict(workload="decode layer hidden=5120 ffn=17408, M=1: Q8_0 + QKV/O/gate_up/down GEMVs",
+                config=dict(workload="decode layer hidden=5120 ffn=17408, M=1: Q8_0 quantization + "
+                                     "QKV/O/gate_up/down GEMVs, fused (one launch per matrix)",
                             weight_bytes_per_step=wbytes, weight_copies=args.copies,
-                            graph=not args.eager, spin_up_steps=layer.spin_up_steps),
-                roofline=roofline, per_kernel=per)
+                            graph=not args.eager, spin_up_steps=spin),
+                roofline=roofline, roofline_gemv=roofline_gemv,
+                layer_two_launch=dict(value=wbytes * steps2 / elapsed2 / 1e9, unit="GB/s", steps=steps2,
+                                      ms_per_step=1e3 * elapsed2 / steps2, spin_up_steps=spin2,
+                                      note="the same step as nvq_quantize_act_q8_0 + nvq_gemv_nvfp4 per matrix "
+                                           "(8 launches)"),
+                per_kernel=per)
     del layer
     if not args.no_stack:
         log("64-layer stack, M = 1 and 8 ...")

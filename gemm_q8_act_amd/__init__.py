@@ -29,7 +29,8 @@ NVQ_GEMV_MAX_M = 15
 # Every symbol include/nvq.h declares.
 EXPORTS = (
     "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_gemm_workspace_bytes",
-    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_dot4",
+    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_fused",
+    "nvq_gemv_nvfp4_dot4",
     "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
     "nvq_status_str", "nvq_last_error",
 )
@@ -50,6 +51,12 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libnvq.so not built at {LIB_PATH}; run gemm_q8_act_amd.build.build()")
+        # torch first: it loads its own HIP runtime (soname libamdhip64.so.7), which
+        # libnvq's dependency then resolves to, so the process has one runtime and the
+        # library sees torch's devices, memory and streams.  Loaded the other way round,
+        # torch would bring a second runtime and libnvq's would find no device.
+        import torch  # noqa: F401
+
         L = ctypes.CDLL(LIB_PATH)
         P, I64, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         sigs = {
@@ -60,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "nvq_pack_q4_1": (ctypes.c_int, [P, P, P, I64, I64, P]),
             "nvq_quantize_act_q8_0": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
+            "nvq_gemv_nvfp4_fused": (ctypes.c_int, [P, F, P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4_dot4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_nvfp4_routed": (ctypes.c_int, [P, P, P, I64, I64, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P, SZ, P]),
@@ -215,6 +223,30 @@ def nvq_gemv_nvfp4(w, w_scale: float, q, d_f16, y, stream=None) -> None:
     _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
     _check(lib().nvq_gemv_nvfp4(_ptr(w), float(w_scale), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
                                 _stream(stream, y)), "nvq_gemv_nvfp4")
+
+
+def nvq_gemv_nvfp4_fused(w, w_scale: float, x, y, q_out=None, d_out=None, stream=None) -> None:
+    """One token: x float32 [1, K] (or [K]) -> y float32 [1, N] (or [N]), Q8_0
+    quantization inside the GEMV launch; q_out int8 [.., K] / d_out 2-byte [.., K/32]
+    optionally receive the codes and scales."""
+    import torch
+
+    K = x.shape[-1]
+    N = y.shape[-1]
+    if x.numel() != K or y.numel() != N:
+        raise ValueError("nvq_gemv_nvfp4_fused takes one token: x [K] or [1, K], y [N] or [1, N]")
+    _need(x, torch.float32, tuple(x.shape), "x")
+    _need(y, torch.float32, tuple(y.shape), "y")
+    if (q_out is None) != (d_out is None):
+        raise ValueError("q_out and d_out are given together or not at all")
+    if q_out is not None:
+        if q_out.dtype != torch.int8 or q_out.numel() != K:
+            raise ValueError("q_out: int8 tensor of K elements required")
+        if d_out.element_size() != 2 or d_out.numel() != K // 32:
+            raise ValueError("d_out: 2-byte tensor of K/32 elements required")
+    _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_nvfp4_fused(_ptr(w), float(w_scale), _ptr(x), N, K, _ptr(y), _ptr(q_out), _ptr(d_out),
+                                      _stream(stream, y)), "nvq_gemv_nvfp4_fused")
 
 
 def nvq_gemv_nvfp4_routed(w, w_scales, ids, q, d_f16, y, stream=None) -> None:

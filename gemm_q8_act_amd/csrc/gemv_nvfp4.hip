@@ -35,6 +35,14 @@
 //    v_perm_b32 table lookups per four codes, summed inside v_dot4_i32_i8 (see
 //    nvq_device.h).  About 13 full-rate instructions per 8 weights: on MI355X this
 //    costs as much time as streaming the bytes, so it is the slower of the two.
+//
+// Fused quantization (gemv_tile_fused, MODE_MX, one token): the block reads the
+// float32 row x instead of its Q8_0 codes.  Each wavefront quantizes exactly the
+// chunks it consumes (v, v + W, ...), one batch at a time, into its own part of the
+// LDS table: the quantization of batch b + 1 runs while that batch's weights are in
+// flight, so no separate quantization launch (and no round trip of the codes through
+// memory) precedes the product, and no block barrier precedes the first MFMA.  The
+// codes are bit-exact with nvq_quantize_act_q8_0 (see q8_0_pack4).
 
 #include "nvq_device.h"
 #include "nvq_launch.h"
@@ -59,6 +67,50 @@ __device__ __forceinline__ uint32_t act_hi_e4m3(uint32_t q) {
 __host__ __device__ constexpr int64_t gemv_tab_bytes(int64_t nch) { return (nch + 1) * 256; }
 __host__ __device__ constexpr int64_t gemv_dtab_off(int64_t nch) { return gemv_tab_bytes(nch) + 16; }
 __host__ __device__ constexpr int64_t gemv_red_off(int64_t nch) { return gemv_dtab_off(nch) + (nch * 4 + 4) * 4; }
+
+// d32 = fl(amax / 127) without the division sequence: q0 = amax * fl(1/127), then one
+// fma correction, d = fma(fma(-q0, 127, amax), fl(1/127), q0).  Checked exhaustively
+// against IEEE float32 division: equal for every non-negative finite float (2^31
+// values, subnormals included).
+__device__ __forceinline__ float div127(float a) {
+  constexpr float kInv127 = 0x1.020408p-7f;  // fl(1 / 127)
+  const float q0 = a * kInv127;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 127.0f, a), kInv127, q0);
+}
+
+// max over the 8 lanes of each aligned 8-lane group (DPP: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror), no LDS traffic
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));
+  return v;
+}
+
+// Q8_0 codes of 4 values of a 32-value block whose scale is d32 = fl(amax / 127):
+// q = clamp(rint(fl(x / d32)), -127, 127), packed one byte each; d32 == 0 gives 0.
+// Each quotient is taken as u = fma(x, r, 128) with r = v_rcp_f32(d32) (1 ulp):
+// |x / d32| <= 127.00002, so |u - 128 - fl(x / d32)| <= 127.00002 (2^-23 + 2^-24) +
+// 2^-18 + 2^-17 < 4.2e-5; whenever u lies more than 2^-14 (6.1e-5) inside the
+// interval of its nearest integer k, k - 128 is also rint(fl(x / d32)) and |k - 128|
+// <= 127.  The biased code k (1..255) is packed with v_cvt_pk_u8_f32 and the bias
+// removed by flipping each byte's top bit.  Quotients nearer a rounding tie, and
+// every quotient of a block with 0 < d32 < 2^-100 (whose reciprocal could leave the
+// normal range), take the IEEE division and the clamp themselves.
+__device__ __forceinline__ uint32_t q8_0_pack4(const float4& v, float d) {
+  const bool exact = d > 0.0f && d < 0x1.0p-100f;
+  const float r = d > 0.0f ? __builtin_amdgcn_rcpf(d) : 0.0f;
+  const float xs[4] = {v.x, v.y, v.z, v.w};
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float u = __builtin_fmaf(xs[i], r, 128.0f);
+    float k = __builtin_rintf(u);
+    if (exact || fabsf(u - k) > 0.49993896484375f) k = fminf(fmaxf(__builtin_rintf(xs[i] / d), -127.0f), 127.0f) + 128.0f;
+    packed = __builtin_amdgcn_cvt_pk_u8_f32(k, (uint32_t)i, packed);
+  }
+  return packed ^ 0x80808080u;
+}
 
 // One 16-row tile of the product (the body of both kernels below).
 template <int MODE, bool DEBUG, int W, int P>
@@ -205,6 +257,126 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ w, int64_t
   }
 }
 
+// One 16-row tile of the product with the Q8_0 quantization of the float32 row x
+// fused in (MODE_MX inner loop, as gemv_tile).  Prologue: thread t loads the float4
+// groups g4 = t + NT u (u < XU; k = 4 g4 .. + 3; 8 consecutive threads hold one
+// 32-value block -- NT and K / 4 are multiples of 8, so a block's 8 groups are all in
+// the row or all past it), then issues the first weight batch, then quantizes its
+// groups into the LDS table while the weights stream in (loads retire in order, so
+// the quantization waits for x only).  Rows longer than XU * NT * 4 load the rest as
+// they go.  q_out / d_out, if not null, receive the row's codes and binary16 scales
+// (block of tile 0).
+template <int W, int P, int XU>
+__device__ __forceinline__ void gemv_tile_fused(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                const float* __restrict__ x, float w_scale, float* __restrict__ y,
+                                                int8_t* __restrict__ q_out, uint16_t* __restrict__ d_out,
+                                                int64_t tile) {
+  constexpr int NT = 64 * W;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int nch = (K + 127) >> 7;
+  const int n4 = K >> 2, nd = K >> 5;
+  uint8_t* tab = smem;
+  uint8_t* zero16 = smem + gemv_tab_bytes(nch);
+  float* dtab = reinterpret_cast<float*>(smem + gemv_dtab_off(nch));
+  float* red = reinterpret_cast<float*>(smem + gemv_red_off(nch));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t ntiles = (N + 15) >> 4;
+  const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
+  const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
+  const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
+
+  // 1. the float32 activations first
+  float4 xv[XU];
+#pragma unroll
+  for (int u = 0; u < XU; ++u) xv[u] = x4[min(tid + NT * u, n4 - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. first batch of weight loads (chunk indices clamped, as in gemv_tile)
+  u32x4 bb[P];
+  uint32_t ss[P];
+  auto issue = [&](int c0) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = min(c0 + W * p, nch - 1);
+      bb[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wt + (int64_t)c * 1024));
+      ss[p] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(st + (int64_t)c * 128));
+    }
+  };
+  int c0 = wave;
+  issue(c0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. quantize into the table (MX layout of gemv_tile)
+  const bool write_q = tile == 0 && q_out != nullptr;
+  auto quant_put = [&](const float4& v, int g4) {
+    const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float d = div127(a);  // = fl(amax / 127)
+    const uint32_t pk = q8_0_pack4(v, d);
+    if (g4 < n4) {
+      const int k = 4 * g4, c = k >> 7, o = k & 127;
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = act_hi_e4m3(pk);
+      *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = pk & 0x0F0F0F0Fu;
+      const _Float16 dh = (_Float16)d;  // the stored binary16 scale (round to nearest even)
+      if ((g4 & 7) == 0) dtab[g4 >> 3] = (float)dh;
+      if (write_q) {
+        *reinterpret_cast<uint32_t*>(q_out + k) = pk;
+        if ((g4 & 7) == 0) d_out[g4 >> 3] = __builtin_bit_cast(uint16_t, dh);
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < XU; ++u) quant_put(xv[u], tid + NT * u);
+  for (int g4 = tid + NT * XU; g4 < n4; g4 += NT) quant_put(x4[g4], g4);
+  // the part of the last chunk past the row's end (K % 128 == 64): zero codes and scales
+  for (int g4 = n4 + tid; g4 < nch * 32; g4 += NT) {
+    const int k = 4 * g4, c = k >> 7, o = k & 127;
+    *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = 0u;
+    *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = 0u;
+  }
+  for (int b = nd + tid; b < nch * 4; b += NT) dtab[b] = 0.0f;
+  if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
+  __syncthreads();
+
+  // 4. compute (the MX loop of gemv_tile)
+  const int sbv = nl >> 1, part = nl & 1;
+  float acc = 0.0f;
+  while (true) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int c = c0 + W * p;
+      if (c >= nch) continue;
+      const uint8_t* pa = (sbv == g) ? tab + c * 256 + part * 128 + 16 * g : zero16;
+      const uint8_t* pb = (sbv == g + 4) ? tab + c * 256 + part * 128 + 64 + 16 * g : zero16;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(pa);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(pb);
+      const v8i av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      const v8i bv = {(int)bb[p][0], (int)bb[p][1], (int)bb[p][2], (int)bb[p][3], 0, 0, 0, 0};
+      const floatx4 D = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 4,
+                                                                        0, 127 + 9, 0, 127);
+      const float i0 = fmaf(D[0], 16.0f, D[1]), i1 = fmaf(D[2], 16.0f, D[3]);
+      const float t = fmaf(i0, ue4m3_to_f32<0>(ss[p]), i1 * ue4m3_to_f32<1>(ss[p]));
+      acc = fmaf(t, dtab[4 * c + g], acc);
+    }
+    c0 += W * P;
+    if (c0 >= nch) break;
+    issue(c0);
+  }
+
+  // 5. reduce the 4 W partial sums of each row
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (tid < 16) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) sum += red[ww * 64 + gg * 16 + tid];
+    const int64_t r = tile * 16 + tid;
+    if (r < N) y[r] = sum * w_scale;
+  }
+}
+
 template <int MODE, bool DEBUG, int W, int P>
 __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __restrict__ w, int64_t N,
                                                             int K, const int8_t* __restrict__ q,
@@ -212,6 +384,15 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
                                                             float w_scale, float* __restrict__ y,
                                                             int32_t* __restrict__ isums) {
   gemv_tile<MODE, DEBUG, W, P>(w, N, K, q, d16, w_scale, y, isums, blockIdx.x);
+}
+
+// Fused quantization + decode GEMV (one token): y = S * W . Q8_0(x).
+template <int W, int P, int XU>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_fused_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                                  const float* __restrict__ x, float w_scale,
+                                                                  float* __restrict__ y, int8_t* __restrict__ q_out,
+                                                                  uint16_t* __restrict__ d_out) {
+  gemv_tile_fused<W, P, XU>(w, N, K, x, w_scale, y, q_out, d_out, blockIdx.x);
 }
 
 // Expert-routed form (the "mul_mat_id" step of a mixture-of-experts layer; "HANDOFF:
@@ -249,7 +430,7 @@ static bool gemv_wide(int64_t ntiles, int64_t nch) { return nch >= 64 && ntiles 
 
 size_t gemv_lds_bytes(int64_t K) {
   const int64_t nch = (K + 127) / 128;
-  return (size_t)(gemv_red_off(nch) + 8 * 64 * 4);  // room for the widest block (W = 8)
+  return (size_t)(gemv_red_off(nch) + 16 * 64 * 4);  // room for the widest block (W = 16)
 }
 
 template <int MODE, bool DEBUG, int W, int P>
@@ -280,6 +461,58 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
   if (mode != 0) return launch_gemv<1, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
   if (gemv_wide(ntiles, nch)) return launch_gemv<0, false, 8, 3>(w, w_scale, q, d16, N, K, y, isums, stream);
   return launch_gemv<0, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
+}
+
+template <int W, int P, int XU>
+static hipError_t launch_fused(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                               int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nch = (K + 127) / 128;
+  const size_t lds = (size_t)(gemv_red_off(nch) + W * 64 * 4);
+  auto fn = gemv_nvfp4_fused_kernel<W, P, XU>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)ntiles), dim3(64 * W), lds, stream, w, N, (int)K, x, w_scale, y, q_out,
+                     d_out);
+  return hipGetLastError();
+}
+
+// XU = the float4 groups per thread that cover the row (at most 9 preloaded)
+template <int W, int P>
+static hipError_t launch_fused_w(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                                 int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
+  const int64_t xu = (K / 4 + 64 * W - 1) / (64 * W);
+  switch (xu < 9 ? xu : 9) {
+    case 1: return launch_fused<W, P, 1>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 2: return launch_fused<W, P, 2>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 3: return launch_fused<W, P, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 4: return launch_fused<W, P, 4>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 5: return launch_fused<W, P, 5>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 6: return launch_fused<W, P, 6>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 7: return launch_fused<W, P, 7>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    case 8: return launch_fused<W, P, 8>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+    default: return launch_fused<W, P, 9>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  }
+}
+
+// Launch shape of the fused kernel, by measurement on the layer shapes (the per-block
+// quantization of the row is the extra cost, so larger blocks pay off on small grids):
+// short rows (at most 12 chunks) 4 wavefronts x 3-chunk batches (4864 x 896: 2.9 us
+// against 3.1 with 4 x 5); fewer than 1024 tiles with long rows 16 x 2 (down 5120 x
+// 17408: 13.9 us against 15.3 with 8 x 3), else 8 x 3 (QKV 7168 x 5120 / O 5120 x 5120:
+// 6.8 / 6.5 us against 7.2 / 7.1 with 4 x 5); many tiles 4 x 5 (gate+up 34816 x 5120:
+// 18.5 us against 18.5 with 8 x 3 and 19.2 with 8 x 2).
+hipError_t launch_gemv_nvfp4_fused(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                                   int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
+  const int64_t ntiles = (N + 15) / 16;
+  const int64_t nch = (K + 127) / 128;
+  if (nch <= 12) return launch_fused_w<4, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  if (ntiles < 1024 && nch >= 64) return launch_fused_w<16, 2>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  if (ntiles < 1024) return launch_fused_w<8, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  return launch_fused_w<4, 5>(w, w_scale, x, N, K, y, q_out, d_out, stream);
 }
 
 template <int W, int P>

@@ -209,6 +209,21 @@ nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const u
   return launched(nvq::launch_gemm_nvfp4(wb, w_scale, q, d_f16, M, N, K, y, nullptr, nullptr, (hipStream_t)stream), "gemv_nvfp4 (tiled)");
 }
 
+nvq_status nvq_gemv_nvfp4_fused(const void* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                                int8_t* q_out, uint16_t* d_out, void* stream) {
+  if (!w || !x || !y) return fail(NVQ_ERR_NULL, "nvq_gemv_nvfp4_fused: NULL pointer");
+  if ((q_out == nullptr) != (d_out == nullptr))
+    return fail(NVQ_ERR_NULL, "nvq_gemv_nvfp4_fused: q_out and d_out are given together or not at all");
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 16) || (q_out && !aligned(q_out, 16)) ||
+      (d_out && !aligned(d_out, 2)))
+    return fail(NVQ_ERR_ALIGN, "nvq_gemv_nvfp4_fused: w, x, y and q_out must be 16-byte aligned, d_out 2-byte");
+  NVQ_TRY(check_dims(1, N, K, 64, 1, 1));
+  if (!gemv_fits_lds(K)) return fail(NVQ_ERR_SHAPE, "nvq_gemv_nvfp4_fused: K=%lld too large for the LDS activation table", (long long)K);
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_nvfp4_fused(static_cast<const uint8_t*>(w), w_scale, x, N, K, y, q_out, d_out,
+                                               (hipStream_t)stream), "gemv_nvfp4_fused");
+}
+
 nvq_status nvq_gemv_nvfp4_routed(const void* w, const float* w_scales, const int32_t* ids, int64_t n_experts,
                                  int64_t n_active, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N,
                                  int64_t K, float* y, void* stream) {

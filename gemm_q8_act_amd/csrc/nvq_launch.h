@@ -17,6 +17,11 @@ hipError_t launch_act_quant(const float* x, int64_t M, int64_t K, int8_t* q, uin
 hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q,
                                 const uint16_t* d16, int64_t N, int64_t K, float* y,
                                 int32_t* isums, int mode, hipStream_t stream);
+// NVFP4, one token: Q8_0 quantization of the float32 row x fused into the M == 1
+// decode GEMV (every block quantizes the row into its LDS table); q_out / d_out, if
+// not null, receive the row's codes and binary16 scales.  K within gemv_lds_bytes.
+hipError_t launch_gemv_nvfp4_fused(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                                   int8_t* q_out, uint16_t* d_out, hipStream_t stream);
 // NVFP4, 2 <= M <= 16 tokens: exact fp16 operands on the fp16 matrix core, one launch
 // (one weight stream) per 16 tokens.  Any K with M * K < 2^32 (32-bit activation
 // offsets; the callers check).  isums != nullptr selects the debug variant (per-16

@@ -176,6 +176,23 @@ nvq_status nvq_quantize_act_q8_0(const float* x, int64_t M, int64_t K,
 nvq_status nvq_gemv_nvfp4(const void* w, float w_scale, const int8_t* q, const uint16_t* d_f16,
                           int64_t M, int64_t N, int64_t K, float* y, void* stream);
 
+/* Decode GEMV of one token with its Q8_0 activation quantization fused in: x [K]
+ * float32 (device, 16-byte aligned), y [N] float32 = the nvq_gemv_nvfp4 result for
+ * the codes and scales nvq_quantize_act_q8_0 gives for x (same Q8_0 definition, bit
+ * for bit; same error bound).  One launch: every block of the decode kernel
+ * quantizes x into its on-chip activation table, so no quantization launch and no
+ * round trip of the codes through memory precede the product.  q_out [K] int8 and
+ * d_out [K/32] binary16 (device; both NULL or both given) receive the codes and
+ * scales it used, e.g. for a later product on the same activations.  N >= 1,
+ * K % 64 == 0, K within the decode kernel's LDS table (about 70000; NVQ_ERR_SHAPE
+ * beyond).  Several tokens take nvq_quantize_act_q8_0 + nvq_gemv_nvfp4 (the batched
+ * kernel streams the weights once for all of them).
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
+ * (the tiled path repacks the Q8_0 activations itself, tiled_unpack_src1) and
+ * section 7 item 1 (decode is bandwidth-bound: every extra pass over memory costs). */
+nvq_status nvq_gemv_nvfp4_fused(const void* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
+                                int8_t* q_out, uint16_t* d_out, void* stream);
+
 /* The same decode GEMV with the per-16 integer sums computed on the vector unit:
  * E2M1 -> int8 by v_perm_b32 table lookups and v_dot4_i32_i8 (one launch per
  * token).  Same arguments, results within the same bound.  K is limited to what

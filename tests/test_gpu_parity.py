@@ -143,6 +143,64 @@ def test_gemv_nvfp4_m1(oracle, N, K, kernel):
     check_y(host(y), yo, awa, f"gemv {kernel} N={N} K={K}")
 
 
+# ---------------------------------------------------------------------------
+# Fused Q8_0 quantization + decode GEMV (one token)
+# ---------------------------------------------------------------------------
+
+def _fused_run(w, ws, x, N):
+    """One fused launch on the float32 row x; returns y, q_out, d_out on the host."""
+    torch = torch_dev()
+    K = x.shape[-1]
+    y = torch.full((1, N), float("nan"), dtype=torch.float32, device="cuda")
+    qo = torch.full((1, K), 99, dtype=torch.int8, device="cuda")
+    do = torch.full((1, K // 32), 0x7E00, dtype=torch.int16, device="cuda")
+    nvq.nvq_gemv_nvfp4_fused(w, ws, to_dev(x.reshape(1, K)), y, qo, do)
+    return host(y), host(qo), host(do).view(np.uint16)
+
+
+# (N, K): several tiles with a ragged last one; K % 128 == 64; one to nine float4
+# groups per thread and the in-block loop past nine (K = 20544 and 65536); the
+# 8-wavefront launch (down projection: K = 17408, few tiles)
+FUSED_SHAPES = [(4864, 896), (1, 64), (37, 128), (129, 640), (33, 320), (1000, 4096), (300, 5120),
+                (130, 17408), (20, 20544), (40, 65536), (70, 9216), (17, 2304)]
+
+
+@pytest.mark.parametrize("N,K", FUSED_SHAPES)
+def test_gemv_fused(oracle, N, K):
+    """y against the oracle's product on the oracle's own Q8_0 of x; the codes and
+    scales the kernel used (q_out, d_out) bit-exact with the oracle's."""
+    say(f"gemv fused N={N} K={K}")
+    codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("test", "fused", N * 3 + K), "uniform")
+    w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    x = synth.activations(1, K, synth.seed_for("test", "fused_x", K), outliers=True)
+    y, qk, dk = _fused_run(w, ws, x, N)
+    qo, do, _ = oracle.quantize_q8_0(x)
+    assert (qk == qo).all() and (dk == do).all()
+    yo, awa = oracle.matmul_nvfp4(codes, scales, ws, qo, do)
+    check_y(y, yo, awa, f"fused N={N} K={K}")
+
+
+def test_gemv_fused_edge_and_tie_rows(oracle):
+    """Rows whose Q8_0 decisions are delicate, one fused launch each: all-zero blocks,
+    exact ties, binary16-subnormal and zero d, float32-subnormal blocks (d32 = 0 and
+    d32 = 2^-149), large values, a single non-zero, and 48 rows of quotients on or
+    within a few ulps of rounding ties."""
+    say("gemv fused edge and near-tie rows")
+    N, K = 40, 1024
+    codes, scales, ws = synth.nvfp4_weights(N, K, 4040, "uniform")
+    w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    rows = np.concatenate([_edge_rows(K), _near_tie_rows(48, K, 4041)])
+    for i, x in enumerate(rows):
+        y, qk, dk = _fused_run(w, ws, x[None, :], N)
+        qo, do, _ = oracle.quantize_q8_0(x[None, :])
+        assert (qk == qo).all() and (dk == do).all(), f"row {i}"
+        yo, awa = oracle.matmul_nvfp4(codes, scales, ws, qo, do)
+        if np.abs(yo).max() > 0:
+            check_y(y, yo, awa, f"fused edge row {i}")
+        else:
+            assert (y == 0).all(), f"row {i}"
+
+
 @pytest.mark.parametrize("M", [1, 3])
 @pytest.mark.parametrize("path", [nvq.NVQ_PATH_GEMV, nvq.NVQ_PATH_GEMV_DOT4])
 def test_gemv_isums_bit_exact(oracle, M, path):
@@ -304,6 +362,21 @@ def test_layer_gemv_full_size(oracle, name, N, K, kernel):
     cols = sample_cols(N, 64, N)
     yo, awa = c.oracle_y(oracle, cols=cols)
     check_y(host(y)[:, cols], yo, awa, f"layer {name}")
+
+
+@pytest.mark.parametrize("name,N,K", list(synth.LAYER))
+def test_layer_gemv_fused_full_size(oracle, name, N, K):
+    """The layer set through the fused quantization + GEMV, sampled columns."""
+    say(f"layer gemv fused {name} N={N} K={K}")
+    codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name), "uniform")
+    w = to_dev(nvq.nvq_pack_nvfp4(codes, scales))
+    x = synth.activations(1, K, synth.seed_for("layer", "x_" + name))
+    y, qk, dk = _fused_run(w, ws, x, N)
+    qo, do, _ = oracle.quantize_q8_0(x)
+    assert (qk == qo).all() and (dk == do).all()
+    cols = sample_cols(N, 64, N + 1)
+    yo, awa = oracle.matmul_nvfp4(codes, scales, ws, qo, do, cols=cols)
+    check_y(y[:, cols], yo, awa, f"fused layer {name}")
 
 
 @pytest.mark.parametrize("M", [256, 2048])
@@ -629,6 +702,7 @@ def test_side_stream_and_graph_replay():
     ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
     ys41 = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
     yr = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
+    yf = torch.empty((1, N), dtype=torch.float32, device="cuda")
     need = max(nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms)
     wsp = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
@@ -644,9 +718,11 @@ def test_side_stream_and_graph_replay():
                 nvq.nvq_gemm_nvfp4(w, ws, q, d, ys[M], workspace=wsp)
                 nvq.nvq_gemm_q4_1(w41, q, d, b, ys41[M], workspace=wsp)
         nvq.nvq_gemv_nvfp4_routed(wr, wsc, ids, qd[1][0], qd[1][1], yr)
+        nvq.nvq_gemv_nvfp4_fused(w, ws, xs[1], yf)
 
     def snapshot():
-        return [host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
+        return ([host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
+                + [host(yf).copy()])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -666,7 +742,7 @@ def test_side_stream_and_graph_replay():
         torch.cuda.synchronize()
         for M in xs:
             xs[M].copy_(saved[M])
-        for y in list(ys.values()) + list(ys41.values()) + [yr]:
+        for y in list(ys.values()) + list(ys41.values()) + [yr, yf]:
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
