@@ -875,7 +875,34 @@ def summarize_clock(run_dir):
               f"clock_MHz p50={np.median(mhz):6.0f} min={mhz.min():6.0f} max={mhz.max():6.0f}")
 
 
+def summarize_counters(run_dir):
+    """Per (kernel, grid) average over dispatches of every counter of a rocprofv3 --pmc
+    run (``*counter_collection.csv`` in ``run_dir``), with the average dispatch time."""
+    import collections
+    import csv
+
+    path = next(os.path.join(run_dir, f) for f in os.listdir(run_dir) if f.endswith("counter_collection.csv"))
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    dur = {}
+    for r in csv.DictReader(open(path)):
+        k = (r["Kernel_Name"].split("(")[0][:70], r.get("Grid_Size", ""))
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+        if "Start_Timestamp" in r:
+            dur[(k, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    for k, cs in acc.items():
+        n = len(disp[k])
+        us = [v for (kk, _), v in dur.items() if kk == k]
+        print(f"{k[0]} grid={k[1]} dispatches={n} avg_us={sum(us) / max(1, len(us)):.2f}")
+        for c, v in sorted(cs.items()):
+            print(f"    {c:28s} {v / n:16.1f}")
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(sys.argv[2])
+        return
     if len(sys.argv) == 3 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2])
         return
