@@ -157,9 +157,17 @@ class Layer:
             nvq.nvq_gemv_nvfp4_fused(m["w"][copy], m["ws"], m["x"], m["y"])
 
 
-def kernel_src_hash():
+# the sources each measured kernel is built from (its traffic record is valid while
+# they are unchanged)
+KERNEL_SOURCES = {
+    "gemv_nvfp4_gate_up": ("gemv_nvfp4.hip", "nvq_device.h"),
+    "gemv_nvfp4_fused_gate_up": ("gemv_nvfp4.hip", "nvq_device.h"),
+}
+
+
+def kernel_src_hash(kernel_key):
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "gemm_q8_act_amd", "csrc"))):
+    for f in sorted(KERNEL_SOURCES[kernel_key]):
         with open(os.path.join(ROOT, "gemm_q8_act_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -175,7 +183,7 @@ def load_traffic(kernel_key):
     with open(path) as f:
         t = json.load(f)
     e = t.get(kernel_key)
-    if not e or e.get("src_hash") != kernel_src_hash():
+    if not e or e.get("src_hash") != kernel_src_hash(kernel_key):
         return None
     return e.get("bytes_per_launch")
 
@@ -829,7 +837,8 @@ def summarize_pmc(fetch_csv, write_csv):
             vf, vw = float(np.mean([v for _, _, v in gf])), float(np.mean(gw)) if gw else 0.0
             res[key] = dict(
                 kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
-                bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=alg, src_hash=kernel_src_hash())
+                bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=alg,
+                src_hash=kernel_src_hash(key))
     print(json.dumps(res, indent=1))
 
 

@@ -703,7 +703,15 @@ def test_side_stream_and_graph_replay():
     ys41 = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in xs}
     yr = torch.empty((1, 2, N), dtype=torch.float32, device="cuda")
     yf = torch.empty((1, N), dtype=torch.float32, device="cuda")
-    need = max(nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms)
+    Nk, Kk = 17408, 256
+    ck, sk, wsk = synth.nvfp4_weights(Nk, Kk, 64, "uniform")
+    wk = to_dev(nvq.nvq_pack_nvfp4(ck, sk))
+    xk = to_dev(synth.activations(64, Kk, 65))
+    qk = torch.empty((64, Kk), dtype=torch.int8, device="cuda")
+    dk = torch.empty((64, Kk // 32), dtype=torch.int16, device="cuda")
+    yk = torch.empty((64, Nk), dtype=torch.float32, device="cuda")
+    need = max([nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms]
+               + [nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 64, Nk, Kk)])
     wsp = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
 
@@ -719,10 +727,13 @@ def test_side_stream_and_graph_replay():
                 nvq.nvq_gemm_q4_1(w41, q, d, b, ys41[M], workspace=wsp)
         nvq.nvq_gemv_nvfp4_routed(wr, wsc, ids, qd[1][0], qd[1][1], yr)
         nvq.nvq_gemv_nvfp4_fused(w, ws, xs[1], yf)
+        # 68 tiles of 256 x 64 in 3 K parts (a prefill-like grid on few stages)
+        nvq.nvq_quantize_act_q8_0(xk, qk, dk)
+        nvq.nvq_gemm_nvfp4(wk, ws, qk, dk, yk, workspace=wsp)
 
     def snapshot():
         return ([host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
-                + [host(yf).copy()])
+                + [host(yf).copy(), host(yk).copy()])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -738,11 +749,13 @@ def test_side_stream_and_graph_replay():
     for rep in range(3):
         for M in xs:                      # eager work between replays, then inputs restored
             xs[M].mul_(-1.0)
+        xk.mul_(-1.0)
         seq()
         torch.cuda.synchronize()
         for M in xs:
             xs[M].copy_(saved[M])
-        for y in list(ys.values()) + list(ys41.values()) + [yr, yf]:
+        xk.mul_(-1.0)
+        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk]:
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()

@@ -14,11 +14,14 @@ pytestmark = pytest.mark.gpu
 
 def test_noalloc_gemm_matches_workspace_gemm(oracle):
     torch = torch_dev()
-    # (M, N, K): 2048 x 17408 x 5120 needs 64 MiB of partials (256 work items), 256 x
-    # 17408 x 5120 51 MiB, 300 x 2560 x 1280 12 parts per split tile, 100 x 520 x 1024
-    # 16 parts (256 x 128 tiles), 40 x 70 x 64 a single stage (no split, no scratch)
-    shapes = [(2048, 17408, 5120), (256, 17408, 5120), (300, 2560, 1280), (100, 520, 1024), (40, 70, 64)]
+    # (M, N, K): 256 x 16384 x 4096 and 2048 x 17408 x 5120 need all 64 MiB (64 tiles in
+    # 4 parts, 32 tiles in 8 parts), 256 x 17408 x 5120 51 MiB (68 tiles in 3 parts), 300 x
+    # 2560 x 1280 12 parts per split tile, 100 x 520 x 1024 16 parts (256 x 128 tiles), 40 x
+    # 70 x 64 a single stage (no split, no scratch)
+    shapes = [(256, 16384, 4096), (2048, 17408, 5120), (256, 17408, 5120), (300, 2560, 1280), (100, 520, 1024),
+              (40, 70, 64)]
     assert nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 2048, 17408, 5120) == 64 << 20
+    assert nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 256, 16384, 4096) == 64 << 20
     for M, N, K in shapes:
         say(f"noalloc gemm M={M} N={N} K={K}")
         c = NvCase(M, N, K, synth.seed_for("test", "noalloc", M), w_scale=1.25, outliers=True)
