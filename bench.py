@@ -703,18 +703,24 @@ def stack_layers(M, weights_from=None):
     return layers
 
 
-def time_stack(layers, steps, eager=False):
+def time_stack(layers, steps, eager=False, fused=False):
     """One token step over the 64-layer stack = 256 GEMVs (+ their input
-    quantization) back to back on one stream, one captured graph per step."""
+    quantization) back to back on one stream, one captured graph per step.
+    ``fused`` (M = 1): one launch per matrix, the quantization inside the GEMV;
+    otherwise a quantization launch + a GEMV launch per matrix."""
     import torch
 
     M = layers[0].M
     torch.cuda.synchronize()
     wbytes = sum(l.weight_bytes() for l in layers)
-    alg = sum(gemv_alg_bytes(M, m["N"], m["K"]) for l in layers for m in l.mats)
+    if fused:
+        alg = sum(fused_alg_bytes(m["N"], m["K"]) for l in layers for m in l.mats)
+    else:
+        alg = sum(gemv_alg_bytes(M, m["N"], m["K"]) for l in layers for m in l.mats)
+    step = (lambda l: l.step_fused(0)) if fused else (lambda l: l.step(0))
     for _ in range(2):
         for l in layers:
-            l.step(0)
+            step(l)
     torch.cuda.synchronize()
     graph = None
     if not eager:  # one stack step (256 quantizations + 256 GEMVs) per graph replay
@@ -724,7 +730,7 @@ def time_stack(layers, steps, eager=False):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=s_cap):
                 for l in layers:
-                    l.step(0)
+                    step(l)
         torch.cuda.current_stream().wait_stream(s_cap)
         torch.cuda.synchronize()
     # untimed warm-up steps for about SPIN_UP_S seconds right before the timed region
@@ -736,7 +742,7 @@ def time_stack(layers, steps, eager=False):
             graph.replay()
         else:
             for l in layers:
-                l.step(0)
+                step(l)
         torch.cuda.synchronize()
         warm += 1
     t0 = time.perf_counter()
@@ -745,7 +751,7 @@ def time_stack(layers, steps, eager=False):
             graph.replay()
         else:
             for l in layers:
-                l.step(0)
+                step(l)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     gbps = wbytes * steps / el / 1e9
@@ -754,19 +760,22 @@ def time_stack(layers, steps, eager=False):
                 weight_bytes_per_step=wbytes, alg_bytes_per_step=alg,
                 roofline=dict(bound="hbm", achieved=alg * steps / el / 1e9, peak=HBM_PEAK_GBS, unit="GB/s",
                               frac=alg * steps / el / 1e9 / HBM_PEAK_GBS, traffic=None,
-                              scope="whole stack step: 256 Q8_0 launches + 256 GEMVs; algorithmic bytes = "
-                                    "weights + Q8_0 activations + fp32 outputs"),
+                              scope=("whole stack step: 256 fused quantization + GEMV launches; algorithmic "
+                                     "bytes = weights + fp32 activations + fp32 outputs") if fused else
+                                    ("whole stack step: 256 Q8_0 launches + 256 GEMVs; algorithmic bytes = "
+                                     "weights + Q8_0 activations + fp32 outputs")),
                 graph=not eager)
 
 
 def run_stack(args):
     """--stack: the 64-layer stack alone at M = --tokens, as the one JSON line."""
     M = args.tokens
-    r = time_stack(stack_layers(M), max(2, min(args.steps, 50)), args.eager)
+    r = time_stack(stack_layers(M), max(2, min(args.steps, 50)), args.eager, fused=M == 1)
     line = dict(metric=METRIC, value=r["weight_GBps"], unit="GB/s", n_gpus=1, steps=r["steps"],
                 warmup=r["warmup_steps"], ms_per_step=r["ms_per_step"], higher_is_better=True, scaling="weak",
                 vs_baseline=None, dtype="int8/fp32", data="synthetic",
-                config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408",
+                config=dict(workload=f"64-layer decode stack, M={M}, hidden 5120, ffn 17408"
+                                     + (", fused quantization + GEMV launches" if M == 1 else ""),
                             weight_bytes=r["weight_bytes_per_step"], graph=r["graph"]),
                 roofline=r["roofline"])
     print(json.dumps(line), flush=True)
@@ -992,12 +1001,15 @@ def main():
         log("64-layer stack, M = 1 and 8 ...")
         nst = max(5, min(args.steps, 40))
         st1 = stack_layers(1)
-        s1 = time_stack(st1, nst, args.eager)
+        s1 = time_stack(st1, nst, args.eager, fused=True)
+        s1b = time_stack(st1, nst, args.eager)
         st8 = stack_layers(8, weights_from=st1)
         s8 = time_stack(st8, nst, args.eager)
-        line["stack"] = {"M1": s1, "M8": s8,
+        line["stack"] = {"M1": s1, "M1_two_launch": s1b, "M8": s8,
                          "workload": "64 layers of the layer set (QKV/O/gate_up/down), 11.9 GB of NVFP4 weights "
-                                     "resident, one graph replay per token step; M=8 is batched decode"}
+                                     "resident, one graph replay per token step; M1: one fused quantization + "
+                                     "GEMV launch per matrix; M1_two_launch: a Q8_0 launch + a GEMV launch per "
+                                     "matrix; M8: batched decode (a Q8_0 launch + a batched GEMV per matrix)"}
         del st1, st8
         torch.cuda.empty_cache()
     if not args.no_extras:
