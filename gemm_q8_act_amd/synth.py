@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the NVFP4 / Q4_1 x Q8_0 product.
+"""Seeded synthetic inputs for the NVFP4 / Q4_1 / Q4_K x Q8_0 product.
 
 This module only draws random numbers; it holds none of the product's arithmetic
 (no decode, no quantization, no dot products).  Both the GPU path's tests/benchmark
@@ -17,6 +17,11 @@ workloads this library targets):
 * Q4_1 weights: codes uniform 0..15, per 32 weights d ~ U[1e-3, 2e-2] and
   m ~ U[-0.1, 0], drawn in float32 and stored as binary16 (numpy's
   round-to-nearest-even conversion).
+* Q4_K weights (the pages give the block size only; this recipe mirrors the Q4_1 one
+  at the sub-block level): codes uniform 0..15, per 32 weights a 6-bit scale and a
+  6-bit min uniform 0..63, per 256 weights d ~ U[2e-5, 3e-4] and dmin ~ U[0, 1.6e-3]
+  (so d * sc lies in [0, 0.019] and dmin * mn in [0, 0.1]), drawn in float32 and
+  stored as binary16; N = K = 4096 like the Q4_1 workload.
 * Expert routing (the mixture-of-experts decode step): 256 experts of shape
   N = K = 2048 (the pages give K = 2048, 256 experts, 6 active; N is taken equal to
   K), NVFP4 weights as above with a per-expert scale uniform in [0.5, 2]; each
@@ -35,6 +40,7 @@ WORKLOADS = {
     "layer": dict(M=1, mats=LAYER),
     "prefill": dict(Ms=(256, 2048), N=17408, K=5120),
     "q4_1": dict(Ms=(1, 512), N=4096, K=4096),
+    "q4_k": dict(Ms=(1, 512), N=4096, K=4096),
     "stack": dict(Ms=(1, 8), layers=64, mats=LAYER),
     "moe": dict(M=1, experts=256, active=6, N=2048, K=2048),
 }
@@ -81,6 +87,19 @@ def q4_1_weights(N: int, K: int, seed: int):
     return qw, d.astype(np.float16).view(np.uint16), m.astype(np.float16).view(np.uint16)
 
 
+def q4_k_weights(N: int, K: int, seed: int):
+    """Returns (qw uint8 [N, K] in 0..15, sc uint8 [N, K/32] in 0..63, mn uint8 [N, K/32]
+    in 0..63, d uint16 [N, K/256], dmin uint16 [N, K/256])."""
+    assert K % 256 == 0
+    r = rng(seed)
+    qw = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+    d = r.uniform(2e-5, 3e-4, size=(N, K // 256)).astype(np.float32)
+    dmin = r.uniform(0.0, 1.6e-3, size=(N, K // 256)).astype(np.float32)
+    return qw, sc, mn, d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16)
+
+
 def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
     """int32 [M, A]: for each token A distinct experts, uniform over E."""
     r = rng(seed)
@@ -90,6 +109,6 @@ def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
 def seed_for(workload: str, tensor: str, index: int = 0) -> int:
     """Fixed, documented seed per (workload, tensor, index)."""
     base = {"gemv_small": 100, "layer": 200, "prefill": 300, "q4_1": 400, "stack": 500,
-            "moe": 600, "test": 900}[workload]
+            "moe": 600, "q4_k": 700, "test": 900}[workload]
     tag = sum((i + 1) * ord(ch) for i, ch in enumerate(tensor)) % 997
     return base * 1_000_003 + tag * 1009 + index

@@ -1,4 +1,4 @@
-"""Plain-C oracle for the NVFP4 x Q8_0 and Q4_1 x Q8_0 quantized matrix product.
+"""Plain-C oracle for the NVFP4 x Q8_0, Q4_1 x Q8_0 and Q4_K x Q8_0 quantized matrix product.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module.  The GPU library never calls
@@ -9,6 +9,8 @@ library's packed layout.  It works on the logical representation:
   ``scales`` uint8 [N, K/16] (UE4M3), one float32 per-tensor scale.
 * Q4_1 weights: ``qw`` uint8 [N, K] (0..15), ``dw``/``mw`` uint16 [N, K/32]
   (binary16 bits of d and m).
+* Q4_K weights: ``qw`` uint8 [N, K] (0..15), ``sc``/``mn`` uint8 [N, K/32] (6-bit
+  sub-block scales and mins), ``d``/``dmin`` uint16 [N, K/256] (binary16 bits).
 * Q8_0 activations: ``q`` int8 [M, K], ``d16`` uint16 [M, K/32], ``bsum16``
   int16 [M, K/16].
 
@@ -77,6 +79,8 @@ class Oracle:
                                                  _P, _I64, _P, _P]
         lib.nvqo_matmul_q4_1.restype = None
         lib.nvqo_matmul_q4_1.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+        lib.nvqo_matmul_q4_k.restype = None
+        lib.nvqo_matmul_q4_k.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         self.lib = lib
         self.path = path
 
@@ -175,6 +179,30 @@ class Oracle:
                                   _ptr(c), nc, _ptr(y), _ptr(awa))
         return y, awa
 
+    # -- Q4_K --------------------------------------------------------------------
+    def isums_q4_k(self, qw: np.ndarray, q: np.ndarray) -> np.ndarray:
+        """Per-16 sums of unsigned codes times activation codes: those of Q4_1."""
+        return self.isums_q4_1(qw, q)
+
+    def matmul_q4_k(self, qw, sc, mn, d, dmin, q, d16, cols=None):
+        qw = np.ascontiguousarray(qw, np.uint8)
+        sc = np.ascontiguousarray(sc, np.uint8)
+        mn = np.ascontiguousarray(mn, np.uint8)
+        d = np.ascontiguousarray(d, np.uint16)
+        dmin = np.ascontiguousarray(dmin, np.uint16)
+        q = np.ascontiguousarray(q, np.int8)
+        d16 = np.ascontiguousarray(d16, np.uint16)
+        N, K = qw.shape
+        M = q.shape[0]
+        assert K % 256 == 0 and sc.shape == (N, K // 32) and d.shape == (N, K // 256)
+        c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+        nc = N if c is None else len(c)
+        y = np.empty((M, nc), np.float32)
+        awa = np.empty((M, nc), np.float64)
+        self.lib.nvqo_matmul_q4_k(_ptr(qw), _ptr(sc), _ptr(mn), _ptr(d), _ptr(dmin), _ptr(q), _ptr(d16),
+                                  M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
+        return y, awa
+
     # -- several host threads over disjoint output columns --------------------
     def matmul_threads(self, fmt: str, weights: tuple, q, d16, cols, threads: int):
         """Run matmul_<fmt> over ``cols`` split into ``threads`` disjoint slices, one
@@ -183,7 +211,7 @@ class Oracle:
         cols = np.asarray(cols, np.int64)
         parts = [p for p in np.array_split(cols, max(1, threads)) if len(p)]
         res = [None] * len(parts)
-        fn = self.matmul_nvfp4 if fmt == "nvfp4" else self.matmul_q4_1
+        fn = {"nvfp4": self.matmul_nvfp4, "q4_1": self.matmul_q4_1, "q4_k": self.matmul_q4_k}[fmt]
 
         def run(i):
             res[i] = fn(*weights, q, d16, cols=parts[i])

@@ -315,3 +315,55 @@ void nvqo_matmul_q4_1(const uint8_t* qw, const uint16_t* dw, const uint16_t* mw,
     free(w);
     free(a);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Q4_K x Q8_0                                                                */
+/* ------------------------------------------------------------------------- */
+
+/* Q4_K ([HANDOFF] section 1 names Q4_K among the patch's formats; the llama.cpp
+ * 2-bit GGUF tutorial's GGML type table gives its block: 256 values in 144 bytes).
+ * Reading (the pages give the block size only): a super-block of 256 weights holds a
+ * binary16 scale d and a binary16 min scale dmin, and each of its eight 32-weight
+ * sub-blocks j a 6-bit scale sc_j and a 6-bit min mn_j; with 4-bit codes q,
+ *     weight = d * sc_j * q - dmin * mn_j,
+ * 2 + 2 + 16 * 6 / 8 + 256 / 2 = 144 bytes.  The per-16 integer sums are those of
+ * Q4_1 (unsigned codes times activation codes), nvqo_isums_q4_1. */
+static void dequant_q4_k_row(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                             const uint16_t* d, const uint16_t* dmin, int64_t K, double* w)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        int64_t s = k / 256, j = k / 32;
+        w[k] = nvqo_f16_to_f64(d[s]) * (double)sc[j] * (double)qw[k]
+             - nvqo_f16_to_f64(dmin[s]) * (double)mn[j];
+    }
+}
+
+void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                      const uint16_t* d, const uint16_t* dmin,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa)
+{
+    if (!cols)
+        ncols = N;
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!w || !a) {
+        free(w);
+        free(a);
+        return;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        dequant_q8_0_row(q + m * K, d16 + m * (K / 32), K, a + m * K);
+    for (int64_t jc = 0; jc < ncols; ++jc) {
+        int64_t n = cols ? cols[jc] : jc;
+        dequant_q4_k_row(qw + n * K, sc + n * (K / 32), mn + n * (K / 32), d + n * (K / 256),
+                         dmin + n * (K / 256), K, w);
+        for (int64_t m = 0; m < M; ++m)
+            dot_rows(w, a + m * K, K, &y[m * ncols + jc],
+                     abs_wa ? &abs_wa[m * ncols + jc] : NULL);
+    }
+    free(w);
+    free(a);
+}

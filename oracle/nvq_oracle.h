@@ -1,6 +1,6 @@
 /*
- * nvq_oracle.h -- plain scalar C reference for the NVFP4 x Q8_0 (and Q4_1 x Q8_0)
- * quantized matrix product.
+ * nvq_oracle.h -- plain scalar C reference for the NVFP4 x Q8_0 (and Q4_1 / Q4_K x
+ * Q8_0) quantized matrix product.
  *
  * TEST INFRASTRUCTURE ONLY.  This code exists to check the GPU library, never to
  * serve results.  Only the test suite, the package smoke check and the CPU-baseline
@@ -97,6 +97,18 @@ void nvqo_isums_q4_1(const uint8_t* qw, const int8_t* q,
                      int64_t M, int64_t N, int64_t K, int32_t* isums);
 
 void nvqo_matmul_q4_1(const uint8_t* qw, const uint16_t* dw, const uint16_t* mw,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa);
+
+/* ---- Q4_K weights ---------------------------------------------------------- */
+
+/* qw [N][K] one byte per weight (0..15); sc, mn [N][K/32] 6-bit sub-block scales and
+ * mins (0..63); d, dmin [N][K/256] fp16 bits; W = d*sc*q - dmin*mn.  K % 256 == 0.
+ * Outputs and cols as nvqo_matmul_nvfp4.  Integer sums: nvqo_isums_q4_1. */
+void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                      const uint16_t* d, const uint16_t* dmin,
                       const int8_t* q, const uint16_t* d16,
                       int64_t M, int64_t N, int64_t K,
                       const int64_t* cols, int64_t ncols,

@@ -330,4 +330,38 @@ def battery(o) -> list[tuple[str, bool, str]]:
     ref0 = (f16_bits_to_f64(d16) * bs32) @ f16_bits_to_f64(mw).T
     ok15 &= (np.abs(y0 - ref0) <= np.spacing(np.abs(ref0).astype(np.float32))).all()
     pin("matmul_q4_1_bruteforce_and_zero_scale", ok15)
+
+    # P16: Q4_K -- brute force on its own definition (numpy float64, the block size of
+    # the GGML type table), the reduction to Q4_1 when every per-32 scale d*sc and min
+    # dmin*mn is a binary16 value, and the zero-min case
+    facts = page_facts()["q4_k_block"]
+    SB = facts["values_per_block"]
+    r = _rng(18)
+    M, N, K = 3, 4, 2 * SB
+    qw = r.integers(0, 16, (N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    dd = r.uniform(2e-5, 3e-4, (N, K // SB)).astype(np.float16).view(np.uint16)
+    dm = r.uniform(0.0, 1.6e-3, (N, K // SB)).astype(np.float16).view(np.uint16)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    q, d16, bs = o.quantize_q8_0(x)
+    Wd = (np.repeat(f16_bits_to_f64(dd), SB, axis=1) * np.repeat(sc.astype(np.float64), 32, axis=1) * qw
+          - np.repeat(f16_bits_to_f64(dm), SB, axis=1) * np.repeat(mn.astype(np.float64), 32, axis=1))
+    Ad = np.repeat(f16_bits_to_f64(d16), 32, axis=1) * q.astype(np.float64)
+    yref = Ad @ Wd.T
+    y, awa = o.matmul_q4_k(qw, sc, mn, dd, dm, q, d16)
+    ok16k = (np.abs(y.astype(np.float64) - yref) <= np.spacing(np.abs(yref).astype(np.float32))).all()
+    ok16k &= np.allclose(awa, np.abs(Ad) @ np.abs(Wd).T, rtol=1e-12, atol=0)
+    # powers of two d = 2^-12, dmin = 2^-9: d*sc and dmin*mn are binary16 values
+    dp = np.full((N, K // SB), 2.0 ** -12, np.float16).view(np.uint16)
+    mp = np.full((N, K // SB), 2.0 ** -9, np.float16).view(np.uint16)
+    dw41 = (2.0 ** -12 * sc.astype(np.float64)).astype(np.float16).view(np.uint16)
+    mw41 = (-(2.0 ** -9) * mn.astype(np.float64)).astype(np.float16).view(np.uint16)
+    yk, _ = o.matmul_q4_k(qw, sc, mn, dp, mp, q, d16)
+    y1, _ = o.matmul_q4_1(qw, dw41, mw41, q, d16)
+    ok16k &= bool((yk == y1).all())
+    ymin0, _ = o.matmul_q4_k(qw, sc, np.zeros_like(mn), dd, dm, q, d16)
+    ref0 = Ad @ (Wd + np.repeat(f16_bits_to_f64(dm), SB, axis=1) * np.repeat(mn.astype(np.float64), 32, axis=1)).T
+    ok16k &= bool((np.abs(ymin0.astype(np.float64) - ref0) <= np.spacing(np.abs(ref0).astype(np.float32))).all())
+    pin("matmul_q4_k_bruteforce_q4_1_reduction_zero_min", bool(ok16k))
     return out

@@ -28,6 +28,9 @@ MUTANTS = {
     "routed_expert_codes": ("nvqo_matmul_nvfp4(codes + e * N * K,", "nvqo_matmul_nvfp4(codes + (E - 1 - e) * N * K,"),
     "q4_1_offset_dropped": ("w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k] + nvqo_f16_to_f64(mw[k / 32]);",
                             "w[k] = nvqo_f16_to_f64(dw[k / 32]) * (double)qw[k];"),
+    "q4_k_first_subblock_scale": ("int64_t s = k / 256, j = k / 32;", "int64_t s = k / 256, j = (k / 256) * 8;"),
+    "q4_k_min_sign": ("             - nvqo_f16_to_f64(dmin[s]) * (double)mn[j];", "             + nvqo_f16_to_f64(dmin[s]) * (double)mn[j];"),
+    "q4_k_scales_swapped": ("w[k] = nvqo_f16_to_f64(d[s]) * (double)sc[j] * (double)qw[k]", "w[k] = nvqo_f16_to_f64(dmin[s]) * (double)sc[j] * (double)qw[k]"),
     "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed",
                            "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed"),
 }
