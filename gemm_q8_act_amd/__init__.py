@@ -1,5 +1,5 @@
 """gemm_q8_act_amd -- Python binding of libnvq, the MI355X (gfx950) library for
-NVFP4 x Q8_0 and Q4_1 x Q8_0 quantized matrix products.
+NVFP4 x Q8_0, Q4_1 x Q8_0 and Q4_K x Q8_0 quantized matrix products.
 
 This module only marshals arguments: every step of the computation runs in the
 HIP kernels of ``libnvq.so`` behind the C ABI declared in ``include/nvq.h``.  The
@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_DIR, "libnvq.so")
 NVQ_OK = 0
 NVQ_FMT_NVFP4 = 0
 NVQ_FMT_Q4_1 = 1
+NVQ_FMT_Q4_K = 2
 NVQ_PATH_GEMV = 0
 NVQ_PATH_GEMM = 1
 NVQ_PATH_GEMV_DOT4 = 2
@@ -28,10 +29,11 @@ NVQ_GEMV_MAX_M = 15
 
 # Every symbol include/nvq.h declares.
 EXPORTS = (
-    "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_gemm_workspace_bytes",
-    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4", "nvq_gemv_nvfp4_fused",
-    "nvq_gemv_nvfp4_dot4",
-    "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1", "nvq_debug_isums",
+    "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_q4_k_weight_bytes", "nvq_gemm_workspace_bytes",
+    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_pack_q4_k", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4",
+    "nvq_gemv_nvfp4_fused", "nvq_gemv_nvfp4_dot4",
+    "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1",
+    "nvq_gemv_q4_k", "nvq_gemm_q4_k", "nvq_debug_isums",
     "nvq_status_str", "nvq_last_error",
 )
 
@@ -62,9 +64,11 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "nvq_nvfp4_weight_bytes": (SZ, [I64, I64]),
             "nvq_q4_1_weight_bytes": (SZ, [I64, I64]),
+            "nvq_q4_k_weight_bytes": (SZ, [I64, I64]),
             "nvq_gemm_workspace_bytes": (SZ, [ctypes.c_int, I64, I64, I64]),
             "nvq_pack_nvfp4": (ctypes.c_int, [P, P, I64, I64, P]),
             "nvq_pack_q4_1": (ctypes.c_int, [P, P, P, I64, I64, P]),
+            "nvq_pack_q4_k": (ctypes.c_int, [P, P, P, P, P, I64, I64, P]),
             "nvq_quantize_act_q8_0": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_nvfp4_fused": (ctypes.c_int, [P, F, P, I64, I64, P, P, P, P]),
@@ -74,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "nvq_gemm_nvfp4_noalloc": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+            "nvq_gemv_q4_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
+            "nvq_gemm_q4_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_debug_isums": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P, P, I64, I64, I64, P, P]),
             "nvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "nvq_last_error": (ctypes.c_char_p, []),
@@ -142,6 +148,10 @@ def nvq_nvfp4_weight_bytes(N: int, K: int) -> int:
 
 def nvq_q4_1_weight_bytes(N: int, K: int) -> int:
     return int(lib().nvq_q4_1_weight_bytes(N, K))
+
+
+def nvq_q4_k_weight_bytes(N: int, K: int) -> int:
+    return int(lib().nvq_q4_k_weight_bytes(N, K))
 
 
 def nvq_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
@@ -335,6 +345,56 @@ def nvq_gemm_q4_1(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
                                _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q4_1")
 
 
+def nvq_pack_q4_k(q: np.ndarray, sc: np.ndarray, mn: np.ndarray, d_f16: np.ndarray,
+                  dmin_f16: np.ndarray) -> np.ndarray:
+    """q uint8 [N, K] (0..15), sc / mn uint8 [N, K/32] (0..63), d_f16 / dmin_f16 uint16
+    [N, K/256] -> packed uint8 buffer."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.uint8)
+    mn = np.ascontiguousarray(mn, dtype=np.uint8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.uint16)
+    dmin_f16 = np.ascontiguousarray(dmin_f16, dtype=np.uint16)
+    N, K = q.shape
+    if sc.shape != (N, K // 32) or mn.shape != (N, K // 32):
+        raise ValueError("sc and mn must be [N, K/32]")
+    if d_f16.shape != (N, K // 256) or dmin_f16.shape != (N, K // 256):
+        raise ValueError("d_f16 and dmin_f16 must be [N, K/256]")
+    nbytes = nvq_q4_k_weight_bytes(N, K)
+    out = np.empty(max(nbytes, 1), np.uint8)
+    _check(lib().nvq_pack_q4_k(*(a.ctypes.data_as(ctypes.c_void_p) for a in (q, sc, mn, d_f16, dmin_f16)), N, K,
+                               out.ctypes.data_as(ctypes.c_void_p)), "nvq_pack_q4_k")
+    return out[:nbytes]
+
+
+def nvq_gemv_q4_k(w, q, d_f16, bsum16, y, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _need(bsum16, torch.int16, (M, K // 16), "bsum16")
+    _weights(w, nvq_q4_k_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_q4_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
+                               _stream(stream, y)), "nvq_gemv_q4_k")
+
+
+def nvq_gemm_q4_k(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _need(bsum16, torch.int16, (M, K // 16), "bsum16")
+    _weights(w, nvq_q4_k_weight_bytes(N, K), "w")
+    if workspace is None:
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_Q4_K, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvq_gemm_q4_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
+                               _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q4_k")
+
+
 def nvq_debug_isums(fmt: int, path: int, w, q, N: int, isums, stream=None) -> None:
     """isums int32 [M, N, K/16]: integer per-16 sums from the chosen production path."""
     import torch
@@ -342,7 +402,8 @@ def nvq_debug_isums(fmt: int, path: int, w, q, N: int, isums, stream=None) -> No
     M, K = q.shape
     _need(q, torch.int8, (M, K), "q")
     _need(isums, torch.int32, (M, N, K // 16), "isums")
-    nbytes = nvq_nvfp4_weight_bytes(N, K) if fmt == NVQ_FMT_NVFP4 else nvq_q4_1_weight_bytes(N, K)
+    nbytes = {NVQ_FMT_NVFP4: nvq_nvfp4_weight_bytes, NVQ_FMT_Q4_1: nvq_q4_1_weight_bytes,
+              NVQ_FMT_Q4_K: nvq_q4_k_weight_bytes}.get(fmt, nvq_q4_1_weight_bytes)(N, K)
     _weights(w, nbytes, "w")
     _check(lib().nvq_debug_isums(int(fmt), int(path), _ptr(w), _ptr(q), M, N, K, _ptr(isums),
                                  _stream(stream, q)), "nvq_debug_isums")

@@ -111,11 +111,19 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K) {
   return (size_t)(N * K / 2 + N * K / 8);
 }
 
+size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
+  return (size_t)(N * K / 2 + N * (K / 256) * 16);
+}
+
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
-  // M > 16: fp32 partial tiles of the K-split work items that fill the last round
-  // over the compute units.
-  if ((fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1) || M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
-  return fmt == NVQ_FMT_NVFP4 ? nvq::gemm_nvfp4_workspace(M, N, K) : nvq::gemm_q4_1_workspace(M, N, K);
+  // fp32 partial tiles of the K-split work items that fill the last round over the
+  // compute units (two-term kernels only).
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
+  if (fmt == NVQ_FMT_NVFP4) return nvq::gemm_nvfp4_workspace(M, N, K);
+  if (fmt == NVQ_FMT_Q4_1) return nvq::gemm_q4_1_workspace(M, N, K);
+  if (fmt == NVQ_FMT_Q4_K && K % 256 == 0) return nvq::gemm_q4_k_workspace(M, N, K);
+  return 0;
 }
 
 nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3, int64_t N, int64_t K,
@@ -168,6 +176,36 @@ nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t
   for (int64_t i = 0; i < nb; ++i) {
     const uint32_t pair = (uint32_t)d_f16[i] | ((uint32_t)m_f16[i] << 16);
     std::memcpy(dst + nc + 4 * i, &pair, 4);
+  }
+  g_err[0] = '\0';
+  return NVQ_OK;
+}
+
+nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
+                         const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host) {
+  if (!q || !sc || !mn || !d_f16 || !dmin_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_q4_k: NULL pointer");
+  if (nvq_q4_k_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_q4_k: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  uint8_t* dst = static_cast<uint8_t*>(dst_host);
+  const int64_t nc = N * K / 2;
+  for (int64_t i = 0; i < nc; ++i) {
+    const uint8_t a = q[2 * i], b = q[2 * i + 1];
+    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_q4_k: code > 15 at weight %lld", (long long)(2 * i));
+    dst[i] = (uint8_t)(a | (b << 4));
+  }
+  // one 16-byte header per (row, 256 weights): d, dmin, then sc_0..7, mn_0..7 as 6-bit
+  // fields of a little-endian 96-bit number
+  const int64_t nsb = N * K / 256;
+  for (int64_t i = 0; i < nsb; ++i) {
+    uint8_t h[16] = {};
+    std::memcpy(h, &d_f16[i], 2);
+    std::memcpy(h + 2, &dmin_f16[i], 2);
+    for (int f = 0; f < 16; ++f) {
+      const uint8_t v = f < 8 ? sc[8 * i + f] : mn[8 * i + f - 8];
+      if (v > 63) return fail(NVQ_ERR_RANGE, "nvq_pack_q4_k: %s > 63 at sub-block %lld", f < 8 ? "scale" : "min", (long long)(8 * i + f % 8));
+      for (int bit = 0; bit < 6; ++bit)
+        if ((v >> bit) & 1) h[4 + (6 * f + bit) / 8] |= (uint8_t)(1u << ((6 * f + bit) % 8));
+    }
+    std::memcpy(dst + nc + 16 * i, h, 16);
   }
   g_err[0] = '\0';
   return NVQ_OK;
@@ -320,14 +358,41 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
                                         static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q4_1");
 }
 
+nvq_status nvq_gemv_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_q4_k"));
+  if (!bsum16) return fail(NVQ_ERR_NULL, "nvq_gemv_q4_k: bsum16 is required");
+  if (!aligned(bsum16, 2)) return fail(NVQ_ERR_ALIGN, "nvq_gemv_q4_k: bsum16 must be 2-byte aligned");
+  NVQ_TRY(check_dims(M, N, K, 256, 1, NVQ_GEMV_MAX_M));
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_q4_k(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        (hipStream_t)stream), "gemv_q4_k");
+}
+
+nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_q4_k"));
+  if (!bsum16) return fail(NVQ_ERR_NULL, "nvq_gemm_q4_k: bsum16 is required");
+  if (!aligned(bsum16, 2)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q4_k: bsum16 must be 2-byte aligned");
+  NVQ_TRY(check_dims(M, N, K, 256, 16, kMaxM));
+  const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_Q4_K, M, N, K);
+  if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_q4_k: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q4_k: workspace must be 16-byte aligned");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemm_q4_k(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q4_k");
+}
+
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,
                            int64_t N, int64_t K, int32_t* isums, void* stream) {
-  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1) return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d", fmt);
+  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1 && fmt != NVQ_FMT_Q4_K) return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d", fmt);
   if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM && !(path == NVQ_PATH_GEMV_DOT4 && fmt == NVQ_FMT_NVFP4))
     return fail(NVQ_ERR_RANGE, "nvq_debug_isums: path=%d", path);
   if (!w || !q || !isums) return fail(NVQ_ERR_NULL, "nvq_debug_isums: NULL pointer");
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(isums, 4)) return fail(NVQ_ERR_ALIGN, "nvq_debug_isums: w and q must be 16-byte aligned, isums 4-byte");
-  NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : 32, 1, kMaxM));
+  NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : (fmt == NVQ_FMT_Q4_K ? 256 : 32), 1, kMaxM));
   if (M > kMaxElems / (N * (K / 16))) return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: output too large");
   if (fmt == NVQ_FMT_NVFP4 && path == NVQ_PATH_GEMV && M > 1 && (M < 16 ? M : 16) * K >= (int64_t(1) << 32))
     return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the batched kernel (16 * K < 2^32)", (long long)K);
@@ -342,9 +407,11 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   // batched kernel for M >= 2, 16 tokens per launch).
   if (path == NVQ_PATH_GEMM) {
     if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_nvfp4");
+    if (fmt == NVQ_FMT_Q4_K) return launched(nvq::launch_gemm_q4_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_k");
     return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_1");
   }
   if (fmt == NVQ_FMT_Q4_1) return launched(nvq::launch_gemv_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_1");
+  if (fmt == NVQ_FMT_Q4_K) return launched(nvq::launch_gemv_q4_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_k");
   if (path == NVQ_PATH_GEMV) {
     if (M > 1) return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, st), "debug gemv_nvfp4 (batched)");
     if (!gemv_fits_lds(K)) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemv_nvfp4 (tiled)");

@@ -20,6 +20,18 @@
 //
 // GEMM, M > 16 and K % 64 == 0: both operands as two binary16 terms, so the matrix
 // core accumulates whole rows (see gemm_q4_1_f16x2_kernel below).
+//
+// Q4_K (the same patch's "Q4_K" format; the llama.cpp 2-bit GGUF tutorial's GGML type
+// table gives its block, 256 values in 144 bytes): a 256-weight super-block holds
+// binary16 d and dmin, and each 32-weight sub-block j a 6-bit scale sc_j and a 6-bit
+// min mn_j, weight = d*sc_j*c - dmin*mn_j.  Per 32-block that is a Q4_1 block with
+// scale d*sc_j and offset -dmin*mn_j (each product exact in fp32: 11 x 6 significant
+// bits), so both Q4_1 kernels above run it with a format parameter that only changes
+// where a block's (scale, offset) pair comes from (q4_block_scales).  Device layout:
+// the codes as Q4_1 ([N][K/2], byte i = codes 2i low, 2i+1 high nibble), then one
+// 16-byte header per (row, super-block): binary16 d, binary16 dmin, and the 16 6-bit
+// fields sc_0..sc_7, mn_0..mn_7, field f at bits [6f, 6f + 6) of the 96-bit
+// little-endian number in bytes 4..15.
 #include <algorithm>
 
 #include "ksplit.h"
@@ -41,7 +53,49 @@ __device__ __forceinline__ int dot8_u4(uint32_t c, uint32_t qe, uint32_t qo, int
   return acc;
 }
 
-template <int LPR, int UPL, bool MULTI, bool DEBUG>
+constexpr int kQ41 = 1, kQ4K = 2;  // weight formats of the kernels below (the NVQ_FMT_* values)
+
+// Q4_K: the (scale, offset) of sub-block j of the super-block with header h (see the
+// layout above), as float32 (both products exact)
+__device__ __forceinline__ void q4k_block_scales(const u32x4& h, int j, float& dw, float& mw) {
+  const uint64_t lo = (uint64_t)h[2] << 32 | h[1], hi = (uint64_t)h[3] << 32 | h[2];
+  const uint32_t sc = (uint32_t)(j < 6 ? lo >> (6 * j) : hi >> (6 * j - 32)) & 63u;
+  const uint32_t mn = (uint32_t)(hi >> (16 + 6 * j)) & 63u;  // field 8 + j (bit 48 + 6 j >= 32)
+  dw = f16_bits_to_f32((uint16_t)(h[0] & 0xFFFFu)) * (float)sc;
+  mw = -(f16_bits_to_f32((uint16_t)(h[0] >> 16)) * (float)mn);
+}
+
+// The scale source of a weight format: Q4_1 one 4-byte (d, m) binary16 pair per
+// 32-block after the codes; Q4_K one 16-byte header per 256-block after the codes.
+template <int FMT>
+struct BlockScales {
+  static constexpr int kWords = FMT == kQ4K ? 4 : 1;
+  const uint32_t* base;  // first word of the scale region
+  int64_t per_row;       // words per weight row
+  __device__ BlockScales(const uint8_t* w, int64_t N, int K)
+      : base(reinterpret_cast<const uint32_t*>(w + N * (int64_t)(K >> 1))),
+        per_row(FMT == kQ4K ? (int64_t)(K >> 8) * 4 : (int64_t)(K >> 5)) {}
+  // the raw words that hold 32-block b of a row
+  __device__ __forceinline__ void load(int64_t row, int64_t b, uint32_t* v) const {
+    if constexpr (FMT == kQ4K) {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(base + row * per_row + 4 * (b >> 3));
+      v[0] = h[0]; v[1] = h[1]; v[2] = h[2]; v[3] = h[3];
+    } else {
+      v[0] = base[row * per_row + b];
+    }
+  }
+  // (scale, offset) of 32-block b from its raw words
+  __device__ __forceinline__ static void decode(const uint32_t* v, int64_t b, float& dw, float& mw) {
+    if constexpr (FMT == kQ4K) {
+      q4k_block_scales(u32x4{v[0], v[1], v[2], v[3]}, (int)(b & 7), dw, mw);
+    } else {
+      dw = f16_bits_to_f32((uint16_t)(v[0] & 0xFFFFu));
+      mw = f16_bits_to_f32((uint16_t)(v[0] >> 16));
+    }
+  }
+};
+
+template <int FMT, int LPR, int UPL, bool MULTI, bool DEBUG>
 __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __restrict__ w,
                                                            int64_t N, int K,
                                                            const int8_t* __restrict__ q,
@@ -59,11 +113,12 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
   const int units = K >> 5;
   const int64_t crow = K >> 1;
   const int64_t nb = K >> 5;
-  const uint32_t* __restrict__ dm = reinterpret_cast<const uint32_t*>(w + N * crow);
+  const BlockScales<FMT> bsc(w, N, K);
+  constexpr int PW = BlockScales<FMT>::kWords;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
 
   uint4 cw[RG][UPL];
-  uint32_t pw[RG][UPL];
+  uint32_t pw[RG][UPL][PW];  // raw scale words of each unit's 32-block (not read for the debug sums)
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int64_t row = row0 + r * RPG + slot;
@@ -72,10 +127,12 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
       const int u = sub + LPR * j;
       if (row < N && u < units) {
         cw[r][j] = *reinterpret_cast<const uint4*>(w + row * crow + 16 * (int64_t)u);
-        pw[r][j] = dm[row * nb + u];
+        if (!DEBUG) bsc.load(row, u, pw[r][j]);
+        else for (int e = 0; e < PW; ++e) pw[r][j][e] = 0u;
       } else {
         cw[r][j] = make_uint4(0u, 0u, 0u, 0u);
-        pw[r][j] = 0u;
+#pragma unroll
+        for (int e = 0; e < PW; ++e) pw[r][j][e] = 0u;
       }
     }
   }
@@ -135,8 +192,8 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
               isums[(m * N + row) * (K >> 4) + 2 * u + 1] = i1;
             }
           } else {
-            const float dw = f16_bits_to_f32((uint16_t)(pw[r][j] & 0xFFFFu));
-            const float mw = f16_bits_to_f32((uint16_t)(pw[r][j] >> 16));
+            float dw, mw;
+            BlockScales<FMT>::decode(pw[r][j], sub + LPR * j, dw, mw);
             acc = fmaf(da[tb][j], fmaf(dw, (float)(i0 + i1), mw * bs[tb][j]), acc);
           }
         }
@@ -356,27 +413,27 @@ __global__ __launch_bounds__(256) void gemm_q4_1_kernel(const uint8_t* __restric
 namespace {
 typedef void (*gemv_q41_fn)(const uint8_t*, int64_t, int, const int8_t*, const uint16_t*,
                             const int16_t*, float*, int32_t*, int);
-template <int LPR, bool MULTI, bool DEBUG>
+template <int FMT, int LPR, bool MULTI, bool DEBUG>
 gemv_q41_fn pick_q41(int upl) {
   switch (upl) {
-    case 1: return gemv_q4_1_m1_kernel<LPR, 1, MULTI, DEBUG>;
-    case 2: return gemv_q4_1_m1_kernel<LPR, 2, MULTI, DEBUG>;
-    case 3: return gemv_q4_1_m1_kernel<LPR, 3, MULTI, DEBUG>;
-    case 4: return gemv_q4_1_m1_kernel<LPR, 4, MULTI, DEBUG>;
-    case 5: return gemv_q4_1_m1_kernel<LPR, 5, MULTI, DEBUG>;
-    case 6: return gemv_q4_1_m1_kernel<LPR, 6, MULTI, DEBUG>;
-    case 7: return gemv_q4_1_m1_kernel<LPR, 7, MULTI, DEBUG>;
-    case 8: return gemv_q4_1_m1_kernel<LPR, 8, MULTI, DEBUG>;
-    case 9: return gemv_q4_1_m1_kernel<LPR, 9, MULTI, DEBUG>;
-    case 10: return gemv_q4_1_m1_kernel<LPR, 10, MULTI, DEBUG>;
+    case 1: return gemv_q4_1_m1_kernel<FMT, LPR, 1, MULTI, DEBUG>;
+    case 2: return gemv_q4_1_m1_kernel<FMT, LPR, 2, MULTI, DEBUG>;
+    case 3: return gemv_q4_1_m1_kernel<FMT, LPR, 3, MULTI, DEBUG>;
+    case 4: return gemv_q4_1_m1_kernel<FMT, LPR, 4, MULTI, DEBUG>;
+    case 5: return gemv_q4_1_m1_kernel<FMT, LPR, 5, MULTI, DEBUG>;
+    case 6: return gemv_q4_1_m1_kernel<FMT, LPR, 6, MULTI, DEBUG>;
+    case 7: return gemv_q4_1_m1_kernel<FMT, LPR, 7, MULTI, DEBUG>;
+    case 8: return gemv_q4_1_m1_kernel<FMT, LPR, 8, MULTI, DEBUG>;
+    case 9: return gemv_q4_1_m1_kernel<FMT, LPR, 9, MULTI, DEBUG>;
+    case 10: return gemv_q4_1_m1_kernel<FMT, LPR, 10, MULTI, DEBUG>;
     default: return nullptr;
   }
 }
 // one token (or the debug sums) at a time, or TB tokens per pass
-template <int LPR>
+template <int FMT, int LPR>
 gemv_q41_fn pick_q41_for(int upl, bool multi, bool debug) {
-  if (debug) return pick_q41<LPR, false, true>(upl);
-  return multi ? pick_q41<LPR, true, false>(upl) : pick_q41<LPR, false, false>(upl);
+  if (debug) return pick_q41<FMT, LPR, false, true>(upl);
+  return multi ? pick_q41<FMT, LPR, true, false>(upl) : pick_q41<FMT, LPR, false, false>(upl);
 }
 template <int BM, int BN, bool DEBUG>
 hipError_t launch_q41_tile(const uint8_t* w, const int8_t* q, const uint16_t* d16,
@@ -418,27 +475,38 @@ static void gemv_m1_config(int64_t K, int* lpr_out, int* upl_out) {
   *upl_out = best_upl;
 }
 
-hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
-                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
-                            int32_t* isums, hipStream_t stream) {
+// rows this GEMV kernel takes (at most kQ41MaxUPL 32-blocks per lane at 64 lanes per row)
+static bool q41_gemv_fits(int64_t K) {
+  int lpr = 0, upl = 0;
+  gemv_m1_config(K, &lpr, &upl);
+  return lpr != 0;
+}
+
+template <int FMT>
+static hipError_t launch_gemv_q4x(const uint8_t* w, const int8_t* q, const uint16_t* d16, const int16_t* bsum16,
+                                  int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
   const bool debug = isums != nullptr;
   int lpr = 0, upl = 0;
   gemv_m1_config(K, &lpr, &upl);
-  if (lpr == 0) {
-    // very long rows: the tiled kernel handles any K
-    return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
-  }
   gemv_q41_fn fn = nullptr;
   const bool multi = M > 1;
-  if (lpr == 64) fn = pick_q41_for<64>(upl, multi, debug);
-  if (lpr == 32) fn = pick_q41_for<32>(upl, multi, debug);
-  if (lpr == 16) fn = pick_q41_for<16>(upl, multi, debug);
+  if (lpr == 64) fn = pick_q41_for<FMT, 64>(upl, multi, debug);
+  if (lpr == 32) fn = pick_q41_for<FMT, 32>(upl, multi, debug);
+  if (lpr == 16) fn = pick_q41_for<FMT, 16>(upl, multi, debug);
   if (!fn) return hipErrorInvalidValue;
   const int64_t rows_per_block = 4 * (64 / lpr) * q41_rg(upl);
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, stream, w, N, (int)K, q, d16, bsum16,
                      y, isums, (int)M);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream) {
+  // very long rows: the tiled kernel handles any K
+  if (!q41_gemv_fits(K)) return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  return launch_gemv_q4x<kQ41>(w, q, d16, bsum16, M, N, K, y, isums, stream);
 }
 
 // ---------------------------------------------------------------------------------
@@ -519,7 +587,7 @@ size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K) {
   }
 }
 
-template <class C, bool DEBUG>
+template <class C, int FMT, bool DEBUG>
 __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
                                                                  const int8_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ d16, int64_t M,
@@ -544,8 +612,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   }
   const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
   const int64_t crow = K >> 1;  // code bytes per weight row
-  const int nb32 = K >> 5;
-  const uint32_t* __restrict__ dmw = reinterpret_cast<const uint32_t*>(w + N * crow);
+  const int nb32 = K >> 5;      // activation scales per token row
+  const BlockScales<FMT> bsc(w, N, K);
+  constexpr int PW = BlockScales<FMT>::kWords;
 
   // staging task of this thread: CPT weight codes of row wrow at k-offset CPT wq of
   // the stage, all in one 32-block, with that block's (d, m); ABT activation codes of
@@ -554,25 +623,35 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const int wrow = tid / TPR, wq = tid % TPR;
   const int64_t wr = min(n0 + wrow, N - 1);
   const uint8_t* __restrict__ wbase = w + wr * crow + (CPT / 2) * wq;
-  const uint32_t* __restrict__ dmbase = dmw + wr * nb32 + (CPT * wq) / 32;
+  const int wblk = (CPT * wq) / 32;  // this thread's 32-block within a 64-k stage
   const int arow = tid / APR, aoff = ABT * (tid % APR);
   const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
   const bool dtask = 2 * BM >= kQThreads || tid < 2 * BM;
   const int drow = tid % BM, dblk = (tid / BM) & 1;
   const uint16_t* __restrict__ dbase = DEBUG ? nullptr : d16 + min(m0 + drow, M - 1) * nb32 + dblk;
   bool anybig = false;  // this thread staged an activation scale d >= 512
-  constexpr uint32_t kUnitDM = 0x00003C00u;  // DEBUG weight block: d = 1, m = 0
-  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm, dr; };
+  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm[PW]; uint32_t dr; int blk; };
+  // (scale, offset) of a staged 32-block; DEBUG: d = 1, m = 0 for every weight block
+  auto block_scales = [&](const uint32_t* v, int64_t b, float& dwf, float& mwf) {
+    if constexpr (DEBUG) {
+      dwf = 1.0f;
+      mwf = 0.0f;
+    } else {
+      BlockScales<FMT>::decode(v, b, dwf, mwf);
+    }
+  };
 
   // row scale 2^s: the largest bound |m| + 15|d| of this row's blocks in [t0, t1),
   // taken by the TPR threads that stage the row, placed in [2^14, 2^15).  A zero row
   // takes s = 0; a non-finite d or m gives a non-finite row anyway.
   float bmax = 0.0f;
-  const uint32_t* __restrict__ dmrow = dmw + wr * nb32;
 #pragma unroll 4
   for (int b = 2 * t0 + wq; b < 2 * t1; b += TPR) {
-    const uint32_t v = DEBUG ? kUnitDM : dmrow[b];
-    bmax = fmaxf(bmax, fabsf(f16_bits_to_f32((uint16_t)(v >> 16))) + 15.0f * fabsf(f16_bits_to_f32((uint16_t)(v & 0xFFFFu))));
+    uint32_t v[PW] = {};
+    if (!DEBUG) bsc.load(wr, b, v);
+    float dwf, mwf;
+    block_scales(v, b, dwf, mwf);
+    bmax = fmaxf(bmax, fabsf(mwf) + 15.0f * fabsf(dwf));
   }
   bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
   if constexpr (TPR == 4) bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
@@ -585,7 +664,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 
   auto gload = [&](int t, Stage& x) {
     x.wc = load_words<CPT / 8>(wbase + (int64_t)t * 32);
-    x.dm = DEBUG ? kUnitDM : dmbase[2 * t];
+    x.blk = 2 * t + wblk;
+    if (!DEBUG) bsc.load(wr, x.blk, x.dm);
     x.a = load_words<ABT / 4>(abase + 64 * t);
     if constexpr (DEBUG) x.dr = 0x3C00u;  // d = 1
     else x.dr = dtask ? dbase[2 * t] : 0u;
@@ -598,8 +678,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
     _Float16* ll = reinterpret_cast<_Float16*>(st + C::kStageW);
     uint8_t* la = st + 2 * C::kStageW;
     uint16_t* ld = reinterpret_cast<uint16_t*>(st + 2 * C::kStageW + C::kStageA);
-    const float dw = rscale * f16_bits_to_f32((uint16_t)(x.dm & 0xFFFFu));
-    const float mw = rscale * f16_bits_to_f32((uint16_t)(x.dm >> 16));
+    float dwf, mwf;
+    block_scales(x.dm, x.blk, dwf, mwf);
+    const float dw = rscale * dwf, mw = rscale * mwf;
 #pragma unroll
     for (int h = 0; h < CPT / 8; ++h) {
       const uint32_t cw = x.wc.v[h];
@@ -795,29 +876,44 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 }
 
 namespace {
-// isums != nullptr: the DEBUG instance (per-16 sums, no workspace, no reduction)
-template <class C>
+// isums != nullptr: the DEBUG instance (per-16 sums, no workspace, no reduction).
+// split = false: one work item per tile (no workspace), for the GEMV entry's long rows.
+template <class C, int FMT>
 hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
-                            int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream) {
-  const KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
+                            int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream,
+                            bool split = true) {
+  KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
+  if (!split) {
+    plan.split = 1;
+    plan.split_tiles = 0;
+    plan.full = plan.tiles;
+  }
   const int64_t items = plan.full + plan.split_tiles * plan.split;
   if (isums) {
-    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, true>),
+    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, FMT, true>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (ea != hipSuccess) return ea;
-    hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, true>), dim3((unsigned)items), dim3(kQThreads), C::kLds, stream,
-                       w, N, (int)K, q, d16, M, y, nullptr, isums, plan);
+    hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, FMT, true>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
+                       stream, w, N, (int)K, q, d16, M, y, nullptr, isums, plan);
     return hipGetLastError();
   }
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
-  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, false>),
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4_1_f16x2_kernel<C, FMT, false>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (ea != hipSuccess) return ea;
-  hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, false>), dim3((unsigned)items), dim3(kQThreads), C::kLds, stream,
-                     w, N, (int)K, q, d16, M, y, workspace, nullptr, plan);
+  hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, FMT, false>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
+                     stream, w, N, (int)K, q, d16, M, y, workspace, nullptr, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
   return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
+}
+
+// which kernel runs a Q4_K product of this shape: the GEMV kernel up to 16 tokens
+// (rows up to 20480 weights), else the two-term kernel (K % 256 == 0 always)
+Q41Path q4k_path(int64_t M, int64_t K) {
+  if (M <= kQ41GemvMaxM && q41_gemv_fits(K)) return kQ41Gemv;
+  if (M <= 64) return kQ41Mid;
+  return M <= 128 ? kQ41M128 : kQ41Big;
 }
 }  // namespace
 
@@ -826,11 +922,40 @@ hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
                             int32_t* isums, float* workspace, hipStream_t stream) {
   switch (q41_path(M, K)) {
     case kQ41Gemv: return launch_gemv_q4_1(w, q, d16, bsum16, M, N, K, y, isums, stream);
-    case kQ41Big: return launch_q41_f16x2<Q41Big>(w, q, d16, M, N, K, y, isums, workspace, stream);
-    case kQ41Mid: return launch_q41_f16x2<Q41Mid>(w, q, d16, M, N, K, y, isums, workspace, stream);
-    case kQ41M128: return launch_q41_f16x2<Q41M128>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big, kQ41>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41Mid: return launch_q41_f16x2<Q41Mid, kQ41>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128, kQ41>(w, q, d16, M, N, K, y, isums, workspace, stream);
     default: return launch_q41_tiled(w, q, d16, bsum16, M, N, K, y, isums, stream);
   }
+}
+
+size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K) {
+  switch (q4k_path(M, K)) {
+    case kQ41Mid: return ksplit_workspace<Q41Mid>(M, N, K);
+    case kQ41M128: return ksplit_workspace<Q41M128>(M, N, K);
+    case kQ41Big: return ksplit_workspace<Q41Big>(M, N, K);
+    default: return 0;
+  }
+}
+
+hipError_t launch_gemm_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, float* workspace, hipStream_t stream) {
+  switch (q4k_path(M, K)) {
+    case kQ41Gemv: return launch_gemv_q4x<kQ4K>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big, kQ4K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128, kQ4K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    default: return launch_q41_f16x2<Q41Mid, kQ4K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+  }
+}
+
+// The GEMV entry (M <= 16): the GEMV kernel, or for rows past its reach the two-term
+// kernel with one work item per tile (no workspace)
+hipError_t launch_gemv_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream) {
+  if (q41_gemv_fits(K)) return launch_gemv_q4x<kQ4K>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  return launch_q41_f16x2<Q41Mid, kQ4K>(w, q, d16, M, N, K, y, isums, nullptr, stream, false);
 }
 
 }  // namespace nvq

@@ -1,5 +1,5 @@
 /*
- * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 x Q8_0) quantized matrix
+ * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 / Q4_K x Q8_0) quantized matrix
  * products on AMD Instinct MI355X (gfx950).
  *
  * What is computed.  Weights W [N][K] ("out x in", row-major) are stored 4-bit;
@@ -11,9 +11,10 @@
  *     bias-trick paragraph): NVFP4 weights in 64-weight blocks, one UE4M3 scale
  *     per 16 weights, integer partial sums per 16-subblock, per-16 activation code
  *     sums; batch-1 decode uses a vector dot, larger batches a tiled matmul;
- *     section 1 names the Q4_1 kernels of the same work.
+ *     section 1 names the Q4_1 kernels of the same work and Q4_K among its formats.
  *   The llama.cpp 2-bit GGUF tutorial (spke.com, article 4846), GGML type table:
- *     Q8_0 is 32 values in 34 bytes (32 int8 codes + one fp16 scale).
+ *     Q8_0 is 32 values in 34 bytes (32 int8 codes + one fp16 scale); Q4_K is 256
+ *     values in 144 bytes.
  *
  * Element formats (bit-exact definitions):
  *   E2M1 code c (4 bits): sign = bit 3, exponent e = bits 2..1 (bias 1), mantissa
@@ -25,6 +26,10 @@
  *     S = float32 per-tensor scale (argument w_scale).
  *   Q4_1 weight: W[n][k] = d[n][k/32] * q[n][k] + m[n][k/32], q in 0..15,
  *     d and m IEEE binary16.
+ *   Q4_K weight (the pages give only its block size; this is the reading taken):
+ *     W[n][k] = d[n][k/256] * sc[n][k/32] * q[n][k] - dmin[n][k/256] * mn[n][k/32],
+ *     q in 0..15, sc and mn 6-bit (0..63), d and dmin IEEE binary16; 2 + 2 + 12 + 128
+ *     = 144 bytes per 256 weights.
  *   Q8_0 activation, per row and per 32 consecutive k:
  *     amax = max |x|; d32 = amax / 127 (IEEE float32 division);
  *     d = binary16(d32) rounded to nearest even (stored);
@@ -55,6 +60,14 @@
  *                           k = 2i in bits 0..3 and of k = 2i+1 in bits 4..7.
  *     [N*K/2, +N*K/8)       per 32 weights a 4-byte pair: binary16 d in the low
  *                           half, binary16 m in the high half, row-major [N][K/32].
+ *   Q4_K, row-major, nvq_q4_k_weight_bytes(N, K) = N*K*144/256 bytes:
+ *     [0, N*K/2)            codes, as Q4_1.
+ *     [N*K/2, +N*K/16)      per 256 weights a 16-byte header, row-major [N][K/256]:
+ *                           bytes 0-1 binary16 d, bytes 2-3 binary16 dmin, bytes
+ *                           4-15 the 16 6-bit fields sc_0..sc_7, mn_0..mn_7 of its
+ *                           eight 32-weight sub-blocks, field f at bits
+ *                           [6f, 6f + 6) of those 12 bytes read as one
+ *                           little-endian 96-bit number.
  *
  * Conventions for every entry point:
  *   - All array arguments of the compute entries are DEVICE pointers owned by the
@@ -97,6 +110,7 @@ typedef int nvq_status;
 
 #define NVQ_FMT_NVFP4 0
 #define NVQ_FMT_Q4_1  1
+#define NVQ_FMT_Q4_K  2
 #define NVQ_PATH_GEMV      0  /* decode GEMV, matrix-core inner loop (production) */
 #define NVQ_PATH_GEMM      1  /* tiled GEMM */
 #define NVQ_PATH_GEMV_DOT4 2  /* decode GEMV, v_perm + v_dot4 inner loop (NVFP4 only) */
@@ -118,8 +132,14 @@ size_t nvq_nvfp4_weight_bytes(int64_t N, int64_t K);
  * table (Q4_1: 32 weights per block, 4-bit codes plus a binary16 scale and offset). */
 size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
 
-/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 need for this shape (fmt
- * is NVQ_FMT_*): with M > 16 and K % 64 == 0, the fp32 partial tiles of the K-split
+/* Bytes of a packed Q4_K weight buffer [N][K]: N*K*144/256.  0 if N < 1 or K is not a
+ * positive multiple of 256.  Follows: the llama.cpp 2-bit GGUF tutorial, GGML type
+ * table (Q4_K: 256 values in 144 bytes). */
+size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K);
+
+/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 / nvq_gemm_q4_k need for this
+ * shape (fmt is NVQ_FMT_*): with M > 16 and K % 64 == 0 (Q4_K: K % 256 == 0, and also
+ * M <= 16 with K > 20480), the fp32 partial tiles of the K-split
  * work items that even out the last round of tiles over the chip's 256 compute units
  * (at most 64 MiB: 256 work items x 512 threads x 128 floats); otherwise 0.  Pure
  * function.  When it is 0 the workspace pointer may be NULL.  (A scheduling detail
@@ -144,6 +164,16 @@ nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3,
  * flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_1 weights in the same work). */
 nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t* m_f16,
                          int64_t N, int64_t K, void* dst_host);
+
+/* q: [N][K] bytes (0..15); sc, mn: [N][K/32] bytes (6-bit, 0..63); d_f16, dmin_f16:
+ * [N][K/256] binary16 bit patterns.  Writes nvq_q4_k_weight_bytes(N, K) bytes to
+ * dst_host.  K % 256 == 0.  NVQ_ERR_RANGE if a code exceeds 15 or a scale or min
+ * exceeds 63.  Host memory only, caller-owned.
+ * Follows: the llama.cpp 2-bit GGUF tutorial, GGML type table (Q4_K: 256 values in
+ * 144 bytes) and "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_K
+ * among the formats of the same work). */
+nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
+                         const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host);
 
 /* ---- activation quantization ------------------------------------------------ */
 
@@ -273,13 +303,33 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
                          const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- Q4_K products ------------------------------------------------------------ */
+
+/* Q4_K GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 256 == 0; arguments
+ * as the Q4_1 entries (bsum16 required: the min term multiplies each 32-block's
+ * activation code sum), workspace of nvq_gemm_workspace_bytes(NVQ_FMT_Q4_K, M, N, K)
+ * bytes for the GEMM.  Per 32-block a Q4_K weight is a Q4_1 weight with scale
+ * d * sc and offset -dmin * mn (both exact in float32), and the Q4_1 kernels run it:
+ * the integer-dot GEMV for rows up to 20480 weights, the two-term binary16 kernel
+ * above that and for M > 16.  Same error bound as the NVFP4 entries.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_K among the
+ * patch's formats, beside its Q4_1 vec_dot and tiled kernels); the llama.cpp 2-bit
+ * GGUF tutorial, GGML type table (Q4_K block). */
+nvq_status nvq_gemv_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream);
+nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- debug: integer per-16 partial sums --------------------------------------- */
 
 /* isums [M][N][K/16] int32 (device, overwritten) = for each 16-subblock,
  * sum_j L(code) * q (NVFP4, with L(c) = 2*E2M1(c), an integer in -12..12) or
- * sum_j code * q (Q4_1, unsigned codes).  fmt: NVQ_FMT_*.  path picks the product
- * entry whose kernel computes the sums, run with unit scales (UE4M3 = 1, d = 1; Q4_1
- * d = 1, m = 0) through its own weight loads, code expansion and integer or
+ * sum_j code * q (Q4_1 and Q4_K, unsigned codes).  fmt: NVQ_FMT_*.  path picks the
+ * product entry whose kernel computes the sums, run with unit scales (UE4M3 = 1,
+ * d = 1; Q4_1 / Q4_K block scale 1, offset 0) through its own weight loads, code
+ * expansion and integer or
  * matrix-core contraction -- the kernel that entry dispatches for this M:
  *   NVQ_PATH_GEMV      nvq_gemv_nvfp4 / nvq_gemv_q4_1: NVFP4 M = 1 the matrix-core
  *                      decode kernel (the tiled kernel past its LDS table), M >= 2 the
@@ -288,10 +338,11 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
  *                      tiled kernel, 2 <= M <= 16 the batched kernel, M > 16 the
  *                      two-term kernel of M's tile height with its K-split work items;
  *                      Q4_1 M <= 16 the GEMV kernel, M > 16 the two-term kernel
- *                      (K % 64 == 0) or the tiled kernel;
+ *                      (K % 64 == 0) or the tiled kernel; Q4_K as its entries
+ *                      dispatch (GEMV kernel, or the two-term kernel);
  *   NVQ_PATH_GEMV_DOT4 nvq_gemv_nvfp4_dot4 (NVFP4 only): the v_dot4 decode kernel,
  *                      one launch per token.
- * K % 64 == 0 (NVFP4) or K % 32 == 0 (Q4_1).
+ * K % 64 == 0 (NVFP4), K % 32 == 0 (Q4_1) or K % 256 == 0 (Q4_K).
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
  * (one int32 sum per 16-subblock, lane k of the sum = subblock k/2) and bias-trick
  * paragraph; the integer sums are unique, so they are checked bit for bit. */

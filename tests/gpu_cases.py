@@ -90,6 +90,21 @@ class Q41Case:
         return o.matmul_q4_1(self.qw, self.dw, self.mw, self.qh, self.dh, cols=cols)
 
 
+class Q4KCase:
+    """Seeded Q4_K case; ``weights`` = (qw, sc, mn, d, dmin) and ``x`` replace the seeded ones."""
+
+    def __init__(self, M, N, K, seed, weights=None, x=None):
+        self.M, self.N, self.K = M, N, K
+        self.qw, self.sc, self.mn, self.dd, self.dm = weights if weights is not None else synth.q4_k_weights(N, K, seed)
+        self.x = x if x is not None else synth.activations(M, K, seed + 1)
+        self.w = to_dev(nvq.nvq_pack_q4_k(self.qw, self.sc, self.mn, self.dd, self.dm))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_q4_k(self.qw, self.sc, self.mn, self.dd, self.dm, self.qh, self.dh, cols=cols)
+
+
 def sample_cols(N: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
     """First/last columns, both sides of tile boundaries, plus seeded random ones."""
     base = {0, 1, N - 1, N - 2}

@@ -2,6 +2,7 @@
 header declares, the sizes and packers follow the documented layout, and every
 argument error is reported before any HIP call (so these run on a CPU host)."""
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -132,6 +133,58 @@ def test_pack_q4_1_layout():
     assert ((pairs & 0xFFFF) == d).all() and ((pairs >> 16) == m).all()
 
 
+def test_q4_k_block_size_matches_type_table():
+    # the GGML type table of the llama.cpp 2-bit GGUF tutorial: Q4_K = 256 values in 144 bytes
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))["q4_k_block"]
+    vb, bb = facts["values_per_block"], facts["bytes_per_block"]
+    assert nvq.nvq_q4_k_weight_bytes(1, vb) == bb
+    assert nvq.nvq_q4_k_weight_bytes(4096, 4096) == 4096 * (4096 // vb) * bb
+    assert nvq.nvq_q4_k_weight_bytes(3, 128) == 0          # K % 256 != 0
+    assert nvq.nvq_q4_k_weight_bytes(0, 256) == 0
+
+
+def test_pack_q4_k_layout():
+    # decode the documented layout independently: codes as Q4_1, then per (row, 256
+    # weights) 16 bytes = d, dmin, and 16 6-bit fields (sc_0..7, mn_0..7) of a 96-bit
+    # little-endian number
+    r = np.random.Generator(np.random.PCG64(7))
+    N, K = 3, 512
+    q = r.integers(0, 16, (N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    d = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    dm = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    buf = nvq.nvq_pack_q4_k(q, sc, mn, d, dm)
+    assert buf.size == N * K * 144 // 256
+    cb = buf[: N * K // 2].reshape(N, K // 2)
+    assert (cb & 0xF == q[:, 0::2]).all() and (cb >> 4 == q[:, 1::2]).all()
+    hdr = buf[N * K // 2:].reshape(N, K // 256, 16)
+    assert (hdr[..., 0:2].copy().view(np.uint16)[..., 0] == d).all()
+    assert (hdr[..., 2:4].copy().view(np.uint16)[..., 0] == dm).all()
+    for n in range(N):
+        for b in range(K // 256):
+            big = int.from_bytes(bytes(hdr[n, b, 4:16]), "little")
+            fields = [(big >> (6 * f)) & 63 for f in range(16)]
+            assert fields[:8] == list(sc[n, 8 * b: 8 * b + 8]) and fields[8:] == list(mn[n, 8 * b: 8 * b + 8])
+
+
+@pytest.mark.parametrize("bad", ["code16", "scale64", "min64"])
+def test_pack_q4_k_rejects_invalid(bad):
+    q = np.zeros((1, 256), np.uint8)
+    sc = np.zeros((1, 8), np.uint8)
+    mn = np.zeros((1, 8), np.uint8)
+    d = np.zeros((1, 1), np.uint16)
+    if bad == "code16":
+        q[0, 7] = 16
+    elif bad == "scale64":
+        sc[0, 3] = 64
+    else:
+        mn[0, 6] = 64
+    with pytest.raises(nvq.NvqError) as e:
+        nvq.nvq_pack_q4_k(q, sc, mn, d, d)
+    assert e.value.status == -3
+
+
 @pytest.mark.parametrize("bad", ["code16", "scale_bit7", "scale_nan"])
 def test_pack_nvfp4_rejects_invalid(bad):
     codes = np.zeros((1, 64), np.uint8)
@@ -200,6 +253,15 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_debug_isums(1, 2, A16, A16, 1, 8, 64, A16, None) == -3    # dot4 path is NVFP4 only
     assert L.nvq_gemv_nvfp4_dot4(A16, 1.0, A16, A16, 16, 8, 64, A16, None) == -2
     assert L.nvq_debug_isums(1, 0, A16, A16, 1, 8, 48, A16, None) == -2
+    assert L.nvq_debug_isums(2, 0, A16, A16, 1, 8, 128, A16, None) == -2   # Q4_K: K % 256
+    # Q4_K entries: K % 256, bsum16 required, M ranges, workspace for the two-term kernel
+    assert L.nvq_gemv_q4_k(A16, A16, A16, A2, 1, 8, 128, A16, None) == -2
+    assert L.nvq_gemv_q4_k(A16, A16, A16, None, 1, 8, 256, A16, None) == -1
+    assert L.nvq_gemv_q4_k(A16, A16, A16, A2, 16, 8, 256, A16, None) == -2
+    assert L.nvq_gemm_q4_k(A16, A16, A16, A2, 15, 8, 256, A16, None, 0, None) == -2
+    assert L.nvq_gemm_workspace_bytes(2, 100, 8, 768) > 0
+    assert L.nvq_gemm_workspace_bytes(2, 100, 8, 640) == 0                  # K % 256 != 0
+    assert L.nvq_gemm_q4_k(A16, A16, A16, A2, 100, 8, 768, A16, None, 0, None) == -7
 
 
 def test_routed_gemv_validation_without_gpu():
