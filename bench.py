@@ -1020,14 +1020,14 @@ def main():
     gf = gu["fused_GBps"]
     roofline = dict(bound="hbm", achieved=gf, peak=HBM_PEAK_GBS, unit="GB/s", frac=gf / HBM_PEAK_GBS,
                     traffic=load_traffic("gemv_nvfp4_fused_gate_up"),
-                    kernel="gemv_nvfp4_fused_kernel<4,5,5> (Q8_0 quantization + matrix-core decode GEMV, one "
+                    kernel="gemv_nvfp4_fused_kernel<8,5,3> (Q8_0 quantization + matrix-core decode GEMV, one "
                            "launch), gate+up N=34816 K=5120",
                     scope="the dominant kernel of the step alone (the fused gate+up GEMV, 54 % of the step's "
                           "weight bytes); `value` is the whole layer step (4 fused launches)",
                     us_per_launch=gu["fused_us"], alg_bytes_per_launch=gu["fused_alg_bytes"])
     roofline_gemv = dict(bound="hbm", achieved=gu["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=gu["GBps"] / HBM_PEAK_GBS, traffic=load_traffic("gemv_nvfp4_gate_up"),
-                         kernel="gemv_nvfp4_kernel<0,false,4,5> (matrix-core decode GEMV on Q8_0 input), gate+up",
+                         kernel="gemv_nvfp4_kernel<0,false,8,5> (matrix-core decode GEMV on Q8_0 input), gate+up",
                          us_per_launch=gu["us_avg"], alg_bytes_per_launch=gu["alg_bytes"])
     line = dict(metric=METRIC, value=gbps, unit="GB/s", n_gpus=1, steps=steps, warmup=args.warmup,
                 ms_per_step=1e3 * elapsed / steps, higher_is_better=True, scaling="weak", vs_baseline=None,

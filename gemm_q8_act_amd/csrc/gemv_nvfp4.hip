@@ -423,9 +423,10 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_routed_kernel(const uint8_t
                             nullptr, blockIdx.x);
 }
 
-// Launch shape: 4 wavefronts x 5-chunk batches, or 8 x 3 for long rows over few tiles
+// Launch shape: 4 wavefronts x 5-chunk batches; 8 x 3 for long rows over few tiles
 // (the down projection: K = 17408 over 320 tiles), where more wavefronts per tile keep
-// more loads in flight per block.
+// more loads in flight per block; 8 x 5 from 1024 tiles up (gate+up 34816 x 5120:
+// 16.9 us against 17.2 with 4 x 5; QKV and O, under 1024 tiles, are 5 % slower with it).
 static bool gemv_wide(int64_t ntiles, int64_t nch) { return nch >= 64 && ntiles <= 1024; }
 
 size_t gemv_lds_bytes(int64_t K) {
@@ -460,6 +461,7 @@ hipError_t launch_gemv_nvfp4_m1(const uint8_t* w, float w_scale, const int8_t* q
                      : launch_gemv<1, true, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
   if (mode != 0) return launch_gemv<1, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
   if (gemv_wide(ntiles, nch)) return launch_gemv<0, false, 8, 3>(w, w_scale, q, d16, N, K, y, isums, stream);
+  if (ntiles >= 1024) return launch_gemv<0, false, 8, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
   return launch_gemv<0, false, 4, 5>(w, w_scale, q, d16, N, K, y, isums, stream);
 }
 
@@ -501,18 +503,19 @@ static hipError_t launch_fused_w(const uint8_t* w, float w_scale, const float* x
 // Launch shape of the fused kernel, by measurement on the layer shapes (the per-block
 // quantization of the row is the extra cost, so larger blocks pay off on small grids):
 // short rows (at most 12 chunks) 4 wavefronts x 3-chunk batches (4864 x 896: 2.9 us
-// against 3.1 with 4 x 5); fewer than 1024 tiles with long rows 16 x 2 (down 5120 x
-// 17408: 13.9 us against 15.3 with 8 x 3), else 8 x 3 (QKV 7168 x 5120 / O 5120 x 5120:
-// 6.8 / 6.5 us against 7.2 / 7.1 with 4 x 5); many tiles 4 x 5 (gate+up 34816 x 5120:
-// 18.5 us against 18.5 with 8 x 3 and 19.2 with 8 x 2).
+// against 3.1 with 4 x 5); fewer than 1024 tiles with long rows 16 x 3 (down 5120 x
+// 17408: 13.3 us against 13.9 with 16 x 2 and 15.1 with 8 x 3), else 8 x 3 (QKV
+// 7168 x 5120 / O 5120 x 5120: 6.7 / 6.5 us against 7.1 / 7.0 with 4 x 5); many tiles
+// 8 x 5 (gate+up 34816 x 5120: 18.2 us against 18.4 with 4 x 5 and 8 x 3).  The layer
+// step of the four took 44.1 us against 44.8 with the former 16 x 2 / 4 x 5 choice.
 hipError_t launch_gemv_nvfp4_fused(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
                                    int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   const int64_t nch = (K + 127) / 128;
   if (nch <= 12) return launch_fused_w<4, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
-  if (ntiles < 1024 && nch >= 64) return launch_fused_w<16, 2>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  if (ntiles < 1024 && nch >= 64) return launch_fused_w<16, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
   if (ntiles < 1024) return launch_fused_w<8, 3>(w, w_scale, x, N, K, y, q_out, d_out, stream);
-  return launch_fused_w<4, 5>(w, w_scale, x, N, K, y, q_out, d_out, stream);
+  return launch_fused_w<8, 5>(w, w_scale, x, N, K, y, q_out, d_out, stream);
 }
 
 template <int W, int P>
