@@ -710,8 +710,17 @@ def test_side_stream_and_graph_replay():
     qk = torch.empty((64, Kk), dtype=torch.int8, device="cuda")
     dk = torch.empty((64, Kk // 32), dtype=torch.int16, device="cuda")
     yk = torch.empty((64, Nk), dtype=torch.float32, device="cuda")
+    # Q4_K (K % 256 == 0): GEMV at M = 1 and the two-term GEMM with K-split parts at M = 100
+    K4 = 768
+    w4k = to_dev(nvq.nvq_pack_q4_k(*synth.q4_k_weights(N, K4, 66)))
+    x4k = {M: to_dev(synth.activations(M, K4, 67 + M)) for M in (1, 100)}
+    qd4k = {M: (torch.empty((M, K4), dtype=torch.int8, device="cuda"),
+                torch.empty((M, K4 // 32), dtype=torch.int16, device="cuda"),
+                torch.empty((M, K4 // 16), dtype=torch.int16, device="cuda")) for M in x4k}
+    y4k = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
     need = max([nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms]
-               + [nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 64, Nk, Kk)])
+               + [nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 64, Nk, Kk),
+                  nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_K, 100, N, K4)])
     wsp = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
 
@@ -730,10 +739,14 @@ def test_side_stream_and_graph_replay():
         # 68 tiles of 256 x 64 in 3 K parts (a prefill-like grid on few stages)
         nvq.nvq_quantize_act_q8_0(xk, qk, dk)
         nvq.nvq_gemm_nvfp4(wk, ws, qk, dk, yk, workspace=wsp)
+        for M, x in x4k.items():
+            q, d, b = qd4k[M]
+            nvq.nvq_quantize_act_q8_0(x, q, d, b)
+            (nvq.nvq_gemv_q4_k if M == 1 else nvq.nvq_gemm_q4_k)(w4k, q, d, b, y4k[M], **({} if M == 1 else {"workspace": wsp}))
 
     def snapshot():
         return ([host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
-                + [host(yf).copy(), host(yk).copy()])
+                + [host(yf).copy(), host(yk).copy()] + [host(y4k[M]).copy() for M in x4k])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -750,12 +763,16 @@ def test_side_stream_and_graph_replay():
         for M in xs:                      # eager work between replays, then inputs restored
             xs[M].mul_(-1.0)
         xk.mul_(-1.0)
+        for x in x4k.values():
+            x.mul_(-1.0)
         seq()
         torch.cuda.synchronize()
         for M in xs:
             xs[M].copy_(saved[M])
         xk.mul_(-1.0)
-        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk]:
+        for x in x4k.values():
+            x.mul_(-1.0)
+        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk] + list(y4k.values()):
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
