@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the NVFP4 / Q4_1 / Q4_K x Q8_0 product.
+"""Seeded synthetic inputs for the NVFP4 / Q4_1 / Q4_K / IQ4_XS x Q8_0 product.
 
 This module only draws random numbers; it holds none of the product's arithmetic
 (no decode, no quantization, no dot products).  Both the GPU path's tests/benchmark
@@ -22,6 +22,11 @@ workloads this library targets):
   6-bit min uniform 0..63, per 256 weights d ~ U[2e-5, 3e-4] and dmin ~ U[0, 1.6e-3]
   (so d * sc lies in [0, 0.019] and dmin * mn in [0, 0.1]), drawn in float32 and
   stored as binary16; N = K = 4096 like the Q4_1 workload.
+* IQ4_XS weights (the pages give the block size only): codes uniform 0..15; a value
+  table of 16 distinct int8 values drawn uniformly from -127..127 and sorted (the
+  non-linear table the format indexes; the pages do not print one); per 32 weights a
+  6-bit scale uniform 0..63 (used as ls - 32); per 256 weights d ~ U[5e-5, 2e-4]
+  (weights of magnitude up to ~0.8, most below 0.1); N = K = 4096.
 * Expert routing (the mixture-of-experts decode step): 256 experts of shape
   N = K = 2048 (the pages give K = 2048, 256 experts, 6 active; N is taken equal to
   K), NVFP4 weights as above with a per-expert scale uniform in [0.5, 2]; each
@@ -41,6 +46,7 @@ WORKLOADS = {
     "prefill": dict(Ms=(256, 2048), N=17408, K=5120),
     "q4_1": dict(Ms=(1, 512), N=4096, K=4096),
     "q4_k": dict(Ms=(1, 512), N=4096, K=4096),
+    "iq4_xs": dict(Ms=(1, 512), N=4096, K=4096),
     "stack": dict(Ms=(1, 8), layers=64, mats=LAYER),
     "moe": dict(M=1, experts=256, active=6, N=2048, K=2048),
 }
@@ -100,6 +106,18 @@ def q4_k_weights(N: int, K: int, seed: int):
     return qw, sc, mn, d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16)
 
 
+def iq4_xs_weights(N: int, K: int, seed: int):
+    """Returns (qw uint8 [N, K] in 0..15, ls uint8 [N, K/32] in 0..63, d uint16 [N, K/256],
+    table int8 [16])."""
+    assert K % 256 == 0
+    r = rng(seed)
+    qw = r.integers(0, 16, size=(N, K), dtype=np.uint8)
+    ls = r.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+    d = r.uniform(5e-5, 2e-4, size=(N, K // 256)).astype(np.float32)
+    table = np.sort(r.choice(np.arange(-127, 128), size=16, replace=False)).astype(np.int8)
+    return qw, ls, d.astype(np.float16).view(np.uint16), table
+
+
 def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
     """int32 [M, A]: for each token A distinct experts, uniform over E."""
     r = rng(seed)
@@ -109,6 +127,6 @@ def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
 def seed_for(workload: str, tensor: str, index: int = 0) -> int:
     """Fixed, documented seed per (workload, tensor, index)."""
     base = {"gemv_small": 100, "layer": 200, "prefill": 300, "q4_1": 400, "stack": 500,
-            "moe": 600, "q4_k": 700, "test": 900}[workload]
+            "moe": 600, "q4_k": 700, "iq4_xs": 800, "test": 900}[workload]
     tag = sum((i + 1) * ord(ch) for i, ch in enumerate(tensor)) % 997
     return base * 1_000_003 + tag * 1009 + index

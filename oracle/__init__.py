@@ -1,4 +1,4 @@
-"""Plain-C oracle for the NVFP4 x Q8_0, Q4_1 x Q8_0 and Q4_K x Q8_0 quantized matrix product.
+"""Plain-C oracle for the NVFP4, Q4_1, Q4_K and IQ4_XS x Q8_0 quantized matrix product.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module.  The GPU library never calls
@@ -11,6 +11,9 @@ library's packed layout.  It works on the logical representation:
   (binary16 bits of d and m).
 * Q4_K weights: ``qw`` uint8 [N, K] (0..15), ``sc``/``mn`` uint8 [N, K/32] (6-bit
   sub-block scales and mins), ``d``/``dmin`` uint16 [N, K/256] (binary16 bits).
+* IQ4_XS weights: ``qw`` uint8 [N, K] (0..15, indices into ``table`` int8 [16]),
+  ``ls`` uint8 [N, K/32] (6-bit sub-block scales, used as ls - 32), ``d`` uint16
+  [N, K/256].
 * Q8_0 activations: ``q`` int8 [M, K], ``d16`` uint16 [M, K/32], ``bsum16``
   int16 [M, K/16].
 
@@ -79,6 +82,10 @@ class Oracle:
                                                  _P, _I64, _P, _P]
         lib.nvqo_matmul_q4_1.restype = None
         lib.nvqo_matmul_q4_1.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+        lib.nvqo_isums_iq4_xs.restype = None
+        lib.nvqo_isums_iq4_xs.argtypes = [_P, _P, _P, _I64, _I64, _I64, _P]
+        lib.nvqo_matmul_iq4_xs.restype = None
+        lib.nvqo_matmul_iq4_xs.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         lib.nvqo_matmul_q4_k.restype = None
         lib.nvqo_matmul_q4_k.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         self.lib = lib
@@ -201,6 +208,36 @@ class Oracle:
         awa = np.empty((M, nc), np.float64)
         self.lib.nvqo_matmul_q4_k(_ptr(qw), _ptr(sc), _ptr(mn), _ptr(d), _ptr(dmin), _ptr(q), _ptr(d16),
                                   M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
+        return y, awa
+
+    # -- IQ4_XS ------------------------------------------------------------------
+    def isums_iq4_xs(self, qw: np.ndarray, table: np.ndarray, q: np.ndarray) -> np.ndarray:
+        qw = np.ascontiguousarray(qw, np.uint8)
+        table = np.ascontiguousarray(table, np.int8)
+        q = np.ascontiguousarray(q, np.int8)
+        N, K = qw.shape
+        M = q.shape[0]
+        assert table.shape == (16,)
+        out = np.empty((M, N, K // 16), np.int32)
+        self.lib.nvqo_isums_iq4_xs(_ptr(qw), _ptr(table), _ptr(q), M, N, K, _ptr(out))
+        return out
+
+    def matmul_iq4_xs(self, qw, ls, d, table, q, d16, cols=None):
+        qw = np.ascontiguousarray(qw, np.uint8)
+        ls = np.ascontiguousarray(ls, np.uint8)
+        d = np.ascontiguousarray(d, np.uint16)
+        table = np.ascontiguousarray(table, np.int8)
+        q = np.ascontiguousarray(q, np.int8)
+        d16 = np.ascontiguousarray(d16, np.uint16)
+        N, K = qw.shape
+        M = q.shape[0]
+        assert K % 256 == 0 and ls.shape == (N, K // 32) and d.shape == (N, K // 256) and table.shape == (16,)
+        c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+        nc = N if c is None else len(c)
+        y = np.empty((M, nc), np.float32)
+        awa = np.empty((M, nc), np.float64)
+        self.lib.nvqo_matmul_iq4_xs(_ptr(qw), _ptr(ls), _ptr(d), _ptr(table), _ptr(q), _ptr(d16), M, N, K,
+                                    _ptr(c), nc, _ptr(y), _ptr(awa))
         return y, awa
 
     # -- several host threads over disjoint output columns --------------------

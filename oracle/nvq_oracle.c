@@ -367,3 +367,65 @@ void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
     free(w);
     free(a);
 }
+
+/* ------------------------------------------------------------------------- */
+/* IQ4_XS x Q8_0                                                              */
+/* ------------------------------------------------------------------------- */
+
+/* IQ4_XS ([HANDOFF] section 1 names IQ4_XS among the patch's formats; the GGUF
+ * tutorial's type table gives its block: 256 values in 136 bytes).  Reading: a
+ * 256-weight super-block holds a binary16 scale d, each of its eight 32-weight
+ * sub-blocks a 6-bit scale ls_j taken as ls_j - 32, and 4-bit codes c that index a
+ * 16-entry int8 value table V (non-linear; the pages do not print it, so it is an
+ * input here):  weight = d * (ls_j - 32) * V[c];  2 + 6 + 128 = 136 bytes.  The per-16
+ * integer sums are sum V[c] * q. */
+void nvqo_isums_iq4_xs(const uint8_t* qw, const int8_t* table, const int8_t* q,
+                       int64_t M, int64_t N, int64_t K, int32_t* isums)
+{
+    int64_t ns = K / 16;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t s = 0; s < ns; ++s) {
+                int32_t acc = 0;
+                for (int j = 0; j < 16; ++j) {
+                    int64_t k = 16 * s + j;
+                    acc += (int32_t)table[qw[n * K + k]] * (int32_t)q[m * K + k];
+                }
+                isums[(m * N + n) * ns + s] = acc;
+            }
+}
+
+static void dequant_iq4_xs_row(const uint8_t* qw, const uint8_t* ls, const uint16_t* d,
+                               const int8_t* table, int64_t K, double* w)
+{
+    for (int64_t k = 0; k < K; ++k)
+        w[k] = nvqo_f16_to_f64(d[k / 256]) * (double)((int)ls[k / 32] - 32) * (double)table[qw[k]];
+}
+
+void nvqo_matmul_iq4_xs(const uint8_t* qw, const uint8_t* ls, const uint16_t* d, const int8_t* table,
+                        const int8_t* q, const uint16_t* d16,
+                        int64_t M, int64_t N, int64_t K,
+                        const int64_t* cols, int64_t ncols,
+                        float* y, double* abs_wa)
+{
+    if (!cols)
+        ncols = N;
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!w || !a) {
+        free(w);
+        free(a);
+        return;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        dequant_q8_0_row(q + m * K, d16 + m * (K / 32), K, a + m * K);
+    for (int64_t jc = 0; jc < ncols; ++jc) {
+        int64_t n = cols ? cols[jc] : jc;
+        dequant_iq4_xs_row(qw + n * K, ls + n * (K / 32), d + n * (K / 256), table, K, w);
+        for (int64_t m = 0; m < M; ++m)
+            dot_rows(w, a + m * K, K, &y[m * ncols + jc],
+                     abs_wa ? &abs_wa[m * ncols + jc] : NULL);
+    }
+    free(w);
+    free(a);
+}

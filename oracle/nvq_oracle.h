@@ -1,6 +1,6 @@
 /*
- * nvq_oracle.h -- plain scalar C reference for the NVFP4 x Q8_0 (and Q4_1 / Q4_K x
- * Q8_0) quantized matrix product.
+ * nvq_oracle.h -- plain scalar C reference for the NVFP4 x Q8_0 (and Q4_1 / Q4_K /
+ * IQ4_XS x Q8_0) quantized matrix product.
  *
  * TEST INFRASTRUCTURE ONLY.  This code exists to check the GPU library, never to
  * serve results.  Only the test suite, the package smoke check and the CPU-baseline
@@ -113,6 +113,21 @@ void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
                       int64_t M, int64_t N, int64_t K,
                       const int64_t* cols, int64_t ncols,
                       float* y, double* abs_wa);
+
+/* ---- IQ4_XS weights --------------------------------------------------------- */
+
+/* qw [N][K] one byte per weight (0..15, an index into table); table [16] int8 values;
+ * ls [N][K/32] 6-bit sub-block scales (0..63, used as ls - 32); d [N][K/256] fp16 bits;
+ * W = d * (ls - 32) * table[qw].  K % 256 == 0.  isums [M][N][K/16] = sum over 16 of
+ * table[qw] * q.  Outputs and cols as nvqo_matmul_nvfp4. */
+void nvqo_isums_iq4_xs(const uint8_t* qw, const int8_t* table, const int8_t* q,
+                       int64_t M, int64_t N, int64_t K, int32_t* isums);
+
+void nvqo_matmul_iq4_xs(const uint8_t* qw, const uint8_t* ls, const uint16_t* d, const int8_t* table,
+                        const int8_t* q, const uint16_t* d16,
+                        int64_t M, int64_t N, int64_t K,
+                        const int64_t* cols, int64_t ncols,
+                        float* y, double* abs_wa);
 
 #ifdef __cplusplus
 }

@@ -364,4 +364,39 @@ def battery(o) -> list[tuple[str, bool, str]]:
     ref0 = Ad @ (Wd + np.repeat(f16_bits_to_f64(dm), SB, axis=1) * np.repeat(mn.astype(np.float64), 32, axis=1)).T
     ok16k &= bool((np.abs(ymin0.astype(np.float64) - ref0) <= np.spacing(np.abs(ref0).astype(np.float32))).all())
     pin("matmul_q4_k_bruteforce_q4_1_reduction_zero_min", bool(ok16k))
+
+    # P17: IQ4_XS -- per-16 sums and y by brute force on its definition (a seeded int8
+    # value table), the reduction to Q4_1 when the table is the affine c - 8 and every
+    # per-32 scale is a binary16 value, and invariance under relabelling the table
+    facts = page_facts()["iq4_xs_block"]
+    SB = facts["values_per_block"]
+    r = _rng(19)
+    M, N, K = 3, 4, 2 * SB
+    qw = r.integers(0, 16, (N, K), dtype=np.uint8)
+    ls = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    dd = r.uniform(1e-4, 1e-3, (N, K // SB)).astype(np.float16).view(np.uint16)
+    table = np.sort(r.choice(np.arange(-128, 128), 16, replace=False)).astype(np.int8)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    q, d16, bs = o.quantize_q8_0(x)
+    Vq = table.astype(np.int64)[qw]
+    isum_ref = (q.astype(np.int64)[:, None, :] * Vq[None]).reshape(M, N, K // 16, 16).sum(axis=3)
+    ok17 = bool((o.isums_iq4_xs(qw, table, q) == isum_ref).all())
+    Wd = (np.repeat(f16_bits_to_f64(dd), SB, axis=1) * np.repeat(ls.astype(np.float64) - 32.0, 32, axis=1)
+          * Vq.astype(np.float64))
+    Ad = np.repeat(f16_bits_to_f64(d16), 32, axis=1) * q.astype(np.float64)
+    yref = Ad @ Wd.T
+    y, awa = o.matmul_iq4_xs(qw, ls, dd, table, q, d16)
+    ok17 &= bool((np.abs(y.astype(np.float64) - yref) <= np.spacing(np.abs(yref).astype(np.float32))).all())
+    ok17 &= bool(np.allclose(awa, np.abs(Ad) @ np.abs(Wd).T, rtol=1e-12, atol=0))
+    aff = (np.arange(16) - 8).astype(np.int8)
+    dp = np.full((N, K // SB), 2.0 ** -10, np.float16).view(np.uint16)
+    D = 2.0 ** -10 * (ls.astype(np.float64) - 32.0)
+    yx, _ = o.matmul_iq4_xs(qw, ls, dp, aff, q, d16)
+    y1, _ = o.matmul_q4_1(qw, D.astype(np.float16).view(np.uint16), (-8.0 * D).astype(np.float16).view(np.uint16),
+                          q, d16)
+    ok17 &= bool((yx == y1).all())
+    perm = r.permutation(16)                                   # new table slot i holds old entry perm[i]
+    yp, _ = o.matmul_iq4_xs(np.argsort(perm).astype(np.uint8)[qw], ls, dd, table[perm], q, d16)
+    ok17 &= bool((yp == y).all())
+    pin("iq4_xs_bruteforce_q4_1_reduction_relabel", ok17)
     return out

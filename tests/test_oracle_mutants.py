@@ -31,6 +31,10 @@ MUTANTS = {
     "q4_k_first_subblock_scale": ("int64_t s = k / 256, j = k / 32;", "int64_t s = k / 256, j = (k / 256) * 8;"),
     "q4_k_min_sign": ("             - nvqo_f16_to_f64(dmin[s]) * (double)mn[j];", "             + nvqo_f16_to_f64(dmin[s]) * (double)mn[j];"),
     "q4_k_scales_swapped": ("w[k] = nvqo_f16_to_f64(d[s]) * (double)sc[j] * (double)qw[k]", "w[k] = nvqo_f16_to_f64(dmin[s]) * (double)sc[j] * (double)qw[k]"),
+    "iq4_xs_table_index": ("acc += (int32_t)table[qw[n * K + k]] * (int32_t)q[m * K + k];",
+                           "acc += (int32_t)table[qw[n * K + k] ^ 1] * (int32_t)q[m * K + k];"),
+    "iq4_xs_scale_offset": ("(double)((int)ls[k / 32] - 32)", "(double)((int)ls[k / 32] - 31)"),
+    "iq4_xs_code_not_looked_up": ("* (double)table[qw[k]];", "* (double)qw[k];"),
     "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed",
                            "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed"),
 }
