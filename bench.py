@@ -14,9 +14,9 @@ Infinity Cache.  Inputs are resident in HBM before the timed region.
 Also measured in the same run (reported as sub-objects of the JSON line): the
 64-layer stack of the same layer shapes at M = 1 and M = 8 (11.9 GB of weights per
 step); the prefill GEMM TFLOP/s at M = 2048 (and 256), N = 17408, K = 5120; the
-small GEMV (N = 4864, K = 896), the Q4_1 and Q4_K GEMVs (HBM-cold, rotating over
->= 1 GB of weight copies) and GEMMs (N = K = 4096); the oracle's CPU throughput on the
-same layer.
+small GEMV (N = 4864, K = 896), the Q4_1, Q4_K and IQ4_XS GEMVs (HBM-cold, rotating
+over >= 1 GB of weight copies) and GEMMs (N = K = 4096); the oracle's CPU throughput on
+the same layer.
 ``--stack`` measures only the stack (M = ``--tokens``).
 
 Roofline: per-kernel durations come from HIP events recorded on the stream the
@@ -74,7 +74,7 @@ def parse():
     p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
     p.add_argument("--only-moe", action="store_true", help="time only the expert-routed decode step (profiling)")
-    p.add_argument("--only-q4-1", action="store_true", help="time only the Q4_1 and Q4_K GEMV and GEMM (profiling)")
+    p.add_argument("--only-q4-1", action="store_true", help="time only the Q4_1, Q4_K and IQ4_XS GEMVs and GEMMs (profiling)")
     p.add_argument("--traffic-probe", action="store_true",
                    help="for rocprofv3 --pmc runs: one 256 MiB device copy (calibration) and 4 gate+up "
                         "GEMV launches over distinct weight copies, then exit")
@@ -493,7 +493,8 @@ def time_extras():
                                              "launch from float32 input, quant_plus_gemv_us the two launches")
     out.update(time_act_quant())
     out.update(time_q4_1())
-    out.update(time_q4_k())
+    out.update(time_q4x("q4_k"))
+    out.update(time_q4x("iq4_xs"))
     out["moe_routed_gemv"] = time_moe()
     return out
 
@@ -563,9 +564,9 @@ def time_q4_1():
     return out
 
 
-def time_q4_k():
-    """Q4_K N = K = 4096 (the Q4_1 workload's shape): the GEMV at M = 1 (HBM-cold) and
-    the GEMM at M = 512."""
+def time_q4x(fmt):
+    """Q4_K or IQ4_XS (``fmt``) at N = K = 4096 (the Q4_1 workload's shape): the GEMV at
+    M = 1 (HBM-cold) and the GEMM at M = 512."""
     import torch
 
     import gemm_q8_act_amd as nvq
@@ -573,36 +574,47 @@ def time_q4_k():
 
     out = {}
     N = K = 4096
-    w = dev_tensor(nvq.nvq_pack_q4_k(*synth.q4_k_weights(N, K, synth.seed_for("q4_k", "w"))))
-    wbytes = nvq.nvq_q4_k_weight_bytes(N, K)
+    if fmt == "q4_k":
+        w = dev_tensor(nvq.nvq_pack_q4_k(*synth.q4_k_weights(N, K, synth.seed_for("q4_k", "w"))))
+        wbytes, abytes = nvq.nvq_q4_k_weight_bytes(N, K), K * 17 // 16 + K // 8
+        gemv = lambda wi, q, d, b, y: nvq.nvq_gemv_q4_k(wi, q, d, b, y)
+        gemm = lambda q, d, b, y, ws: nvq.nvq_gemm_q4_k(w, q, d, b, y, workspace=ws)
+        ffmt, kname, blk = nvq.NVQ_FMT_Q4_K, "gemv_q4_1_m1_kernel<Q4_K> (v_dot4 on unsigned codes)", "144"
+    else:
+        qw, ls, dd, table = synth.iq4_xs_weights(N, K, synth.seed_for("iq4_xs", "w"))
+        w = dev_tensor(nvq.nvq_pack_iq4_xs(qw, ls, dd))
+        wbytes, abytes = nvq.nvq_iq4_xs_weight_bytes(N, K), K * 17 // 16
+        gemv = lambda wi, q, d, b, y: nvq.nvq_gemv_iq4_xs(wi, table, q, d, y)
+        gemm = lambda q, d, b, y, ws: nvq.nvq_gemm_iq4_xs(w, table, q, d, y, workspace=ws)
+        ffmt, kname, blk = nvq.NVQ_FMT_IQ4_XS, "gemv_q4_1_m1_kernel<IQ4_XS> (table lookups + v_dot4)", "136"
     for M in (1, 512):
-        x = dev_tensor(synth.activations(M, K, synth.seed_for("q4_k", "x") + M))
+        x = dev_tensor(synth.activations(M, K, synth.seed_for(fmt, "x") + M))
         q = torch.empty((M, K), dtype=torch.int8, device="cuda")
         d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
         b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         nvq.nvq_quantize_act_q8_0(x, q, d, b)
         if M == 1:
-            byts = wbytes + K * 17 // 16 + K // 8 + 4 * N
-            us_hot = _event_time(lambda: nvq.nvq_gemv_q4_k(w, q, d, b, y), 200)
+            byts = wbytes + abytes + 4 * N
+            us_hot = _event_time(lambda: gemv(w, q, d, b, y), 200)
             copies = [w] + [w.clone() for _ in range(-(-(1 << 30) // wbytes) - 1)]
-            us = rotated_time(lambda wi: nvq.nvq_gemv_q4_k(wi, q, d, b, y), copies)
+            us = rotated_time(lambda wi: gemv(wi, q, d, b, y), copies)
             gbps = byts / (us * 1e-6) / 1e9
-            out["q4_k_gemv_N4096_K4096"] = dict(
+            out[f"{fmt}_gemv_N4096_K4096"] = dict(
                 us_avg=us, GBps=gbps, alg_bytes=byts, copies=len(copies),
                 roofline=dict(bound="hbm", achieved=gbps, peak=HBM_PEAK_GBS, unit="GB/s", frac=gbps / HBM_PEAK_GBS,
-                              traffic=None, kernel="gemv_q4_1_m1_kernel<Q4_K> (v_dot4 on unsigned codes)"),
+                              traffic=None, kernel=kname),
                 us_cache_resident=us_hot,
-                note=f"HBM-cold over {len(copies)} distinct weight copies (>= 1 GB); 144 bytes per 256 weights")
+                note=f"HBM-cold over {len(copies)} distinct weight copies (>= 1 GB); {blk} bytes per 256 weights")
             del copies
         else:
-            need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_K, M, N, K)
+            need = nvq.nvq_gemm_workspace_bytes(ffmt, M, N, K)
             wsq = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-            us = _event_time(lambda: nvq.nvq_gemm_q4_k(w, q, d, b, y, workspace=wsq), 20)
+            us = _event_time(lambda: gemm(q, d, b, y, wsq), 20)
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            out["q4_k_gemm_M512_N4096_K4096"] = dict(
+            out[f"{fmt}_gemm_M512_N4096_K4096"] = dict(
                 us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
-                note="the Q4_1 two-term kernel with Q4_K block scales (three fp16 MFMA passes per product)")
+                note="the Q4_1 two-term kernel with this format's block scales (three fp16 MFMA passes per product)")
     return out
 
 
@@ -1006,7 +1018,8 @@ def main():
         return
     if args.only_q4_1:
         log(json.dumps(time_q4_1()))
-        log(json.dumps(time_q4_k()))
+        log(json.dumps(time_q4x("q4_k")))
+        log(json.dumps(time_q4x("iq4_xs")))
         return
 
     log("decode layer ...")

@@ -1,5 +1,5 @@
 """gemm_q8_act_amd -- Python binding of libnvq, the MI355X (gfx950) library for
-NVFP4 x Q8_0, Q4_1 x Q8_0 and Q4_K x Q8_0 quantized matrix products.
+NVFP4, Q4_1, Q4_K and IQ4_XS x Q8_0 quantized matrix products.
 
 This module only marshals arguments: every step of the computation runs in the
 HIP kernels of ``libnvq.so`` behind the C ABI declared in ``include/nvq.h``.  The
@@ -22,6 +22,7 @@ NVQ_OK = 0
 NVQ_FMT_NVFP4 = 0
 NVQ_FMT_Q4_1 = 1
 NVQ_FMT_Q4_K = 2
+NVQ_FMT_IQ4_XS = 3
 NVQ_PATH_GEMV = 0
 NVQ_PATH_GEMM = 1
 NVQ_PATH_GEMV_DOT4 = 2
@@ -29,11 +30,13 @@ NVQ_GEMV_MAX_M = 15
 
 # Every symbol include/nvq.h declares.
 EXPORTS = (
-    "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_q4_k_weight_bytes", "nvq_gemm_workspace_bytes",
-    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_pack_q4_k", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4",
+    "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_q4_k_weight_bytes", "nvq_iq4_xs_weight_bytes",
+    "nvq_gemm_workspace_bytes",
+    "nvq_pack_nvfp4", "nvq_pack_q4_1", "nvq_pack_q4_k", "nvq_pack_iq4_xs", "nvq_quantize_act_q8_0", "nvq_gemv_nvfp4",
     "nvq_gemv_nvfp4_fused", "nvq_gemv_nvfp4_dot4",
     "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1",
-    "nvq_gemv_q4_k", "nvq_gemm_q4_k", "nvq_debug_isums",
+    "nvq_gemv_q4_k", "nvq_gemm_q4_k", "nvq_gemv_iq4_xs", "nvq_gemm_iq4_xs", "nvq_debug_isums",
+    "nvq_debug_isums_iq4_xs",
     "nvq_status_str", "nvq_last_error",
 )
 
@@ -65,10 +68,12 @@ def lib() -> ctypes.CDLL:
             "nvq_nvfp4_weight_bytes": (SZ, [I64, I64]),
             "nvq_q4_1_weight_bytes": (SZ, [I64, I64]),
             "nvq_q4_k_weight_bytes": (SZ, [I64, I64]),
+            "nvq_iq4_xs_weight_bytes": (SZ, [I64, I64]),
             "nvq_gemm_workspace_bytes": (SZ, [ctypes.c_int, I64, I64, I64]),
             "nvq_pack_nvfp4": (ctypes.c_int, [P, P, I64, I64, P]),
             "nvq_pack_q4_1": (ctypes.c_int, [P, P, P, I64, I64, P]),
             "nvq_pack_q4_k": (ctypes.c_int, [P, P, P, P, P, I64, I64, P]),
+            "nvq_pack_iq4_xs": (ctypes.c_int, [P, P, P, I64, I64, P]),
             "nvq_quantize_act_q8_0": (ctypes.c_int, [P, I64, I64, P, P, P, P]),
             "nvq_gemv_nvfp4": (ctypes.c_int, [P, F, P, P, I64, I64, I64, P, P]),
             "nvq_gemv_nvfp4_fused": (ctypes.c_int, [P, F, P, I64, I64, P, P, P, P]),
@@ -80,6 +85,9 @@ def lib() -> ctypes.CDLL:
             "nvq_gemm_q4_1": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_gemv_q4_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
             "nvq_gemm_q4_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+            "nvq_gemv_iq4_xs": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
+            "nvq_gemm_iq4_xs": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+            "nvq_debug_isums_iq4_xs": (ctypes.c_int, [P, ctypes.c_int, P, P, I64, I64, I64, P, P]),
             "nvq_debug_isums": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P, P, I64, I64, I64, P, P]),
             "nvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "nvq_last_error": (ctypes.c_char_p, []),
@@ -152,6 +160,10 @@ def nvq_q4_1_weight_bytes(N: int, K: int) -> int:
 
 def nvq_q4_k_weight_bytes(N: int, K: int) -> int:
     return int(lib().nvq_q4_k_weight_bytes(N, K))
+
+
+def nvq_iq4_xs_weight_bytes(N: int, K: int) -> int:
+    return int(lib().nvq_iq4_xs_weight_bytes(N, K))
 
 
 def nvq_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
@@ -393,6 +405,71 @@ def nvq_gemm_q4_k(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvq_gemm_q4_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
                                _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q4_k")
+
+
+def nvq_pack_iq4_xs(q: np.ndarray, ls: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
+    """q uint8 [N, K] (0..15), ls uint8 [N, K/32] (0..63), d_f16 uint16 [N, K/256] ->
+    packed uint8 buffer (the value table is passed to the products)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    ls = np.ascontiguousarray(ls, dtype=np.uint8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.uint16)
+    N, K = q.shape
+    if ls.shape != (N, K // 32) or d_f16.shape != (N, K // 256):
+        raise ValueError("ls must be [N, K/32] and d_f16 [N, K/256]")
+    nbytes = nvq_iq4_xs_weight_bytes(N, K)
+    out = np.empty(max(nbytes, 1), np.uint8)
+    _check(lib().nvq_pack_iq4_xs(*(a.ctypes.data_as(ctypes.c_void_p) for a in (q, ls, d_f16)), N, K,
+                                 out.ctypes.data_as(ctypes.c_void_p)), "nvq_pack_iq4_xs")
+    return out[:nbytes]
+
+
+def _table(table) -> np.ndarray:
+    t = np.ascontiguousarray(table, dtype=np.int8)
+    if t.shape != (16,):
+        raise ValueError("table must hold 16 int8 values")
+    return t
+
+
+def nvq_gemv_iq4_xs(w, table, q, d_f16, y, stream=None) -> None:
+    import torch
+
+    t = _table(table)
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_iq4_xs_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_iq4_xs(_ptr(w), t.ctypes.data_as(ctypes.c_void_p), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
+                                 _stream(stream, y)), "nvq_gemv_iq4_xs")
+
+
+def nvq_gemm_iq4_xs(w, table, q, d_f16, y, workspace=None, stream=None) -> None:
+    import torch
+
+    t = _table(table)
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_iq4_xs_weight_bytes(N, K), "w")
+    if workspace is None:
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_IQ4_XS, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvq_gemm_iq4_xs(_ptr(w), t.ctypes.data_as(ctypes.c_void_p), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y),
+                                 _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_iq4_xs")
+
+
+def nvq_debug_isums_iq4_xs(table, path: int, w, q, N: int, isums, stream=None) -> None:
+    """isums int32 [M, N, K/16]: sum of table[code] * q per 16, from the dispatched kernel."""
+    import torch
+
+    t = _table(table)
+    M, K = q.shape
+    _need(q, torch.int8, (M, K), "q")
+    _need(isums, torch.int32, (M, N, K // 16), "isums")
+    _weights(w, nvq_iq4_xs_weight_bytes(N, K), "w")
+    _check(lib().nvq_debug_isums_iq4_xs(t.ctypes.data_as(ctypes.c_void_p), int(path), _ptr(w), _ptr(q), M, N, K,
+                                        _ptr(isums), _stream(stream, q)), "nvq_debug_isums_iq4_xs")
 
 
 def nvq_debug_isums(fmt: int, path: int, w, q, N: int, isums, stream=None) -> None:

@@ -116,13 +116,18 @@ size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K) {
   return (size_t)(N * K / 2 + N * (K / 256) * 16);
 }
 
+size_t nvq_iq4_xs_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
+  return (size_t)(N * K / 2 + N * (K / 256) * 8);
+}
+
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
   // fp32 partial tiles of the K-split work items that fill the last round over the
   // compute units (two-term kernels only).
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
   if (fmt == NVQ_FMT_NVFP4) return nvq::gemm_nvfp4_workspace(M, N, K);
   if (fmt == NVQ_FMT_Q4_1) return nvq::gemm_q4_1_workspace(M, N, K);
-  if (fmt == NVQ_FMT_Q4_K && K % 256 == 0) return nvq::gemm_q4_k_workspace(M, N, K);
+  if ((fmt == NVQ_FMT_Q4_K || fmt == NVQ_FMT_IQ4_XS) && K % 256 == 0) return nvq::gemm_q4_k_workspace(M, N, K);
   return 0;
 }
 
@@ -206,6 +211,36 @@ nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn,
         if ((v >> bit) & 1) h[4 + (6 * f + bit) / 8] |= (uint8_t)(1u << ((6 * f + bit) % 8));
     }
     std::memcpy(dst + nc + 16 * i, h, 16);
+  }
+  g_err[0] = '\0';
+  return NVQ_OK;
+}
+
+nvq_status nvq_pack_iq4_xs(const uint8_t* q, const uint8_t* ls, const uint16_t* d_f16, int64_t N, int64_t K,
+                           void* dst_host) {
+  if (!q || !ls || !d_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_iq4_xs: NULL pointer");
+  if (nvq_iq4_xs_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_iq4_xs: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  uint8_t* dst = static_cast<uint8_t*>(dst_host);
+  const int64_t nc = N * K / 2;
+  for (int64_t i = 0; i < nc; ++i) {
+    const uint8_t a = q[2 * i], b = q[2 * i + 1];
+    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_iq4_xs: code > 15 at weight %lld", (long long)(2 * i));
+    dst[i] = (uint8_t)(a | (b << 4));
+  }
+  // one 8-byte header per (row, 256 weights): d, then ls_0..7 as 6-bit fields of a
+  // little-endian 48-bit number
+  const int64_t nsb = N * K / 256;
+  for (int64_t i = 0; i < nsb; ++i) {
+    uint64_t f = 0;
+    for (int j = 0; j < 8; ++j) {
+      const uint8_t v = ls[8 * i + j];
+      if (v > 63) return fail(NVQ_ERR_RANGE, "nvq_pack_iq4_xs: scale > 63 at sub-block %lld", (long long)(8 * i + j));
+      f |= (uint64_t)v << (6 * j);
+    }
+    uint8_t h[8];
+    std::memcpy(h, &d_f16[i], 2);
+    for (int b = 0; b < 6; ++b) h[2 + b] = (uint8_t)(f >> (8 * b));
+    std::memcpy(dst + nc + 8 * i, h, 8);
   }
   g_err[0] = '\0';
   return NVQ_OK;
@@ -383,6 +418,44 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
   NVQ_TRY(check_device());
   return launched(nvq::launch_gemm_q4_k(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
                                         static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q4_k");
+}
+
+nvq_status nvq_gemv_iq4_xs(const void* w, const int8_t* table, const int8_t* q, const uint16_t* d_f16, int64_t M,
+                           int64_t N, int64_t K, float* y, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_iq4_xs"));
+  if (!table) return fail(NVQ_ERR_NULL, "nvq_gemv_iq4_xs: table is required");
+  NVQ_TRY(check_dims(M, N, K, 256, 1, NVQ_GEMV_MAX_M));
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_iq4_xs(static_cast<const uint8_t*>(w), table, q, d_f16, M, N, K, y, nullptr,
+                                          (hipStream_t)stream), "gemv_iq4_xs");
+}
+
+nvq_status nvq_gemm_iq4_xs(const void* w, const int8_t* table, const int8_t* q, const uint16_t* d_f16, int64_t M,
+                           int64_t N, int64_t K, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_iq4_xs"));
+  if (!table) return fail(NVQ_ERR_NULL, "nvq_gemm_iq4_xs: table is required");
+  NVQ_TRY(check_dims(M, N, K, 256, 16, kMaxM));
+  const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_IQ4_XS, M, N, K);
+  if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_iq4_xs: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_iq4_xs: workspace must be 16-byte aligned");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemm_iq4_xs(static_cast<const uint8_t*>(w), table, q, d_f16, M, N, K, y, nullptr,
+                                          static_cast<float*>(workspace), (hipStream_t)stream), "gemm_iq4_xs");
+}
+
+nvq_status nvq_debug_isums_iq4_xs(const int8_t* table, int path, const void* w, const int8_t* q, int64_t M,
+                                  int64_t N, int64_t K, int32_t* isums, void* stream) {
+  if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM) return fail(NVQ_ERR_RANGE, "nvq_debug_isums_iq4_xs: path=%d", path);
+  if (!table || !w || !q || !isums) return fail(NVQ_ERR_NULL, "nvq_debug_isums_iq4_xs: NULL pointer");
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(isums, 4)) return fail(NVQ_ERR_ALIGN, "nvq_debug_isums_iq4_xs: w and q must be 16-byte aligned, isums 4-byte");
+  NVQ_TRY(check_dims(M, N, K, 256, 1, kMaxM));
+  if (M > kMaxElems / (N * (K / 16))) return fail(NVQ_ERR_SHAPE, "nvq_debug_isums_iq4_xs: output too large");
+  NVQ_TRY(check_device());
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  hipStream_t st = (hipStream_t)stream;
+  if (path == NVQ_PATH_GEMM)
+    return launched(nvq::launch_gemm_iq4_xs(wb, table, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_iq4_xs");
+  return launched(nvq::launch_gemv_iq4_xs(wb, table, q, nullptr, M, N, K, nullptr, isums, st), "debug gemv_iq4_xs");
 }
 
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,

@@ -81,4 +81,12 @@ hipError_t launch_gemm_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d
                             int32_t* isums, float* workspace, hipStream_t stream);
 size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K);
 
+// IQ4_XS (K % 256 == 0; table: the 16 int8 values the codes index, host memory) on the
+// same kernels and with the same dispatch as Q4_K; its workspace is gemm_q4_k_workspace's.
+hipError_t launch_gemv_iq4_xs(const uint8_t* w, const int8_t* table, const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream);
+hipError_t launch_gemm_iq4_xs(const uint8_t* w, const int8_t* table, const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, float* workspace,
+                              hipStream_t stream);
+
 }  // namespace nvq

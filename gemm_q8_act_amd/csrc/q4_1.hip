@@ -41,7 +41,14 @@
 namespace nvq {
 
 constexpr int kQ41MaxUPL = 10;
-__host__ __device__ constexpr int q41_rg(int upl) { return upl >= 7 ? 1 : (upl >= 4 ? 2 : 4); }
+// Row groups per wavefront (rows = RG x 64 / LPR): fewer for one token, where the
+// kernel is latency-bound and more wavefronts in flight pay (N = K = 4096 at M = 1: Q4_1
+// 4.39 us with 2 against 4.53 with 4; Q4_K 4.46 against 4.68), and one for IQ4_XS,
+// whose table lookups make each unit's vector work ~6x longer (5.2 us against 7.3 with 4).
+// fmt: the weight format (NVQ_FMT_* value, 3 = IQ4_XS).
+__host__ __device__ constexpr int q41_rg(int upl, bool multi, int fmt) {
+  return fmt == 3 ? 1 : (upl >= 7 ? 1 : (upl >= 4 || !multi ? 2 : 4));
+}
 // tokens whose activations a GEMV wavefront holds at once (8 UPL registers each)
 __host__ __device__ constexpr int q41_tb(int upl) { return upl <= 2 ? 4 : (upl <= 4 ? 2 : 1); }
 
@@ -53,7 +60,24 @@ __device__ __forceinline__ int dot8_u4(uint32_t c, uint32_t qe, uint32_t qo, int
   return acc;
 }
 
-constexpr int kQ41 = 1, kQ4K = 2;  // weight formats of the kernels below (the NVQ_FMT_* values)
+constexpr int kQ41 = 1, kQ4K = 2, kIQ4 = 3;  // weight formats of the kernels below (the NVQ_FMT_* values)
+
+// IQ4_XS: 4 values of a 16-entry byte table (words t0..t3 = entries 0-3, .., 12-15) for
+// 4 index bytes idx (each 0..15): entries 0..7 and 8..15 by one v_perm_b32 each, then
+// a third picks per byte by the index's bit 3
+__device__ __forceinline__ uint32_t lut16(uint32_t idx, const u32x4& t) {
+  const uint32_t i7 = idx & 0x07070707u;
+  const uint32_t lo = perm(t[1], t[0], i7);
+  const uint32_t hi = perm(t[3], t[2], i7);
+  return perm(hi, lo, 0x03020100u | ((idx & 0x08080808u) >> 1));
+}
+// sum over 8 codes (one packed word) of table[code] * q: the int8 table values against
+// the even / odd activation codes
+__device__ __forceinline__ int iq4_dot8(uint32_t c, uint32_t qe, uint32_t qo, int acc, const u32x4& t) {
+  acc = dot4(lut16(c & 0x0F0F0F0Fu, t), qe, acc);
+  acc = dot4(lut16((c >> 4) & 0x0F0F0F0Fu, t), qo, acc);
+  return acc;
+}
 
 // Q4_K: the (scale, offset) of sub-block j of the super-block with header h (see the
 // layout above), as float32 (both products exact)
@@ -66,20 +90,27 @@ __device__ __forceinline__ void q4k_block_scales(const u32x4& h, int j, float& d
 }
 
 // The scale source of a weight format: Q4_1 one 4-byte (d, m) binary16 pair per
-// 32-block after the codes; Q4_K one 16-byte header per 256-block after the codes.
+// 32-block after the codes; Q4_K one 16-byte header per 256-block after the codes;
+// IQ4_XS one 8-byte header per 256-block (binary16 d, then the eight 6-bit sub-block
+// scales ls_j as a little-endian 48-bit number; scale d * (ls_j - 32), no offset).
+// kBound bounds |weight| / |scale| + |offset| / |scale| per block (the code range).
 template <int FMT>
 struct BlockScales {
-  static constexpr int kWords = FMT == kQ4K ? 4 : 1;
+  static constexpr int kWords = FMT == kQ4K ? 4 : (FMT == kIQ4 ? 2 : 1);
+  static constexpr float kBound = FMT == kIQ4 ? 128.0f : 15.0f;
   const uint32_t* base;  // first word of the scale region
   int64_t per_row;       // words per weight row
   __device__ BlockScales(const uint8_t* w, int64_t N, int K)
       : base(reinterpret_cast<const uint32_t*>(w + N * (int64_t)(K >> 1))),
-        per_row(FMT == kQ4K ? (int64_t)(K >> 8) * 4 : (int64_t)(K >> 5)) {}
+        per_row(FMT == kQ4K ? (int64_t)(K >> 8) * 4 : (FMT == kIQ4 ? (int64_t)(K >> 8) * 2 : (int64_t)(K >> 5))) {}
   // the raw words that hold 32-block b of a row
   __device__ __forceinline__ void load(int64_t row, int64_t b, uint32_t* v) const {
     if constexpr (FMT == kQ4K) {
       const u32x4 h = *reinterpret_cast<const u32x4*>(base + row * per_row + 4 * (b >> 3));
       v[0] = h[0]; v[1] = h[1]; v[2] = h[2]; v[3] = h[3];
+    } else if constexpr (FMT == kIQ4) {
+      const u32x2 h = *reinterpret_cast<const u32x2*>(base + row * per_row + 2 * (b >> 3));
+      v[0] = h[0]; v[1] = h[1];
     } else {
       v[0] = base[row * per_row + b];
     }
@@ -88,6 +119,11 @@ struct BlockScales {
   __device__ __forceinline__ static void decode(const uint32_t* v, int64_t b, float& dw, float& mw) {
     if constexpr (FMT == kQ4K) {
       q4k_block_scales(u32x4{v[0], v[1], v[2], v[3]}, (int)(b & 7), dw, mw);
+    } else if constexpr (FMT == kIQ4) {
+      const uint64_t f = (uint64_t)v[1] << 16 | (v[0] >> 16);  // the 48 bits of ls_0 .. ls_7
+      const int ls = (int)((f >> (6 * (b & 7))) & 63u);
+      dw = f16_bits_to_f32((uint16_t)(v[0] & 0xFFFFu)) * (float)(ls - 32);
+      mw = 0.0f;
     } else {
       dw = f16_bits_to_f32((uint16_t)(v[0] & 0xFFFFu));
       mw = f16_bits_to_f32((uint16_t)(v[0] >> 16));
@@ -102,8 +138,8 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
                                                            const uint16_t* __restrict__ d16,
                                                            const int16_t* __restrict__ bsum16,
                                                            float* __restrict__ y,
-                                                           int32_t* __restrict__ isums, int M) {
-  constexpr int RG = q41_rg(UPL);
+                                                           int32_t* __restrict__ isums, int M, u32x4 vtab) {
+  constexpr int RG = q41_rg(UPL, MULTI, FMT);
   constexpr int RPG = 64 / LPR;
   constexpr int RPW = RPG * RG;
   const int lane = threadIdx.x & 63;
@@ -161,7 +197,9 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
           split_even_odd(b.z, b.w, qe[tb][j][3], qo[tb][j][3]);
           if (!DEBUG) {
             da[tb][j] = f16_bits_to_f32(d16[m * nb + u]);
-            bs[tb][j] = (float)((int)bsum16[m * 2 * nb + 2 * u] + (int)bsum16[m * 2 * nb + 2 * u + 1]);
+            // IQ4_XS has no offset term (and takes no bsum16)
+            bs[tb][j] = FMT == kIQ4 ? 0.0f
+                                    : (float)((int)bsum16[m * 2 * nb + 2 * u] + (int)bsum16[m * 2 * nb + 2 * u + 1]);
           } else {
             da[tb][j] = bs[tb][j] = 0.0f;
           }
@@ -183,8 +221,14 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < UPL; ++j) {
-          const int i0 = dot8_u4(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], dot8_u4(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0));
-          const int i1 = dot8_u4(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], dot8_u4(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0));
+          int i0, i1;
+          if constexpr (FMT == kIQ4) {  // table values of the codes
+            i0 = iq4_dot8(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], iq4_dot8(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0, vtab), vtab);
+            i1 = iq4_dot8(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], iq4_dot8(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0, vtab), vtab);
+          } else {
+            i0 = dot8_u4(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], dot8_u4(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0));
+            i1 = dot8_u4(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], dot8_u4(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0));
+          }
           if (DEBUG) {
             const int u = sub + LPR * j;
             if (row < N && u < units) {
@@ -412,7 +456,7 @@ __global__ __launch_bounds__(256) void gemm_q4_1_kernel(const uint8_t* __restric
 
 namespace {
 typedef void (*gemv_q41_fn)(const uint8_t*, int64_t, int, const int8_t*, const uint16_t*,
-                            const int16_t*, float*, int32_t*, int);
+                            const int16_t*, float*, int32_t*, int, u32x4);
 template <int FMT, int LPR, bool MULTI, bool DEBUG>
 gemv_q41_fn pick_q41(int upl) {
   switch (upl) {
@@ -484,7 +528,8 @@ static bool q41_gemv_fits(int64_t K) {
 
 template <int FMT>
 static hipError_t launch_gemv_q4x(const uint8_t* w, const int8_t* q, const uint16_t* d16, const int16_t* bsum16,
-                                  int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
+                                  int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream,
+                                  u32x4 vtab = u32x4{0u, 0u, 0u, 0u}) {
   const bool debug = isums != nullptr;
   int lpr = 0, upl = 0;
   gemv_m1_config(K, &lpr, &upl);
@@ -494,10 +539,10 @@ static hipError_t launch_gemv_q4x(const uint8_t* w, const int8_t* q, const uint1
   if (lpr == 32) fn = pick_q41_for<FMT, 32>(upl, multi, debug);
   if (lpr == 16) fn = pick_q41_for<FMT, 16>(upl, multi, debug);
   if (!fn) return hipErrorInvalidValue;
-  const int64_t rows_per_block = 4 * (64 / lpr) * q41_rg(upl);
+  const int64_t rows_per_block = 4 * (64 / lpr) * q41_rg(upl, multi && !debug, FMT);
   const int64_t grid = (N + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, stream, w, N, (int)K, q, d16, bsum16,
-                     y, isums, (int)M);
+                     y, isums, (int)M, vtab);
   return hipGetLastError();
 }
 
@@ -592,7 +637,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
                                                                  const int8_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ d16, int64_t M,
                                                                  float* __restrict__ y, float* __restrict__ part_ws,
-                                                                 int32_t* __restrict__ isums, KSplitPlan plan) {
+                                                                 int32_t* __restrict__ isums, KSplitPlan plan,
+                                                                 u32x4 vtab) {
   constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
   constexpr int LRW = kQLRW, LRA = kQLRA, CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -651,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
     if (!DEBUG) bsc.load(wr, b, v);
     float dwf, mwf;
     block_scales(v, b, dwf, mwf);
-    bmax = fmaxf(bmax, fabsf(mwf) + 15.0f * fabsf(dwf));
+    bmax = fmaxf(bmax, fabsf(mwf) + BlockScales<FMT>::kBound * fabsf(dwf));
   }
   bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
   if constexpr (TPR == 4) bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
@@ -680,14 +726,26 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
     uint16_t* ld = reinterpret_cast<uint16_t*>(st + 2 * C::kStageW + C::kStageA);
     float dwf, mwf;
     block_scales(x.dm, x.blk, dwf, mwf);
-    const float dw = rscale * dwf, mw = rscale * mwf;
+    const float dw = rscale * dwf;
+    // IQ4_XS: the weight is dw * table[c]; the table is read as table + 128 (bytes
+    // 0..255, exact floats), so w = fma(dw, table[c] + 128, -128 dw): one rounding of
+    // the exact dw * table[c], as the Q4 formats' fma(dw, c, mw)
+    const float mw = FMT == kIQ4 ? -128.0f * dw : rscale * mwf;
 #pragma unroll
     for (int h = 0; h < CPT / 8; ++h) {
       const uint32_t cw = x.wc.v[h];
+      uint32_t ve = 0u, vo = 0u;  // IQ4_XS: biased table values of the even / odd codes
+      if constexpr (FMT == kIQ4) {
+        const u32x4 tb = vtab ^ u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+        ve = lut16(cw & 0x0F0F0F0Fu, tb);
+        vo = lut16((cw >> 4) & 0x0F0F0F0Fu, tb);
+      }
       half8_t vh, vl;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float c = (float)((cw >> (4 * j)) & 0xFu);  // byte j/2: code 2i low nibble, 2i+1 high
+        // byte j/2 of the codes: code 2i low nibble, 2i+1 high
+        const float c = FMT == kIQ4 ? (float)(((j & 1 ? vo : ve) >> (8 * (j >> 1))) & 0xFFu)
+                                    : (float)((cw >> (4 * j)) & 0xFu);
         const float wf = fmaf(dw, c, mw);
         const _Float16 hi = (_Float16)wf;
         vh[j] = hi;
@@ -881,7 +939,7 @@ namespace {
 template <class C, int FMT>
 hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
                             int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream,
-                            bool split = true) {
+                            bool split = true, u32x4 vtab = u32x4{0u, 0u, 0u, 0u}) {
   KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
   if (!split) {
     plan.split = 1;
@@ -894,7 +952,7 @@ hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d
                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
     if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, FMT, true>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
-                       stream, w, N, (int)K, q, d16, M, y, nullptr, isums, plan);
+                       stream, w, N, (int)K, q, d16, M, y, nullptr, isums, plan, vtab);
     return hipGetLastError();
   }
   if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
@@ -902,7 +960,7 @@ hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d
                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
   if (ea != hipSuccess) return ea;
   hipLaunchKernelGGL((gemm_q4_1_f16x2_kernel<C, FMT, false>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
-                     stream, w, N, (int)K, q, d16, M, y, workspace, nullptr, plan);
+                     stream, w, N, (int)K, q, d16, M, y, workspace, nullptr, plan, vtab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.split_tiles == 0) return e;
   return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
@@ -947,6 +1005,32 @@ hipError_t launch_gemm_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d
     case kQ41M128: return launch_q41_f16x2<Q41M128, kQ4K>(w, q, d16, M, N, K, y, isums, workspace, stream);
     default: return launch_q41_f16x2<Q41Mid, kQ4K>(w, q, d16, M, N, K, y, isums, workspace, stream);
   }
+}
+
+// IQ4_XS: the value table as 4 words (entries 4i .. 4i + 3 in word i, int8 bytes)
+static u32x4 table_words(const int8_t* table) {
+  u32x4 t = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 16; ++i) t[i / 4] |= (uint32_t)(uint8_t)table[i] << (8 * (i % 4));
+  return t;
+}
+
+hipError_t launch_gemm_iq4_xs(const uint8_t* w, const int8_t* table, const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, float* workspace,
+                              hipStream_t stream) {
+  const u32x4 t = table_words(table);
+  switch (q4k_path(M, K)) {
+    case kQ41Gemv: return launch_gemv_q4x<kIQ4>(w, q, d16, nullptr, M, N, K, y, isums, stream, t);
+    case kQ41Big: return launch_q41_f16x2<Q41Big, kIQ4>(w, q, d16, M, N, K, y, isums, workspace, stream, true, t);
+    case kQ41M128: return launch_q41_f16x2<Q41M128, kIQ4>(w, q, d16, M, N, K, y, isums, workspace, stream, true, t);
+    default: return launch_q41_f16x2<Q41Mid, kIQ4>(w, q, d16, M, N, K, y, isums, workspace, stream, true, t);
+  }
+}
+
+hipError_t launch_gemv_iq4_xs(const uint8_t* w, const int8_t* table, const int8_t* q, const uint16_t* d16,
+                              int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, hipStream_t stream) {
+  const u32x4 t = table_words(table);
+  if (q41_gemv_fits(K)) return launch_gemv_q4x<kIQ4>(w, q, d16, nullptr, M, N, K, y, isums, stream, t);
+  return launch_q41_f16x2<Q41Mid, kIQ4>(w, q, d16, M, N, K, y, isums, nullptr, stream, false, t);
 }
 
 // The GEMV entry (M <= 16): the GEMV kernel, or for rows past its reach the two-term

@@ -1,6 +1,6 @@
 /*
- * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 / Q4_K x Q8_0) quantized matrix
- * products on AMD Instinct MI355X (gfx950).
+ * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 / Q4_K / IQ4_XS x Q8_0) quantized
+ * matrix products on AMD Instinct MI355X (gfx950).
  *
  * What is computed.  Weights W [N][K] ("out x in", row-major) are stored 4-bit;
  * activations X [M][K] (M tokens) are quantized on the fly to Q8_0; the product is
@@ -11,10 +11,11 @@
  *     bias-trick paragraph): NVFP4 weights in 64-weight blocks, one UE4M3 scale
  *     per 16 weights, integer partial sums per 16-subblock, per-16 activation code
  *     sums; batch-1 decode uses a vector dot, larger batches a tiled matmul;
- *     section 1 names the Q4_1 kernels of the same work and Q4_K among its formats.
+ *     section 1 names the Q4_1 kernels of the same work and Q4_K and IQ4_XS among its
+ *     formats.
  *   The llama.cpp 2-bit GGUF tutorial (spke.com, article 4846), GGML type table:
  *     Q8_0 is 32 values in 34 bytes (32 int8 codes + one fp16 scale); Q4_K is 256
- *     values in 144 bytes.
+ *     values in 144 bytes, IQ4_XS 256 values in 136 bytes.
  *
  * Element formats (bit-exact definitions):
  *   E2M1 code c (4 bits): sign = bit 3, exponent e = bits 2..1 (bias 1), mantissa
@@ -30,6 +31,11 @@
  *     W[n][k] = d[n][k/256] * sc[n][k/32] * q[n][k] - dmin[n][k/256] * mn[n][k/32],
  *     q in 0..15, sc and mn 6-bit (0..63), d and dmin IEEE binary16; 2 + 2 + 12 + 128
  *     = 144 bytes per 256 weights.
+ *   IQ4_XS weight (the pages give only its block size; the rule taken is the GGML
+ *     format's, with its 16-entry value table as an argument, since the pages print
+ *     none): W[n][k] = d[n][k/256] * (ls[n][k/32] - 32) * table[c[n][k]], c in 0..15,
+ *     ls 6-bit (0..63), table 16 int8 values, d IEEE binary16; 2 + 6 + 128 = 136 bytes
+ *     per 256 weights.
  *   Q8_0 activation, per row and per 32 consecutive k:
  *     amax = max |x|; d32 = amax / 127 (IEEE float32 division);
  *     d = binary16(d32) rounded to nearest even (stored);
@@ -68,6 +74,12 @@
  *                           eight 32-weight sub-blocks, field f at bits
  *                           [6f, 6f + 6) of those 12 bytes read as one
  *                           little-endian 96-bit number.
+ *   IQ4_XS, row-major, nvq_iq4_xs_weight_bytes(N, K) = N*K*136/256 bytes:
+ *     [0, N*K/2)            codes, as Q4_1.
+ *     [N*K/2, +N*K/32)      per 256 weights an 8-byte header, row-major [N][K/256]:
+ *                           bytes 0-1 binary16 d, bytes 2-7 the eight 6-bit fields
+ *                           ls_0..ls_7, field j at bits [6j, 6j + 6) of those 6 bytes
+ *                           read as one little-endian 48-bit number.
  *
  * Conventions for every entry point:
  *   - All array arguments of the compute entries are DEVICE pointers owned by the
@@ -111,6 +123,7 @@ typedef int nvq_status;
 #define NVQ_FMT_NVFP4 0
 #define NVQ_FMT_Q4_1  1
 #define NVQ_FMT_Q4_K  2
+#define NVQ_FMT_IQ4_XS 3
 #define NVQ_PATH_GEMV      0  /* decode GEMV, matrix-core inner loop (production) */
 #define NVQ_PATH_GEMM      1  /* tiled GEMM */
 #define NVQ_PATH_GEMV_DOT4 2  /* decode GEMV, v_perm + v_dot4 inner loop (NVFP4 only) */
@@ -137,9 +150,15 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
  * table (Q4_K: 256 values in 144 bytes). */
 size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K);
 
-/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 / nvq_gemm_q4_k need for this
- * shape (fmt is NVQ_FMT_*): with M > 16 and K % 64 == 0 (Q4_K: K % 256 == 0, and also
- * M <= 16 with K > 20480), the fp32 partial tiles of the K-split
+/* Bytes of a packed IQ4_XS weight buffer [N][K]: N*K*136/256.  0 if N < 1 or K is not
+ * a positive multiple of 256.  Follows: the llama.cpp 2-bit GGUF tutorial, GGML type
+ * table (IQ4_XS: 256 values in 136 bytes). */
+size_t nvq_iq4_xs_weight_bytes(int64_t N, int64_t K);
+
+/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 / nvq_gemm_q4_k /
+ * nvq_gemm_iq4_xs need for this shape (fmt is NVQ_FMT_*): with M > 16 and K % 64 == 0
+ * (Q4_K, IQ4_XS: K % 256 == 0, and also M <= 16 with K > 20480), the fp32 partial
+ * tiles of the K-split
  * work items that even out the last round of tiles over the chip's 256 compute units
  * (at most 64 MiB: 256 work items x 512 threads x 128 floats); otherwise 0.  Pure
  * function.  When it is 0 the workspace pointer may be NULL.  (A scheduling detail
@@ -174,6 +193,16 @@ nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t
  * among the formats of the same work). */
 nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
                          const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host);
+
+/* q: [N][K] bytes (0..15, indices into the value table); ls: [N][K/32] bytes (6-bit,
+ * 0..63); d_f16: [N][K/256] binary16 bit patterns.  Writes nvq_iq4_xs_weight_bytes(N, K)
+ * bytes to dst_host.  K % 256 == 0.  NVQ_ERR_RANGE if a code exceeds 15 or a scale 63.
+ * The value table is not part of the buffer; the products take it.  Host memory only.
+ * Follows: the llama.cpp 2-bit GGUF tutorial, GGML type table (IQ4_XS: 256 values in
+ * 136 bytes) and "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (IQ4_XS
+ * among the formats of the same work). */
+nvq_status nvq_pack_iq4_xs(const uint8_t* q, const uint8_t* ls, const uint16_t* d_f16, int64_t N, int64_t K,
+                           void* dst_host);
 
 /* ---- activation quantization ------------------------------------------------ */
 
@@ -322,6 +351,24 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
                          const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- IQ4_XS products ---------------------------------------------------------- */
+
+/* IQ4_XS GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 256 == 0; table: the
+ * 16 int8 values the codes index (HOST memory, read during the call; the kernels
+ * receive it by value).  No bsum16 (the format has no offset term).  Workspace of
+ * nvq_gemm_workspace_bytes(NVQ_FMT_IQ4_XS, M, N, K) bytes for the GEMM.  The Q4_1 / Q4_K
+ * kernels run it: per 32-block the scale d * (ls - 32) (exact in float32), the codes
+ * mapped through the table by v_perm_b32 lookups -- int8 values into v_dot4_i32_i8 in
+ * the GEMV kernel, exact float values into the two-term binary16 weights of the GEMM.
+ * Same error bound as the NVFP4 entries.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (IQ4_XS among the
+ * patch's formats); the llama.cpp 2-bit GGUF tutorial, GGML type table (IQ4_XS block). */
+nvq_status nvq_gemv_iq4_xs(const void* w, const int8_t* table, const int8_t* q, const uint16_t* d_f16,
+                           int64_t M, int64_t N, int64_t K, float* y, void* stream);
+nvq_status nvq_gemm_iq4_xs(const void* w, const int8_t* table, const int8_t* q, const uint16_t* d_f16,
+                           int64_t M, int64_t N, int64_t K, float* y, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 /* ---- debug: integer per-16 partial sums --------------------------------------- */
 
 /* isums [M][N][K/16] int32 (device, overwritten) = for each 16-subblock,
@@ -348,6 +395,15 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
  * paragraph; the integer sums are unique, so they are checked bit for bit. */
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q,
                            int64_t M, int64_t N, int64_t K, int32_t* isums, void* stream);
+
+/* The same for IQ4_XS weights, whose sums need the value table (host memory):
+ * isums [M][N][K/16] = sum_j table[code] * q, from the kernel nvq_gemv_iq4_xs
+ * (path NVQ_PATH_GEMV) or nvq_gemm_iq4_xs (NVQ_PATH_GEMM, any M >= 1) dispatches for
+ * the shape, with unit block scales.  K % 256 == 0.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map (one
+ * int32 sum per 16-subblock). */
+nvq_status nvq_debug_isums_iq4_xs(const int8_t* table, int path, const void* w, const int8_t* q,
+                                  int64_t M, int64_t N, int64_t K, int32_t* isums, void* stream);
 
 /* ---- errors ------------------------------------------------------------------- */
 

@@ -105,6 +105,21 @@ class Q4KCase:
         return o.matmul_q4_k(self.qw, self.sc, self.mn, self.dd, self.dm, self.qh, self.dh, cols=cols)
 
 
+class IQ4Case:
+    """Seeded IQ4_XS case; ``weights`` = (qw, ls, d, table) and ``x`` replace the seeded ones."""
+
+    def __init__(self, M, N, K, seed, weights=None, x=None):
+        self.M, self.N, self.K = M, N, K
+        self.qw, self.ls, self.dd, self.table = weights if weights is not None else synth.iq4_xs_weights(N, K, seed)
+        self.x = x if x is not None else synth.activations(M, K, seed + 1)
+        self.w = to_dev(nvq.nvq_pack_iq4_xs(self.qw, self.ls, self.dd))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_iq4_xs(self.qw, self.ls, self.dd, self.table, self.qh, self.dh, cols=cols)
+
+
 def sample_cols(N: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
     """First/last columns, both sides of tile boundaries, plus seeded random ones."""
     base = {0, 1, N - 1, N - 2}

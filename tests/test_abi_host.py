@@ -168,6 +168,48 @@ def test_pack_q4_k_layout():
             assert fields[:8] == list(sc[n, 8 * b: 8 * b + 8]) and fields[8:] == list(mn[n, 8 * b: 8 * b + 8])
 
 
+def test_iq4_xs_block_size_matches_type_table():
+    # the GGML type table of the llama.cpp 2-bit GGUF tutorial: IQ4_XS = 256 values in 136 bytes
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "page_facts.json")))["iq4_xs_block"]
+    vb, bb = facts["values_per_block"], facts["bytes_per_block"]
+    assert nvq.nvq_iq4_xs_weight_bytes(1, vb) == bb
+    assert nvq.nvq_iq4_xs_weight_bytes(4096, 4096) == 4096 * (4096 // vb) * bb
+    assert nvq.nvq_iq4_xs_weight_bytes(3, 128) == 0
+
+
+def test_pack_iq4_xs_layout():
+    # codes as Q4_1, then per (row, 256 weights) 8 bytes = d and 8 6-bit fields (ls_0..7)
+    # of a 48-bit little-endian number
+    r = np.random.Generator(np.random.PCG64(8))
+    N, K = 3, 512
+    q = r.integers(0, 16, (N, K), dtype=np.uint8)
+    ls = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    d = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    buf = nvq.nvq_pack_iq4_xs(q, ls, d)
+    assert buf.size == N * K * 136 // 256
+    cb = buf[: N * K // 2].reshape(N, K // 2)
+    assert (cb & 0xF == q[:, 0::2]).all() and (cb >> 4 == q[:, 1::2]).all()
+    hdr = buf[N * K // 2:].reshape(N, K // 256, 8)
+    assert (hdr[..., 0:2].copy().view(np.uint16)[..., 0] == d).all()
+    for n in range(N):
+        for b in range(K // 256):
+            big = int.from_bytes(bytes(hdr[n, b, 2:8]), "little")
+            assert [(big >> (6 * j)) & 63 for j in range(8)] == list(ls[n, 8 * b: 8 * b + 8])
+
+
+@pytest.mark.parametrize("bad", ["code16", "scale64"])
+def test_pack_iq4_xs_rejects_invalid(bad):
+    q = np.zeros((1, 256), np.uint8)
+    ls = np.zeros((1, 8), np.uint8)
+    if bad == "code16":
+        q[0, 9] = 16
+    else:
+        ls[0, 5] = 64
+    with pytest.raises(nvq.NvqError) as e:
+        nvq.nvq_pack_iq4_xs(q, ls, np.zeros((1, 1), np.uint16))
+    assert e.value.status == -3
+
+
 @pytest.mark.parametrize("bad", ["code16", "scale64", "min64"])
 def test_pack_q4_k_rejects_invalid(bad):
     q = np.zeros((1, 256), np.uint8)
@@ -262,6 +304,15 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_gemm_workspace_bytes(2, 100, 8, 768) > 0
     assert L.nvq_gemm_workspace_bytes(2, 100, 8, 640) == 0                  # K % 256 != 0
     assert L.nvq_gemm_q4_k(A16, A16, A16, A2, 100, 8, 768, A16, None, 0, None) == -7
+    # IQ4_XS entries: the value table is required, K % 256, workspace; generic debug entry rejects the format
+    assert L.nvq_gemv_iq4_xs(A16, None, A16, A16, 1, 8, 256, A16, None) == -1
+    assert L.nvq_gemv_iq4_xs(A16, A16, A16, A16, 1, 8, 128, A16, None) == -2
+    assert L.nvq_gemm_iq4_xs(A16, A16, A16, A16, 15, 8, 256, A16, None, 0, None) == -2
+    assert L.nvq_gemm_workspace_bytes(3, 100, 8, 768) == L.nvq_gemm_workspace_bytes(2, 100, 8, 768) > 0
+    assert L.nvq_gemm_iq4_xs(A16, A16, A16, A16, 100, 8, 768, A16, None, 0, None) == -7
+    assert L.nvq_debug_isums(3, 0, A16, A16, 1, 8, 256, A16, None) == -3
+    assert L.nvq_debug_isums_iq4_xs(None, 0, A16, A16, 1, 8, 256, A16, None) == -1
+    assert L.nvq_debug_isums_iq4_xs(A16, 2, A16, A16, 1, 8, 256, A16, None) == -3
 
 
 def test_routed_gemv_validation_without_gpu():

@@ -718,6 +718,9 @@ def test_side_stream_and_graph_replay():
                 torch.empty((M, K4 // 32), dtype=torch.int16, device="cuda"),
                 torch.empty((M, K4 // 16), dtype=torch.int16, device="cuda")) for M in x4k}
     y4k = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
+    qwx, lsx, ddx, tabx = synth.iq4_xs_weights(N, K4, 68)
+    wx = to_dev(nvq.nvq_pack_iq4_xs(qwx, lsx, ddx))
+    yx = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
     need = max([nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms]
                + [nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 64, Nk, Kk),
                   nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_K, 100, N, K4)])
@@ -743,10 +746,12 @@ def test_side_stream_and_graph_replay():
             q, d, b = qd4k[M]
             nvq.nvq_quantize_act_q8_0(x, q, d, b)
             (nvq.nvq_gemv_q4_k if M == 1 else nvq.nvq_gemm_q4_k)(w4k, q, d, b, y4k[M], **({} if M == 1 else {"workspace": wsp}))
+            (nvq.nvq_gemv_iq4_xs if M == 1 else nvq.nvq_gemm_iq4_xs)(wx, tabx, q, d, yx[M], **({} if M == 1 else {"workspace": wsp}))
 
     def snapshot():
         return ([host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
-                + [host(yf).copy(), host(yk).copy()] + [host(y4k[M]).copy() for M in x4k])
+                + [host(yf).copy(), host(yk).copy()] + [host(y4k[M]).copy() for M in x4k]
+                + [host(yx[M]).copy() for M in x4k])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -772,7 +777,7 @@ def test_side_stream_and_graph_replay():
         xk.mul_(-1.0)
         for x in x4k.values():
             x.mul_(-1.0)
-        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk] + list(y4k.values()):
+        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk] + list(y4k.values()) + list(yx.values()):
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
