@@ -460,7 +460,8 @@ nvq_status nvq_debug_isums_iq4_xs(const int8_t* table, int path, const void* w, 
 
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,
                            int64_t N, int64_t K, int32_t* isums, void* stream) {
-  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1 && fmt != NVQ_FMT_Q4_K) return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d", fmt);
+  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1 && fmt != NVQ_FMT_Q4_K)
+    return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d (IQ4_XS sums need its value table: nvq_debug_isums_iq4_xs)", fmt);
   if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM && !(path == NVQ_PATH_GEMV_DOT4 && fmt == NVQ_FMT_NVFP4))
     return fail(NVQ_ERR_RANGE, "nvq_debug_isums: path=%d", path);
   if (!w || !q || !isums) return fail(NVQ_ERR_NULL, "nvq_debug_isums: NULL pointer");

@@ -1,4 +1,5 @@
-// q4_1.hip -- Q4_1 weights x Q8_0 activations on gfx950 (GEMV and tiled MFMA).
+// q4_1.hip -- Q4_1 (and Q4_K, IQ4_XS) weights x Q8_0 activations on gfx950 (GEMV and
+// tiled MFMA).
 //
 // Q4_1 ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1: the same work
 // carries Q4_1 vec_dot and tiled kernels): per 32 weights an fp16 scale d and
@@ -26,12 +27,21 @@
 // binary16 d and dmin, and each 32-weight sub-block j a 6-bit scale sc_j and a 6-bit
 // min mn_j, weight = d*sc_j*c - dmin*mn_j.  Per 32-block that is a Q4_1 block with
 // scale d*sc_j and offset -dmin*mn_j (each product exact in fp32: 11 x 6 significant
-// bits), so both Q4_1 kernels above run it with a format parameter that only changes
-// where a block's (scale, offset) pair comes from (q4_block_scales).  Device layout:
+// bits), so the GEMV and two-term kernels run it with a format parameter that only
+// changes where a block's (scale, offset) pair comes from (BlockScales).  Device layout:
 // the codes as Q4_1 ([N][K/2], byte i = codes 2i low, 2i+1 high nibble), then one
 // 16-byte header per (row, super-block): binary16 d, binary16 dmin, and the 16 6-bit
 // fields sc_0..sc_7, mn_0..mn_7, field f at bits [6f, 6f + 6) of the 96-bit
 // little-endian number in bytes 4..15.
+//
+// IQ4_XS (also named by the patch; 256 values in 136 bytes in the type table): a
+// binary16 d per 256 weights, a 6-bit scale ls_j per 32 (used as ls_j - 32), and 4-bit
+// codes that index a 16-entry int8 value table V, weight = d*(ls_j - 32)*V[c].  The
+// same two kernels run it: per 32-block the scale d*(ls_j - 32) (exact in fp32) and no
+// offset, the codes mapped through V by v_perm_b32 lookups (lut16) -- int8 values for
+// v_dot4 in the GEMV, exact float values for the two-term weights of the GEMM.  Layout:
+// the codes as Q4_1, then one 8-byte header per (row, super-block): binary16 d and the
+// eight 6-bit ls_j as a little-endian 48-bit number.  V is a call argument.
 #include <algorithm>
 
 #include "ksplit.h"
@@ -583,6 +593,8 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 // binary16, lo = 0) and the activation split is hi = q, lo = 0; the three MFMAs of a
 // 16-k half with a zero accumulator give 2^11 sum c * q, exact in fp32 (every partial
 // sum is a multiple of 2^11 below 2^26), and the row factor 2^-11 makes it an integer.
+// IQ4_XS: the bound is 128, so w' = 2^7 V[c] (|V| <= 128: exact in binary16), and the
+// sums 2^7 sum V[c] * q (below 2^25) are exact the same way.
 // ---------------------------------------------------------------------------------
 namespace {
 constexpr int kQThreads = 512;
