@@ -908,6 +908,14 @@ def summarize_pmc(fetch_csv, write_csv):
     print(json.dumps(res, indent=1))
 
 
+def short_kernel_name(name):
+    """A kernel's name with its template arguments and without its parameter list,
+    namespaces and return type: ``gemm_q4_1_f16x2_kernel<Q41Cfg<2, 4, 2, 2>, 1, false>``."""
+    name = name.replace("(anonymous namespace)::", "").replace("nvq::", "")
+    name = name.split("(")[0]
+    return name[5:] if name.startswith("void ") else name
+
+
 def summarize_trace(path):
     """Per-(kernel, grid) summary of a rocprofv3 kernel_trace.csv."""
     import collections
@@ -918,11 +926,11 @@ def summarize_trace(path):
     for r in rows:
         dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
-        agg[(r["Kernel_Name"].split("(")[0], grid)].append(dur)
+        agg[(short_kernel_name(r["Kernel_Name"]), grid)].append(dur)
     out = []
     for (name, grid), d in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
         d = np.array(d, np.float64) / 1e3
-        out.append(f"{name[:60]:60s} grid={grid:>16s} n={len(d):5d} avg_us={d.mean():9.2f} "
+        out.append(f"{name[:66]:66s} grid={grid:>16s} n={len(d):5d} avg_us={d.mean():9.2f} "
                    f"p50_us={np.median(d):9.2f} min_us={d.min():9.2f} total_us={d.sum():11.1f}")
     print("\n".join(out))
 
@@ -961,7 +969,7 @@ def summarize_counters(run_dir):
     disp = collections.defaultdict(set)
     dur = {}
     for r in csv.DictReader(open(path)):
-        k = (r["Kernel_Name"].split("(")[0][:70], r.get("Grid_Size", ""))
+        k = (short_kernel_name(r["Kernel_Name"])[:80], r.get("Grid_Size", ""))
         acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[k].add(r["Dispatch_Id"])
         if "Start_Timestamp" in r:
