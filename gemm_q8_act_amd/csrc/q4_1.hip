@@ -43,6 +43,7 @@
 // the codes as Q4_1, then one 8-byte header per (row, super-block): binary16 d and the
 // eight 6-bit ls_j as a little-endian 48-bit number.  V is a call argument.
 #include <algorithm>
+#include <type_traits>
 
 #include "ksplit.h"
 #include "nvq_device.h"
@@ -583,9 +584,11 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 // v_mfma_f32_32x32x16_f16 products; block tile BN = 32 WN TN weight rows by
 // BM = 32 WM TM tokens (256 x 64 for 16 < M <= 64, 128 x 128 up to M = 128,
 // 128 x 256 above).  LDS holds two 64-k stages: the two weight planes (fp16 hi,
-// lo), raw int8 activation codes and their binary16 scales; each wavefront splits its
-// activation fragments in registers.  Work items and the ordered K-split reduction
-// follow the NVFP4 large-M kernel.
+// lo), the activation codes and their binary16 scales; each wavefront splits its
+// activation fragments in registers.  With 128 or 256 tokens per tile the codes are
+// staged already converted to binary16 (one conversion per block instead of one per
+// wavefront column that reads them; the 256 x 64 tile's two stages have no room for
+// it).  Work items and the ordered K-split reduction follow the NVFP4 large-M kernel.
 //
 // DEBUG instance (the integer per-16 sums sum c * q of this kernel's data path): the
 // same staging and MFMAs with d = 1 and m = 0 for every weight block and d = 1 for
@@ -599,14 +602,17 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 namespace {
 constexpr int kQThreads = 512;
 constexpr int kQLRW = 72;  // halves per LDS weight row (64 k + 8 pad)
-constexpr int kQLRA = 72;  // bytes per LDS activation row (64 codes + 8 pad)
+constexpr int kQLRA = 72;  // codes per LDS activation row (64 + 8 pad)
 
 template <int WN_, int WM_, int TN_, int TM_>
 struct Q41Cfg {
   static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_;
   static constexpr int BN = 32 * WN * TN, BM = 32 * WM * TM;
   static constexpr int kAcc = 16 * TN * TM;  // fp32 accumulators per thread
-  static constexpr int kStageW = BN * kQLRW * 2, kStageA = BM * kQLRA, kStageD = BM * 4;
+  // A16: activation codes staged as binary16 values (converted once per block rather
+  // than once per wavefront that reads them) where the two LDS stages have room
+  static constexpr bool A16 = BM >= 128;
+  static constexpr int kStageW = BN * kQLRW * 2, kStageA = BM * kQLRA * (A16 ? 2 : 1), kStageD = BM * 4;
   static constexpr int kStage = 2 * kStageW + kStageA + kStageD;
   static constexpr int kLds = 2 * kStage + BN * 4;  // + 2^-s of each weight row
   static constexpr int CPT = BN * 64 / kQThreads;   // weight codes staged per thread
@@ -766,7 +772,18 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
       *reinterpret_cast<half8_t*>(lh + wrow * LRW + CPT * wq + 8 * h) = vh;
       *reinterpret_cast<half8_t*>(ll + wrow * LRW + CPT * wq + 8 * h) = vl;
     }
-    store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
+    if constexpr (C::A16) {
+#pragma unroll
+      for (int v = 0; v < ABT / 4; v += 2) {
+        half2_t p0, p1, p2, p3;
+        i8x4_to_f16x4(x.a.v[v], p0, p1);
+        i8x4_to_f16x4(x.a.v[v + 1], p2, p3);
+        *reinterpret_cast<half8_t*>(reinterpret_cast<_Float16*>(la) + arow * LRA + aoff + 4 * v) =
+            half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+    } else {
+      store_words<ABT / 4>(la + arow * LRA + aoff, x.a);
+    }
     if (dtask) {
       uint32_t dr = x.dr;
       if constexpr (!DEBUG) {
@@ -783,7 +800,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = floatx16{};
   const int fr = lane & 31, fk = 8 * (lane >> 5);
-  struct Frag { half8_t ah[2][TN], al[2][TN]; uint2 raw[2][TM]; uint32_t dd[TM]; };
+  // a fragment's activation codes: 8 binary16 values (A16) or 8 int8 codes
+  using Raw = std::conditional_t<C::A16, half8_t, uint2>;
+  struct Frag { half8_t ah[2][TN], al[2][TN]; Raw raw[2][TM]; uint32_t dd[TM]; };
   auto fread = [&](int b, int u, Frag& f) {
     const uint8_t* st = smem + b * C::kStage;
     const _Float16* lh = reinterpret_cast<const _Float16*>(st);
@@ -803,7 +822,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
       const int r = wm * (32 * TM) + 32 * j + fr;
       f.dd[j] = ld[2 * r + u];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) f.raw[h][j] = *reinterpret_cast<const uint2*>(la + r * LRA + 32 * u + 16 * h + fk);
+      for (int h = 0; h < 2; ++h) {
+        const int e = r * LRA + 32 * u + 16 * h + fk;  // element offset in the activation plane
+        if constexpr (C::A16) f.raw[h][j] = *reinterpret_cast<const Raw*>(reinterpret_cast<const _Float16*>(la) + e);
+        else f.raw[h][j] = *reinterpret_cast<const Raw*>(la + e);
+      }
     }
   };
   const float* rinv = reinterpret_cast<const float*>(smem + 2 * C::kStage);
@@ -817,8 +840,16 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
         const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)f.dd[j]);
         const half2_t d2 = {dh, dh};
         half2_t a0, a1, c0, c1;
-        i8x4_to_f16x4(f.raw[h][j].x, a0, a1);
-        i8x4_to_f16x4(f.raw[h][j].y, c0, c1);
+        if constexpr (C::A16) {
+          const half8_t r = f.raw[h][j];
+          a0 = half2_t{r[0], r[1]};
+          a1 = half2_t{r[2], r[3]};
+          c0 = half2_t{r[4], r[5]};
+          c1 = half2_t{r[6], r[7]};
+        } else {
+          i8x4_to_f16x4(f.raw[h][j].x, a0, a1);
+          i8x4_to_f16x4(f.raw[h][j].y, c0, c1);
+        }
         const half2_t h0 = a0 * d2, h1 = a1 * d2, h2 = c0 * d2, h3 = c1 * d2;
         const half2_t l0 = __builtin_elementwise_fma(a0, d2, -h0);
         const half2_t l1 = __builtin_elementwise_fma(a1, d2, -h1);
@@ -870,6 +901,9 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   for (int t = t0; t < t1; ++t) {
     const int b = (t - t0) & 1;
     fread(b, 1, f1);
+    // keep the substep-1 fragment reads ahead of the staging work: left to itself the
+    // scheduler sinks each read next to its first MFMA and waits on it there
+    __builtin_amdgcn_sched_barrier(0);
     lstore(b ^ 1, x, 0);
     mfmas(f0, t, 0);
     gload(min(t + 2, t1 - 1), x);
