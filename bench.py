@@ -38,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -166,11 +167,19 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed: a comment edit does
+    not change the kernel a traffic record was taken on."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_src_hash(kernel_key):
     h = hashlib.sha256()
     for f in sorted(KERNEL_SOURCES[kernel_key]):
-        with open(os.path.join(ROOT, "gemm_q8_act_amd", "csrc", f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(ROOT, "gemm_q8_act_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

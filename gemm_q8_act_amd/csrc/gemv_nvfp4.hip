@@ -37,12 +37,12 @@
 //    costs as much time as streaming the bytes, so it is the slower of the two.
 //
 // Fused quantization (gemv_tile_fused, MODE_MX, one token): the block reads the
-// float32 row x instead of its Q8_0 codes.  Each wavefront quantizes exactly the
-// chunks it consumes (v, v + W, ...), one batch at a time, into its own part of the
-// LDS table: the quantization of batch b + 1 runs while that batch's weights are in
-// flight, so no separate quantization launch (and no round trip of the codes through
-// memory) precedes the product, and no block barrier precedes the first MFMA.  The
-// codes are bit-exact with nvq_quantize_act_q8_0 (see q8_0_pack4).
+// float32 row x instead of its Q8_0 codes and quantizes the whole row into its LDS
+// table.  The row's float4 loads are issued first, then the first batch of weight
+// loads, and the quantization runs while that batch is in flight; one block barrier
+// then publishes the table.  No separate quantization launch (and no round trip of
+// the codes through memory) precedes the product.  The codes are bit-exact with
+// nvq_quantize_act_q8_0 (see q8_0_pack4).
 
 #include "nvq_device.h"
 #include "nvq_launch.h"
