@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
     p.add_argument("--only-moe", action="store_true", help="time only the expert-routed decode step (profiling)")
     p.add_argument("--only-q4-1", action="store_true", help="time only the Q4_1, Q4_K and IQ4_XS GEMVs and GEMMs (profiling)")
+    p.add_argument("--floors", action="store_true",
+                   help="loads-only floors of the decode GEMV launch shapes on the layer set, and the measured "
+                        "ceilings, as one JSON line")
     p.add_argument("--traffic-probe", action="store_true",
                    help="for rocprofv3 --pmc runs: one 256 MiB device copy (calibration) and 4 gate+up "
                         "GEMV launches over distinct weight copies, then exit")
@@ -405,6 +408,111 @@ def torch_reference_rates():
     return dict(copy_GBps=2 * n / copy_s / 1e9, sum_read_GBps=n / read_s / 1e9,
                 note="torch kernels on 1 GiB: device copy (read+write bytes), float32 sum (read bytes); "
                      "not a ceiling")
+
+
+def measured_ceilings():
+    """Ceilings measured with the library's own probes (include/nvq_probe.h): the
+    streaming-read rate over 4 GiB (16-byte non-temporal loads, best of four grid
+    sizes) and the rate of back-to-back fp16 MFMAs (v_mfma_f32_32x32x16_f16, two
+    wavefronts per SIMD) on constant and on hashed operands -- the board lowers its
+    clock when the operands toggle many bits, so the second is what a GEMM on real
+    data can at most issue."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    read = {}
+    for blocks in (2048, 4096, 8192, 16384):
+        sink = torch.empty(4 * blocks, dtype=torch.int32, device="cuda")
+        us = _event_time(lambda: nvq.nvq_probe_read(src, blocks, sink), 5)
+        read[blocks] = n / (us * 1e-6) / 1e9
+    del src
+    torch.cuda.empty_cache()
+    blocks, iters = 512, 4000
+    out = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * 12 * iters * 32768
+    mfma = {}
+    for kind, rnd in (("constant", False), ("random", True)):
+        us = _event_time(lambda: nvq.nvq_probe_mfma(blocks, iters, rnd, out), 20)
+        mfma[kind] = flops / (us * 1e-6) / 1e12
+    best = max(read, key=read.get)
+    return dict(read_GBps=read[best], read_bytes=n, read_blocks=best,
+                read_GBps_by_blocks={str(k): v for k, v in read.items()},
+                mfma_fp16_constant_TFLOPs=mfma["constant"], mfma_fp16_random_TFLOPs=mfma["random"],
+                note="nvq_probe_read (4 GiB, 256-thread blocks, 8 loads in flight per thread) and nvq_probe_mfma "
+                     "(512 blocks x 256 threads, 12 MFMAs per iteration, constant / hashed fp16 operands)")
+
+
+def time_floors():
+    """Loads-only floors of the single-token decode GEMV on the layer set: for every
+    matrix, nvq_probe_gemv_loads (the GEMV's weight loads and nothing else) with the
+    plain and fused GEMVs' own launch shapes and over a sweep of K splits (blocks per
+    tile) and launch shapes, each HBM-cold (launches rotating over >= 1 GB of weight
+    copies), next to the GEMVs themselves timed the same way."""
+    import torch
+
+    import gemm_q8_act_amd as nvq
+    from gemm_q8_act_amd import synth
+
+    # the launch shapes nvq_gemv_nvfp4 (M = 1) and nvq_gemv_nvfp4_fused pick for a shape
+    def plain_shape(N, K):
+        ntiles, nch = (N + 15) // 16, (K + 127) // 128
+        if nch >= 64 and ntiles <= 1024:
+            return (8, 3)
+        return (8, 5) if ntiles >= 1024 else (4, 5)
+
+    def fused_shape(N, K):
+        ntiles, nch = (N + 15) // 16, (K + 127) // 128
+        if nch <= 12:
+            return (4, 3)
+        if ntiles < 1024:
+            return (16, 3) if nch >= 64 else (8, 3)
+        return (8, 5)
+
+    out = {}
+    for name, N, K in synth.LAYER:
+        codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("layer", name, 0), "uniform")
+        w = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+        wbytes = nvfp4_bytes(N, K)
+        copies = [w] + [w.clone() for _ in range(-(-(1 << 30) // wbytes) - 1)]
+        x = dev_tensor(synth.activations(1, K, synth.seed_for("layer", "x_" + name, 0)))
+        q = torch.empty((1, K), dtype=torch.int8, device="cuda")
+        d = torch.empty((1, K // 32), dtype=torch.int16, device="cuda")
+        y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        nvq.nvq_quantize_act_q8_0(x, q, d)
+        ntiles, nch = (N + 15) // 16, (K + 127) // 128
+        sink = torch.empty(16 * ntiles * 8, dtype=torch.int32, device="cuda")
+
+        def floor(S, W, P):
+            return rotated_time(lambda wi: nvq.nvq_probe_gemv_loads(wi, N, K, S, W, P, sink), copies)
+
+        gemv_us = rotated_time(lambda wi: nvq.nvq_gemv_nvfp4(wi, ws, q, d, y), copies)
+        fused_us = rotated_time(lambda wi: nvq.nvq_gemv_nvfp4_fused(wi, ws, x, y), copies)
+        pw, pp = plain_shape(N, K)
+        fw, fp = fused_shape(N, K)
+        sweep = {}
+        for S in (1, 2, 4, 8):
+            if S > nch:
+                continue
+            for W, P in ((4, 5), (8, 3), (8, 5), (16, 3)):
+                sweep[f"S{S}_W{W}_P{P}"] = floor(S, W, P)
+        best = min(sweep, key=sweep.get)
+        fl_plain = sweep[f"S1_W{pw}_P{pp}"]
+        fl_fused = sweep.get(f"S1_W{fw}_P{fp}") or floor(1, fw, fp)
+        gb = lambda us: wbytes / (us * 1e-6) / 1e9
+        out[name] = dict(N=N, K=K, weight_bytes=wbytes, copies=len(copies),
+                         gemv_us=gemv_us, gemv_GBps=gb(gemv_us), fused_us=fused_us, fused_GBps=gb(fused_us),
+                         floor_plain_shape=dict(shape=f"S1_W{pw}_P{pp}", us=fl_plain, GBps=gb(fl_plain)),
+                         floor_fused_shape=dict(shape=f"S1_W{fw}_P{fp}", us=fl_fused, GBps=gb(fl_fused)),
+                         floor_best=dict(shape=best, us=sweep[best], GBps=gb(sweep[best])),
+                         gemv_vs_floor=fl_plain / gemv_us, fused_vs_floor=fl_fused / fused_us,
+                         sweep_us=sweep)
+        del copies
+        torch.cuda.empty_cache()
+    return out
 
 
 def torch_fp16_gemm_rate(M=2048, N=17408, K=5120, reps=20):
@@ -1033,6 +1141,13 @@ def main():
     if args.only_moe:
         log(json.dumps(time_moe()))
         return
+    if args.floors:
+        log("ceilings ...")
+        c = measured_ceilings()
+        log("loads-only floors ...")
+        f = time_floors()
+        print(json.dumps(dict(ceilings=c, floors=f)), flush=True)
+        return
     if args.only_q4_1:
         log(json.dumps(time_q4_1()))
         log(json.dumps(time_q4x("q4_k")))
@@ -1090,6 +1205,15 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_extras:
         line["torch_reference_rates"] = torch_reference_rates()
+        log("measured ceilings ...")
+        ceil = measured_ceilings()
+        line["ceilings"] = ceil
+        for r in (line["roofline"], line["roofline_gemv"]):
+            r["frac_of_measured_read"] = r["achieved"] / ceil["read_GBps"]
+        if "stack" in line:
+            for k in ("M1", "M1_two_launch", "M8"):
+                rr = line["stack"][k]["roofline"]
+                rr["frac_of_measured_read"] = rr["achieved"] / ceil["read_GBps"]
     if not args.no_gemm:
         log("prefill gemm ...")
         g = {f"M{M}": time_gemm(M) for M in (2048, 256)}
@@ -1104,6 +1228,10 @@ def main():
                                           note="algorithmic flops 2*M*N*K; the hi/lo split issues twice "
                                                "that on the matrix cores"),
                             runs=g, vendor_fp16_gemm=torch_fp16_gemm_rate())
+        if "ceilings" in line:
+            rg = line["gemm"]["roofline"]
+            rg["mfma_issued_TFLOPs"] = 2.0 * g2["TFLOPs"]
+            rg["frac_of_measured_mfma_random"] = 2.0 * g2["TFLOPs"] / line["ceilings"]["mfma_fp16_random_TFLOPs"]
     if not args.no_extras:
         log("extras ...")
         line["extras"] = time_extras()

@@ -28,7 +28,7 @@ NVQ_PATH_GEMM = 1
 NVQ_PATH_GEMV_DOT4 = 2
 NVQ_GEMV_MAX_M = 15
 
-# Every symbol include/nvq.h declares.
+# Every symbol include/nvq.h and include/nvq_probe.h declare.
 EXPORTS = (
     "nvq_nvfp4_weight_bytes", "nvq_q4_1_weight_bytes", "nvq_q4_k_weight_bytes", "nvq_iq4_xs_weight_bytes",
     "nvq_gemm_workspace_bytes",
@@ -38,6 +38,7 @@ EXPORTS = (
     "nvq_gemv_q4_k", "nvq_gemm_q4_k", "nvq_gemv_iq4_xs", "nvq_gemm_iq4_xs", "nvq_debug_isums",
     "nvq_debug_isums_iq4_xs",
     "nvq_status_str", "nvq_last_error",
+    "nvq_probe_read", "nvq_probe_gemv_loads", "nvq_probe_mfma",
 )
 
 
@@ -91,6 +92,9 @@ def lib() -> ctypes.CDLL:
             "nvq_debug_isums": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P, P, I64, I64, I64, P, P]),
             "nvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "nvq_last_error": (ctypes.c_char_p, []),
+            "nvq_probe_read": (ctypes.c_int, [P, SZ, ctypes.c_int, P, P]),
+            "nvq_probe_gemv_loads": (ctypes.c_int, [P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]),
+            "nvq_probe_mfma": (ctypes.c_int, [ctypes.c_int, I64, ctypes.c_int, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -484,3 +488,40 @@ def nvq_debug_isums(fmt: int, path: int, w, q, N: int, isums, stream=None) -> No
     _weights(w, nbytes, "w")
     _check(lib().nvq_debug_isums(int(fmt), int(path), _ptr(w), _ptr(q), M, N, K, _ptr(isums),
                                  _stream(stream, q)), "nvq_debug_isums")
+
+
+# ---------------------------------------------------------------------------
+# measurement probes (include/nvq_probe.h): ceilings, not part of the product path
+# ---------------------------------------------------------------------------
+
+def nvq_probe_read(src, blocks: int, sink, stream=None) -> None:
+    """Stream every byte of the device tensor ``src`` (size a multiple of 16) with
+    16-byte non-temporal loads over ``blocks`` blocks of 256 threads; ``sink``: int32
+    or uint32 device tensor of >= 4 * blocks elements."""
+    nbytes = src.numel() * src.element_size()
+    if sink.element_size() != 4 or sink.numel() < 4 * blocks:
+        raise ValueError("sink: 4-byte tensor of at least 4 * blocks elements required")
+    _check(lib().nvq_probe_read(_ptr(src), nbytes, int(blocks), _ptr(sink), _stream(stream, src)), "nvq_probe_read")
+
+
+def nvq_probe_gemv_loads(w, N: int, K: int, splits: int, waves: int, batch: int, sink, stream=None) -> None:
+    """The weight loads of the single-token decode GEMV over packed NVFP4 ``w`` (N x K)
+    and nothing else; ``sink``: 4-byte device tensor of >= waves * ceil(N/16) * splits
+    elements."""
+    _weights(w, nvq_nvfp4_weight_bytes(N, K), "w")
+    if sink.element_size() != 4 or sink.numel() < waves * ((N + 15) // 16) * splits:
+        raise ValueError("sink: 4-byte tensor of at least waves * ceil(N/16) * splits elements required")
+    _check(lib().nvq_probe_gemv_loads(_ptr(w), int(N), int(K), int(splits), int(waves), int(batch), _ptr(sink),
+                                      _stream(stream, w)), "nvq_probe_gemv_loads")
+
+
+def nvq_probe_mfma(blocks: int, iters: int, random_operands: bool, out, stream=None) -> None:
+    """Back-to-back v_mfma_f32_32x32x16_f16 on register operands; ``out``: float32
+    device tensor of >= 256 * blocks elements.  Flops per call:
+    blocks * 4 * 12 * iters * 32768."""
+    import torch
+
+    if out.dtype != torch.float32 or out.numel() < 256 * blocks:
+        raise ValueError("out: float32 tensor of at least 256 * blocks elements required")
+    _check(lib().nvq_probe_mfma(int(blocks), int(iters), 1 if random_operands else 0, _ptr(out), _stream(stream, out)),
+           "nvq_probe_mfma")

@@ -6,6 +6,7 @@
 // current device's architecture checked (gfx950 only; there is no other code
 // path) and the kernel enqueued on the caller's stream.
 #include "nvq.h"
+#include "nvq_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -498,6 +499,46 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   }
   g_err[0] = '\0';
   return NVQ_OK;
+}
+
+// ---- measurement probes (include/nvq_probe.h) ----
+
+nvq_status nvq_probe_read(const void* src, size_t bytes, int blocks, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(NVQ_ERR_NULL, "nvq_probe_read: NULL pointer");
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(NVQ_ERR_ALIGN, "nvq_probe_read: src must be 16-byte aligned, sink 4-byte");
+  if (bytes == 0 || bytes % 16 != 0 || bytes >= (size_t(1) << 46))
+    return fail(NVQ_ERR_SHAPE, "nvq_probe_read: bytes=%zu must be a positive multiple of 16", bytes);
+  if (blocks < 1 || blocks > 65536) return fail(NVQ_ERR_SHAPE, "nvq_probe_read: blocks=%d outside [1, 65536]", blocks);
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_probe_read(src, (int64_t)(bytes / 16), blocks, sink, (hipStream_t)stream), "probe_read");
+}
+
+nvq_status nvq_probe_gemv_loads(const void* w, int64_t N, int64_t K, int splits, int waves, int batch,
+                                uint32_t* sink, void* stream) {
+  if (!w || !sink) return fail(NVQ_ERR_NULL, "nvq_probe_gemv_loads: NULL pointer");
+  if (!aligned(w, 16) || !aligned(sink, 4))
+    return fail(NVQ_ERR_ALIGN, "nvq_probe_gemv_loads: w must be 16-byte aligned, sink 4-byte");
+  NVQ_TRY(check_dims(1, N, K, 64, 1, 1));
+  const int64_t nch = (K + 127) / 128;
+  if (splits < 1 || splits > 8 || splits > nch)
+    return fail(NVQ_ERR_RANGE, "nvq_probe_gemv_loads: splits=%d outside [1, min(8, %lld)]", splits, (long long)nch);
+  if ((waves != 4 && waves != 8 && waves != 16) || (batch != 3 && batch != 5))
+    return fail(NVQ_ERR_RANGE, "nvq_probe_gemv_loads: waves=%d, batch=%d not in {4, 8, 16} x {3, 5}", waves, batch);
+  if (((N + 15) / 16) * splits >= (int64_t(1) << 31))
+    return fail(NVQ_ERR_SHAPE, "nvq_probe_gemv_loads: grid too large");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_probe_gemv_loads(static_cast<const uint8_t*>(w), N, K, splits, waves, batch, sink,
+                                               (hipStream_t)stream), "probe_gemv_loads");
+}
+
+nvq_status nvq_probe_mfma(int blocks, int64_t iters, int random_operands, float* out, void* stream) {
+  if (!out) return fail(NVQ_ERR_NULL, "nvq_probe_mfma: NULL pointer");
+  if (!aligned(out, 4)) return fail(NVQ_ERR_ALIGN, "nvq_probe_mfma: out must be 4-byte aligned");
+  if (blocks < 1 || blocks > 65536) return fail(NVQ_ERR_SHAPE, "nvq_probe_mfma: blocks=%d outside [1, 65536]", blocks);
+  if (iters < 1 || iters > (int64_t(1) << 31)) return fail(NVQ_ERR_SHAPE, "nvq_probe_mfma: iters=%lld outside [1, 2^31]", (long long)iters);
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_probe_mfma(blocks, iters, random_operands, out, (hipStream_t)stream), "probe_mfma");
 }
 
 }  // extern "C"

@@ -89,4 +89,13 @@ hipError_t launch_gemm_iq4_xs(const uint8_t* w, const int8_t* table, const int8_
                               int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, float* workspace,
                               hipStream_t stream);
 
+// Measurement probes (probe.hip): a streaming read of n16 16-byte units over `blocks`
+// blocks of 256 threads (sink: 4 words per block); the decode GEMV's weight loads
+// alone for waves in {4, 8, 16}, batch in {3, 5} and `splits` blocks per tile (sink:
+// waves words per block); a register-only MFMA loop (out: 256 floats per block).
+hipError_t launch_probe_read(const void* src, int64_t n16, int blocks, uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_gemv_loads(const uint8_t* w, int64_t N, int64_t K, int splits, int waves, int batch,
+                                   uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_mfma(int blocks, int64_t iters, int random_operands, float* out, hipStream_t stream);
+
 }  // namespace nvq

@@ -14,12 +14,15 @@ import gemm_q8_act_amd as nvq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvq.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 def declared_symbols():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvq_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(nvq_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_binding_exports():
@@ -336,3 +339,34 @@ def test_status_strings():
                     (-4, "NVQ_ERR_ALIGN"), (-5, "NVQ_ERR_DEVICE"), (-6, "NVQ_ERR_HIP"),
                     (-7, "NVQ_ERR_WORKSPACE")]:
         assert nvq.status_str(s) == name
+
+
+# ---- measurement probes: every argument error is reported before any HIP call ----
+
+ERR_NULL, ERR_SHAPE, ERR_RANGE, ERR_ALIGN = -1, -2, -3, -4  # include/nvq.h
+
+
+def test_probe_rejects():
+    L = nvq.lib()
+    P = ctypes.c_void_p
+    buf = P(16 * 1024)  # never dereferenced: validation fails first
+    sink = P(4096)
+    # read: NULL, alignment, size, block count
+    assert L.nvq_probe_read(None, 1024, 4, sink, None) == ERR_NULL
+    assert L.nvq_probe_read(P(16 * 1024 + 8), 1024, 4, sink, None) == ERR_ALIGN
+    assert L.nvq_probe_read(buf, 1000, 4, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_read(buf, 0, 4, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_read(buf, 1024, 0, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_read(buf, 1024, 65537, sink, None) == ERR_SHAPE
+    # gemv loads: shape, splits, launch shape
+    assert L.nvq_probe_gemv_loads(buf, 64, 100, 1, 4, 5, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_gemv_loads(buf, 64, 256, 3, 4, 5, sink, None) == ERR_RANGE  # 2 chunks < 3 splits
+    assert L.nvq_probe_gemv_loads(buf, 64, 5120, 9, 4, 5, sink, None) == ERR_RANGE
+    assert L.nvq_probe_gemv_loads(buf, 64, 5120, 1, 6, 5, sink, None) == ERR_RANGE
+    assert L.nvq_probe_gemv_loads(buf, 64, 5120, 1, 8, 4, sink, None) == ERR_RANGE
+    assert L.nvq_probe_gemv_loads(None, 64, 5120, 1, 8, 5, sink, None) == ERR_NULL
+    # mfma: blocks, iterations
+    assert L.nvq_probe_mfma(0, 10, 0, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_mfma(8, 0, 0, sink, None) == ERR_SHAPE
+    assert L.nvq_probe_mfma(8, 10, 0, None, None) == ERR_NULL
+    assert "blocks" in nvq.last_error() or "NULL" in nvq.last_error()
