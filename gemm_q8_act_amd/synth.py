@@ -47,6 +47,8 @@ WORKLOADS = {
     "q4_1": dict(Ms=(1, 512), N=4096, K=4096),
     "q4_k": dict(Ms=(1, 512), N=4096, K=4096),
     "iq4_xs": dict(Ms=(1, 512), N=4096, K=4096),
+    "q5_k": dict(Ms=(1, 512), N=4096, K=4096),
+    "q6_k": dict(Ms=(1, 512), N=4096, K=4096),
     "stack": dict(Ms=(1, 8), layers=64, mats=LAYER),
     "moe": dict(M=1, experts=256, active=6, N=2048, K=2048),
 }
@@ -106,6 +108,30 @@ def q4_k_weights(N: int, K: int, seed: int):
     return qw, sc, mn, d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16)
 
 
+def q5_k_weights(N: int, K: int, seed: int):
+    """Returns (qw uint8 [N, K] in 0..31, sc uint8 [N, K/32] in 0..63, mn uint8 [N, K/32]
+    in 0..63, d uint16 [N, K/256], dmin uint16 [N, K/256])."""
+    assert K % 256 == 0
+    r = rng(seed)
+    qw = r.integers(0, 32, size=(N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, size=(N, K // 32), dtype=np.uint8)
+    d = r.uniform(1e-5, 1.5e-4, size=(N, K // 256)).astype(np.float32)
+    dmin = r.uniform(0.0, 1.6e-3, size=(N, K // 256)).astype(np.float32)
+    return qw, sc, mn, d.astype(np.float16).view(np.uint16), dmin.astype(np.float16).view(np.uint16)
+
+
+def q6_k_weights(N: int, K: int, seed: int):
+    """Returns (qw uint8 [N, K] in 0..63 (used as qw - 32), sc int8 [N, K/16] in
+    -128..127, d uint16 [N, K/256])."""
+    assert K % 256 == 0
+    r = rng(seed)
+    qw = r.integers(0, 64, size=(N, K), dtype=np.uint8)
+    sc = r.integers(-128, 128, size=(N, K // 16), dtype=np.int16).astype(np.int8)
+    d = r.uniform(2e-6, 3e-5, size=(N, K // 256)).astype(np.float32)
+    return qw, sc, d.astype(np.float16).view(np.uint16)
+
+
 def iq4_xs_weights(N: int, K: int, seed: int):
     """Returns (qw uint8 [N, K] in 0..15, ls uint8 [N, K/32] in 0..63, d uint16 [N, K/256],
     table int8 [16])."""
@@ -127,6 +153,6 @@ def expert_ids(M: int, A: int, E: int, seed: int) -> np.ndarray:
 def seed_for(workload: str, tensor: str, index: int = 0) -> int:
     """Fixed, documented seed per (workload, tensor, index)."""
     base = {"gemv_small": 100, "layer": 200, "prefill": 300, "q4_1": 400, "stack": 500,
-            "moe": 600, "q4_k": 700, "iq4_xs": 800, "test": 900}[workload]
+            "moe": 600, "q4_k": 700, "iq4_xs": 800, "test": 900, "q5_k": 1000, "q6_k": 1100}[workload]
     tag = sum((i + 1) * ord(ch) for i, ch in enumerate(tensor)) % 997
     return base * 1_000_003 + tag * 1009 + index

@@ -1,4 +1,4 @@
-"""Plain-C oracle for the NVFP4, Q4_1, Q4_K and IQ4_XS x Q8_0 quantized matrix product.
+"""Plain-C oracle for the NVFP4, Q4_1, Q4_K, Q5_K, Q6_K and IQ4_XS x Q8_0 quantized matrix product.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import this module.  The GPU library never calls
@@ -11,6 +11,9 @@ library's packed layout.  It works on the logical representation:
   (binary16 bits of d and m).
 * Q4_K weights: ``qw`` uint8 [N, K] (0..15), ``sc``/``mn`` uint8 [N, K/32] (6-bit
   sub-block scales and mins), ``d``/``dmin`` uint16 [N, K/256] (binary16 bits).
+* Q5_K weights: as Q4_K with ``qw`` 0..31.
+* Q6_K weights: ``qw`` uint8 [N, K] (0..63, used as qw - 32), ``sc`` int8 [N, K/16],
+  ``d`` uint16 [N, K/256].
 * IQ4_XS weights: ``qw`` uint8 [N, K] (0..15, indices into ``table`` int8 [16]),
   ``ls`` uint8 [N, K/32] (6-bit sub-block scales, used as ls - 32), ``d`` uint16
   [N, K/256].
@@ -88,6 +91,12 @@ class Oracle:
         lib.nvqo_matmul_iq4_xs.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         lib.nvqo_matmul_q4_k.restype = None
         lib.nvqo_matmul_q4_k.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+        lib.nvqo_matmul_q5_k.restype = None
+        lib.nvqo_matmul_q5_k.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
+        lib.nvqo_isums_q6_k.restype = None
+        lib.nvqo_isums_q6_k.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+        lib.nvqo_matmul_q6_k.restype = None
+        lib.nvqo_matmul_q6_k.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _P]
         self.lib = lib
         self.path = path
 
@@ -208,6 +217,58 @@ class Oracle:
         awa = np.empty((M, nc), np.float64)
         self.lib.nvqo_matmul_q4_k(_ptr(qw), _ptr(sc), _ptr(mn), _ptr(d), _ptr(dmin), _ptr(q), _ptr(d16),
                                   M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
+        return y, awa
+
+    # -- Q5_K --------------------------------------------------------------------
+    def isums_q5_k(self, qw: np.ndarray, q: np.ndarray) -> np.ndarray:
+        """Per-16 sums of the unsigned 5-bit codes times activation codes."""
+        return self.isums_q4_1(qw, q)
+
+    def matmul_q5_k(self, qw, sc, mn, d, dmin, q, d16, cols=None):
+        qw = np.ascontiguousarray(qw, np.uint8)
+        sc = np.ascontiguousarray(sc, np.uint8)
+        mn = np.ascontiguousarray(mn, np.uint8)
+        d = np.ascontiguousarray(d, np.uint16)
+        dmin = np.ascontiguousarray(dmin, np.uint16)
+        q = np.ascontiguousarray(q, np.int8)
+        d16 = np.ascontiguousarray(d16, np.uint16)
+        N, K = qw.shape
+        M = q.shape[0]
+        assert K % 256 == 0 and sc.shape == (N, K // 32) and d.shape == (N, K // 256)
+        c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+        nc = N if c is None else len(c)
+        y = np.empty((M, nc), np.float32)
+        awa = np.empty((M, nc), np.float64)
+        self.lib.nvqo_matmul_q5_k(_ptr(qw), _ptr(sc), _ptr(mn), _ptr(d), _ptr(dmin), _ptr(q), _ptr(d16),
+                                  M, N, K, _ptr(c), nc, _ptr(y), _ptr(awa))
+        return y, awa
+
+    # -- Q6_K --------------------------------------------------------------------
+    def isums_q6_k(self, qw: np.ndarray, q: np.ndarray) -> np.ndarray:
+        """Per-16 sums of (code - 32) times activation codes."""
+        qw = np.ascontiguousarray(qw, np.uint8)
+        q = np.ascontiguousarray(q, np.int8)
+        N, K = qw.shape
+        M = q.shape[0]
+        out = np.empty((M, N, K // 16), np.int32)
+        self.lib.nvqo_isums_q6_k(_ptr(qw), _ptr(q), M, N, K, _ptr(out))
+        return out
+
+    def matmul_q6_k(self, qw, sc, d, q, d16, cols=None):
+        qw = np.ascontiguousarray(qw, np.uint8)
+        sc = np.ascontiguousarray(sc, np.int8)
+        d = np.ascontiguousarray(d, np.uint16)
+        q = np.ascontiguousarray(q, np.int8)
+        d16 = np.ascontiguousarray(d16, np.uint16)
+        N, K = qw.shape
+        M = q.shape[0]
+        assert K % 256 == 0 and sc.shape == (N, K // 16) and d.shape == (N, K // 256)
+        c = None if cols is None else np.ascontiguousarray(cols, np.int64)
+        nc = N if c is None else len(c)
+        y = np.empty((M, nc), np.float32)
+        awa = np.empty((M, nc), np.float64)
+        self.lib.nvqo_matmul_q6_k(_ptr(qw), _ptr(sc), _ptr(d), _ptr(q), _ptr(d16), M, N, K,
+                                  _ptr(c), nc, _ptr(y), _ptr(awa))
         return y, awa
 
     # -- IQ4_XS ------------------------------------------------------------------

@@ -369,6 +369,113 @@ void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Q5_K and Q6_K x Q8_0                                                       */
+/* ------------------------------------------------------------------------- */
+
+/* Q5_K ([HANDOFF] section 1 names "Q4_K/Q5_K/Q6_K" among the patch's formats; the
+ * pages give neither its block nor its rule).  Reading (the GGML format's, known from
+ * outside the pages): Q4_K's super-block of 256 weights with binary16 d and dmin and
+ * per 32-weight sub-block j a 6-bit scale sc_j and min mn_j, but 5-bit codes c:
+ *     weight = d * sc_j * c - dmin * mn_j,   c in 0..31,
+ * 2 + 2 + 12 + 32 (the codes' fifth bits) + 128 = 176 bytes.  The per-16 integer sums
+ * are sum c * q, nvqo_isums_q4_1 applied to the 5-bit codes. */
+static void dequant_q5_k_row(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                             const uint16_t* d, const uint16_t* dmin, int64_t K, double* w)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        double scale = nvqo_f16_to_f64(d[k / 256]) * (double)sc[k / 32];
+        double offset = nvqo_f16_to_f64(dmin[k / 256]) * (double)mn[k / 32];
+        w[k] = scale * (double)qw[k] - offset;
+    }
+}
+
+void nvqo_matmul_q5_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                      const uint16_t* d, const uint16_t* dmin,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa)
+{
+    if (!cols)
+        ncols = N;
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!w || !a) {
+        free(w);
+        free(a);
+        return;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        dequant_q8_0_row(q + m * K, d16 + m * (K / 32), K, a + m * K);
+    for (int64_t jc = 0; jc < ncols; ++jc) {
+        int64_t n = cols ? cols[jc] : jc;
+        dequant_q5_k_row(qw + n * K, sc + n * (K / 32), mn + n * (K / 32), d + n * (K / 256),
+                         dmin + n * (K / 256), K, w);
+        for (int64_t m = 0; m < M; ++m)
+            dot_rows(w, a + m * K, K, &y[m * ncols + jc],
+                     abs_wa ? &abs_wa[m * ncols + jc] : NULL);
+    }
+    free(w);
+    free(a);
+}
+
+/* Q6_K (named beside Q5_K; no block or rule in the pages).  Reading (the GGML
+ * format's): a super-block of 256 weights holds a binary16 scale d and one signed
+ * 8-bit scale sc_s per 16 weights; 6-bit codes c are stored with an offset of 32:
+ *     weight = d * sc_s * (c - 32),   c in 0..63,   s = k / 16,
+ * 128 (low four bits) + 64 (high two bits) + 16 + 2 = 210 bytes.  The per-16 integer
+ * sums are sum (c - 32) * q. */
+void nvqo_isums_q6_k(const uint8_t* qw, const int8_t* q,
+                     int64_t M, int64_t N, int64_t K, int32_t* isums)
+{
+    int64_t ns = K / 16;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t s = 0; s < ns; ++s) {
+                int32_t acc = 0;
+                for (int j = 0; j < 16; ++j) {
+                    int64_t k = 16 * s + j;
+                    acc += ((int32_t)qw[n * K + k] - 32) * (int32_t)q[m * K + k];
+                }
+                isums[(m * N + n) * ns + s] = acc;
+            }
+}
+
+static void dequant_q6_k_row(const uint8_t* qw, const int8_t* sc, const uint16_t* d, int64_t K, double* w)
+{
+    for (int64_t k = 0; k < K; ++k)
+        w[k] = nvqo_f16_to_f64(d[k / 256]) * (double)sc[k / 16] * (double)((int)qw[k] - 32);
+}
+
+void nvqo_matmul_q6_k(const uint8_t* qw, const int8_t* sc, const uint16_t* d,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa)
+{
+    if (!cols)
+        ncols = N;
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    if (!w || !a) {
+        free(w);
+        free(a);
+        return;
+    }
+    for (int64_t m = 0; m < M; ++m)
+        dequant_q8_0_row(q + m * K, d16 + m * (K / 32), K, a + m * K);
+    for (int64_t jc = 0; jc < ncols; ++jc) {
+        int64_t n = cols ? cols[jc] : jc;
+        dequant_q6_k_row(qw + n * K, sc + n * (K / 16), d + n * (K / 256), K, w);
+        for (int64_t m = 0; m < M; ++m)
+            dot_rows(w, a + m * K, K, &y[m * ncols + jc],
+                     abs_wa ? &abs_wa[m * ncols + jc] : NULL);
+    }
+    free(w);
+    free(a);
+}
+
+/* ------------------------------------------------------------------------- */
 /* IQ4_XS x Q8_0                                                              */
 /* ------------------------------------------------------------------------- */
 

@@ -114,6 +114,30 @@ void nvqo_matmul_q4_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
                       const int64_t* cols, int64_t ncols,
                       float* y, double* abs_wa);
 
+/* ---- Q5_K and Q6_K weights -------------------------------------------------- */
+
+/* Q5_K: qw [N][K] one byte per weight (0..31); sc, mn [N][K/32] 6-bit sub-block scales
+ * and mins (0..63); d, dmin [N][K/256] fp16 bits; W = d*sc*qw - dmin*mn.  K % 256 == 0.
+ * Integer sums: nvqo_isums_q4_1 (sum qw * q). */
+void nvqo_matmul_q5_k(const uint8_t* qw, const uint8_t* sc, const uint8_t* mn,
+                      const uint16_t* d, const uint16_t* dmin,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa);
+
+/* Q6_K: qw [N][K] one byte per weight (0..63); sc [N][K/16] int8 scales; d [N][K/256]
+ * fp16 bits; W = d * sc * (qw - 32).  K % 256 == 0.  isums [M][N][K/16] = sum over 16
+ * of (qw - 32) * q. */
+void nvqo_isums_q6_k(const uint8_t* qw, const int8_t* q,
+                     int64_t M, int64_t N, int64_t K, int32_t* isums);
+
+void nvqo_matmul_q6_k(const uint8_t* qw, const int8_t* sc, const uint16_t* d,
+                      const int8_t* q, const uint16_t* d16,
+                      int64_t M, int64_t N, int64_t K,
+                      const int64_t* cols, int64_t ncols,
+                      float* y, double* abs_wa);
+
 /* ---- IQ4_XS weights --------------------------------------------------------- */
 
 /* qw [N][K] one byte per weight (0..15, an index into table); table [16] int8 values;

@@ -399,4 +399,67 @@ def battery(o) -> list[tuple[str, bool, str]]:
     yp, _ = o.matmul_iq4_xs(np.argsort(perm).astype(np.uint8)[qw], ls, dd, table[perm], q, d16)
     ok17 &= bool((yp == y).all())
     pin("iq4_xs_bruteforce_q4_1_reduction_relabel", ok17)
+
+    # P18: Q5_K (no block or rule in the pages: the GGML format's reading, 256-weight
+    # super-blocks) -- per-16 sums and y by brute force on its definition, and the split
+    # of each 5-bit code c = c_lo + 16 c_hi: the product equals the Q4_K product of the
+    # low nibbles plus that of the fifth bits with scale 16 d and no min (the fifth bit
+    # weighs 16, the min is applied once)
+    SB = 256
+    r = _rng(20)
+    M, N, K = 3, 4, 2 * SB
+    qw = r.integers(0, 32, (N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    dd = r.uniform(1e-5, 1.5e-4, (N, K // SB)).astype(np.float16).view(np.uint16)
+    dm = r.uniform(0.0, 1.6e-3, (N, K // SB)).astype(np.float16).view(np.uint16)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    q, d16, bs = o.quantize_q8_0(x)
+    isum_ref = (q.astype(np.int64)[:, None, :] * qw.astype(np.int64)[None]).reshape(M, N, K // 16, 16).sum(axis=3)
+    ok18 = bool((o.isums_q5_k(qw, q) == isum_ref).all())
+    Wd = (np.repeat(f16_bits_to_f64(dd), SB, axis=1) * np.repeat(sc.astype(np.float64), 32, axis=1) * qw
+          - np.repeat(f16_bits_to_f64(dm), SB, axis=1) * np.repeat(mn.astype(np.float64), 32, axis=1))
+    Ad = np.repeat(f16_bits_to_f64(d16), 32, axis=1) * q.astype(np.float64)
+    yref = Ad @ Wd.T
+    y, awa = o.matmul_q5_k(qw, sc, mn, dd, dm, q, d16)
+    ok18 &= bool((np.abs(y.astype(np.float64) - yref) <= np.spacing(np.abs(yref).astype(np.float32))).all())
+    ok18 &= bool(np.allclose(awa, np.abs(Ad) @ np.abs(Wd).T, rtol=1e-12, atol=0))
+    d16x = (f16_bits_to_f64(dd) * 16.0).astype(np.float16).view(np.uint16)    # exact: a power of two
+    ylo, _ = o.matmul_q4_k(qw & 15, sc, mn, dd, dm, q, d16)
+    yhi, _ = o.matmul_q4_k(qw >> 4, sc, np.zeros_like(mn), d16x, np.zeros_like(dm), q, d16)
+    ysplit = ylo.astype(np.float64) + yhi.astype(np.float64)
+    ok18 &= bool((np.abs(y.astype(np.float64) - ysplit) <= 4 * np.spacing(np.abs(awa).astype(np.float32))).all())
+    pin("q5_k_bruteforce_and_fifth_bit_split", ok18)
+
+    # P19: Q6_K (the GGML format's reading) -- per-16 sums and y by brute force on its
+    # definition (one signed scale per 16 weights, codes offset by 32), the reduction to
+    # Q4_K when every code lies in 32..47 and the two 16-scales of each 32-block are equal
+    # (codes c - 32, mins 0), and the sign symmetry c -> 64 - c, which negates y exactly
+    r = _rng(21)
+    M, N, K = 3, 4, 2 * SB
+    qw = r.integers(0, 64, (N, K), dtype=np.uint8)
+    sc = r.integers(-128, 128, (N, K // 16)).astype(np.int8)
+    dd = r.uniform(2e-6, 3e-5, (N, K // SB)).astype(np.float16).view(np.uint16)
+    x = r.standard_normal((M, K)).astype(np.float32)
+    q, d16, bs = o.quantize_q8_0(x)
+    Cq = qw.astype(np.int64) - 32
+    isum_ref = (q.astype(np.int64)[:, None, :] * Cq[None]).reshape(M, N, K // 16, 16).sum(axis=3)
+    ok19 = bool((o.isums_q6_k(qw, q) == isum_ref).all())
+    Wd = (np.repeat(f16_bits_to_f64(dd), SB, axis=1) * np.repeat(sc.astype(np.float64), 16, axis=1)
+          * Cq.astype(np.float64))
+    Ad = np.repeat(f16_bits_to_f64(d16), 32, axis=1) * q.astype(np.float64)
+    yref = Ad @ Wd.T
+    y, awa = o.matmul_q6_k(qw, sc, dd, q, d16)
+    ok19 &= bool((np.abs(y.astype(np.float64) - yref) <= np.spacing(np.abs(yref).astype(np.float32))).all())
+    ok19 &= bool(np.allclose(awa, np.abs(Ad) @ np.abs(Wd).T, rtol=1e-12, atol=0))
+    c4 = r.integers(32, 48, (N, K), dtype=np.uint8)
+    s32 = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    y6, _ = o.matmul_q6_k(c4, np.repeat(s32, 2, axis=1).astype(np.int8), dd, q, d16)
+    y4, _ = o.matmul_q4_k(c4 - 32, s32, np.zeros_like(s32), dd, np.zeros_like(dd), q, d16)
+    ok19 &= bool((y6 == y4).all())
+    c1 = r.integers(1, 64, (N, K), dtype=np.uint8)
+    yp, _ = o.matmul_q6_k(c1, sc, dd, q, d16)
+    yn, _ = o.matmul_q6_k((64 - c1.astype(np.int32)).astype(np.uint8), sc, dd, q, d16)
+    ok19 &= bool((yn == -yp).all())
+    pin("q6_k_bruteforce_q4_k_reduction_sign_symmetry", ok19)
     return out

@@ -35,6 +35,13 @@ MUTANTS = {
                            "acc += (int32_t)table[qw[n * K + k] ^ 1] * (int32_t)q[m * K + k];"),
     "iq4_xs_scale_offset": ("(double)((int)ls[k / 32] - 32)", "(double)((int)ls[k / 32] - 31)"),
     "iq4_xs_code_not_looked_up": ("* (double)table[qw[k]];", "* (double)qw[k];"),
+    "q5_k_fifth_bit_dropped": ("w[k] = scale * (double)qw[k] - offset;", "w[k] = scale * (double)(qw[k] & 15) - offset;"),
+    "q5_k_min_per_super_block": ("double offset = nvqo_f16_to_f64(dmin[k / 256]) * (double)mn[k / 32];",
+                                 "double offset = nvqo_f16_to_f64(dmin[k / 256]) * (double)mn[(k / 256) * 8];"),
+    "q6_k_offset_31": ("* (double)((int)qw[k] - 32);", "* (double)((int)qw[k] - 31);"),
+    "q6_k_scale_per_32": ("(double)sc[k / 16] * (double)((int)qw[k] - 32)", "(double)sc[k / 32] * (double)((int)qw[k] - 32)"),
+    "q6_k_isums_unsigned": ("acc += ((int32_t)qw[n * K + k] - 32) * (int32_t)q[m * K + k];",
+                            "acc += (int32_t)qw[n * K + k] * (int32_t)q[m * K + k];"),
     "transposed_product": ("dot_rows(w, a + m * K, K, &y[m * ncols + j],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed",
                            "dot_rows(w, a + m * K, K, &y[j * M + m],\n                     abs_wa ? &abs_wa[m * ncols + j] : NULL);\n    }\n    free(w);\n    free(a);\n}\n\n/* Expert-routed"),
 }
