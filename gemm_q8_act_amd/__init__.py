@@ -23,6 +23,8 @@ NVQ_FMT_NVFP4 = 0
 NVQ_FMT_Q4_1 = 1
 NVQ_FMT_Q4_K = 2
 NVQ_FMT_IQ4_XS = 3
+NVQ_FMT_Q5_K = 4
+NVQ_FMT_Q6_K = 5
 NVQ_PATH_GEMV = 0
 NVQ_PATH_GEMM = 1
 NVQ_PATH_GEMV_DOT4 = 2
@@ -37,6 +39,8 @@ EXPORTS = (
     "nvq_gemv_nvfp4_routed", "nvq_gemm_nvfp4", "nvq_gemm_nvfp4_noalloc", "nvq_gemv_q4_1", "nvq_gemm_q4_1",
     "nvq_gemv_q4_k", "nvq_gemm_q4_k", "nvq_gemv_iq4_xs", "nvq_gemm_iq4_xs", "nvq_debug_isums",
     "nvq_debug_isums_iq4_xs",
+    "nvq_q5_k_weight_bytes", "nvq_q6_k_weight_bytes", "nvq_pack_q5_k", "nvq_pack_q6_k",
+    "nvq_gemv_q5_k", "nvq_gemm_q5_k", "nvq_gemv_q6_k", "nvq_gemm_q6_k",
     "nvq_status_str", "nvq_last_error",
     "nvq_probe_read", "nvq_probe_gemv_loads", "nvq_probe_mfma",
 )
@@ -92,6 +96,14 @@ def lib() -> ctypes.CDLL:
             "nvq_debug_isums": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, P, P, I64, I64, I64, P, P]),
             "nvq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
             "nvq_last_error": (ctypes.c_char_p, []),
+            "nvq_q5_k_weight_bytes": (SZ, [I64, I64]),
+            "nvq_q6_k_weight_bytes": (SZ, [I64, I64]),
+            "nvq_pack_q5_k": (ctypes.c_int, [P, P, P, P, P, I64, I64, P]),
+            "nvq_pack_q6_k": (ctypes.c_int, [P, P, P, I64, I64, P]),
+            "nvq_gemv_q5_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P]),
+            "nvq_gemm_q5_k": (ctypes.c_int, [P, P, P, P, I64, I64, I64, P, P, SZ, P]),
+            "nvq_gemv_q6_k": (ctypes.c_int, [P, P, P, I64, I64, I64, P, P]),
+            "nvq_gemm_q6_k": (ctypes.c_int, [P, P, P, I64, I64, I64, P, P, SZ, P]),
             "nvq_probe_read": (ctypes.c_int, [P, SZ, ctypes.c_int, P, P]),
             "nvq_probe_gemv_loads": (ctypes.c_int, [P, I64, I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]),
             "nvq_probe_mfma": (ctypes.c_int, [ctypes.c_int, I64, ctypes.c_int, P, P]),
@@ -409,6 +421,107 @@ def nvq_gemm_q4_k(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().nvq_gemm_q4_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
                                _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q4_k")
+
+
+def nvq_q5_k_weight_bytes(N: int, K: int) -> int:
+    return int(lib().nvq_q5_k_weight_bytes(N, K))
+
+
+def nvq_q6_k_weight_bytes(N: int, K: int) -> int:
+    return int(lib().nvq_q6_k_weight_bytes(N, K))
+
+
+def nvq_pack_q5_k(q: np.ndarray, sc: np.ndarray, mn: np.ndarray, d_f16: np.ndarray,
+                  dmin_f16: np.ndarray) -> np.ndarray:
+    """q uint8 [N, K] (0..31), sc / mn uint8 [N, K/32] (0..63), d_f16 / dmin_f16 uint16
+    [N, K/256] -> packed uint8 buffer."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.uint8)
+    mn = np.ascontiguousarray(mn, dtype=np.uint8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.uint16)
+    dmin_f16 = np.ascontiguousarray(dmin_f16, dtype=np.uint16)
+    N, K = q.shape
+    if sc.shape != (N, K // 32) or mn.shape != (N, K // 32):
+        raise ValueError("sc and mn must be [N, K/32]")
+    if d_f16.shape != (N, K // 256) or dmin_f16.shape != (N, K // 256):
+        raise ValueError("d_f16 and dmin_f16 must be [N, K/256]")
+    nbytes = nvq_q5_k_weight_bytes(N, K)
+    out = np.empty(max(nbytes, 1), np.uint8)
+    _check(lib().nvq_pack_q5_k(*(a.ctypes.data_as(ctypes.c_void_p) for a in (q, sc, mn, d_f16, dmin_f16)), N, K,
+                               out.ctypes.data_as(ctypes.c_void_p)), "nvq_pack_q5_k")
+    return out[:nbytes]
+
+
+def nvq_pack_q6_k(q: np.ndarray, sc: np.ndarray, d_f16: np.ndarray) -> np.ndarray:
+    """q uint8 [N, K] (0..63), sc int8 [N, K/16], d_f16 uint16 [N, K/256] -> packed uint8
+    buffer."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.int8)
+    d_f16 = np.ascontiguousarray(d_f16, dtype=np.uint16)
+    N, K = q.shape
+    if sc.shape != (N, K // 16) or d_f16.shape != (N, K // 256):
+        raise ValueError("sc must be [N, K/16] and d_f16 [N, K/256]")
+    nbytes = nvq_q6_k_weight_bytes(N, K)
+    out = np.empty(max(nbytes, 1), np.uint8)
+    _check(lib().nvq_pack_q6_k(*(a.ctypes.data_as(ctypes.c_void_p) for a in (q, sc, d_f16)), N, K,
+                               out.ctypes.data_as(ctypes.c_void_p)), "nvq_pack_q6_k")
+    return out[:nbytes]
+
+
+def nvq_gemv_q5_k(w, q, d_f16, bsum16, y, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _need(bsum16, torch.int16, (M, K // 16), "bsum16")
+    _weights(w, nvq_q5_k_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_q5_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
+                               _stream(stream, y)), "nvq_gemv_q5_k")
+
+
+def nvq_gemm_q5_k(w, q, d_f16, bsum16, y, workspace=None, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _need(bsum16, torch.int16, (M, K // 16), "bsum16")
+    _weights(w, nvq_q5_k_weight_bytes(N, K), "w")
+    if workspace is None:
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_Q5_K, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvq_gemm_q5_k(_ptr(w), _ptr(q), _ptr(d_f16), _ptr(bsum16), M, N, K, _ptr(y),
+                               _ptr(workspace), ws_bytes, _stream(stream, y)), "nvq_gemm_q5_k")
+
+
+def nvq_gemv_q6_k(w, q, d_f16, y, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_q6_k_weight_bytes(N, K), "w")
+    _check(lib().nvq_gemv_q6_k(_ptr(w), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y), _stream(stream, y)),
+           "nvq_gemv_q6_k")
+
+
+def nvq_gemm_q6_k(w, q, d_f16, y, workspace=None, stream=None) -> None:
+    import torch
+
+    M, K = _acts(q, d_f16)
+    N = y.shape[1]
+    _need(y, torch.float32, (M, N), "y")
+    _weights(w, nvq_q6_k_weight_bytes(N, K), "w")
+    if workspace is None:
+        need = lib().nvq_gemm_workspace_bytes(NVQ_FMT_Q6_K, M, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=y.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvq_gemm_q6_k(_ptr(w), _ptr(q), _ptr(d_f16), M, N, K, _ptr(y), _ptr(workspace), ws_bytes,
+                               _stream(stream, y)), "nvq_gemm_q6_k")
 
 
 def nvq_pack_iq4_xs(q: np.ndarray, ls: np.ndarray, d_f16: np.ndarray) -> np.ndarray:

@@ -117,6 +117,16 @@ size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K) {
   return (size_t)(N * K / 2 + N * (K / 256) * 16);
 }
 
+size_t nvq_q5_k_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
+  return (size_t)(N * (K / 256) * 176);
+}
+
+size_t nvq_q6_k_weight_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
+  return (size_t)(N * (K / 256) * 210);
+}
+
 size_t nvq_iq4_xs_weight_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < 256 || K % 256 != 0 || N >= kMaxDim || K >= kMaxDim || N > kMaxElems / K) return 0;
   return (size_t)(N * K / 2 + N * (K / 256) * 8);
@@ -128,7 +138,8 @@ size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
   if (fmt == NVQ_FMT_NVFP4) return nvq::gemm_nvfp4_workspace(M, N, K);
   if (fmt == NVQ_FMT_Q4_1) return nvq::gemm_q4_1_workspace(M, N, K);
-  if ((fmt == NVQ_FMT_Q4_K || fmt == NVQ_FMT_IQ4_XS) && K % 256 == 0) return nvq::gemm_q4_k_workspace(M, N, K);
+  if ((fmt == NVQ_FMT_Q4_K || fmt == NVQ_FMT_IQ4_XS || fmt == NVQ_FMT_Q5_K || fmt == NVQ_FMT_Q6_K) && K % 256 == 0)
+    return nvq::gemm_q4_k_workspace(M, N, K);
   return 0;
 }
 
@@ -167,17 +178,62 @@ nvq_status nvq_pack_nvfp4(const uint8_t* codes, const uint8_t* ue4m3, int64_t N,
   return NVQ_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The packers check every input before writing any byte of dst.
+nvq_status check_max(const uint8_t* v, int64_t n, unsigned maxv, const char* who, const char* what) {
+  for (int64_t i = 0; i < n; ++i)
+    if (v[i] > maxv) return fail(NVQ_ERR_RANGE, "%s: %s > %u at index %lld", who, what, maxv, (long long)i);
+  return NVQ_OK;
+}
+
+// codes (their low four bits) two per byte: code 2i in bits 0..3, 2i+1 in bits 4..7
+void pack_nibbles(const uint8_t* q, int64_t n, uint8_t* dst) {
+  for (int64_t i = 0; i < n / 2; ++i) dst[i] = (uint8_t)((q[2 * i] & 15) | ((q[2 * i + 1] & 15) << 4));
+}
+
+// 16-byte K-quant header per 256 weights: d, dmin, then sc_0..7, mn_0..7 as 6-bit
+// fields of a little-endian 96-bit number
+void pack_kq_headers(const uint8_t* sc, const uint8_t* mn, const uint16_t* d, const uint16_t* dmin, int64_t nsb,
+                     uint8_t* dst) {
+  for (int64_t i = 0; i < nsb; ++i) {
+    uint8_t h[16] = {};
+    std::memcpy(h, &d[i], 2);
+    std::memcpy(h + 2, &dmin[i], 2);
+    for (int f = 0; f < 16; ++f) {
+      const uint8_t v = f < 8 ? sc[8 * i + f] : mn[8 * i + f - 8];
+      for (int bit = 0; bit < 6; ++bit)
+        if ((v >> bit) & 1) h[4 + (6 * f + bit) / 8] |= (uint8_t)(1u << ((6 * f + bit) % 8));
+    }
+    std::memcpy(dst + 16 * i, h, 16);
+  }
+}
+
+// bit `bit` of 32 codes as one word: even codes k = 2e at bit e, odd codes k = 2e + 1 at
+// bit 16 + e (the arrangement the kernels' even / odd code planes read)
+uint32_t pack_code_bits(const uint8_t* q32, int bit) {
+  uint32_t w = 0;
+  for (int e = 0; e < 16; ++e) {
+    w |= (uint32_t)((q32[2 * e] >> bit) & 1) << e;
+    w |= (uint32_t)((q32[2 * e + 1] >> bit) & 1) << (16 + e);
+  }
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
 nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t* m_f16,
                          int64_t N, int64_t K, void* dst_host) {
   if (!q || !d_f16 || !m_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_q4_1: NULL pointer");
   if (nvq_q4_1_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_q4_1: N=%lld K=%lld (K %% 32 == 0 required)", (long long)N, (long long)K);
+  NVQ_TRY(check_max(q, N * K, 15, "nvq_pack_q4_1", "code"));
   uint8_t* dst = static_cast<uint8_t*>(dst_host);
   const int64_t nc = N * K / 2;
-  for (int64_t i = 0; i < nc; ++i) {
-    const uint8_t a = q[2 * i], b = q[2 * i + 1];
-    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_q4_1: code > 15 at weight %lld", (long long)(2 * i));
-    dst[i] = (uint8_t)(a | (b << 4));
-  }
+  pack_nibbles(q, N * K, dst);
   const int64_t nb = N * K / 32;
   for (int64_t i = 0; i < nb; ++i) {
     const uint32_t pair = (uint32_t)d_f16[i] | ((uint32_t)m_f16[i] << 16);
@@ -191,28 +247,49 @@ nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn,
                          const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host) {
   if (!q || !sc || !mn || !d_f16 || !dmin_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_q4_k: NULL pointer");
   if (nvq_q4_k_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_q4_k: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  NVQ_TRY(check_max(q, N * K, 15, "nvq_pack_q4_k", "code"));
+  NVQ_TRY(check_max(sc, N * K / 32, 63, "nvq_pack_q4_k", "scale"));
+  NVQ_TRY(check_max(mn, N * K / 32, 63, "nvq_pack_q4_k", "min"));
   uint8_t* dst = static_cast<uint8_t*>(dst_host);
-  const int64_t nc = N * K / 2;
-  for (int64_t i = 0; i < nc; ++i) {
-    const uint8_t a = q[2 * i], b = q[2 * i + 1];
-    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_q4_k: code > 15 at weight %lld", (long long)(2 * i));
-    dst[i] = (uint8_t)(a | (b << 4));
+  pack_nibbles(q, N * K, dst);
+  pack_kq_headers(sc, mn, d_f16, dmin_f16, N * K / 256, dst + N * K / 2);
+  g_err[0] = '\0';
+  return NVQ_OK;
+}
+
+nvq_status nvq_pack_q5_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
+                         const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host) {
+  if (!q || !sc || !mn || !d_f16 || !dmin_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_q5_k: NULL pointer");
+  if (nvq_q5_k_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_q5_k: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  NVQ_TRY(check_max(q, N * K, 31, "nvq_pack_q5_k", "code"));
+  NVQ_TRY(check_max(sc, N * K / 32, 63, "nvq_pack_q5_k", "scale"));
+  NVQ_TRY(check_max(mn, N * K / 32, 63, "nvq_pack_q5_k", "min"));
+  uint8_t* dst = static_cast<uint8_t*>(dst_host);
+  pack_nibbles(q, N * K, dst);
+  pack_kq_headers(sc, mn, d_f16, dmin_f16, N * K / 256, dst + N * K / 2);
+  uint8_t* hb = dst + N * K / 2 + N * K / 16;
+  for (int64_t b = 0; b < N * K / 32; ++b) {
+    const uint32_t w4 = pack_code_bits(q + 32 * b, 4);
+    std::memcpy(hb + 4 * b, &w4, 4);
   }
-  // one 16-byte header per (row, 256 weights): d, dmin, then sc_0..7, mn_0..7 as 6-bit
-  // fields of a little-endian 96-bit number
-  const int64_t nsb = N * K / 256;
-  for (int64_t i = 0; i < nsb; ++i) {
-    uint8_t h[16] = {};
-    std::memcpy(h, &d_f16[i], 2);
-    std::memcpy(h + 2, &dmin_f16[i], 2);
-    for (int f = 0; f < 16; ++f) {
-      const uint8_t v = f < 8 ? sc[8 * i + f] : mn[8 * i + f - 8];
-      if (v > 63) return fail(NVQ_ERR_RANGE, "nvq_pack_q4_k: %s > 63 at sub-block %lld", f < 8 ? "scale" : "min", (long long)(8 * i + f % 8));
-      for (int bit = 0; bit < 6; ++bit)
-        if ((v >> bit) & 1) h[4 + (6 * f + bit) / 8] |= (uint8_t)(1u << ((6 * f + bit) % 8));
-    }
-    std::memcpy(dst + nc + 16 * i, h, 16);
+  g_err[0] = '\0';
+  return NVQ_OK;
+}
+
+nvq_status nvq_pack_q6_k(const uint8_t* q, const int8_t* sc, const uint16_t* d_f16, int64_t N, int64_t K,
+                         void* dst_host) {
+  if (!q || !sc || !d_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_q6_k: NULL pointer");
+  if (nvq_q6_k_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_q6_k: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  NVQ_TRY(check_max(q, N * K, 63, "nvq_pack_q6_k", "code"));
+  uint8_t* dst = static_cast<uint8_t*>(dst_host);
+  pack_nibbles(q, N * K, dst);
+  std::memcpy(dst + N * K / 2, sc, (size_t)(N * K / 16));
+  uint8_t* hb = dst + N * K / 2 + N * K / 16;
+  for (int64_t b = 0; b < N * K / 32; ++b) {
+    const uint32_t w[2] = {pack_code_bits(q + 32 * b, 4), pack_code_bits(q + 32 * b, 5)};
+    std::memcpy(hb + 8 * b, w, 8);
   }
+  std::memcpy(dst + N * K / 2 + N * K / 16 + N * K / 4, d_f16, (size_t)(N * K / 256) * 2);
   g_err[0] = '\0';
   return NVQ_OK;
 }
@@ -221,23 +298,17 @@ nvq_status nvq_pack_iq4_xs(const uint8_t* q, const uint8_t* ls, const uint16_t* 
                            void* dst_host) {
   if (!q || !ls || !d_f16 || !dst_host) return fail(NVQ_ERR_NULL, "nvq_pack_iq4_xs: NULL pointer");
   if (nvq_iq4_xs_weight_bytes(N, K) == 0) return fail(NVQ_ERR_SHAPE, "nvq_pack_iq4_xs: N=%lld K=%lld (K %% 256 == 0 required)", (long long)N, (long long)K);
+  NVQ_TRY(check_max(q, N * K, 15, "nvq_pack_iq4_xs", "code"));
+  NVQ_TRY(check_max(ls, N * K / 32, 63, "nvq_pack_iq4_xs", "scale"));
   uint8_t* dst = static_cast<uint8_t*>(dst_host);
   const int64_t nc = N * K / 2;
-  for (int64_t i = 0; i < nc; ++i) {
-    const uint8_t a = q[2 * i], b = q[2 * i + 1];
-    if ((a | b) > 15) return fail(NVQ_ERR_RANGE, "nvq_pack_iq4_xs: code > 15 at weight %lld", (long long)(2 * i));
-    dst[i] = (uint8_t)(a | (b << 4));
-  }
+  pack_nibbles(q, N * K, dst);
   // one 8-byte header per (row, 256 weights): d, then ls_0..7 as 6-bit fields of a
   // little-endian 48-bit number
   const int64_t nsb = N * K / 256;
   for (int64_t i = 0; i < nsb; ++i) {
     uint64_t f = 0;
-    for (int j = 0; j < 8; ++j) {
-      const uint8_t v = ls[8 * i + j];
-      if (v > 63) return fail(NVQ_ERR_RANGE, "nvq_pack_iq4_xs: scale > 63 at sub-block %lld", (long long)(8 * i + j));
-      f |= (uint64_t)v << (6 * j);
-    }
+    for (int j = 0; j < 8; ++j) f |= (uint64_t)ls[8 * i + j] << (6 * j);
     uint8_t h[8];
     std::memcpy(h, &d_f16[i], 2);
     for (int b = 0; b < 6; ++b) h[2 + b] = (uint8_t)(f >> (8 * b));
@@ -421,6 +492,54 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
                                         static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q4_k");
 }
 
+nvq_status nvq_gemv_q5_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_q5_k"));
+  if (!bsum16) return fail(NVQ_ERR_NULL, "nvq_gemv_q5_k: bsum16 is required");
+  if (!aligned(bsum16, 2)) return fail(NVQ_ERR_ALIGN, "nvq_gemv_q5_k: bsum16 must be 2-byte aligned");
+  NVQ_TRY(check_dims(M, N, K, 256, 1, NVQ_GEMV_MAX_M));
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_q5_k(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        (hipStream_t)stream), "gemv_q5_k");
+}
+
+nvq_status nvq_gemm_q5_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_q5_k"));
+  if (!bsum16) return fail(NVQ_ERR_NULL, "nvq_gemm_q5_k: bsum16 is required");
+  if (!aligned(bsum16, 2)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q5_k: bsum16 must be 2-byte aligned");
+  NVQ_TRY(check_dims(M, N, K, 256, 16, kMaxM));
+  const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_Q5_K, M, N, K);
+  if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_q5_k: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q5_k: workspace must be 16-byte aligned");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemm_q5_k(static_cast<const uint8_t*>(w), q, d_f16, bsum16, M, N, K, y, nullptr,
+                                        static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q5_k");
+}
+
+nvq_status nvq_gemv_q6_k(const void* w, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
+                         float* y, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_q6_k"));
+  NVQ_TRY(check_dims(M, N, K, 256, 1, NVQ_GEMV_MAX_M));
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemv_q6_k(static_cast<const uint8_t*>(w), q, d_f16, M, N, K, y, nullptr,
+                                        (hipStream_t)stream), "gemv_q6_k");
+}
+
+nvq_status nvq_gemm_q6_k(const void* w, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
+                         float* y, void* workspace, size_t ws_bytes, void* stream) {
+  NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemm_q6_k"));
+  NVQ_TRY(check_dims(M, N, K, 256, 16, kMaxM));
+  const size_t need = nvq_gemm_workspace_bytes(NVQ_FMT_Q6_K, M, N, K);
+  if (ws_bytes < need || (need && !workspace)) return fail(NVQ_ERR_WORKSPACE, "nvq_gemm_q6_k: workspace of %zu bytes required", need);
+  if (need && !aligned(workspace, 16)) return fail(NVQ_ERR_ALIGN, "nvq_gemm_q6_k: workspace must be 16-byte aligned");
+  NVQ_TRY(check_device());
+  return launched(nvq::launch_gemm_q6_k(static_cast<const uint8_t*>(w), q, d_f16, M, N, K, y, nullptr,
+                                        static_cast<float*>(workspace), (hipStream_t)stream), "gemm_q6_k");
+}
+
 nvq_status nvq_gemv_iq4_xs(const void* w, const int8_t* table, const int8_t* q, const uint16_t* d_f16, int64_t M,
                            int64_t N, int64_t K, float* y, void* stream) {
   NVQ_TRY(check_common(w, q, d_f16, y, "nvq_gemv_iq4_xs"));
@@ -461,13 +580,14 @@ nvq_status nvq_debug_isums_iq4_xs(const int8_t* table, int path, const void* w, 
 
 nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, int64_t M,
                            int64_t N, int64_t K, int32_t* isums, void* stream) {
-  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1 && fmt != NVQ_FMT_Q4_K)
+  if (fmt != NVQ_FMT_NVFP4 && fmt != NVQ_FMT_Q4_1 && fmt != NVQ_FMT_Q4_K && fmt != NVQ_FMT_Q5_K && fmt != NVQ_FMT_Q6_K)
     return fail(NVQ_ERR_RANGE, "nvq_debug_isums: fmt=%d (IQ4_XS sums need its value table: nvq_debug_isums_iq4_xs)", fmt);
+  const bool kq = fmt == NVQ_FMT_Q4_K || fmt == NVQ_FMT_Q5_K || fmt == NVQ_FMT_Q6_K;
   if (path != NVQ_PATH_GEMV && path != NVQ_PATH_GEMM && !(path == NVQ_PATH_GEMV_DOT4 && fmt == NVQ_FMT_NVFP4))
     return fail(NVQ_ERR_RANGE, "nvq_debug_isums: path=%d", path);
   if (!w || !q || !isums) return fail(NVQ_ERR_NULL, "nvq_debug_isums: NULL pointer");
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(isums, 4)) return fail(NVQ_ERR_ALIGN, "nvq_debug_isums: w and q must be 16-byte aligned, isums 4-byte");
-  NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : (fmt == NVQ_FMT_Q4_K ? 256 : 32), 1, kMaxM));
+  NVQ_TRY(check_dims(M, N, K, fmt == NVQ_FMT_NVFP4 ? 64 : (kq ? 256 : 32), 1, kMaxM));
   if (M > kMaxElems / (N * (K / 16))) return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: output too large");
   if (fmt == NVQ_FMT_NVFP4 && path == NVQ_PATH_GEMV && M > 1 && (M < 16 ? M : 16) * K >= (int64_t(1) << 32))
     return fail(NVQ_ERR_SHAPE, "nvq_debug_isums: K=%lld too large for the batched kernel (16 * K < 2^32)", (long long)K);
@@ -483,10 +603,14 @@ nvq_status nvq_debug_isums(int fmt, int path, const void* w, const int8_t* q, in
   if (path == NVQ_PATH_GEMM) {
     if (fmt == NVQ_FMT_NVFP4) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_nvfp4");
     if (fmt == NVQ_FMT_Q4_K) return launched(nvq::launch_gemm_q4_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_k");
+    if (fmt == NVQ_FMT_Q5_K) return launched(nvq::launch_gemm_q5_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q5_k");
+    if (fmt == NVQ_FMT_Q6_K) return launched(nvq::launch_gemm_q6_k(wb, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q6_k");
     return launched(nvq::launch_gemm_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemm_q4_1");
   }
   if (fmt == NVQ_FMT_Q4_1) return launched(nvq::launch_gemv_q4_1(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_1");
   if (fmt == NVQ_FMT_Q4_K) return launched(nvq::launch_gemv_q4_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q4_k");
+  if (fmt == NVQ_FMT_Q5_K) return launched(nvq::launch_gemv_q5_k(wb, q, nullptr, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q5_k");
+  if (fmt == NVQ_FMT_Q6_K) return launched(nvq::launch_gemv_q6_k(wb, q, nullptr, M, N, K, nullptr, isums, st), "debug gemv_q6_k");
   if (path == NVQ_PATH_GEMV) {
     if (M > 1) return launched(nvq::launch_gemv_nvfp4_batch_f16(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, st), "debug gemv_nvfp4 (batched)");
     if (!gemv_fits_lds(K)) return launched(nvq::launch_gemm_nvfp4(wb, 1.0f, q, nullptr, M, N, K, nullptr, isums, nullptr, st), "debug gemv_nvfp4 (tiled)");

@@ -89,6 +89,19 @@ hipError_t launch_gemm_iq4_xs(const uint8_t* w, const int8_t* table, const int8_
                               int64_t M, int64_t N, int64_t K, float* y, int32_t* isums, float* workspace,
                               hipStream_t stream);
 
+// Q5_K and Q6_K (K % 256 == 0) on the same kernels and with the same dispatch as Q4_K;
+// their workspace is gemm_q4_k_workspace's.  Q6_K takes no bsum16.
+hipError_t launch_gemv_q5_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream);
+hipError_t launch_gemm_q5_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, float* workspace, hipStream_t stream);
+hipError_t launch_gemv_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* isums, hipStream_t stream);
+hipError_t launch_gemm_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream);
+
 // Measurement probes (probe.hip): a streaming read of n16 16-byte units over `blocks`
 // blocks of 256 threads (sink: 4 words per block); the decode GEMV's weight loads
 // alone for waves in {4, 8, 16}, batch in {3, 5} and `splits` blocks per tile (sink:

@@ -58,7 +58,7 @@ constexpr int kQ41MaxUPL = 10;
 // whose table lookups make each unit's vector work ~6x longer (5.2 us against 7.3 with 4).
 // fmt: the weight format (NVQ_FMT_* value, 3 = IQ4_XS).
 __host__ __device__ constexpr int q41_rg(int upl, bool multi, int fmt) {
-  return fmt == 3 ? 1 : (upl >= 7 ? 1 : (upl >= 4 || !multi ? 2 : 4));
+  return fmt == 3 || fmt == 5 ? 1 : (upl >= 7 ? 1 : (upl >= 4 || !multi ? 2 : 4));
 }
 // tokens whose activations a GEMV wavefront holds at once (8 UPL registers each)
 __host__ __device__ constexpr int q41_tb(int upl) { return upl <= 2 ? 4 : (upl <= 4 ? 2 : 1); }
@@ -71,7 +71,28 @@ __device__ __forceinline__ int dot8_u4(uint32_t c, uint32_t qe, uint32_t qo, int
   return acc;
 }
 
-constexpr int kQ41 = 1, kQ4K = 2, kIQ4 = 3;  // weight formats of the kernels below (the NVQ_FMT_* values)
+// weight formats of the kernels below (the NVQ_FMT_* values)
+constexpr int kQ41 = 1, kQ4K = 2, kIQ4 = 3, kQ5K = 4, kQ6K = 5;
+
+// 4 bits (x & 15) spread to the low bit of each byte: bit t -> bit 8 t (the four
+// shifted copies x, x << 7, x << 14, x << 21 overlap in no bit, so the product adds
+// without carries)
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return ((x & 15u) * 0x00204081u) & 0x01010101u; }
+
+// The even (ce) and odd (co) code bytes of word i (codes 8 i .. 8 i + 7 of a 32-block)
+// from the packed low nibbles cwi and the format's high-bit words h: Q5_K adds the
+// fifth bit (h[0]), Q6_K the fifth and sixth (h[0], h[1]); bit e of a high-bit word
+// belongs to even code 2 e, bit 16 + e to odd code 2 e + 1.
+template <int HW>
+__device__ __forceinline__ void code_bytes(uint32_t cwi, int i, const uint32_t* h, uint32_t& ce, uint32_t& co) {
+  ce = cwi & 0x0F0F0F0Fu;
+  co = (cwi >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+  for (int b = 0; b < HW; ++b) {
+    ce |= spread4(h[b] >> (4 * i)) << (4 + b);
+    co |= spread4(h[b] >> (16 + 4 * i)) << (4 + b);
+  }
+}
 
 // IQ4_XS: 4 values of a 16-entry byte table (words t0..t3 = entries 0-3, .., 12-15) for
 // 4 index bytes idx (each 0..15): entries 0..7 and 8..15 by one v_perm_b32 each, then
@@ -107,16 +128,27 @@ __device__ __forceinline__ void q4k_block_scales(const u32x4& h, int j, float& d
 // kBound bounds |weight| / |scale| + |offset| / |scale| per block (the code range).
 template <int FMT>
 struct BlockScales {
-  static constexpr int kWords = FMT == kQ4K ? 4 : (FMT == kIQ4 ? 2 : 1);
-  static constexpr float kBound = FMT == kIQ4 ? 128.0f : 15.0f;
+  static constexpr bool kKq = FMT == kQ4K || FMT == kQ5K;  // the 16-byte K-quant header
+  static constexpr int kWords = kKq ? 4 : (FMT == kIQ4 ? 2 : 1);
+  // bound of |code value| (Q4: 15, Q5_K: 31, Q6_K: |c - 32| <= 32, IQ4_XS: |V| <= 128)
+  static constexpr float kBound = FMT == kIQ4 ? 128.0f : (FMT == kQ5K ? 31.0f : (FMT == kQ6K ? 32.0f : 15.0f));
   const uint32_t* base;  // first word of the scale region
-  int64_t per_row;       // words per weight row
+  int64_t per_row;       // words per weight row (Q6_K: bytes of int8 scales per row)
+  const uint16_t* dbase;  // Q6_K: the binary16 d of each 256-block, [N][K/256]
   __device__ BlockScales(const uint8_t* w, int64_t N, int K)
       : base(reinterpret_cast<const uint32_t*>(w + N * (int64_t)(K >> 1))),
-        per_row(FMT == kQ4K ? (int64_t)(K >> 8) * 4 : (FMT == kIQ4 ? (int64_t)(K >> 8) * 2 : (int64_t)(K >> 5))) {}
-  // the raw words that hold 32-block b of a row
+        per_row(kKq ? (int64_t)(K >> 8) * 4
+                    : (FMT == kIQ4 ? (int64_t)(K >> 8) * 2 : (FMT == kQ6K ? (int64_t)(K >> 4) : (int64_t)(K >> 5)))),
+        dbase(FMT == kQ6K ? reinterpret_cast<const uint16_t*>(w + N * (int64_t)(K >> 1) + N * (int64_t)(K >> 4) +
+                                                              N * (int64_t)(K >> 2))
+                          : nullptr) {}
+  // the raw words that hold 32-block b of a row (Q6_K: its two int8 scales in bits
+  // 0..15, the super-block's binary16 d in bits 16..31)
   __device__ __forceinline__ void load(int64_t row, int64_t b, uint32_t* v) const {
-    if constexpr (FMT == kQ4K) {
+    if constexpr (FMT == kQ6K) {
+      const uint16_t pair = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(base) + row * per_row)[b];
+      v[0] = (uint32_t)pair | ((uint32_t)dbase[row * (per_row >> 4) + (b >> 3)] << 16);
+    } else if constexpr (kKq) {
       const u32x4 h = *reinterpret_cast<const u32x4*>(base + row * per_row + 4 * (b >> 3));
       v[0] = h[0]; v[1] = h[1]; v[2] = h[2]; v[3] = h[3];
     } else if constexpr (FMT == kIQ4) {
@@ -126,9 +158,15 @@ struct BlockScales {
       v[0] = base[row * per_row + b];
     }
   }
-  // (scale, offset) of 32-block b from its raw words
+  // (scale, offset) of 32-block b from its raw words; Q6_K: the larger of its two
+  // 16-scales and no offset (what bounds the block; the products use decode_half)
   __device__ __forceinline__ static void decode(const uint32_t* v, int64_t b, float& dw, float& mw) {
-    if constexpr (FMT == kQ4K) {
+    if constexpr (FMT == kQ6K) {
+      const float d = f16_bits_to_f32((uint16_t)(v[0] >> 16));
+      const int s0 = (int8_t)(v[0] & 0xFFu), s1 = (int8_t)((v[0] >> 8) & 0xFFu);
+      dw = d * (float)max(abs(s0), abs(s1));
+      mw = 0.0f;
+    } else if constexpr (kKq) {
       q4k_block_scales(u32x4{v[0], v[1], v[2], v[3]}, (int)(b & 7), dw, mw);
     } else if constexpr (FMT == kIQ4) {
       const uint64_t f = (uint64_t)v[1] << 16 | (v[0] >> 16);  // the 48 bits of ls_0 .. ls_7
@@ -138,6 +176,35 @@ struct BlockScales {
     } else {
       dw = f16_bits_to_f32((uint16_t)(v[0] & 0xFFFFu));
       mw = f16_bits_to_f32((uint16_t)(v[0] >> 16));
+    }
+  }
+  // Q6_K: the scale d * sc of 16-block half (0, 1) of the 32-block (exact in fp32)
+  __device__ __forceinline__ static float decode_half(const uint32_t* v, int half) {
+    const int sc = (int8_t)((v[0] >> (8 * half)) & 0xFFu);
+    return f16_bits_to_f32((uint16_t)(v[0] >> 16)) * (float)sc;
+  }
+};
+
+// The high-bit words of Q5_K (one per 32-block: the codes' fifth bits) and Q6_K (two:
+// fifth and sixth bits), row-major after the scale region.
+template <int FMT>
+struct HighBits {
+  static constexpr int kHW = FMT == kQ5K ? 1 : (FMT == kQ6K ? 2 : 0);
+  static constexpr int kSlots = kHW > 0 ? kHW : 1;  // register slots (unused without high bits)
+  const uint32_t* base;
+  int64_t per_row;  // words per weight row
+  __device__ HighBits(const uint8_t* w, int64_t N, int K)
+      : base(reinterpret_cast<const uint32_t*>(w + N * (int64_t)(K >> 1) + N * (int64_t)(K >> 4))),
+        per_row((int64_t)(K >> 5) * kHW) {}
+  __device__ __forceinline__ void load(int64_t row, int64_t b, uint32_t* h) const {
+    if constexpr (kHW == 1) {
+      h[0] = base[row * per_row + b];
+    } else if constexpr (kHW == 2) {
+      const u32x2 t = *reinterpret_cast<const u32x2*>(base + row * per_row + 2 * b);
+      h[0] = t[0];
+      h[1] = t[1];
+    } else {
+      h[0] = 0u;
     }
   }
 };
@@ -162,10 +229,13 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
   const int64_t nb = K >> 5;
   const BlockScales<FMT> bsc(w, N, K);
   constexpr int PW = BlockScales<FMT>::kWords;
+  const HighBits<FMT> hbits(w, N, K);
+  constexpr int HW = HighBits<FMT>::kHW, HS = HighBits<FMT>::kSlots;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
 
   uint4 cw[RG][UPL];
   uint32_t pw[RG][UPL][PW];  // raw scale words of each unit's 32-block (not read for the debug sums)
+  uint32_t hw[RG][UPL][HS];  // Q5_K / Q6_K: the unit's high-bit words
 #pragma unroll
   for (int r = 0; r < RG; ++r) {
     const int64_t row = row0 + r * RPG + slot;
@@ -176,10 +246,14 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
         cw[r][j] = *reinterpret_cast<const uint4*>(w + row * crow + 16 * (int64_t)u);
         if (!DEBUG) bsc.load(row, u, pw[r][j]);
         else for (int e = 0; e < PW; ++e) pw[r][j][e] = 0u;
+        if (HW > 0) hbits.load(row, u, hw[r][j]);
+        else hw[r][j][0] = 0u;
       } else {
         cw[r][j] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int e = 0; e < PW; ++e) pw[r][j][e] = 0u;
+#pragma unroll
+        for (int e = 0; e < HS; ++e) hw[r][j][e] = 0u;
       }
     }
   }
@@ -208,9 +282,10 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
           split_even_odd(b.z, b.w, qe[tb][j][3], qo[tb][j][3]);
           if (!DEBUG) {
             da[tb][j] = f16_bits_to_f32(d16[m * nb + u]);
-            // IQ4_XS has no offset term (and takes no bsum16)
-            bs[tb][j] = FMT == kIQ4 ? 0.0f
-                                    : (float)((int)bsum16[m * 2 * nb + 2 * u] + (int)bsum16[m * 2 * nb + 2 * u + 1]);
+            // IQ4_XS and Q6_K have no offset term (and take no bsum16)
+            bs[tb][j] = FMT == kIQ4 || FMT == kQ6K
+                            ? 0.0f
+                            : (float)((int)bsum16[m * 2 * nb + 2 * u] + (int)bsum16[m * 2 * nb + 2 * u + 1]);
           } else {
             da[tb][j] = bs[tb][j] = 0.0f;
           }
@@ -236,6 +311,25 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
           if constexpr (FMT == kIQ4) {  // table values of the codes
             i0 = iq4_dot8(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], iq4_dot8(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0, vtab), vtab);
             i1 = iq4_dot8(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], iq4_dot8(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0, vtab), vtab);
+          } else if constexpr (HW > 0) {
+            // 5- or 6-bit codes c (0..63 fit a signed byte); Q6_K's values are c - 32: the
+            // bytes 0xE0 (-32) dotted with the same activation codes add -32 sum q
+            const uint32_t cws[4] = {cw[r][j].x, cw[r][j].y, cw[r][j].z, cw[r][j].w};
+            int is[2] = {0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              uint32_t ce, co;
+              code_bytes<HW>(cws[i], i, hw[r][j], ce, co);
+              int a = dot4(ce, qe[tb][j][i], is[i >> 1]);
+              a = dot4(co, qo[tb][j][i], a);
+              if constexpr (FMT == kQ6K) {
+                a = dot4(0xE0E0E0E0u, qe[tb][j][i], a);
+                a = dot4(0xE0E0E0E0u, qo[tb][j][i], a);
+              }
+              is[i >> 1] = a;
+            }
+            i0 = is[0];
+            i1 = is[1];
           } else {
             i0 = dot8_u4(cw[r][j].y, qe[tb][j][1], qo[tb][j][1], dot8_u4(cw[r][j].x, qe[tb][j][0], qo[tb][j][0], 0));
             i1 = dot8_u4(cw[r][j].w, qe[tb][j][3], qo[tb][j][3], dot8_u4(cw[r][j].z, qe[tb][j][2], qo[tb][j][2], 0));
@@ -246,6 +340,11 @@ __global__ __launch_bounds__(256) void gemv_q4_1_m1_kernel(const uint8_t* __rest
               isums[(m * N + row) * (K >> 4) + 2 * u] = i0;
               isums[(m * N + row) * (K >> 4) + 2 * u + 1] = i1;
             }
+          } else if constexpr (FMT == kQ6K) {
+            // one scale per 16-block half
+            const float dw0 = BlockScales<FMT>::decode_half(pw[r][j], 0);
+            const float dw1 = BlockScales<FMT>::decode_half(pw[r][j], 1);
+            acc = fmaf(da[tb][j], fmaf(dw0, (float)i0, dw1 * (float)i1), acc);
           } else {
             float dw, mw;
             BlockScales<FMT>::decode(pw[r][j], sub + LPR * j, dw, mw);
@@ -679,6 +778,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const int nb32 = K >> 5;      // activation scales per token row
   const BlockScales<FMT> bsc(w, N, K);
   constexpr int PW = BlockScales<FMT>::kWords;
+  const HighBits<FMT> hbits(w, N, K);
+  constexpr int HW = HighBits<FMT>::kHW, HS = HighBits<FMT>::kSlots;
 
   // staging task of this thread: CPT weight codes of row wrow at k-offset CPT wq of
   // the stage, all in one 32-block, with that block's (d, m); ABT activation codes of
@@ -694,7 +795,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   const int drow = tid % BM, dblk = (tid / BM) & 1;
   const uint16_t* __restrict__ dbase = DEBUG ? nullptr : d16 + min(m0 + drow, M - 1) * nb32 + dblk;
   bool anybig = false;  // this thread staged an activation scale d >= 512
-  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm[PW]; uint32_t dr; int blk; };
+  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm[PW]; uint32_t hb[HS]; uint32_t dr; int blk; };
   // (scale, offset) of a staged 32-block; DEBUG: d = 1, m = 0 for every weight block
   auto block_scales = [&](const uint32_t* v, int64_t b, float& dwf, float& mwf) {
     if constexpr (DEBUG) {
@@ -730,6 +831,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
     x.wc = load_words<CPT / 8>(wbase + (int64_t)t * 32);
     x.blk = 2 * t + wblk;
     if (!DEBUG) bsc.load(wr, x.blk, x.dm);
+    if (HW > 0) hbits.load(wr, x.blk, x.hb);
     x.a = load_words<ABT / 4>(abase + 64 * t);
     if constexpr (DEBUG) x.dr = 0x3C00u;  // d = 1
     else x.dr = dtask ? dbase[2 * t] : 0u;
@@ -744,14 +846,30 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
     uint16_t* ld = reinterpret_cast<uint16_t*>(st + 2 * C::kStageW + C::kStageA);
     float dwf, mwf;
     block_scales(x.dm, x.blk, dwf, mwf);
-    const float dw = rscale * dwf;
+    float dw = rscale * dwf;
     // IQ4_XS: the weight is dw * table[c]; the table is read as table + 128 (bytes
     // 0..255, exact floats), so w = fma(dw, table[c] + 128, -128 dw): one rounding of
     // the exact dw * table[c], as the Q4 formats' fma(dw, c, mw)
-    const float mw = FMT == kIQ4 ? -128.0f * dw : rscale * mwf;
+    float mw = FMT == kIQ4 ? -128.0f * dw : rscale * mwf;
+    // Q5_K / Q6_K: this thread's high bits of its CPT codes (even codes from bit
+    // ebase of a high-bit word, odd codes from bit 16 + ebase)
+    const int ebase = ((CPT * wq) & 31) >> 1;
+    uint32_t he[HS], ho[HS];
+#pragma unroll
+    for (int b = 0; b < HS; ++b) {
+      he[b] = x.hb[b] >> ebase;
+      ho[b] = x.hb[b] >> (16 + ebase);
+    }
 #pragma unroll
     for (int h = 0; h < CPT / 8; ++h) {
       const uint32_t cw = x.wc.v[h];
+      if constexpr (FMT == kQ6K) {
+        // the 16-block half of these 8 codes: w = d sc (c - 32) = fma(dw, c, -32 dw),
+        // exact in fp32 (d sc c has at most 11 + 7 + 6 significant bits)
+        const int half = ((CPT * wq + 8 * h) >> 4) & 1;
+        dw = rscale * (DEBUG ? 1.0f : BlockScales<FMT>::decode_half(x.dm, half));
+        mw = -32.0f * dw;
+      }
       uint32_t ve = 0u, vo = 0u;  // IQ4_XS: biased table values of the even / odd codes
       if constexpr (FMT == kIQ4) {
         const u32x4 tb = vtab ^ u32x4{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
@@ -762,8 +880,10 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         // byte j/2 of the codes: code 2i low nibble, 2i+1 high
-        const float c = FMT == kIQ4 ? (float)(((j & 1 ? vo : ve) >> (8 * (j >> 1))) & 0xFFu)
-                                    : (float)((cw >> (4 * j)) & 0xFu);
+        uint32_t ci = (cw >> (4 * j)) & 0xFu;
+#pragma unroll
+        for (int b = 0; b < HW; ++b) ci |= (((j & 1 ? ho[b] : he[b]) >> (4 * h + (j >> 1))) & 1u) << (4 + b);
+        const float c = FMT == kIQ4 ? (float)(((j & 1 ? vo : ve) >> (8 * (j >> 1))) & 0xFFu) : (float)ci;
         const float wf = fmaf(dw, c, mw);
         const _Float16 hi = (_Float16)wf;
         vh[j] = hi;
@@ -1086,6 +1206,41 @@ hipError_t launch_gemv_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d
                             int32_t* isums, hipStream_t stream) {
   if (q41_gemv_fits(K)) return launch_gemv_q4x<kQ4K>(w, q, d16, bsum16, M, N, K, y, isums, stream);
   return launch_q41_f16x2<Q41Mid, kQ4K>(w, q, d16, M, N, K, y, isums, nullptr, stream, false);
+}
+
+// Q5_K and Q6_K: the same two kernels and dispatch as Q4_K (Q6_K takes no bsum16)
+hipError_t launch_gemv_q5_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, hipStream_t stream) {
+  if (q41_gemv_fits(K)) return launch_gemv_q4x<kQ5K>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+  return launch_q41_f16x2<Q41Mid, kQ5K>(w, q, d16, M, N, K, y, isums, nullptr, stream, false);
+}
+
+hipError_t launch_gemm_q5_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
+                            const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                            int32_t* isums, float* workspace, hipStream_t stream) {
+  switch (q4k_path(M, K)) {
+    case kQ41Gemv: return launch_gemv_q4x<kQ5K>(w, q, d16, bsum16, M, N, K, y, isums, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big, kQ5K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128, kQ5K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    default: return launch_q41_f16x2<Q41Mid, kQ5K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+  }
+}
+
+hipError_t launch_gemv_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* isums, hipStream_t stream) {
+  if (q41_gemv_fits(K)) return launch_gemv_q4x<kQ6K>(w, q, d16, nullptr, M, N, K, y, isums, stream);
+  return launch_q41_f16x2<Q41Mid, kQ6K>(w, q, d16, M, N, K, y, isums, nullptr, stream, false);
+}
+
+hipError_t launch_gemm_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
+                            int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream) {
+  switch (q4k_path(M, K)) {
+    case kQ41Gemv: return launch_gemv_q4x<kQ6K>(w, q, d16, nullptr, M, N, K, y, isums, stream);
+    case kQ41Big: return launch_q41_f16x2<Q41Big, kQ6K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    case kQ41M128: return launch_q41_f16x2<Q41M128, kQ6K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+    default: return launch_q41_f16x2<Q41Mid, kQ6K>(w, q, d16, M, N, K, y, isums, workspace, stream);
+  }
 }
 
 }  // namespace nvq

@@ -1,5 +1,5 @@
 /*
- * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 / Q4_K / IQ4_XS x Q8_0) quantized
+ * nvq.h -- C ABI of libnvq: NVFP4 x Q8_0 (and Q4_1 / Q4_K / Q5_K / Q6_K / IQ4_XS x Q8_0) quantized
  * matrix products on AMD Instinct MI355X (gfx950).
  *
  * What is computed.  Weights W [N][K] ("out x in", row-major) are stored 4-bit;
@@ -11,8 +11,8 @@
  *     bias-trick paragraph): NVFP4 weights in 64-weight blocks, one UE4M3 scale
  *     per 16 weights, integer partial sums per 16-subblock, per-16 activation code
  *     sums; batch-1 decode uses a vector dot, larger batches a tiled matmul;
- *     section 1 names the Q4_1 kernels of the same work and Q4_K and IQ4_XS among its
- *     formats.
+ *     section 1 names the Q4_1 kernels of the same work and IQ4_XS and Q4_K / Q5_K /
+ *     Q6_K among its formats.
  *   The llama.cpp 2-bit GGUF tutorial (spke.com, article 4846), GGML type table:
  *     Q8_0 is 32 values in 34 bytes (32 int8 codes + one fp16 scale); Q4_K is 256
  *     values in 144 bytes, IQ4_XS 256 values in 136 bytes.
@@ -31,6 +31,12 @@
  *     W[n][k] = d[n][k/256] * sc[n][k/32] * q[n][k] - dmin[n][k/256] * mn[n][k/32],
  *     q in 0..15, sc and mn 6-bit (0..63), d and dmin IEEE binary16; 2 + 2 + 12 + 128
  *     = 144 bytes per 256 weights.
+ *   Q5_K weight (the pages give neither its block nor its rule; the rule taken is the
+ *     GGML format's): as Q4_K with 5-bit codes q in 0..31; 2 + 2 + 12 + 32 + 128 = 176
+ *     bytes per 256 weights.
+ *   Q6_K weight (likewise the GGML format's rule): W[n][k] = d[n][k/256] *
+ *     sc[n][k/16] * (q[n][k] - 32), q in 0..63, sc signed 8-bit, d IEEE binary16;
+ *     128 + 64 + 16 + 2 = 210 bytes per 256 weights.
  *   IQ4_XS weight (the pages give only its block size; the rule taken is the GGML
  *     format's, with its 16-entry value table as an argument, since the pages print
  *     none): W[n][k] = d[n][k/256] * (ls[n][k/32] - 32) * table[c[n][k]], c in 0..15,
@@ -74,6 +80,20 @@
  *                           eight 32-weight sub-blocks, field f at bits
  *                           [6f, 6f + 6) of those 12 bytes read as one
  *                           little-endian 96-bit number.
+ *   Q5_K, row-major, nvq_q5_k_weight_bytes(N, K) = N*K*176/256 bytes:
+ *     [0, N*K/2)            the codes' low four bits, as Q4_1.
+ *     [N*K/2, +N*K/16)      the 16-byte headers, as Q4_K.
+ *     [N*K/2 + N*K/16, +N*K/8)  per 32 weights a 4-byte little-endian word of the
+ *                           codes' fifth bits, row-major [N][K/32]: bit e (0..15) of
+ *                           the code of k = 2e, bit 16 + e of the code of k = 2e + 1
+ *                           (k counted within the 32-block).
+ *   Q6_K, row-major, nvq_q6_k_weight_bytes(N, K) = N*K*210/256 bytes:
+ *     [0, N*K/2)            the codes' low four bits, as Q4_1.
+ *     [N*K/2, +N*K/16)      the int8 scales, row-major [N][K/16].
+ *     [N*K/2 + N*K/16, +N*K/4)  per 32 weights two 4-byte words, row-major [N][K/32]:
+ *                           the codes' fifth bits, then their sixth bits, each
+ *                           arranged as Q5_K's fifth-bit word.
+ *     [N*K/2 + N*K/16 + N*K/4, +N*K/128)  binary16 d, row-major [N][K/256].
  *   IQ4_XS, row-major, nvq_iq4_xs_weight_bytes(N, K) = N*K*136/256 bytes:
  *     [0, N*K/2)            codes, as Q4_1.
  *     [N*K/2, +N*K/32)      per 256 weights an 8-byte header, row-major [N][K/256]:
@@ -124,6 +144,8 @@ typedef int nvq_status;
 #define NVQ_FMT_Q4_1  1
 #define NVQ_FMT_Q4_K  2
 #define NVQ_FMT_IQ4_XS 3
+#define NVQ_FMT_Q5_K  4
+#define NVQ_FMT_Q6_K  5
 #define NVQ_PATH_GEMV      0  /* decode GEMV, matrix-core inner loop (production) */
 #define NVQ_PATH_GEMM      1  /* tiled GEMM */
 #define NVQ_PATH_GEMV_DOT4 2  /* decode GEMV, v_perm + v_dot4 inner loop (NVFP4 only) */
@@ -150,14 +172,22 @@ size_t nvq_q4_1_weight_bytes(int64_t N, int64_t K);
  * table (Q4_K: 256 values in 144 bytes). */
 size_t nvq_q4_k_weight_bytes(int64_t N, int64_t K);
 
+/* Bytes of a packed Q5_K / Q6_K weight buffer [N][K]: N*K*176/256 / N*K*210/256.  0 if
+ * N < 1 or K is not a positive multiple of 256.  Follows: "HANDOFF: flint CPU
+ * optimization (Q4_1 + NVFP4)", section 1 (Q5_K and Q6_K among the patch's formats; the
+ * pages give no block size for them, these are the GGML formats' 176 and 210 bytes). */
+size_t nvq_q5_k_weight_bytes(int64_t N, int64_t K);
+size_t nvq_q6_k_weight_bytes(int64_t N, int64_t K);
+
 /* Bytes of a packed IQ4_XS weight buffer [N][K]: N*K*136/256.  0 if N < 1 or K is not
  * a positive multiple of 256.  Follows: the llama.cpp 2-bit GGUF tutorial, GGML type
  * table (IQ4_XS: 256 values in 136 bytes). */
 size_t nvq_iq4_xs_weight_bytes(int64_t N, int64_t K);
 
-/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 / nvq_gemm_q4_k /
- * nvq_gemm_iq4_xs need for this shape (fmt is NVQ_FMT_*): with M > 16 and K % 64 == 0
- * (Q4_K, IQ4_XS: K % 256 == 0, and also M <= 16 with K > 20480), the fp32 partial
+/* Device workspace bytes nvq_gemm_nvfp4 / nvq_gemm_q4_1 / nvq_gemm_q4_k / nvq_gemm_q5_k /
+ * nvq_gemm_q6_k / nvq_gemm_iq4_xs need for this shape (fmt is NVQ_FMT_*): with M > 16
+ * and K % 64 == 0 (Q4_K, Q5_K, Q6_K, IQ4_XS: K % 256 == 0, and also M <= 16 with
+ * K > 20480), the fp32 partial
  * tiles of the K-split
  * work items that even out the last round of tiles over the chip's 256 compute units
  * (at most 64 MiB: 256 work items x 512 threads x 128 floats); otherwise 0.  Pure
@@ -193,6 +223,23 @@ nvq_status nvq_pack_q4_1(const uint8_t* q, const uint16_t* d_f16, const uint16_t
  * among the formats of the same work). */
 nvq_status nvq_pack_q4_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
                          const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host);
+
+/* q: [N][K] bytes (0..31); sc, mn: [N][K/32] bytes (6-bit, 0..63); d_f16, dmin_f16:
+ * [N][K/256] binary16 bit patterns.  Writes nvq_q5_k_weight_bytes(N, K) bytes to
+ * dst_host.  K % 256 == 0.  NVQ_ERR_RANGE if a code exceeds 31 or a scale or min 63.
+ * Host memory only, caller-owned.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q5_K among the
+ * formats of the same work; its rule is the GGML format's, not the pages'). */
+nvq_status nvq_pack_q5_k(const uint8_t* q, const uint8_t* sc, const uint8_t* mn, const uint16_t* d_f16,
+                         const uint16_t* dmin_f16, int64_t N, int64_t K, void* dst_host);
+
+/* q: [N][K] bytes (0..63, used as q - 32); sc: [N][K/16] int8 scales; d_f16: [N][K/256]
+ * binary16 bit patterns.  Writes nvq_q6_k_weight_bytes(N, K) bytes to dst_host.
+ * K % 256 == 0.  NVQ_ERR_RANGE if a code exceeds 63.  Host memory only.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q6_K among the
+ * formats of the same work; its rule is the GGML format's, not the pages'). */
+nvq_status nvq_pack_q6_k(const uint8_t* q, const int8_t* sc, const uint16_t* d_f16, int64_t N, int64_t K,
+                         void* dst_host);
 
 /* q: [N][K] bytes (0..15, indices into the value table); ls: [N][K/32] bytes (6-bit,
  * 0..63); d_f16: [N][K/256] binary16 bit patterns.  Writes nvq_iq4_xs_weight_bytes(N, K)
@@ -351,6 +398,31 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
                          const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- Q5_K and Q6_K products ------------------------------------------------ */
+
+/* Q5_K GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 256 == 0; arguments and
+ * workspace (NVQ_FMT_Q5_K) as the Q4_K entries, bsum16 required.  Per 32-block a Q5_K
+ * weight is the Q4_K block's scale d * sc and offset -dmin * mn on a 5-bit code: the
+ * GEMV kernel splices the fifth bits into the code bytes before v_dot4_i32_i8, the
+ * two-term kernel into the float code (bound 31 instead of 15).
+ * Q6_K GEMV and GEMM: no bsum16 (no offset term); workspace NVQ_FMT_Q6_K.  One scale
+ * d * sc per 16 weights on the values q - 32: the GEMV kernel sums (q - 32) * a as
+ * v_dot4 of the 6-bit code bytes plus v_dot4 of bytes -32, per 16-block half; the
+ * two-term kernel forms d * sc * (q - 32) exactly in float32 (bound 32).
+ * Same kernels, dispatch and error bound as the Q4_K entries.
+ * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q5_K and Q6_K
+ * among the patch's formats); the rules are the GGML formats' (the pages give none). */
+nvq_status nvq_gemv_q5_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* stream);
+nvq_status nvq_gemm_q5_k(const void* w, const int8_t* q, const uint16_t* d_f16,
+                         const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
+                         void* workspace, size_t ws_bytes, void* stream);
+nvq_status nvq_gemv_q6_k(const void* w, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
+                         float* y, void* stream);
+nvq_status nvq_gemm_q6_k(const void* w, const int8_t* q, const uint16_t* d_f16, int64_t M, int64_t N, int64_t K,
+                         float* y, void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- IQ4_XS products ---------------------------------------------------------- */
 
 /* IQ4_XS GEMV (1 <= M <= NVQ_GEMV_MAX_M) and GEMM (M >= 16); K % 256 == 0; table: the
@@ -373,9 +445,10 @@ nvq_status nvq_gemm_iq4_xs(const void* w, const int8_t* table, const int8_t* q, 
 
 /* isums [M][N][K/16] int32 (device, overwritten) = for each 16-subblock,
  * sum_j L(code) * q (NVFP4, with L(c) = 2*E2M1(c), an integer in -12..12) or
- * sum_j code * q (Q4_1 and Q4_K, unsigned codes).  fmt: NVQ_FMT_*.  path picks the
+ * sum_j code * q (Q4_1, Q4_K and Q5_K, unsigned codes) or sum_j (code - 32) * q (Q6_K).
+ * fmt: NVQ_FMT_* (not IQ4_XS).  path picks the
  * product entry whose kernel computes the sums, run with unit scales (UE4M3 = 1,
- * d = 1; Q4_1 / Q4_K block scale 1, offset 0) through its own weight loads, code
+ * d = 1; Q4_1 / Q4_K / Q5_K / Q6_K block scale 1, offset 0 or -32) through its own weight loads, code
  * expansion and integer or
  * matrix-core contraction -- the kernel that entry dispatches for this M:
  *   NVQ_PATH_GEMV      nvq_gemv_nvfp4 / nvq_gemv_q4_1: NVFP4 M = 1 the matrix-core
@@ -385,11 +458,11 @@ nvq_status nvq_gemm_iq4_xs(const void* w, const int8_t* table, const int8_t* q, 
  *                      tiled kernel, 2 <= M <= 16 the batched kernel, M > 16 the
  *                      two-term kernel of M's tile height with its K-split work items;
  *                      Q4_1 M <= 16 the GEMV kernel, M > 16 the two-term kernel
- *                      (K % 64 == 0) or the tiled kernel; Q4_K as its entries
- *                      dispatch (GEMV kernel, or the two-term kernel);
+ *                      (K % 64 == 0) or the tiled kernel; Q4_K, Q5_K, Q6_K as
+ *                      their entries dispatch (GEMV kernel, or the two-term kernel);
  *   NVQ_PATH_GEMV_DOT4 nvq_gemv_nvfp4_dot4 (NVFP4 only): the v_dot4 decode kernel,
  *                      one launch per token.
- * K % 64 == 0 (NVFP4), K % 32 == 0 (Q4_1) or K % 256 == 0 (Q4_K).
+ * K % 64 == 0 (NVFP4), K % 32 == 0 (Q4_1) or K % 256 == 0 (Q4_K, Q5_K, Q6_K).
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 3, Code map
  * (one int32 sum per 16-subblock, lane k of the sum = subblock k/2) and bias-trick
  * paragraph; the integer sums are unique, so they are checked bit for bit. */

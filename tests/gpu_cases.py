@@ -105,6 +105,36 @@ class Q4KCase:
         return o.matmul_q4_k(self.qw, self.sc, self.mn, self.dd, self.dm, self.qh, self.dh, cols=cols)
 
 
+class Q5KCase:
+    """Seeded Q5_K case; ``weights`` = (qw, sc, mn, d, dmin) and ``x`` replace the seeded ones."""
+
+    def __init__(self, M, N, K, seed, weights=None, x=None):
+        self.M, self.N, self.K = M, N, K
+        self.qw, self.sc, self.mn, self.dd, self.dm = weights if weights is not None else synth.q5_k_weights(N, K, seed)
+        self.x = x if x is not None else synth.activations(M, K, seed + 1)
+        self.w = to_dev(nvq.nvq_pack_q5_k(self.qw, self.sc, self.mn, self.dd, self.dm))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_q5_k(self.qw, self.sc, self.mn, self.dd, self.dm, self.qh, self.dh, cols=cols)
+
+
+class Q6KCase:
+    """Seeded Q6_K case; ``weights`` = (qw, sc, d) and ``x`` replace the seeded ones."""
+
+    def __init__(self, M, N, K, seed, weights=None, x=None):
+        self.M, self.N, self.K = M, N, K
+        self.qw, self.sc, self.dd = weights if weights is not None else synth.q6_k_weights(N, K, seed)
+        self.x = x if x is not None else synth.activations(M, K, seed + 1)
+        self.w = to_dev(nvq.nvq_pack_q6_k(self.qw, self.sc, self.dd))
+        self.q, self.d, self.b = quantize_gpu(self.x)
+        self.qh, self.dh = host(self.q), host(self.d).view(np.uint16)
+
+    def oracle_y(self, o, cols=None):
+        return o.matmul_q6_k(self.qw, self.sc, self.dd, self.qh, self.dh, cols=cols)
+
+
 class IQ4Case:
     """Seeded IQ4_XS case; ``weights`` = (qw, ls, d, table) and ``x`` replace the seeded ones."""
 

@@ -245,6 +245,113 @@ def test_pack_nvfp4_rejects_invalid(bad):
     assert e.value.status == -3
 
 
+def _code_bits_word(q32, bit):
+    """The documented high-bit word of 32 codes: bit e = bit `bit` of code 2e, bit
+    16 + e = that of code 2e + 1 (independent restatement for the layout tests)."""
+    w = 0
+    for e in range(16):
+        w |= ((int(q32[2 * e]) >> bit) & 1) << e
+        w |= ((int(q32[2 * e + 1]) >> bit) & 1) << (16 + e)
+    return w
+
+
+def test_pack_q5_k_layout():
+    # low nibbles as Q4_1, the Q4_K headers, then per 32 weights the fifth-bit word
+    r = np.random.Generator(np.random.PCG64(9))
+    N, K = 3, 512
+    q = r.integers(0, 32, (N, K), dtype=np.uint8)
+    sc = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    mn = r.integers(0, 64, (N, K // 32), dtype=np.uint8)
+    d = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    dm = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    buf = nvq.nvq_pack_q5_k(q, sc, mn, d, dm)
+    assert buf.size == N * K * 176 // 256 == nvq.nvq_q5_k_weight_bytes(N, K)
+    cb = buf[: N * K // 2].reshape(N, K // 2)
+    assert (cb & 0xF == q[:, 0::2] & 15).all() and (cb >> 4 == q[:, 1::2] & 15).all()
+    # the headers are byte-identical with the Q4_K packer's for the same scales
+    ref4 = nvq.nvq_pack_q4_k(q & 15, sc, mn, d, dm)
+    assert (buf[N * K // 2: N * K // 2 + N * K // 16] == ref4[N * K // 2:]).all()
+    hb = buf[N * K // 2 + N * K // 16:].copy().view(np.uint32).reshape(N, K // 32)
+    for n in range(N):
+        for b in range(K // 32):
+            assert int(hb[n, b]) == _code_bits_word(q[n, 32 * b: 32 * b + 32], 4)
+
+
+def test_pack_q6_k_layout():
+    # low nibbles, int8 scales [N][K/16], two high-bit words per 32 weights, then d
+    r = np.random.Generator(np.random.PCG64(10))
+    N, K = 3, 512
+    q = r.integers(0, 64, (N, K), dtype=np.uint8)
+    sc = r.integers(-128, 128, (N, K // 16)).astype(np.int8)
+    d = r.integers(0, 65536, (N, K // 256), dtype=np.uint32).astype(np.uint16)
+    buf = nvq.nvq_pack_q6_k(q, sc, d)
+    assert buf.size == N * K * 210 // 256 == nvq.nvq_q6_k_weight_bytes(N, K)
+    o1, o2, o3 = N * K // 2, N * K // 2 + N * K // 16, N * K // 2 + N * K // 16 + N * K // 4
+    cb = buf[:o1].reshape(N, K // 2)
+    assert (cb & 0xF == q[:, 0::2] & 15).all() and (cb >> 4 == q[:, 1::2] & 15).all()
+    assert (buf[o1:o2].view(np.int8).reshape(N, K // 16) == sc).all()
+    hb = buf[o2:o3].copy().view(np.uint32).reshape(N, K // 32, 2)
+    for n in range(N):
+        for b in range(K // 32):
+            assert int(hb[n, b, 0]) == _code_bits_word(q[n, 32 * b: 32 * b + 32], 4)
+            assert int(hb[n, b, 1]) == _code_bits_word(q[n, 32 * b: 32 * b + 32], 5)
+    assert (buf[o3:].copy().view(np.uint16).reshape(N, K // 256) == d).all()
+
+
+def test_q5_k_q6_k_sizes():
+    assert nvq.nvq_q5_k_weight_bytes(1, 256) == 176 and nvq.nvq_q6_k_weight_bytes(1, 256) == 210
+    assert nvq.nvq_q5_k_weight_bytes(4096, 4096) == 4096 * 16 * 176
+    assert nvq.nvq_q6_k_weight_bytes(4096, 4096) == 4096 * 16 * 210
+    assert nvq.nvq_q5_k_weight_bytes(3, 128) == 0 and nvq.nvq_q6_k_weight_bytes(0, 256) == 0
+
+
+@pytest.mark.parametrize("bad", ["code32", "scale64", "min64"])
+def test_pack_q5_k_rejects_invalid(bad):
+    q = np.zeros((1, 256), np.uint8)
+    sc = np.zeros((1, 8), np.uint8)
+    mn = np.zeros((1, 8), np.uint8)
+    d = np.zeros((1, 1), np.uint16)
+    if bad == "code32":
+        q[0, 200] = 32
+    elif bad == "scale64":
+        sc[0, 3] = 64
+    else:
+        mn[0, 6] = 64
+    with pytest.raises(nvq.NvqError) as e:
+        nvq.nvq_pack_q5_k(q, sc, mn, d, d)
+    assert e.value.status == -3
+
+
+def test_pack_q6_k_rejects_invalid():
+    q = np.zeros((1, 256), np.uint8)
+    q[0, 255] = 64
+    with pytest.raises(nvq.NvqError) as e:
+        nvq.nvq_pack_q6_k(q, np.zeros((1, 16), np.int8), np.zeros((1, 1), np.uint16))
+    assert e.value.status == -3
+
+
+def test_packers_write_nothing_on_error():
+    # every packer checks its whole input before writing: a bad last code leaves dst as it was
+    L = nvq.lib()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    N, K = 2, 256
+    z32, z256 = np.zeros((N, K // 32), np.uint8), np.zeros((N, K // 256), np.uint16)
+    cases = {
+        "q4_1": (15, lambda q, dst: L.nvq_pack_q4_1(p(q), p(np.zeros((N, K // 32), np.uint16)),
+                                                    p(np.zeros((N, K // 32), np.uint16)), N, K, p(dst))),
+        "q4_k": (15, lambda q, dst: L.nvq_pack_q4_k(p(q), p(z32), p(z32), p(z256), p(z256), N, K, p(dst))),
+        "q5_k": (31, lambda q, dst: L.nvq_pack_q5_k(p(q), p(z32), p(z32), p(z256), p(z256), N, K, p(dst))),
+        "q6_k": (63, lambda q, dst: L.nvq_pack_q6_k(p(q), p(np.zeros((N, K // 16), np.int8)), p(z256), N, K, p(dst))),
+        "iq4_xs": (15, lambda q, dst: L.nvq_pack_iq4_xs(p(q), p(z32), p(z256), N, K, p(dst))),
+    }
+    for name, (cmax, fn) in cases.items():
+        q = np.full((N, K), cmax, np.uint8)
+        q[-1, -1] = cmax + 1
+        dst = np.full(N * K, 0xA5, np.uint8)
+        assert fn(q, dst) == -3, name
+        assert (dst == 0xA5).all(), name
+
+
 def test_pack_shape_errors():
     L = nvq.lib()
     codes = np.zeros((1, 96), np.uint8)
@@ -370,3 +477,22 @@ def test_probe_rejects():
     assert L.nvq_probe_mfma(8, 0, 0, sink, None) == ERR_SHAPE
     assert L.nvq_probe_mfma(8, 10, 0, None, None) == ERR_NULL
     assert "blocks" in nvq.last_error() or "NULL" in nvq.last_error()
+
+
+def test_q5_k_q6_k_validation_without_gpu():
+    L = nvq.lib()
+    st = None
+    # K % 256, M range, bsum16 (Q5_K only), workspace
+    assert L.nvq_gemv_q5_k(A16, A16, A2, A2, 1, 8, 128, A16, st) == -2
+    assert L.nvq_gemv_q5_k(A16, A16, A2, None, 1, 8, 256, A16, st) == -1
+    assert L.nvq_gemv_q5_k(A16, A16, A2, A2, 16, 8, 256, A16, st) == -2
+    assert L.nvq_gemv_q6_k(A16, A16, A2, 1, 8, 320, A16, st) == -2
+    assert L.nvq_gemv_q6_k(A16, MIS, A2, 1, 8, 256, A16, st) == -4
+    need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q6_K, 40, 4096, 4096)
+    assert need > 0 and need == nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q5_K, 40, 4096, 4096)
+    assert L.nvq_gemm_q6_k(A16, A16, A2, 40, 4096, 4096, A16, None, 0, st) == -7
+    assert L.nvq_gemm_q5_k(A16, A16, A2, A2, 40, 4096, 4096, A16, None, need - 1, st) == -7
+    assert L.nvq_gemm_q5_k(A16, A16, A2, A2, 8, 64, 256, A16, None, 0, st) == -2   # M < 16
+    assert L.nvq_debug_isums(nvq.NVQ_FMT_Q6_K, 1, A16, A16, 1, 8, 320, A16, st) == -2
+    assert L.nvq_debug_isums(6, 1, A16, A16, 1, 8, 256, A16, st) == -3
+

@@ -1,0 +1,145 @@
+"""GPU parity of the Q6_K x Q8_0 entries (nvq_gemv_q6_k, nvq_gemm_q6_k and the Q6_K
+debug sums) against the oracle, through the C ABI binding.  Q6_K follows the GGML
+format's rule stated in include/nvq.h (the pages only name the format): one int8 scale
+per 16 weights on 6-bit codes offset by 32; the oracle computes the same rule as its
+plain definition.  The entries take no bsum16."""
+import numpy as np
+import pytest
+
+import gemm_q8_act_amd as nvq
+from gemm_q8_act_amd import synth
+from gpu_cases import Q6KCase, check_y, host, sample_cols, say, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (1, 33, 256), (4, 70, 512), (8, 300, 4096), (15, 129, 768),
+                                   (3, 33, 20480), (2, 50, 20736)])
+def test_q6_k_gemv(oracle, M, N, K):
+    """GEMV entry: the integer-dot GEMV kernel (rows up to 20480 weights), and past it
+    the two-term kernel with one work item per tile (K = 20736)."""
+    say(f"q6_k gemv M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = Q6KCase(M, N, K, 12001 + M * N)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemv_q6_k(c.w, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q6_k gemv M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 64, 256), (17, 300, 768), (40, 77, 512), (64, 520, 1024),
+                                   (100, 130, 1024), (128, 40, 4096), (257, 77, 256), (16, 70, 20736)])
+def test_q6_k_gemm(oracle, M, N, K):
+    """GEMM entry: M = 16 on the GEMV kernel (or, past 20480 weights per row, the
+    two-term kernel), M > 16 the two-term kernel's three tile heights with K-split
+    parts on small grids, ragged N and M tiles."""
+    say(f"q6_k gemm M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = Q6KCase(M, N, K, 12103 + M + N)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q6_k(c.w, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q6_k gemm M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [512, 1])
+def test_q6_k_full_size(oracle, M):
+    """The benchmarked shape N = K = 4096 (GEMM at M = 512 on sampled columns, GEMV at
+    M = 1 in full)."""
+    say(f"q6_k M={M} N=K=4096")
+    torch = torch_dev()
+    c = Q6KCase(M, 4096, 4096, synth.seed_for("q6_k", "w"))
+    y = torch.empty((M, 4096), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemm_q6_k if M > nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemv_q6_k)(c.w, c.q, c.d, y)
+    cols = sample_cols(4096, 48, 13) if M > 1 else None
+    yo, awa = c.oracle_y(oracle, cols=cols)
+    check_y(host(y) if cols is None else host(y)[:, cols], yo, awa, f"q6_k M={M}")
+
+
+def _q6k_extreme_rows(N, K, seed):
+    """Q6_K rows across the binary16 range: largest d with scales -128 / 127 and codes 0
+    / 63, subnormal d, an all-zero row (scales 0), a row with every code 32 (value 0),
+    very different super-blocks in one row, and scales of alternating sign."""
+    qw, sc, dd = synth.q6_k_weights(N, K, seed)
+    d = dd.view(np.float16).astype(np.float32)
+    d[0], sc[0, ::2], sc[0, 1::2], qw[0, ::3] = 65504.0, -128, 127, 0
+    qw[0, 1::3] = 63
+    d[1] = 6e-8
+    sc[2] = 0
+    qw[3] = 32
+    d[4, ::2] = 2000.0
+    sc[5] = np.where(np.arange(K // 16) % 2 == 0, 100, -100).astype(np.int8)
+    return qw, sc, d.astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("M", [200, 80, 40, 8])
+def test_q6_k_extreme_weight_rows(oracle, M):
+    """Per-row weight magnitudes from ~1e-8 to 3e8 through the three two-term tile
+    shapes (M = 200, 80, 40) and the GEMV kernel (M = 8)."""
+    say(f"q6_k extreme weight rows M={M}")
+    torch = torch_dev()
+    N, K = 70, 768
+    c = Q6KCase(M, N, K, 0, weights=_q6k_extreme_rows(N, K, 1221), x=synth.activations(M, K, 1222))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    (nvq.nvq_gemm_q6_k if M > nvq.NVQ_GEMV_MAX_M else nvq.nvq_gemv_q6_k)(c.w, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q6_k extreme rows M={M}")
+    assert (host(y)[:, 2] == 0.0).all() and (host(y)[:, 3] == 0.0).all()
+
+
+@pytest.mark.parametrize("M", [200, 24])
+def test_q6_k_gemm_activation_range(oracle, M):
+    """Activation blocks with d >= 512 through the two-term kernel's second pass."""
+    say(f"q6_k gemm (M={M}) large activations")
+    torch = torch_dev()
+    N, K = 300, 768
+    x = synth.activations(M, K, 1231)
+    x[5, 3] = 1.0e6
+    x[2, :] *= 1.0e5
+    x[M // 2, K - 32:] = 8.0e6
+    c = Q6KCase(M, N, K, 1230, x=x)
+    assert ((c.dh[2] & 0x7FFF) >= 0x6000).all()
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q6_k(c.w, c.q, c.d, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q6_k large activations M={M}")
+
+
+@pytest.mark.parametrize("path,M,N,K", [(0, 1, 37, 256), (0, 3, 70, 512), (0, 15, 33, 768), (0, 2, 20, 20736),
+                                        (1, 16, 64, 256), (1, 17, 300, 768), (1, 100, 130, 1024),
+                                        (1, 512, 256, 4096), (1, 16, 40, 20736)])
+def test_q6_k_isums_bit_exact(oracle, path, M, N, K):
+    """Integer per-16 sums ((code - 32) times activation codes) of the kernel each Q6_K
+    entry dispatches, bit for bit."""
+    say(f"q6_k isums path={path} M={M} N={N} K={K}")
+    torch = torch_dev()
+    c = Q6KCase(M, N, K, 12207 + M + N)
+    isums = torch.full((M, N, K // 16), -7, dtype=torch.int32, device="cuda")
+    nvq.nvq_debug_isums(nvq.NVQ_FMT_Q6_K, path, c.w, c.q, N, isums)
+    ref = oracle.isums_q6_k(c.qw, c.qh)
+    assert (host(isums) == ref).all()
+    assert np.abs(ref).max() > 0
+
+
+def test_q6_k_gemm_split_determinism_and_guard_bands(oracle):
+    """Junk workspace on entry, bitwise-identical repeats, nothing written outside y."""
+    say("q6_k gemm K-split determinism + guard bands")
+    torch = torch_dev()
+    M, N, K = 100, 260, 1024
+    c = Q6KCase(M, N, K, 12333)
+    need = nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q6_K, M, N, K)
+    assert need > 0
+    guard = 4096
+    outs = []
+    for rep in range(2):
+        buf = torch.full((M * N + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+        y = buf[guard:guard + M * N].view(M, N)
+        ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+        nvq.nvq_gemm_q6_k(c.w, c.q, c.d, y, workspace=ws)
+        torch.cuda.synchronize()
+        b = host(buf)
+        assert (b[:guard] == 12345.0).all() and (b[guard + M * N:] == 12345.0).all()
+        outs.append(b[guard:guard + M * N].copy())
+    assert (outs[0].view(np.uint32) == outs[1].view(np.uint32)).all()
+    yo, awa = c.oracle_y(oracle, cols=np.arange(0, N, 5))
+    check_y(outs[0].reshape(M, N)[:, ::5], yo, awa, "q6_k split determinism case")
