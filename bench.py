@@ -75,7 +75,8 @@ def parse():
     p.add_argument("--tokens", type=int, default=1, help="tokens for --stack (1 or 8)")
     p.add_argument("--only-gemm", action="store_true", help="time only the prefill GEMM (profiling)")
     p.add_argument("--only-moe", action="store_true", help="time only the expert-routed decode step (profiling)")
-    p.add_argument("--only-q4-1", action="store_true", help="time only the Q4_1, Q4_K and IQ4_XS GEMVs and GEMMs (profiling)")
+    p.add_argument("--only-q4-1", action="store_true",
+                   help="time only the Q4_1, Q4_K, Q5_K, Q6_K and IQ4_XS GEMVs and GEMMs (profiling)")
     p.add_argument("--floors", action="store_true",
                    help="loads-only floors of the decode GEMV launch shapes on the layer set, and the measured "
                         "ceilings, as one JSON line")
@@ -611,6 +612,8 @@ def time_extras():
     out.update(time_act_quant())
     out.update(time_q4_1())
     out.update(time_q4x("q4_k"))
+    out.update(time_q4x("q5_k"))
+    out.update(time_q4x("q6_k"))
     out.update(time_q4x("iq4_xs"))
     out["moe_routed_gemv"] = time_moe()
     return out
@@ -682,8 +685,8 @@ def time_q4_1():
 
 
 def time_q4x(fmt):
-    """Q4_K or IQ4_XS (``fmt``) at N = K = 4096 (the Q4_1 workload's shape): the GEMV at
-    M = 1 (HBM-cold) and the GEMM at M = 512."""
+    """Q4_K, Q5_K, Q6_K or IQ4_XS (``fmt``) at N = K = 4096 (the Q4_1 workload's shape):
+    the GEMV at M = 1 (HBM-cold) and the GEMM at M = 512."""
     import torch
 
     import gemm_q8_act_amd as nvq
@@ -697,6 +700,18 @@ def time_q4x(fmt):
         gemv = lambda wi, q, d, b, y: nvq.nvq_gemv_q4_k(wi, q, d, b, y)
         gemm = lambda q, d, b, y, ws: nvq.nvq_gemm_q4_k(w, q, d, b, y, workspace=ws)
         ffmt, kname, blk = nvq.NVQ_FMT_Q4_K, "gemv_q4_1_m1_kernel<Q4_K> (v_dot4 on unsigned codes)", "144"
+    elif fmt == "q5_k":
+        w = dev_tensor(nvq.nvq_pack_q5_k(*synth.q5_k_weights(N, K, synth.seed_for("q5_k", "w"))))
+        wbytes, abytes = nvq.nvq_q5_k_weight_bytes(N, K), K * 17 // 16 + K // 8
+        gemv = lambda wi, q, d, b, y: nvq.nvq_gemv_q5_k(wi, q, d, b, y)
+        gemm = lambda q, d, b, y, ws: nvq.nvq_gemm_q5_k(w, q, d, b, y, workspace=ws)
+        ffmt, kname, blk = nvq.NVQ_FMT_Q5_K, "gemv_q4_1_m1_kernel<Q5_K> (fifth bits spliced, v_dot4)", "176"
+    elif fmt == "q6_k":
+        w = dev_tensor(nvq.nvq_pack_q6_k(*synth.q6_k_weights(N, K, synth.seed_for("q6_k", "w"))))
+        wbytes, abytes = nvq.nvq_q6_k_weight_bytes(N, K), K * 17 // 16
+        gemv = lambda wi, q, d, b, y: nvq.nvq_gemv_q6_k(wi, q, d, y)
+        gemm = lambda q, d, b, y, ws: nvq.nvq_gemm_q6_k(w, q, d, y, workspace=ws)
+        ffmt, kname, blk = nvq.NVQ_FMT_Q6_K, "gemv_q4_1_m1_kernel<Q6_K> (6-bit codes, per-16 scales, v_dot4)", "210"
     else:
         qw, ls, dd, table = synth.iq4_xs_weights(N, K, synth.seed_for("iq4_xs", "w"))
         w = dev_tensor(nvq.nvq_pack_iq4_xs(qw, ls, dd))
@@ -1151,6 +1166,8 @@ def main():
     if args.only_q4_1:
         log(json.dumps(time_q4_1()))
         log(json.dumps(time_q4x("q4_k")))
+        log(json.dumps(time_q4x("q5_k")))
+        log(json.dumps(time_q4x("q6_k")))
         log(json.dumps(time_q4x("iq4_xs")))
         return
 

@@ -721,6 +721,10 @@ def test_side_stream_and_graph_replay():
     qwx, lsx, ddx, tabx = synth.iq4_xs_weights(N, K4, 68)
     wx = to_dev(nvq.nvq_pack_iq4_xs(qwx, lsx, ddx))
     yx = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
+    w5k = to_dev(nvq.nvq_pack_q5_k(*synth.q5_k_weights(N, K4, 69)))
+    w6k = to_dev(nvq.nvq_pack_q6_k(*synth.q6_k_weights(N, K4, 70)))
+    y5k = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
+    y6k = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in x4k}
     need = max([nvq.nvq_gemm_workspace_bytes(f, M, N, K) for f in (nvq.NVQ_FMT_NVFP4, nvq.NVQ_FMT_Q4_1) for M in Ms]
                + [nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_NVFP4, 64, Nk, Kk),
                   nvq.nvq_gemm_workspace_bytes(nvq.NVQ_FMT_Q4_K, 100, N, K4)])
@@ -747,11 +751,14 @@ def test_side_stream_and_graph_replay():
             nvq.nvq_quantize_act_q8_0(x, q, d, b)
             (nvq.nvq_gemv_q4_k if M == 1 else nvq.nvq_gemm_q4_k)(w4k, q, d, b, y4k[M], **({} if M == 1 else {"workspace": wsp}))
             (nvq.nvq_gemv_iq4_xs if M == 1 else nvq.nvq_gemm_iq4_xs)(wx, tabx, q, d, yx[M], **({} if M == 1 else {"workspace": wsp}))
+            (nvq.nvq_gemv_q5_k if M == 1 else nvq.nvq_gemm_q5_k)(w5k, q, d, b, y5k[M], **({} if M == 1 else {"workspace": wsp}))
+            (nvq.nvq_gemv_q6_k if M == 1 else nvq.nvq_gemm_q6_k)(w6k, q, d, y6k[M], **({} if M == 1 else {"workspace": wsp}))
 
     def snapshot():
         return ([host(ys[M]).copy() for M in xs] + [host(ys41[M]).copy() for M in xs] + [host(yr).copy()]
                 + [host(yf).copy(), host(yk).copy()] + [host(y4k[M]).copy() for M in x4k]
-                + [host(yx[M]).copy() for M in x4k])
+                + [host(yx[M]).copy() for M in x4k] + [host(y5k[M]).copy() for M in x4k]
+                + [host(y6k[M]).copy() for M in x4k])
 
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -777,7 +784,8 @@ def test_side_stream_and_graph_replay():
         xk.mul_(-1.0)
         for x in x4k.values():
             x.mul_(-1.0)
-        for y in list(ys.values()) + list(ys41.values()) + [yr, yf, yk] + list(y4k.values()) + list(yx.values()):
+        for y in (list(ys.values()) + list(ys41.values()) + [yr, yf, yk] + list(y4k.values()) + list(yx.values())
+                  + list(y5k.values()) + list(y6k.values())):
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
