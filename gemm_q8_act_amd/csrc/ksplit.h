@@ -11,6 +11,7 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "nvq_device.h"
 
@@ -54,6 +55,13 @@ inline size_t ksplit_workspace(int64_t M, int64_t N, int64_t K) {
 // takes slots e0 + 8 (t / 512) .. + 7 of producer thread t % 512, so each load of a
 // part is a coalesced 2 KB row and one block writes whole 128-byte lines of y.
 // C describes the producer: WM wavefronts along m, TN x TM MFMA tiles per wavefront.
+// producers whose MFMA rows are tokens (C::kRowsM, the integer-MFMA kernel) rather
+// than weight rows
+template <class C, class = void>
+struct ksplit_rows_m : std::false_type {};
+template <class C>
+struct ksplit_rows_m<C, std::void_t<decltype(C::kRowsM)>> : std::integral_constant<bool, C::kRowsM> {};
+
 template <class C>
 __global__ __launch_bounds__(1024) void ksplit_reduce_kernel(const float* __restrict__ part_ws, int64_t N,
                                                              int64_t M, float scale, float* __restrict__ y,
@@ -85,6 +93,21 @@ __global__ __launch_bounds__(1024) void ksplit_reduce_kernel(const float* __rest
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] += v[pp][e];
       }
+  }
+  if constexpr (ksplit_rows_m<C>::value) {
+    // tile ij = (token tile i, weight tile j) with i = ij / TN; slot e0 + 4 h + rr holds
+    // token row 8 ((e0 % 16) / 4 + h) + 4 (lane >> 5) + rr of weight row lane % 32
+    const int ti = ij / TN, tj = ij % TN;
+    const int64_t n = n0 + wn * (32 * TN) + 32 * tj + (lane & 31);
+    if (n >= N) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t m = m0 + wm * (32 * TM) + 32 * ti + 8 * ((e0 & 15) / 4 + h) + 4 * (lane >> 5) + rr;
+        if (m < M) y[m * N + n] = s[4 * h + rr] * scale;
+      }
+    return;
   }
   const int64_t m = m0 + wm * (32 * TM) + 32 * j + (lane & 31);
   if (m >= M) return;

@@ -1,5 +1,5 @@
-// q4_1.hip -- Q4_1 (and Q4_K, IQ4_XS) weights x Q8_0 activations on gfx950 (GEMV and
-// tiled MFMA).
+// q4_1.hip -- Q4_1 (and Q4_K, Q5_K, Q6_K, IQ4_XS) weights x Q8_0 activations on gfx950
+// (GEMV and tiled MFMA).
 //
 // Q4_1 ("HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1: the same work
 // carries Q4_1 vec_dot and tiled kernels): per 32 weights an fp16 scale d and
@@ -19,15 +19,17 @@
 // exact fp32 integer (|P| <= 32*15*127 = 60960), and per element
 // acc += da*(d*P + m*bsum32).
 //
-// GEMM, M > 16 and K % 64 == 0: both operands as two binary16 terms, so the matrix
-// core accumulates whole rows (see gemm_q4_1_f16x2_kernel below).
+// GEMM, M > 16 and K % 64 == 0: the int8 matrix cores sum c*q per 32-block exactly and
+// the vector unit applies the block scales in fp32 (gemm_q4x_i8_kernel below); Q6_K,
+// with one scale per 16 weights, takes both operands as two binary16 terms instead, so
+// the fp16 matrix core accumulates whole rows (gemm_q4_1_f16x2_kernel).
 //
 // Q4_K (the same patch's "Q4_K" format; the llama.cpp 2-bit GGUF tutorial's GGML type
 // table gives its block, 256 values in 144 bytes): a 256-weight super-block holds
 // binary16 d and dmin, and each 32-weight sub-block j a 6-bit scale sc_j and a 6-bit
 // min mn_j, weight = d*sc_j*c - dmin*mn_j.  Per 32-block that is a Q4_1 block with
 // scale d*sc_j and offset -dmin*mn_j (each product exact in fp32: 11 x 6 significant
-// bits), so the GEMV and two-term kernels run it with a format parameter that only
+// bits), so the GEMV and integer-MFMA kernels run it with a format parameter that only
 // changes where a block's (scale, offset) pair comes from (BlockScales).  Device layout:
 // the codes as Q4_1 ([N][K/2], byte i = codes 2i low, 2i+1 high nibble), then one
 // 16-byte header per (row, super-block): binary16 d, binary16 dmin, and the 16 6-bit
@@ -39,7 +41,7 @@
 // codes that index a 16-entry int8 value table V, weight = d*(ls_j - 32)*V[c].  The
 // same two kernels run it: per 32-block the scale d*(ls_j - 32) (exact in fp32) and no
 // offset, the codes mapped through V by v_perm_b32 lookups (lut16) -- int8 values for
-// v_dot4 in the GEMV, exact float values for the two-term weights of the GEMM.  Layout:
+// v_dot4 in the GEMV and for the int8 operands of the GEMM.  Layout:
 // the codes as Q4_1, then one 8-byte header per (row, super-block): binary16 d and the
 // eight 6-bit ls_j as a little-endian 48-bit number.  V is a call argument.
 #include <algorithm>
@@ -665,7 +667,10 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 }
 
 // ---------------------------------------------------------------------------------
-// Two-term fp16 Q4_1 kernel (K % 64 == 0).  The weight w = d*c + m (binary16 d, m;
+// Two-term fp16 kernel (K % 64 == 0), written for Q4_1 and run for Q6_K, whose one
+// scale per 16 weights suits it better than the integer-MFMA kernel below (which would
+// need two half-zeroed MFMAs and twice the vector work per 32-block); every format
+// can still instantiate it.  The weight w = d*c + m (binary16 d, m;
 // c in 0..15) is formed in fp32 as w' = 2^s * w (one rounding) and split into
 // hi = fp16(w') and lo = fp16(w' - hi).  The power of two 2^s is chosen per weight row
 // (over the k range of the work item) from the bound |m| + 15|d| of its blocks so
@@ -1099,13 +1104,355 @@ __global__ __launch_bounds__(512, 1) void gemm_q4_1_f16x2_kernel(const uint8_t* 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Integer-MFMA kernel for the formats with one (scale, offset) per 32 weights: Q4_1,
+// Q4_K, Q5_K, IQ4_XS (K % 64 == 0).  Per 32-block b of a row the weight is
+// w = dw_b * v + mw_b with an integer code value v (Q4_1 / Q4_K: 0..15, Q5_K: 0..31,
+// IQ4_XS: the table value, -128..127, and mw = 0), so
+//     y[m][n] = sum_b da[m][b] * (dw[n][b] * S[m][n][b] + mw[n][b] * Q[m][b]),
+// S = sum over the block of v * q (an integer) and Q = sum of q.  One
+// v_mfma_i32_32x32x32_i8 gives S exactly for 32 tokens x 32 weight rows: its int8
+// operands are the activation codes and the weights' code values, both as staged.
+// The vector unit then takes each S to float and adds (S * dw) * da into a float32
+// accumulator (one rounding per product and sum; no split terms, no second pass for
+// large activation scales).  The offset term is a (K / 32)-deep product of
+// mw[n][b] and da[m][b] * Q[m][b] (an exact float: 11 x 12 significant bits), done by
+// v_mfma_f32_32x32x2f32, two blocks per instruction, into the same accumulators.
+//
+// Conditioning of the offset formats: a weight dw * c + mw can be far smaller than
+// either part (the block's line crosses zero near code c), and the two products would
+// then carry rounding errors of the parts' size.  So each block's codes are staged
+// shifted by the integer z nearest the root -mw / dw (clamped to the code range):
+// w = dw * (c - z) + (mw + dw * z).  With the root in range |mw + dw z| <= |dw| / 2,
+// so both parts of every weight are at most twice the weight; with the root outside,
+// the parts have one sign.  Either way the errors stay a few 2^-24 of sum |w * a|.
+// c - z fits int8 (|c - z| <= 31).
+//
+// MFMA rows are tokens and columns weight rows, so each lane has one weight row
+// (one dw per block and column tile) and 16 tokens, whose binary16 da are read from
+// LDS in the lanes' row order and used as fp16 operands of v_fma_mix.  Block: 512
+// threads, WN x WM wavefronts of (32 TM tokens) x (32 TN weight rows); the tile shapes,
+// work items and K-split parts are those of the two-term kernel, so the workspace is
+// the same.  LDS holds two 64-k stages: the weight code values and the activation
+// codes as int8 rows, the blocks' dw and mw (float32), da (binary16) and da * Q.
+// Q is summed here from the staged codes (v_dot4 against ones).
+//
+// DEBUG instance (the per-16 sums of this kernel's data path): the same staging and
+// int8 MFMAs, one per 16-block, with the weight operand's other 16-k half zeroed
+// (each lane half holds one 16-k half of the block); the sums are written as they are.
+// ---------------------------------------------------------------------------------
+namespace {
+constexpr int kI8Row = 80;  // bytes per LDS code row: 64 codes + 16 pad, 16-byte aligned
+
+template <int WN_, int WM_, int TN_, int TM_>
+struct QI8Cfg {
+  static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = TM_;
+  static constexpr int BN = 32 * WN * TN, BM = 32 * WM * TM;
+  static constexpr int kAcc = 16 * TN * TM;  // fp32 accumulators per thread
+  static constexpr bool kRowsM = true;       // accumulator rows are tokens (K-split reduce)
+  // one stage: weight codes [BN][80], activation codes [BM][80], then per 32-block
+  // b = 0, 1 of the stage: dw [2][BN], mw [2][BN] (float32), da [2][BM] (binary16, in
+  // lane order), da * Q [2][BM] (float32)
+  static constexpr int kOffA = BN * kI8Row;
+  static constexpr int kOffDW = kOffA + BM * kI8Row;
+  static constexpr int kOffMW = kOffDW + 2 * BN * 4;
+  static constexpr int kOffDA = kOffMW + 2 * BN * 4;
+  static constexpr int kOffSA = kOffDA + 2 * BM * 2;
+  static constexpr int kStage = kOffSA + 2 * BM * 4;
+  static constexpr int kLds = 2 * kStage;
+  static constexpr int CPT = BN * 64 / kQThreads;  // weight codes staged per thread
+  static constexpr int TPR = 64 / CPT;             // threads per weight row
+  static constexpr int ABT = BM * 64 / kQThreads;  // activation codes staged per thread
+  static constexpr int APR = 64 / ABT;             // threads per activation row
+  static_assert(WN * WM * 64 == kQThreads, "8 wavefronts");
+  static_assert(CPT == 16 || CPT == 32, "one 32-block per thread and stage");
+  static_assert(ABT == 8 || ABT == 16 || ABT == 32, "activation staging width");
+  static_assert(kLds <= 160 * 1024, "LDS");
+};
+using QI8Big = QI8Cfg<2, 4, 2, 2>;   // 128 weight rows x 256 tokens
+using QI8M128 = QI8Cfg<2, 4, 2, 1>;  // 128 weight rows x 128 tokens
+using QI8Mid = QI8Cfg<4, 2, 2, 1>;   // 256 weight rows x 64 tokens
+
+// position of token r (0..31) of a 32-token tile in the lane-ordered da row: lane half
+// h = (r >> 2) & 1 reads 16 values, element e = 4 (r >> 3) + (r & 3)
+__device__ __forceinline__ int i8_da_slot(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+}  // namespace
+
+template <class C, int FMT, bool DEBUG>
+__global__ __launch_bounds__(512, 1) void gemm_q4x_i8_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+                                                             const int8_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ d16, int64_t M,
+                                                             float* __restrict__ y, float* __restrict__ part_ws,
+                                                             int32_t* __restrict__ isums, KSplitPlan plan,
+                                                             u32x4 vtab) {
+  static_assert(FMT != kQ6K, "per-16 scales: the two-term kernel");
+  constexpr int BN = C::BN, BM = C::BM, WM = C::WM, TN = C::TN, TM = C::TM;
+  constexpr int CPT = C::CPT, TPR = C::TPR, ABT = C::ABT, APR = C::APR;
+  constexpr bool kOffset = FMT != kIQ4;  // formats with an offset term
+  constexpr uint32_t kCodes = FMT == kQ5K ? 32u : 16u;  // code range of the offset formats
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave / WM, wm = wave % WM;
+  const int64_t item = blockIdx.x;
+  int64_t tile, part = -1;
+  int t0 = 0, t1 = plan.stages;
+  if (item < plan.full) {
+    tile = item;
+  } else {
+    const int64_t it = item - plan.full;
+    tile = plan.full + it / plan.split;
+    part = it % plan.split;
+    t0 = (int)(part * plan.stages / plan.split);
+    t1 = (int)((part + 1) * plan.stages / plan.split);
+  }
+  const int64_t n0 = (tile % plan.tiles_n) * BN, m0 = (tile / plan.tiles_n) * BM;
+  const int64_t crow = K >> 1;  // code bytes per weight row
+  const int nb32 = K >> 5;      // activation scales per token row
+  const BlockScales<FMT> bsc(w, N, K);
+  constexpr int PW = BlockScales<FMT>::kWords;
+  const HighBits<FMT> hbits(w, N, K);
+  constexpr int HW = HighBits<FMT>::kHW, HS = HighBits<FMT>::kSlots;
+
+  // staging tasks: CPT codes of weight row wrow at k-offset CPT wq of the stage (all in
+  // 32-block wblk of the stage), the block's scale words and high bits; ABT activation
+  // codes of token arow at k-offset aoff (in block ablk) and the (token, block)'s
+  // binary16 d.  The threads that share a 32-block store the same dw, mw (or da,
+  // da * Q) to the same place, which keeps the staging free of branches.  Rows past
+  // N / M are clamped to valid memory and their results never stored.
+  const int wrow = tid / TPR, wq = tid % TPR;
+  const int64_t wr = min(n0 + wrow, N - 1);
+  const uint8_t* __restrict__ wbase = w + wr * crow + (CPT / 2) * wq;
+  const int wblk = (CPT * wq) >> 5;
+  const int arow = tid / APR, aoff = ABT * (tid % APR), ablk = aoff >> 5;
+  const int8_t* __restrict__ abase = q + min(m0 + arow, M - 1) * K + aoff;
+  const uint16_t* __restrict__ dbase = d16 + min(m0 + arow, M - 1) * nb32 + ablk;
+  struct Stage { Words<ABT / 4> a; Words<CPT / 8> wc; uint32_t dm[PW]; uint32_t hb[HS]; uint32_t dr; int blk; };
+  auto gload = [&](int t, Stage& x) {
+    x.wc = load_words<CPT / 8>(wbase + (int64_t)t * 32);
+    x.blk = 2 * t + wblk;
+    if (!DEBUG) bsc.load(wr, x.blk, x.dm);
+    if (HW > 0) hbits.load(wr, x.blk, x.hb);
+    x.a = load_words<ABT / 4>(abase + 64 * t);
+    x.dr = DEBUG ? 0x3C00u : (uint32_t)dbase[2 * t];
+  };
+  auto lstore = [&](int b, const Stage& x) {
+    uint8_t* st = smem + b * C::kStage;
+    // the block's scale and offset, and its code shift z (offset formats): the code
+    // nearest the root -mw / dw of the block's weight line, clamped to the code range
+    // (0 for a zero or non-finite dw)
+    float dwf = 1.0f, mwf = 0.0f;
+    uint32_t z = 0u;
+    if constexpr (!DEBUG) {
+      BlockScales<FMT>::decode(x.dm, x.blk, dwf, mwf);
+      if constexpr (kOffset) {
+        const float r = -mwf * __builtin_amdgcn_rcpf(dwf);
+        z = (uint32_t)fminf(fmaxf(__builtin_rintf(r), 0.0f), (float)(kCodes - 1));
+        mwf = __builtin_fmaf(dwf, (float)z, mwf);
+      }
+      reinterpret_cast<float*>(st + C::kOffDW)[wblk * BN + wrow] = dwf;
+      if constexpr (kOffset) reinterpret_cast<float*>(st + C::kOffMW)[wblk * BN + wrow] = mwf;
+    }
+    // weight code values as int8 bytes in k order: per packed word (codes 2i in the low,
+    // 2i + 1 in the high nibbles of byte i) the even and odd code bytes (with Q5_K's
+    // fifth bits, or IQ4_XS's table values), interleaved by two v_perm_b32; offset
+    // formats then store c - z: b = c + R - z lies in 1 .. 2R - 1 (no carry between
+    // bytes) and b - R is b ^ R for b >= R, else (b ^ R) with the bits above R set
+    Words<CPT / 4> cv;
+#pragma unroll
+    for (int h = 0; h < CPT / 8; ++h) {
+      uint32_t ce, co;
+      code_bytes<HW>(x.wc.v[h], ((CPT * wq) & 31) / 8 + h, x.hb, ce, co);
+      if constexpr (FMT == kIQ4) {
+        ce = lut16(ce, vtab);
+        co = lut16(co, vtab);
+      }
+      cv.v[2 * h] = perm(co, ce, 0x05010400u);
+      cv.v[2 * h + 1] = perm(co, ce, 0x07030602u);
+    }
+    if constexpr (kOffset && !DEBUG) {
+      constexpr uint32_t kR = 0x01010101u * kCodes;
+#pragma unroll
+      for (int v = 0; v < CPT / 4; ++v) {
+        const uint32_t bb = cv.v[v] + 0x01010101u * (kCodes - z);
+        cv.v[v] = (bb ^ kR) | ((~bb & kR) * (256u / kCodes - 2u));
+      }
+    }
+    store_words<CPT / 4>(st + wrow * kI8Row + CPT * wq, cv);
+    store_words<ABT / 4>(st + C::kOffA + arow * kI8Row + aoff, x.a);
+    if constexpr (!DEBUG) {
+      // sum of the block's codes over the APR / 2 threads that stage it
+      int s = 0;
+#pragma unroll
+      for (int v = 0; v < ABT / 4; ++v) s = dot4(x.a.v[v], 0x01010101u, s);
+      if constexpr (ABT <= 16) s += __shfl_xor(s, 1);
+      if constexpr (ABT == 8) s += __shfl_xor(s, 2);
+      const int r = arow & 31, tb = arow & ~31;
+      reinterpret_cast<uint16_t*>(st + C::kOffDA)[ablk * BM + tb + i8_da_slot(r)] = (uint16_t)x.dr;
+      if constexpr (kOffset)
+        reinterpret_cast<float*>(st + C::kOffSA)[ablk * BM + arow] = f16_bits_to_f32((uint16_t)x.dr) * (float)s;
+    }
+  };
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+  const int fr = lane & 31, hl = lane >> 5;
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef int i32x16 __attribute__((ext_vector_type(16)));
+  // fragments of 32-block u of a stage: A (tokens) and B (weights) 16 codes per lane,
+  // the lane's 16 token scales per token tile, its weight scale per weight tile; with
+  // u = 1 also the stage's offset operands (da * Q of token fr, mw of row fr, block hl)
+  struct Frag { i32x4 a[TM], b[TN]; half8_t da[TM][2]; float dw[TN]; float sa[TM], mw[TN]; };
+  auto fread = [&](int b, int u, Frag& f) {
+    const uint8_t* st = smem + b * C::kStage;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * (32 * TM) + 32 * i;
+      f.a[i] = *reinterpret_cast<const i32x4*>(st + C::kOffA + (r + fr) * kI8Row + 32 * u + 16 * hl);
+      if constexpr (!DEBUG) {
+        const half8_t* dp = reinterpret_cast<const half8_t*>(st + C::kOffDA + 2 * (u * BM + r + 16 * hl));
+        f.da[i][0] = dp[0];
+        f.da[i][1] = dp[1];
+        if (kOffset && u == 1) f.sa[i] = reinterpret_cast<const float*>(st + C::kOffSA)[hl * BM + r + fr];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wn * (32 * TN) + 32 * j + fr;
+      f.b[j] = *reinterpret_cast<const i32x4*>(st + r * kI8Row + 32 * u + 16 * hl);
+      if constexpr (!DEBUG) {
+        f.dw[j] = reinterpret_cast<const float*>(st + C::kOffDW)[u * BN + r];
+        if (kOffset && u == 1) f.mw[j] = reinterpret_cast<const float*>(st + C::kOffMW)[hl * BN + r];
+      }
+    }
+  };
+  const i32x16 zero16 = {};
+  // the products of 32-block u of stage t (t, u only locate the DEBUG sums)
+  auto mfmas = [&](const Frag& f, int t, int u) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (DEBUG) {
+          const int64_t nsb = K >> 4;
+          const int64_t n = n0 + wn * (32 * TN) + 32 * j + fr;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const i32x4 bm = hl == hh ? f.b[j] : i32x4{0, 0, 0, 0};
+            const i32x16 s = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], bm, zero16, 0, 0, 0);
+            const int64_t sb = 4 * (int64_t)t + 2 * u + hh;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int64_t m = m0 + wm * (32 * TM) + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+              if (m < M && n < N) isums[(m * N + n) * nsb + sb] = s[e];
+            }
+          }
+        } else {
+          const i32x16 s = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], zero16, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc[i][j][e] = __builtin_fmaf((float)s[e] * f.dw[j], (float)f.da[i][e >> 3][e & 7], acc[i][j][e]);
+        }
+      }
+    if constexpr (!DEBUG && kOffset) {
+      if (u == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.sa[i], f.mw[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // pipeline over stages t0 .. t1-1 (as the two-term kernel): loads clamped, loop body
+  // branch-free (after the last stage the staging writes a clamped copy nobody reads)
+  Stage x;
+  gload(t0, x);
+  lstore(0, x);
+  gload(min(t0 + 1, t1 - 1), x);
+  __syncthreads();
+  Frag f0, f1;
+  fread(0, 0, f0);
+  for (int t = t0; t < t1; ++t) {
+    const int b = (t - t0) & 1;
+    fread(b, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(b ^ 1, x);
+    mfmas(f0, t, 0);
+    gload(min(t + 2, t1 - 1), x);
+    __syncthreads();
+    fread(b ^ 1, 0, f0);
+    mfmas(f1, t, 1);
+  }
+  if constexpr (DEBUG) return;
+
+  if (part >= 0) {
+    float* dst = part_ws + ((item - plan.full) * C::kAcc) * kQThreads + tid;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dst[((i * TN + j) * 16 + e) * kQThreads] = acc[i][j][e];
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t n = n0 + wn * (32 * TN) + 32 * j + fr;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + wm * (32 * TM) + 32 * i + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (m < M) y[m * N + n] = acc[i][j][e];
+      }
+  }
+}
+
 namespace {
 // isums != nullptr: the DEBUG instance (per-16 sums, no workspace, no reduction).
 // split = false: one work item per tile (no workspace), for the GEMV entry's long rows.
 template <class C, int FMT>
+hipError_t launch_q4x_i8(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N, int64_t K,
+                         float* y, int32_t* isums, float* workspace, hipStream_t stream, bool split, u32x4 vtab) {
+  KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
+  if (!split) {
+    plan.split = 1;
+    plan.split_tiles = 0;
+    plan.full = plan.tiles;
+  }
+  const int64_t items = plan.full + plan.split_tiles * plan.split;
+  if (isums) {
+    hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4x_i8_kernel<C, FMT, true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+    if (ea != hipSuccess) return ea;
+    hipLaunchKernelGGL((gemm_q4x_i8_kernel<C, FMT, true>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
+                       stream, w, N, (int)K, q, d16, M, y, nullptr, isums, plan, vtab);
+    return hipGetLastError();
+  }
+  if (plan.split_tiles && !workspace) return hipErrorInvalidValue;  // callers size it first
+  hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_q4x_i8_kernel<C, FMT, false>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::kLds);
+  if (ea != hipSuccess) return ea;
+  hipLaunchKernelGGL((gemm_q4x_i8_kernel<C, FMT, false>), dim3((unsigned)items), dim3(kQThreads), C::kLds,
+                     stream, w, N, (int)K, q, d16, M, y, workspace, nullptr, plan, vtab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.split_tiles == 0) return e;
+  return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
+}
+
+// The Q4-family GEMM of tile shape C: the integer-MFMA kernel for the formats with one
+// (scale, offset) per 32 weights, the two-term kernel for Q6_K (one scale per 16)
+template <class C, int FMT>
 hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
                             int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream,
                             bool split = true, u32x4 vtab = u32x4{0u, 0u, 0u, 0u}) {
+  if constexpr (FMT != kQ6K)
+    return launch_q4x_i8<QI8Cfg<C::WN, C::WM, C::TN, C::TM>, FMT>(w, q, d16, M, N, K, y, isums, workspace, stream,
+                                                                  split, vtab);
   KSplitPlan plan = ksplit_plan<C::BN, C::BM>(M, N, K);
   if (!split) {
     plan.split = 1;

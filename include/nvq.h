@@ -364,10 +364,11 @@ nvq_status nvq_gemm_nvfp4_noalloc(const void* w, float w_scale, const int8_t* q,
  * 32-block multiplies the sum of that block's activation codes.  Same error bound
  * as the NVFP4 entries.  The GEMM takes a device workspace as nvq_gemm_nvfp4 does,
  * of nvq_gemm_workspace_bytes(NVQ_FMT_Q4_1, M, N, K) bytes (NULL when that is 0).
- * For M > 16 with K % 64 == 0 the GEMM forms each weight in two binary16 terms
- * (after a per-row power-of-two scaling, so any finite d, m are fine) and folds
- * each activation scale into an exact pair of binary16 values, with the same
- * second pass as nvq_gemm_nvfp4 for blocks with d >= 512.
+ * For M > 16 with K % 64 == 0 the GEMM sums code x activation code per 32-block
+ * exactly on the int8 matrix cores and applies d, m and the activation scale in
+ * float32 (any finite d, m and activation scale); each block's codes are taken
+ * relative to the code nearest the block's zero crossing (-m / d), so the scale and
+ * offset parts of a weight never dwarf the weight itself.
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_1 vec_dot
  * and tiled kernels beside the NVFP4 ones) and section 3, bias-trick paragraph (the
  * activation code sums that the offset term needs); the llama.cpp 2-bit GGUF
@@ -386,8 +387,8 @@ nvq_status nvq_gemm_q4_1(const void* w, const int8_t* q, const uint16_t* d_f16,
  * activation code sum), workspace of nvq_gemm_workspace_bytes(NVQ_FMT_Q4_K, M, N, K)
  * bytes for the GEMM.  Per 32-block a Q4_K weight is a Q4_1 weight with scale
  * d * sc and offset -dmin * mn (both exact in float32), and the Q4_1 kernels run it:
- * the integer-dot GEMV for rows up to 20480 weights, the two-term binary16 kernel
- * above that and for M > 16.  Same error bound as the NVFP4 entries.
+ * the integer-dot GEMV for rows up to 20480 weights, the integer-MFMA GEMM above that
+ * and for M > 16.  Same error bound as the NVFP4 entries.
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q4_K among the
  * patch's formats, beside its Q4_1 vec_dot and tiled kernels); the llama.cpp 2-bit
  * GGUF tutorial, GGML type table (Q4_K block). */
@@ -404,12 +405,13 @@ nvq_status nvq_gemm_q4_k(const void* w, const int8_t* q, const uint16_t* d_f16,
  * workspace (NVQ_FMT_Q5_K) as the Q4_K entries, bsum16 required.  Per 32-block a Q5_K
  * weight is the Q4_K block's scale d * sc and offset -dmin * mn on a 5-bit code: the
  * GEMV kernel splices the fifth bits into the code bytes before v_dot4_i32_i8, the
- * two-term kernel into the float code (bound 31 instead of 15).
+ * integer-MFMA GEMM into its int8 code bytes.
  * Q6_K GEMV and GEMM: no bsum16 (no offset term); workspace NVQ_FMT_Q6_K.  One scale
  * d * sc per 16 weights on the values q - 32: the GEMV kernel sums (q - 32) * a as
  * v_dot4 of the 6-bit code bytes plus v_dot4 of bytes -32, per 16-block half; the
- * two-term kernel forms d * sc * (q - 32) exactly in float32 (bound 32).
- * Same kernels, dispatch and error bound as the Q4_K entries.
+ * GEMM forms d * sc * (q - 32) exactly in float32 and splits it into two binary16
+ * terms on the fp16 matrix cores (the per-16 scales would double the integer-MFMA
+ * kernel's vector work).  Same dispatch and error bound as the Q4_K entries.
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (Q5_K and Q6_K
  * among the patch's formats); the rules are the GGML formats' (the pages give none). */
 nvq_status nvq_gemv_q5_k(const void* w, const int8_t* q, const uint16_t* d_f16,
@@ -431,7 +433,7 @@ nvq_status nvq_gemm_q6_k(const void* w, const int8_t* q, const uint16_t* d_f16, 
  * nvq_gemm_workspace_bytes(NVQ_FMT_IQ4_XS, M, N, K) bytes for the GEMM.  The Q4_1 / Q4_K
  * kernels run it: per 32-block the scale d * (ls - 32) (exact in float32), the codes
  * mapped through the table by v_perm_b32 lookups -- int8 values into v_dot4_i32_i8 in
- * the GEMV kernel, exact float values into the two-term binary16 weights of the GEMM.
+ * the GEMV kernel and into the int8 matrix-core operands of the GEMM.
  * Same error bound as the NVFP4 entries.
  * Follows: "HANDOFF: flint CPU optimization (Q4_1 + NVFP4)", section 1 (IQ4_XS among the
  * patch's formats); the llama.cpp 2-bit GGUF tutorial, GGML type table (IQ4_XS block). */
@@ -457,9 +459,11 @@ nvq_status nvq_gemm_iq4_xs(const void* w, const int8_t* table, const int8_t* q, 
  *   NVQ_PATH_GEMM      nvq_gemm_nvfp4 / nvq_gemm_q4_1 (any M >= 1): NVFP4 M = 1 the
  *                      tiled kernel, 2 <= M <= 16 the batched kernel, M > 16 the
  *                      two-term kernel of M's tile height with its K-split work items;
- *                      Q4_1 M <= 16 the GEMV kernel, M > 16 the two-term kernel
- *                      (K % 64 == 0) or the tiled kernel; Q4_K, Q5_K, Q6_K as
- *                      their entries dispatch (GEMV kernel, or the two-term kernel);
+ *                      Q4_1 M <= 16 the GEMV kernel, M > 16 the integer-MFMA
+ *                      kernel (K % 64 == 0; one int8 MFMA per 16-block, the other
+ *                      half of the weight operand zeroed) or the tiled kernel;
+ *                      Q4_K, Q5_K, Q6_K as their entries dispatch (GEMV kernel, or
+ *                      the integer-MFMA kernel; Q6_K the two-term kernel);
  *   NVQ_PATH_GEMV_DOT4 nvq_gemv_nvfp4_dot4 (NVFP4 only): the v_dot4 decode kernel,
  *                      one launch per token.
  * K % 64 == 0 (NVFP4), K % 32 == 0 (Q4_1) or K % 256 == 0 (Q4_K, Q5_K, Q6_K).

@@ -150,6 +150,17 @@ class IQ4Case:
         return o.matmul_iq4_xs(self.qw, self.ls, self.dd, self.table, self.qh, self.dh, cols=cols)
 
 
+def spike_activations(M: int, K: int, seed: int) -> np.ndarray:
+    """One large value (|x| in 500..2000) per 32-block at a position k % 4 == 0, over
+    N(0, 0.1) that quantizes to 0: every block's Q8_0 codes are one +-127 and zeros."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0.0, 0.1, (M, K)).astype(np.float32)
+    nb = K // 32
+    pos = 32 * np.arange(nb)[None, :] + 4 * rng.integers(0, 8, (M, nb))
+    x[np.arange(M)[:, None], pos] = (rng.choice([-1.0, 1.0], (M, nb)) * rng.uniform(500.0, 2000.0, (M, nb)))
+    return x
+
+
 def sample_cols(N: int, count: int, seed: int, tile: int = 128) -> np.ndarray:
     """First/last columns, both sides of tile boundaries, plus seeded random ones."""
     base = {0, 1, N - 1, N - 2}

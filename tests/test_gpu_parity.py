@@ -10,7 +10,8 @@ import pytest
 
 import gemm_q8_act_amd as nvq
 from gemm_q8_act_amd import synth
-from gpu_cases import NvCase, Q41Case, check_y, host, quantize_gpu, sample_cols, say, to_dev, torch_dev
+from gpu_cases import (NvCase, Q41Case, check_y, host, quantize_gpu, sample_cols, say, spike_activations, to_dev,
+                       torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -577,6 +578,38 @@ def test_q4_1_gemm_activation_range(oracle, M):
     nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
     yo, awa = c.oracle_y(oracle)
     check_y(host(y), yo, awa, f"q4_1 large activations M={M}")
+
+
+def _q41_cancelling_rows(N, K, seed):
+    """Q4_1 blocks whose line d * c + m crosses zero at a code z0: m is -d * z0 moved one
+    binary16 ulp toward zero, and every fourth code is z0, so those weights are a few
+    ulps of d * z0 -- thousands of times smaller than either part."""
+    qw, dw, _ = synth.q4_1_weights(N, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    z0 = rng.integers(0, 16, (N, K // 32))
+    d = dw.view(np.float16).astype(np.float32)
+    mb = (-(d * z0)).astype(np.float16).view(np.uint16)
+    mb = np.where((z0 > 0) & ((mb & 0x7FFF) > 0), mb - 1, mb).astype(np.uint16)
+    qw = qw.copy()
+    qw.reshape(N, K // 32, 32)[:, :, ::4] = z0[:, :, None]
+    return qw, dw, mb
+
+
+@pytest.mark.parametrize("M", [200, 100, 40])
+def test_q4_1_gemm_cancelling_weights(oracle, M):
+    """Weights far smaller than their scale and offset parts, met by activation blocks
+    with a single nonzero code on exactly those weights: the GEMM (every tile height)
+    stays within the bound relative to sum |w * a| (the integer-MFMA kernel stages each
+    block's codes shifted to the line's root; a plain scale-and-offset split of these
+    blocks misses the bound on about half of the outputs)."""
+    say(f"q4_1 gemm (M={M}) cancelling weights")
+    torch = torch_dev()
+    N, K = 300, 640
+    c = Q41Case(M, N, K, 0, weights=_q41_cancelling_rows(N, K, 4242), x=spike_activations(M, K, 4243))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q4_1 cancelling weights M={M}")
 
 
 @pytest.mark.parametrize("fmt,M,N", [("nvfp4", 300, 2560), ("nvfp4", 100, 5120), ("nvfp4", 40, 5120),

@@ -7,7 +7,7 @@ import pytest
 
 import gemm_q8_act_amd as nvq
 from gemm_q8_act_amd import synth
-from gpu_cases import Q5KCase, check_y, host, sample_cols, say, torch_dev
+from gpu_cases import Q5KCase, check_y, host, sample_cols, say, spike_activations, torch_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,36 @@ def test_q5_k_extreme_weight_rows(oracle, M):
     yo, awa = c.oracle_y(oracle)
     check_y(host(y), yo, awa, f"q5_k extreme rows M={M}")
     assert (host(y)[:, 2] == 0.0).all()
+
+
+def _cancelling_rows(N, K, seed):
+    """Q5_K super-blocks whose weights d sc c - dmin mn cross zero at a code z0:
+    mn = sc and dmin = fp16(d z0), and every fourth code is z0, so those weights are
+    sc times the binary16 rounding of d z0 (often 0) against parts of sc d z0."""
+    qw, sc, mn, d, dmin = synth.q5_k_weights(N, K, seed)
+    rng = np.random.default_rng(seed + 1)
+    z0 = rng.integers(1, 32, (N, K // 256))
+    df = d.view(np.float16).astype(np.float32)
+    dmin = (df * z0).astype(np.float16).view(np.uint16)
+    sc = np.maximum(sc, 1).astype(np.uint8)
+    qw = qw.copy()
+    qw.reshape(N, K // 256, 256)[:, :, ::4] = z0[:, :, None]
+    return qw, sc, sc.copy(), d, dmin
+
+
+@pytest.mark.parametrize("M", [200, 100, 40])
+def test_q5_k_gemm_cancelling_weights(oracle, M):
+    """Weights far smaller than their scale and offset parts, met by activation blocks
+    with one nonzero code on those weights (every tile height): within the bound
+    relative to sum |w * a|."""
+    say(f"q5_k gemm (M={M}) cancelling weights")
+    torch = torch_dev()
+    N, K = 300, 768
+    c = Q5KCase(M, N, K, 0, weights=_cancelling_rows(N, K, 5252), x=spike_activations(M, K, 5253))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    nvq.nvq_gemm_q5_k(c.w, c.q, c.d, c.b, y)
+    yo, awa = c.oracle_y(oracle)
+    check_y(host(y), yo, awa, f"q5_k cancelling weights M={M}")
 
 
 @pytest.mark.parametrize("M", [200, 24])
