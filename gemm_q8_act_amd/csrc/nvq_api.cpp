@@ -134,12 +134,12 @@ size_t nvq_iq4_xs_weight_bytes(int64_t N, int64_t K) {
 
 size_t nvq_gemm_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
   // fp32 partial tiles of the K-split work items that fill the last round over the
-  // compute units (two-term kernels only).
+  // compute units (the two-term and integer-MFMA GEMM kernels).
   if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return 0;
   if (fmt == NVQ_FMT_NVFP4) return nvq::gemm_nvfp4_workspace(M, N, K);
   if (fmt == NVQ_FMT_Q4_1) return nvq::gemm_q4_1_workspace(M, N, K);
   if ((fmt == NVQ_FMT_Q4_K || fmt == NVQ_FMT_IQ4_XS || fmt == NVQ_FMT_Q5_K || fmt == NVQ_FMT_Q6_K) && K % 256 == 0)
-    return nvq::gemm_q4_k_workspace(M, N, K);
+    return nvq::gemm_q4_k_workspace(M, N, K, fmt == NVQ_FMT_Q6_K);
   return 0;
 }
 

@@ -59,7 +59,7 @@ hipError_t launch_gemv_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, hipStream_t stream);
 
-// Q4_1 GEMM paths (any M >= 1): M <= 16 the GEMV kernel, M > 16 the two-term fp16
+// Q4_1 GEMM paths (any M >= 1): M <= 16 the GEMV kernel, M > 16 the integer-MFMA
 // kernel when K % 64 == 0 (it needs gemm_q4_1_workspace(M, N, K) bytes of device
 // workspace, may be 0), else the tiled kernel.  isums != nullptr selects the debug
 // variant of the kernel the shape dispatches to.
@@ -69,17 +69,19 @@ hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
 size_t gemm_q4_1_workspace(int64_t M, int64_t N, int64_t K);
 
 // Q4_K (K % 256 == 0) on the Q4_1 kernels with the Q4_K block scales.  GEMV entry
-// (M <= 16): the GEMV kernel, or for rows longer than 20480 the two-term kernel with
-// one work item per tile.  GEMM (any M >= 1): M <= 16 (rows up to 20480) the GEMV
-// kernel, else the two-term kernel with gemm_q4_k_workspace(M, N, K) bytes of device
-// workspace (may be 0).  isums != nullptr: the debug sums of the dispatched kernel.
+// (M <= 16): the GEMV kernel, or for rows longer than 20480 the integer-MFMA kernel
+// (Q6_K: the two-term kernel) with one work item per tile.  GEMM (any M >= 1): M <= 16
+// (rows up to 20480) the GEMV
+// kernel, else the integer-MFMA kernel (Q6_K: the two-term kernel) with
+// gemm_q4_k_workspace(M, N, K, fmt is Q6_K) bytes of device workspace (may be 0).
+// isums != nullptr: the debug sums of the dispatched kernel.
 hipError_t launch_gemv_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, hipStream_t stream);
 hipError_t launch_gemm_q4_k(const uint8_t* w, const int8_t* q, const uint16_t* d16,
                             const int16_t* bsum16, int64_t M, int64_t N, int64_t K, float* y,
                             int32_t* isums, float* workspace, hipStream_t stream);
-size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K);
+size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K, bool q6k);
 
 // IQ4_XS (K % 256 == 0; table: the 16 int8 values the codes index, host memory) on the
 // same kernels and with the same dispatch as Q4_K; its workspace is gemm_q4_k_workspace's.

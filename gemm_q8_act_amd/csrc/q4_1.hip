@@ -735,12 +735,16 @@ using Q41Mid = Q41Cfg<4, 2, 2, 1>;   // 256 weight rows x 64 tokens
 // which kernel runs a Q4_1 GEMM of this shape (the GEMV kernel falls back to the
 // tiled one for rows longer than 20480)
 constexpr int kQ41GemvMaxM = 16;
+// The integer-MFMA kernel takes 128 x 128 tiles up to M = 512 (half the K-split parts
+// of the 128 x 256 tile: N = K = 4096, M = 256 / 512: 35.7 / 52.1 us against 37.9 /
+// 53.0), the two-term kernel (Q6_K) only up to M = 128 (at M = 512: 72.9 us against 67.4)
+constexpr int kI8M128Max = 512, kF16M128Max = 128;
 enum Q41Path { kQ41Gemv, kQ41Tiled, kQ41Mid, kQ41M128, kQ41Big };
 Q41Path q41_path(int64_t M, int64_t K) {
   if (M <= kQ41GemvMaxM) return kQ41Gemv;
   if (K % 64 != 0) return kQ41Tiled;
   if (M <= 64) return kQ41Mid;
-  return M <= 128 ? kQ41M128 : kQ41Big;
+  return M <= kI8M128Max ? kQ41M128 : kQ41Big;
 }
 
 }  // namespace
@@ -1331,11 +1335,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q4x_i8_kernel(const uint8_t* __re
   const i32x16 zero16 = {};
   // the products of 32-block u of stage t (t, u only locate the DEBUG sums)
   auto mfmas = [&](const Frag& f, int t, int u) {
+    if constexpr (DEBUG) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (DEBUG) {
+        for (int j = 0; j < TN; ++j) {
           const int64_t nsb = K >> 4;
           const int64_t n = n0 + wn * (32 * TN) + 32 * j + fr;
 #pragma unroll
@@ -1349,13 +1353,23 @@ __global__ __launch_bounds__(512, 1) void gemm_q4x_i8_kernel(const uint8_t* __re
               if (m < M && n < N) isums[(m * N + n) * nsb + sb] = s[e];
             }
           }
-        } else {
-          const i32x16 s = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[j], zero16, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc[i][j][e] = __builtin_fmaf((float)s[e] * f.dw[j], (float)f.da[i][e >> 3][e & 7], acc[i][j][e]);
         }
+    } else {
+      // tile k's MFMA is issued before tile k - 1's sums are scaled, so the vector work
+      // covers the MFMA's latency instead of waiting for its own result
+      constexpr int T = TM * TN;
+      i32x16 sp = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[0], f.b[0], zero16, 0, 0, 0);
+#pragma unroll
+      for (int k = 1; k <= T; ++k) {
+        i32x16 sn = sp;
+        if (k < T) sn = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[k / TN], f.b[k % TN], zero16, 0, 0, 0);
+        const int i = (k - 1) / TN, j = (k - 1) % TN;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc[i][j][e] = __builtin_fmaf((float)sp[e] * f.dw[j], (float)f.da[i][e >> 3][e & 7], acc[i][j][e]);
+        sp = sn;
       }
+    }
     if constexpr (!DEBUG && kOffset) {
       if (u == 1) {
 #pragma unroll
@@ -1479,12 +1493,13 @@ hipError_t launch_q41_f16x2(const uint8_t* w, const int8_t* q, const uint16_t* d
   return launch_ksplit_reduce<C>(workspace, N, M, 1.0f, y, plan, stream);
 }
 
-// which kernel runs a Q4_K product of this shape: the GEMV kernel up to 16 tokens
-// (rows up to 20480 weights), else the two-term kernel (K % 256 == 0 always)
-Q41Path q4k_path(int64_t M, int64_t K) {
+// which kernel runs a Q4_K, Q5_K, IQ4_XS (i8) or Q6_K (!i8) product of this shape: the
+// GEMV kernel up to 16 tokens (rows up to 20480 weights), else the integer-MFMA (or
+// two-term) kernel in the tile shape for M (K % 256 == 0 always)
+Q41Path q4k_path(int64_t M, int64_t K, bool i8 = true) {
   if (M <= kQ41GemvMaxM && q41_gemv_fits(K)) return kQ41Gemv;
   if (M <= 64) return kQ41Mid;
-  return M <= 128 ? kQ41M128 : kQ41Big;
+  return M <= (i8 ? kI8M128Max : kF16M128Max) ? kQ41M128 : kQ41Big;
 }
 }  // namespace
 
@@ -1500,8 +1515,8 @@ hipError_t launch_gemm_q4_1(const uint8_t* w, const int8_t* q, const uint16_t* d
   }
 }
 
-size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K) {
-  switch (q4k_path(M, K)) {
+size_t gemm_q4_k_workspace(int64_t M, int64_t N, int64_t K, bool q6k) {
+  switch (q4k_path(M, K, !q6k)) {
     case kQ41Mid: return ksplit_workspace<Q41Mid>(M, N, K);
     case kQ41M128: return ksplit_workspace<Q41M128>(M, N, K);
     case kQ41Big: return ksplit_workspace<Q41Big>(M, N, K);
@@ -1582,7 +1597,7 @@ hipError_t launch_gemv_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d
 
 hipError_t launch_gemm_q6_k(const uint8_t* w, const int8_t* q, const uint16_t* d16, int64_t M, int64_t N,
                             int64_t K, float* y, int32_t* isums, float* workspace, hipStream_t stream) {
-  switch (q4k_path(M, K)) {
+  switch (q4k_path(M, K, false)) {
     case kQ41Gemv: return launch_gemv_q4x<kQ6K>(w, q, d16, nullptr, M, N, K, y, isums, stream);
     case kQ41Big: return launch_q41_f16x2<Q41Big, kQ6K>(w, q, d16, M, N, K, y, isums, workspace, stream);
     case kQ41M128: return launch_q41_f16x2<Q41M128, kQ6K>(w, q, d16, M, N, K, y, isums, workspace, stream);

@@ -57,7 +57,7 @@ def test_sizes():
     assert nvq.nvq_q4_1_weight_bytes(4096, 4096) == 4096 * 4096 * 5 // 8
     assert nvq.nvq_q4_1_weight_bytes(3, 32) == 3 * 20
     assert nvq.nvq_q4_1_weight_bytes(3, 48) == 0
-    # K-split workspace of the two-term GEMM (M > 16): fp32 partial tiles (one per
+    # K-split workspace of the GEMM kernels (M > 16): fp32 partial tiles (one per
     # 512-thread work item: 256 x 256 tiles with 128 accumulators per thread for
     # M > 128, 256 x 128 with 64 for M <= 128, 256 x 64 with 32 for M <= 64), for the
     # tiles of an incomplete last round over 256 compute units, split up to 16 ways (at
@@ -75,14 +75,18 @@ def test_sizes():
     assert ws(nvq.NVQ_FMT_NVFP4, 64, 17408, 5120) == 68 * 3 * mid_bytes         # 256 x 64 tiles
     assert ws(nvq.NVQ_FMT_NVFP4, 17, 300, 640) == 2 * 10 * mid_bytes
     assert ws(nvq.NVQ_FMT_NVFP4, 16, 17408, 5120) == 0                          # M <= 16: batched GEMV
-    # Q4_1, split up to 16 ways: M > 128 in 128 x 256 tiles with 64 accumulators per
-    # thread, 64 < M <= 128 in 128 x 128 tiles and 16 < M <= 64 in 256 x 64 tiles with 32
+    # Q4_1 (integer-MFMA kernel), split up to 16 ways: M > 512 in 128 x 256 tiles with 64
+    # accumulators per thread, 64 < M <= 512 in 128 x 128 tiles and 16 < M <= 64 in
+    # 256 x 64 tiles with 32
     q41_tile, q41_mid = 512 * 64 * 4, 512 * 32 * 4
     assert ws(nvq.NVQ_FMT_Q4_1, 2048, 4096, 4096) == 0                          # 256 tiles: full rounds
-    assert ws(nvq.NVQ_FMT_Q4_1, 512, 4096, 4096) == 64 * 4 * q41_tile           # 64 tiles, 256 // 64 = 4
-    assert ws(nvq.NVQ_FMT_Q4_1, 300, 19200, 256) == 44 * 4 * q41_tile           # 300 tiles: 44 left, 4 stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 1024, 4096, 4096) == 128 * 2 * q41_tile         # 128 tiles, 256 // 128 = 2
+    assert ws(nvq.NVQ_FMT_Q4_1, 512, 4096, 4096) == 128 * 2 * q41_mid           # 128 x 128 tiles
+    assert ws(nvq.NVQ_FMT_Q4_1, 300, 12800, 256) == 44 * 4 * q41_mid            # 300 tiles: 44 left, 4 stages
+    assert ws(nvq.NVQ_FMT_Q4_1, 300, 19200, 256) == 0                           # 450 tiles: 194 left, 256 // 194 = 1
     assert ws(nvq.NVQ_FMT_Q4_1, 100, 8, 640) == 1 * 10 * q41_mid                # split <= stages
-    assert ws(nvq.NVQ_FMT_Q4_1, 200, 8, 640) == 1 * 10 * q41_tile
+    assert ws(nvq.NVQ_FMT_Q4_1, 200, 8, 640) == 2 * 10 * q41_mid
+    assert ws(nvq.NVQ_FMT_Q4_1, 600, 8, 640) == 3 * 10 * q41_tile
     assert ws(nvq.NVQ_FMT_Q4_1, 64, 4096, 4096) == 16 * 16 * q41_mid            # 16 tiles of 256 rows
     assert ws(nvq.NVQ_FMT_Q4_1, 17, 8, 64) == 0                                 # one stage: no split
     assert ws(nvq.NVQ_FMT_Q4_1, 16, 4096, 4096) == 0                            # M <= 16: tiled kernel
@@ -406,7 +410,7 @@ def test_gemm_validation_without_gpu():
     assert L.nvq_gemv_nvfp4_dot4(A16, 1.0, A16, A16, 16, 8, 64, A16, None) == -2
     assert L.nvq_debug_isums(1, 0, A16, A16, 1, 8, 48, A16, None) == -2
     assert L.nvq_debug_isums(2, 0, A16, A16, 1, 8, 128, A16, None) == -2   # Q4_K: K % 256
-    # Q4_K entries: K % 256, bsum16 required, M ranges, workspace for the two-term kernel
+    # Q4_K entries: K % 256, bsum16 required, M ranges, workspace for the integer-MFMA kernel
     assert L.nvq_gemv_q4_k(A16, A16, A16, A2, 1, 8, 128, A16, None) == -2
     assert L.nvq_gemv_q4_k(A16, A16, A16, None, 1, 8, 256, A16, None) == -1
     assert L.nvq_gemv_q4_k(A16, A16, A16, A2, 16, 8, 256, A16, None) == -2

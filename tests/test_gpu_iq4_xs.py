@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
                                    (3, 33, 20480), (2, 50, 20736)])
 def test_iq4_xs_gemv(oracle, M, N, K):
     """GEMV entry: the integer-dot GEMV kernel with the table lookups, and past 20480
-    weights per row the two-term kernel with one work item per tile."""
+    weights per row the integer-MFMA kernel with one work item per tile."""
     say(f"iq4_xs gemv M={M} N={N} K={K}")
     torch = torch_dev()
     c = IQ4Case(M, N, K, 8001 + M * N)
@@ -29,8 +29,9 @@ def test_iq4_xs_gemv(oracle, M, N, K):
 @pytest.mark.parametrize("M,N,K", [(16, 64, 256), (17, 300, 768), (40, 77, 512), (100, 130, 1024),
                                    (128, 40, 4096), (257, 77, 256), (16, 70, 20736)])
 def test_iq4_xs_gemm(oracle, M, N, K):
-    """GEMM entry: M = 16 on the GEMV kernel (or the two-term kernel past 20480 weights
-    per row), M > 16 the two-term kernel's three tile heights with K-split parts."""
+    """GEMM entry: M = 16 on the GEMV kernel (or the integer-MFMA kernel past 20480
+    weights per row), M > 16 the integer-MFMA kernel's three tile heights with K-split
+    parts."""
     say(f"iq4_xs gemm M={M} N={N} K={K}")
     torch = torch_dev()
     c = IQ4Case(M, N, K, 8103 + M + N)
@@ -68,7 +69,7 @@ def _iq4_special(N, K, seed, table):
 @pytest.mark.parametrize("kind", ["extremes", "affine"])
 def test_iq4_xs_special_rows_and_tables(oracle, M, kind):
     """Tables holding -128 and 127 (the int8 extremes) or the affine c - 8; rows up to
-    65504 * 32 * 128 in magnitude, a zero row; through the two-term tile heights
+    65504 * 32 * 128 in magnitude, a zero row; through the integer-MFMA tile heights
     (M = 200, 40) and the GEMV kernel (M = 8, 1)."""
     say(f"iq4_xs special rows M={M} table={kind}")
     torch = torch_dev()

@@ -471,8 +471,8 @@ def test_q4_1_gemm_full_size(oracle):
                                    (96, 64, 96), (128, 40, 4096), (17, 300, 640), (40, 77, 192),
                                    (64, 520, 1024), (50, 64, 96)])
 def test_q4_1_gemm_large_m(oracle, M, N, K):
-    """M > 16: the two-term fp16 kernels (256 x 64 tiles up to M = 64, 128 x 128 up to
-    M = 128, 128 x 256 above; K % 64 == 0; K-split parts on small grids, ragged N and M
+    """M > 16: the integer-MFMA kernel (256 x 64 tiles up to M = 64, 128 x 128 up to
+    M = 512, 128 x 256 above; K % 64 == 0; K-split parts on small grids, ragged N and M
     tiles, N % 4 != 0) and the tiled kernel (K = 96)."""
     say(f"q4_1 gemm M={M} N={N} K={K}")
     torch = torch_dev()
@@ -484,16 +484,16 @@ def test_q4_1_gemm_large_m(oracle, M, N, K):
 
 
 def test_q4_1_gemm_full_and_split_tiles(oracle):
-    """300 weight tiles: 256 whole-K work items plus 44 tiles split along K."""
-    say("q4_1 gemm M=300 N=19200 K=256")
+    """300 tiles of 128 x 128: 256 whole-K work items plus 44 tiles split along K."""
+    say("q4_1 gemm M=300 N=12800 K=256")
     torch = torch_dev()
-    M, N, K = 300, 19200, 256
+    M, N, K = 300, 12800, 256
     c = Q41Case(M, N, K, 8181)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     nvq.nvq_gemm_q4_1(c.w, c.q, c.d, c.b, y)
     cols = sample_cols(N, 64, 5)
     yo, awa = c.oracle_y(oracle, cols=cols)
-    check_y(host(y)[:, cols], yo, awa, "q4_1 M=300 N=19200")
+    check_y(host(y)[:, cols], yo, awa, "q4_1 M=300 N=12800")
 
 
 def _q41_extreme_rows(N, K, seed):
@@ -514,7 +514,7 @@ def _q41_extreme_rows(N, K, seed):
 @pytest.mark.parametrize("M,N,K", [(200, 70, 640), (80, 70, 640), (40, 70, 640), (8, 70, 640)])
 def test_q4_1_extreme_weight_rows(oracle, M, N, K):
     """Per-row weight magnitudes from 6e-8 to 1e6 in one matrix, through the three
-    two-term GEMM tile shapes (M = 200, 80, 40) and the GEMV (M = 8)."""
+    integer-MFMA GEMM tile shapes (M = 200, 80, 40) and the GEMV (M = 8)."""
     say(f"q4_1 extreme weight rows M={M}")
     torch = torch_dev()
     c = Q41Case(M, N, K, 0, weights=_q41_extreme_rows(N, K, 919), x=synth.activations(M, K, 920))
@@ -553,7 +553,8 @@ def test_q4_1_gemm_split_determinism_and_guard_bands(oracle, M):
 
 def _large_activations(M, K, seed):
     """Activations that reach past the binary16 range once scaled: blocks with d >= 512
-    (the two-term kernels' second pass), one token with every block that large, one
+    (the NVFP4 two-term kernel's second pass; the Q4_1 integer-MFMA kernel applies d in
+    float32), one token with every block that large, one
     block just below the threshold (|d * q| near 60000, main pass), the rest N(0, 1)."""
     x = synth.activations(M, K, seed)
     x[5, 3] = 1.0e6                                        # d ~ 7874
@@ -566,9 +567,9 @@ def _large_activations(M, K, seed):
 
 @pytest.mark.parametrize("M", [200, 96, 24])
 def test_q4_1_gemm_activation_range(oracle, M):
-    """Q4_1 two-term kernels (M > 16): activations whose scaled values pass the binary16
-    range (blocks with d >= 512) are exact through the second pass, every tile height
-    and K-split parts included."""
+    """Q4_1 GEMM (M > 16, the integer-MFMA kernel): activations whose scaled values pass
+    the binary16 range (blocks with d >= 512), every tile height and K-split parts
+    included."""
     say(f"q4_1 gemm (M={M}) large activations")
     torch = torch_dev()
     N, K = 300, 640
@@ -615,9 +616,9 @@ def test_q4_1_gemm_cancelling_weights(oracle, M):
 @pytest.mark.parametrize("fmt,M,N", [("nvfp4", 300, 2560), ("nvfp4", 100, 5120), ("nvfp4", 40, 5120),
                                       ("q4_1", 300, 2560), ("q4_1", 100, 2560), ("q4_1", 40, 5120)])
 def test_gemm_ksplit_many_parts(oracle, fmt, M, N):
-    """20 (or 40) tiles of 20 stages in the last round, each split into 12 (or 6) K
-    parts summed in order; repeat calls bitwise identical.  One shape per token-tile
-    height and format."""
+    """Tiles of 20 stages in a last round far short of the compute units, each split
+    into several K parts (up to 12) summed in order; repeat calls bitwise identical.
+    One shape per token-tile height and format."""
     say(f"{fmt} gemm K-split parts M={M} N={N}")
     torch = torch_dev()
     K = 1280
@@ -668,7 +669,7 @@ def test_q4_1_isums_bit_exact(oracle, path):
         assert (host(isums) == oracle.isums_q4_1(c.qw, c.qh)).all(), (M, N, K)
 
 
-# Q4_1 GEMM dispatch for M > 16: the two-term kernel (K % 64 == 0; its three tile
+# Q4_1 GEMM dispatch for M > 16: the integer-MFMA kernel (K % 64 == 0; its three tile
 # shapes, K-split parts on small grids) or the tiled kernel (K = 96).
 @pytest.mark.parametrize("M,N,K", [(17, 300, 640), (40, 77, 192), (64, 520, 1024), (100, 130, 1024),
                                    (128, 40, 4096), (200, 70, 640), (512, 256, 4096), (20, 33, 96)])
@@ -743,7 +744,7 @@ def test_side_stream_and_graph_replay():
     qk = torch.empty((64, Kk), dtype=torch.int8, device="cuda")
     dk = torch.empty((64, Kk // 32), dtype=torch.int16, device="cuda")
     yk = torch.empty((64, Nk), dtype=torch.float32, device="cuda")
-    # Q4_K (K % 256 == 0): GEMV at M = 1 and the two-term GEMM with K-split parts at M = 100
+    # Q4_K (K % 256 == 0): GEMV at M = 1 and the integer-MFMA GEMM with K-split parts at M = 100
     K4 = 768
     w4k = to_dev(nvq.nvq_pack_q4_k(*synth.q4_k_weights(N, K4, 66)))
     x4k = {M: to_dev(synth.activations(M, K4, 67 + M)) for M in (1, 100)}

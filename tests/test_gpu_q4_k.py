@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
                                    (3, 33, 20480), (2, 50, 20736), (1, 40, 24576)])
 def test_q4_k_gemv(oracle, M, N, K):
     """GEMV entry: the integer-dot GEMV kernel (rows up to 20480 weights), and past it
-    the two-term kernel with one work item per tile (K = 20736, 24576)."""
+    the integer-MFMA kernel with one work item per tile (K = 20736, 24576)."""
     say(f"q4_k gemv M={M} N={N} K={K}")
     torch = torch_dev()
     c = Q4KCase(M, N, K, 7001 + M * N)
@@ -30,7 +30,7 @@ def test_q4_k_gemv(oracle, M, N, K):
                                    (100, 130, 1024), (128, 40, 4096), (257, 77, 256), (16, 70, 20736)])
 def test_q4_k_gemm(oracle, M, N, K):
     """GEMM entry: M = 16 on the GEMV kernel (or, past 20480 weights per row, the
-    two-term kernel with K-split parts), M > 16 the two-term kernel's three tile
+    integer-MFMA kernel with K-split parts), M > 16 the integer-MFMA kernel's three tile
     heights with K-split parts on small grids, ragged N and M tiles."""
     say(f"q4_k gemm M={M} N={N} K={K}")
     torch = torch_dev()
@@ -72,7 +72,7 @@ def _q4k_extreme_rows(N, K, seed):
 
 @pytest.mark.parametrize("M", [200, 80, 40, 8])
 def test_q4_k_extreme_weight_rows(oracle, M):
-    """Per-row weight magnitudes from ~1e-8 to 4e6 through the three two-term tile
+    """Per-row weight magnitudes from ~1e-8 to 4e6 through the three integer-MFMA tile
     shapes (M = 200, 80, 40) and the GEMV kernel (M = 8)."""
     say(f"q4_k extreme weight rows M={M}")
     torch = torch_dev()
@@ -118,7 +118,7 @@ def test_q4_k_gemm_cancelling_weights(oracle, M):
 @pytest.mark.parametrize("M", [200, 24])
 def test_q4_k_gemm_activation_range(oracle, M):
     """Activation blocks with d >= 512 (scaled values past the binary16 range) through
-    the two-term kernel's second pass."""
+    the integer-MFMA kernel (d applied in float32)."""
     say(f"q4_k gemm (M={M}) large activations")
     torch = torch_dev()
     N, K = 300, 768
@@ -139,7 +139,7 @@ def test_q4_k_gemm_activation_range(oracle, M):
                                         (1, 512, 256, 4096), (1, 16, 40, 20736)])
 def test_q4_k_isums_bit_exact(oracle, path, M, N, K):
     """Integer per-16 sums of the kernel each Q4_K entry dispatches (GEMV kernel, or the
-    two-term kernel with its K-split work items), bit for bit."""
+    integer-MFMA kernel with its K-split work items), bit for bit."""
     say(f"q4_k isums path={path} M={M} N={N} K={K}")
     torch = torch_dev()
     c = Q4KCase(M, N, K, 7207 + M + N)

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
                                    (3, 33, 20480), (2, 50, 20736)])
 def test_q5_k_gemv(oracle, M, N, K):
     """GEMV entry: the integer-dot GEMV kernel (rows up to 20480 weights), and past it
-    the two-term kernel with one work item per tile (K = 20736)."""
+    the integer-MFMA kernel with one work item per tile (K = 20736)."""
     say(f"q5_k gemv M={M} N={N} K={K}")
     torch = torch_dev()
     c = Q5KCase(M, N, K, 11001 + M * N)
@@ -30,7 +30,7 @@ def test_q5_k_gemv(oracle, M, N, K):
                                    (100, 130, 1024), (128, 40, 4096), (257, 77, 256), (16, 70, 20736)])
 def test_q5_k_gemm(oracle, M, N, K):
     """GEMM entry: M = 16 on the GEMV kernel (or, past 20480 weights per row, the
-    two-term kernel), M > 16 the two-term kernel's three tile heights with K-split
+    integer-MFMA kernel), M > 16 the integer-MFMA kernel's three tile heights with K-split
     parts on small grids, ragged N and M tiles."""
     say(f"q5_k gemm M={M} N={N} K={K}")
     torch = torch_dev()
@@ -73,7 +73,7 @@ def _q5k_extreme_rows(N, K, seed):
 
 @pytest.mark.parametrize("M", [200, 80, 40, 8])
 def test_q5_k_extreme_weight_rows(oracle, M):
-    """Per-row weight magnitudes from ~1e-8 to 1e8 through the three two-term tile
+    """Per-row weight magnitudes from ~1e-8 to 1e8 through the three integer-MFMA tile
     shapes (M = 200, 80, 40) and the GEMV kernel (M = 8)."""
     say(f"q5_k extreme weight rows M={M}")
     torch = torch_dev()
@@ -118,7 +118,7 @@ def test_q5_k_gemm_cancelling_weights(oracle, M):
 
 @pytest.mark.parametrize("M", [200, 24])
 def test_q5_k_gemm_activation_range(oracle, M):
-    """Activation blocks with d >= 512 through the two-term kernel's second pass."""
+    """Activation blocks with d >= 512 through the integer-MFMA kernel (d applied in float32)."""
     say(f"q5_k gemm (M={M}) large activations")
     torch = torch_dev()
     N, K = 300, 768
