@@ -49,6 +49,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
+INT8_PEAK_TOPS = 5000.0
+# The integer-MFMA Q4-family GEMM is bound by its vector work: per output and 32-block a
+# float conversion, a scale multiply and one fma (3 wave64 instructions per 64 lanes, 4
+# cycles each), against 64 useful flops.  1024 SIMDs x 2.4 GHz / 4 x 64 / 3 x 64 flops:
+I8_GEMM_VALU_CEILING_TFLOPS = 1024 * 2.4e9 / 4 * 64 / 3 * 64 / 1e12
 METRIC = "NVFP4×Q8_0 GEMV weight GB/s (M=1) and GEMM TOPS (M=2048), % of roofline"
 
 
@@ -679,8 +684,12 @@ def time_q4_1():
             us = _event_time(lambda: nvq.nvq_gemm_q4_1(w, q, d, b, y, workspace=wsq), 20)
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
             out["q4_1_gemm_M512_N4096_K4096"] = dict(
-                us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
-                note="fp16 MFMA, three passes per product (weight and activation each split in two terms)")
+                us_avg=us, TFLOPs=tf, frac=tf / INT8_PEAK_TOPS,
+                frac_of_valu_ceiling=tf / I8_GEMM_VALU_CEILING_TFLOPS,
+                note="int8 MFMA (one exact code x activation sum per 32-block), block scales applied in fp32 "
+                     "on the vector unit; frac against the int8 dense peak, frac_of_valu_ceiling against the "
+                     f"{I8_GEMM_VALU_CEILING_TFLOPS:.0f} TFLOP/s the scaling's 3 vector instructions per output "
+                     "and 32-block allow")
     return out
 
 
@@ -744,9 +753,16 @@ def time_q4x(fmt):
             wsq = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
             us = _event_time(lambda: gemm(q, d, b, y, wsq), 20)
             tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
-            out[f"{fmt}_gemm_M512_N4096_K4096"] = dict(
-                us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
-                note="the Q4_1 two-term kernel with this format's block scales (three fp16 MFMA passes per product)")
+            if fmt == "q6_k":
+                out[f"{fmt}_gemm_M512_N4096_K4096"] = dict(
+                    us_avg=us, TFLOPs=tf, frac=tf / FP16_PEAK_TFLOPS,
+                    note="the two-term fp16 kernel (one scale per 16 weights; three fp16 MFMA passes per product)")
+            else:
+                out[f"{fmt}_gemm_M512_N4096_K4096"] = dict(
+                    us_avg=us, TFLOPs=tf, frac=tf / INT8_PEAK_TOPS,
+                    frac_of_valu_ceiling=tf / I8_GEMM_VALU_CEILING_TFLOPS,
+                    note="the Q4_1 integer-MFMA kernel with this format's block scales (frac against the int8 "
+                         "dense peak)")
     return out
 
 
