@@ -173,7 +173,15 @@ class Layer:
 KERNEL_SOURCES = {
     "gemv_nvfp4_gate_up": ("gemv_nvfp4.hip", "nvq_device.h"),
     "gemv_nvfp4_fused_gate_up": ("gemv_nvfp4.hip", "nvq_device.h"),
+    "gemm_nvfp4_m2048": ("gemm_nvfp4.hip", "ksplit.h", "nvq_device.h"),
+    "gemm_q4_1_m512": ("q4_1.hip", "ksplit.h", "nvq_device.h"),
 }
+
+
+def gemm_alg_bytes(fmt, M, N, K):
+    """Algorithmic bytes of one GEMM call: packed weights + Q8_0 codes and scales + fp32 y."""
+    wb = N * K * 9 // 16 if fmt == "nvfp4" else N * K * 5 // 8
+    return wb + M * K + M * (K // 32) * 2 + 4 * M * N
 
 
 def _code_only(text):
@@ -686,6 +694,7 @@ def time_q4_1():
             out["q4_1_gemm_M512_N4096_K4096"] = dict(
                 us_avg=us, TFLOPs=tf, frac=tf / INT8_PEAK_TOPS,
                 frac_of_valu_ceiling=tf / I8_GEMM_VALU_CEILING_TFLOPS,
+                traffic=load_traffic("gemm_q4_1_m512"), alg_bytes_per_launch=gemm_alg_bytes("q4_1", M, N, K),
                 note="int8 MFMA (one exact code x activation sum per 32-block), block scales applied in fp32 "
                      "on the vector unit; frac against the int8 dense peak, frac_of_valu_ceiling against the "
                      f"{I8_GEMM_VALU_CEILING_TFLOPS:.0f} TFLOP/s the scaling's 3 vector instructions per output "
@@ -1017,6 +1026,33 @@ def traffic_probe():
     torch.cuda.synchronize()
     log(f"traffic probe: copy {n} B; 4 x gate+up GEMV and 4 x fused gate+up N={N} K={K}, "
         f"{nvfp4_bytes(N, K)} weight bytes each")
+    del wl, w0, w
+    # the prefill GEMM (M = 2048, N = 17408, K = 5120) and the Q4_1 GEMM (M = 512,
+    # N = K = 4096), two calls each on the bench's inputs
+    for fmt, (M, N, K) in (("nvfp4", (2048, 17408, 5120)), ("q4_1", (512, 4096, 4096))):
+        if fmt == "nvfp4":
+            codes, scales, ws = synth.nvfp4_weights(N, K, synth.seed_for("prefill", "w") + M)
+            w = dev_tensor(nvq.nvq_pack_nvfp4(codes, scales))
+            x = dev_tensor(synth.activations(M, K, synth.seed_for("prefill", "x") + M, outliers=True))
+        else:
+            qw, dw, mw = synth.q4_1_weights(N, K, synth.seed_for("q4_1", "w"))
+            w = dev_tensor(nvq.nvq_pack_q4_1(qw, dw, mw))
+            x = dev_tensor(synth.activations(M, K, synth.seed_for("q4_1", "x") + M))
+        q = torch.empty((M, K), dtype=torch.int8, device="cuda")
+        d = torch.empty((M, K // 32), dtype=torch.int16, device="cuda")
+        b = torch.empty((M, K // 16), dtype=torch.int16, device="cuda")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        nvq.nvq_quantize_act_q8_0(x, q, d, b)
+        fmt_id = nvq.NVQ_FMT_NVFP4 if fmt == "nvfp4" else nvq.NVQ_FMT_Q4_1
+        wsp = torch.empty(max(nvq.nvq_gemm_workspace_bytes(fmt_id, M, N, K), 16), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(2):
+            if fmt == "nvfp4":
+                nvq.nvq_gemm_nvfp4(w, ws, q, d, y, workspace=wsp)
+            else:
+                nvq.nvq_gemm_q4_1(w, q, d, b, y, workspace=wsp)
+        torch.cuda.synchronize()
+        log(f"traffic probe: 2 x {fmt} GEMM M={M} N={N} K={K}")
 
 
 def summarize_pmc(fetch_csv, write_csv):
@@ -1032,7 +1068,7 @@ def summarize_pmc(fetch_csv, write_csv):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
                 acc[r["Dispatch_Id"]] += float(r["Counter_Value"])
-                names[r["Dispatch_Id"]] = (r["Kernel_Name"].split("(")[0], r.get("Grid_Size", ""))
+                names[r["Dispatch_Id"]] = (short_kernel_name(r["Kernel_Name"]), r.get("Grid_Size", ""))
         return [(names[i][0], names[i][1], v) for i, v in acc.items()]
 
     f = dispatches(fetch_csv, "FETCH_SIZE")
@@ -1053,6 +1089,23 @@ def summarize_pmc(fetch_csv, write_csv):
                 kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
                 bytes_per_launch=(vf * ff + vw * fw) * 1024, alg_bytes_per_launch=alg,
                 src_hash=kernel_src_hash(key))
+    # GEMM calls: the main kernel and its K-split reduction, summed per call
+    for key, main, red, alg in (("gemm_nvfp4_m2048", "gemm_nvfp4_kernel<", "ksplit_reduce_kernel<NvCfg<",
+                                 gemm_alg_bytes("nvfp4", 2048, 17408, 5120)),
+                                ("gemm_q4_1_m512", "gemm_q4x_i8_kernel<", "ksplit_reduce_kernel<QI8Cfg<",
+                                 gemm_alg_bytes("q4_1", 512, 4096, 4096))):
+        parts = {}
+        for label, name in (("main", main), ("reduce", red)):
+            gf = [(k, g, v) for k, g, v in f if k.startswith(name)]
+            gw = [v for k, g, v in wr if k.startswith(name)]
+            if gf:
+                vf, vw = float(np.mean([v for _, _, v in gf])), float(np.mean(gw)) if gw else 0.0
+                parts[label] = dict(kernel=gf[0][0], grid=gf[0][1], dispatches=len(gf), fetch_kib=vf, write_kib=vw,
+                                    bytes=(vf * ff + vw * fw) * 1024)
+        if "main" in parts:
+            res[key] = dict(parts=parts, bytes_per_launch=sum(p["bytes"] for p in parts.values()),
+                            alg_bytes_per_launch=alg, src_hash=kernel_src_hash(key),
+                            note="per call: the main kernel plus its K-split reduction")
     print(json.dumps(res, indent=1))
 
 
@@ -1254,7 +1307,8 @@ def main():
         line["gemm"] = dict(metric="NVFP4xQ8_0 prefill GEMM TFLOP/s (M=2048, N=17408, K=5120)",
                             value=g2["TFLOPs"], unit="TFLOP/s",
                             roofline=dict(bound="mfma", achieved=g2["TFLOPs"], peak=FP16_PEAK_TFLOPS,
-                                          unit="TFLOP/s", frac=g2["frac"], traffic=None,
+                                          unit="TFLOP/s", frac=g2["frac"], traffic=load_traffic("gemm_nvfp4_m2048"),
+                                          alg_bytes_per_launch=gemm_alg_bytes("nvfp4", 2048, 17408, 5120),
                                           kernel="gemm_nvfp4_kernel<NvCfg<1,8,8,1>> + ksplit_reduce_kernel (fp16 "
                                                  "MFMA 32x32x16 on the exact hi/lo activation split)",
                                           mfma_issued_frac=2.0 * g2["frac"],
