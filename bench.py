@@ -1201,7 +1201,7 @@ def main():
     SPIN_UP_S = args.spin_up
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {ws}).", file=sys.stderr, flush=True)
         sys.exit(2)
     import torch

@@ -90,3 +90,17 @@ def test_src_hash_ignores_comments():
     b = "int f(int x) {\n  return x + 1; }  // changed comment\n"
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(a.replace("+ 1", "+ 2"))
+
+
+@pytest.mark.parametrize("argv, env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """Only one GPU is measured: asking for more exits with status 2 and says why,
+    before anything touches a device."""
+    import subprocess
+
+    e = dict(os.environ, **env)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                       env=e, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
