@@ -193,10 +193,16 @@ def _code_only(text):
 
 
 def kernel_src_hash(kernel_key):
+    """Hash of the kernel's sources (comments stripped) and of the per-file compiler
+    options they are built with: a record is stale once either changes."""
+    from gemm_q8_act_amd import build as nvq_build
+
     h = hashlib.sha256()
     for f in sorted(KERNEL_SOURCES[kernel_key]):
         with open(os.path.join(ROOT, "gemm_q8_act_amd", "csrc", f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
+        if nvq_build.FILE_FLAGS.get(f):
+            h.update(" ".join(nvq_build.FILE_FLAGS[f]).encode())
     return h.hexdigest()[:16]
 
 
