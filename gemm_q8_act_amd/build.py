@@ -34,9 +34,15 @@ FLAGS = [
 # the scheduler's "unclustered high register pressure" rescheduling stage the integer-MFMA
 # GEMM runs 7 % faster at M = 2048 (146.5 -> 136.4 us at N = K = 4096), IQ4_XS's 4 % at
 # M = 512 and Q6_K's two-term GEMM 1.5 %, every other kernel of the file within 0.5 %,
-# results bit-identical.  The other files keep the default schedule.
+# results bit-identical.  gemv_batch_f16.hip and gemv_nvfp4.hip (decode): the compiler
+# raises a wavefront's priority while it issues its loads, so the weight stream starts
+# sooner: the 64-layer stack at M = 8 3.0 -> 3.04 TB/s (O 7.5 -> 7.3 us, gate+up 20.8 ->
+# 20.3), at M = 1 4.18 -> 4.22 TB/s (fused QKV 6.72 -> 6.63 us, O 6.53 -> 6.42); the same
+# option slows the prefill GEMM 2 %.  The other files keep the default schedule.
 FILE_FLAGS = {
     "q4_1.hip": ["-mllvm", "-amdgpu-disable-unclustered-high-rp-reschedule"],
+    "gemv_batch_f16.hip": ["-mllvm", "-amdgpu-set-wave-priority"],
+    "gemv_nvfp4.hip": ["-mllvm", "-amdgpu-set-wave-priority"],
 }
 
 
