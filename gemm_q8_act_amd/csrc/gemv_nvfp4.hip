@@ -37,14 +37,12 @@
 //    costs as much time as streaming the bytes, so it is the slower of the two.
 //
 // Fused quantization (gemv_tile_fused, MODE_MX, one token): the block reads the
-// float32 row x instead of its Q8_0 codes and quantizes it into its LDS table: in
-// blocks of up to 8 wavefronts each wavefront exactly the chunks it consumes (no block
-// barrier: no wavefront reads another's entries), in 16-wavefront blocks the whole
-// block the whole row, then one block barrier.  The float4 loads are issued first, then
-// the first batch of weight loads, and the quantization runs while that batch is in
-// flight.  No separate quantization launch (and no round trip of the codes through
-// memory) precedes the product.  The codes are bit-exact with nvq_quantize_act_q8_0
-// (see q8_0_pack4).
+// float32 row x instead of its Q8_0 codes and quantizes it into its LDS table, each
+// wavefront exactly the chunks it consumes (no block barrier: no wavefront reads
+// another's entries).  The float4 loads are issued first, then the first batch of
+// weight loads, and the quantization runs while that batch is in flight.  No separate
+// quantization launch (and no round trip of the codes through memory) precedes the
+// product.  The codes are bit-exact with nvq_quantize_act_q8_0 (see q8_0_pack4).
 
 #include "nvq_device.h"
 #include "nvq_launch.h"
@@ -260,16 +258,14 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ w, int64_t
 }
 
 // One 16-row tile of the product with the Q8_0 quantization of the float32 row x
-// fused in (MODE_MX inner loop, as gemv_tile).  Prologue, W <= 8: wavefront v consumes
-// the chunks c = v, v + W, ...; its lane l loads the float4 group 32 c + l % 32 (k =
-// 128 c + 4 (l % 32) .. + 3) of chunks c = v + W (2 u + l / 32), u < XU (8 consecutive
-// lanes hold one 32-value block, all in the row or all past it), then issues the first
+// fused in (MODE_MX inner loop, as gemv_tile).  Prologue: wavefront v consumes the
+// chunks c = v, v + W, ...; its lane l loads the float4 group 32 c + l % 32 (k = 128 c
+// + 4 (l % 32) .. + 3) of chunks c = v + W (2 u + l / 32), u < XU (8 consecutive lanes
+// hold one 32-value block, all in the row or all past it), then issues the first
 // weight batch, then quantizes those groups into the LDS table while the weights
 // stream in (loads retire in order, so the quantization waits for x only); rows with
-// more than 2 XU chunks per wavefront load the rest as they go.  W = 16: thread t takes
-// the groups t + NT u instead, the same way, and a block barrier publishes the table.
-// q_out / d_out, if not null, receive the row's codes and binary16 scales (block of
-// tile 0).
+// more than 2 XU chunks per wavefront load the rest as they go.  q_out / d_out, if not
+// null, receive the row's codes and binary16 scales (block of tile 0).
 template <int W, int P, int XU>
 __device__ __forceinline__ void gemv_tile_fused(const uint8_t* __restrict__ w, int64_t N, int K,
                                                 const float* __restrict__ x, float w_scale, float* __restrict__ y,
@@ -290,23 +286,12 @@ __device__ __forceinline__ void gemv_tile_fused(const uint8_t* __restrict__ w, i
   const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
   const float4* __restrict__ x4 = reinterpret_cast<const float4*>(x);
 
-  // Wavefront-owned quantization (W <= 8): each wavefront quantizes the chunks it
-  // consumes and needs no block barrier.  With 16 wavefronts it would cost registers
-  // (65 against 57 VGPRs: 7 instead of 8 wavefronts per SIMD, so two such blocks no
-  // longer share a compute unit), so those blocks quantize the row cooperatively.
-  constexpr bool kOwnChunks = W <= 8;
   const int xh = lane >> 5, xl = lane & 31;
   float4 xv[XU];
-  if constexpr (kOwnChunks) {
-    // 1. the float32 activations of this wavefront's own chunks first: lane half h takes
-    //    chunks c = wave + W (2 u + h), lane l (of 32) its float4 group 32 c + l
+  // 1. the float32 activations of this wavefront's own chunks first: lane half h takes
+  //    chunks c = wave + W (2 u + h), lane l (of 32) its float4 group 32 c + l
 #pragma unroll
-    for (int u = 0; u < XU; ++u) xv[u] = x4[min(32 * (wave + W * (2 * u + xh)) + xl, n4 - 1)];
-  } else {
-    // 1. the float32 activations first
-#pragma unroll
-    for (int u = 0; u < XU; ++u) xv[u] = x4[min(tid + NT * u, n4 - 1)];
-  }
+  for (int u = 0; u < XU; ++u) xv[u] = x4[min(32 * (wave + W * (2 * u + xh)) + xl, n4 - 1)];
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. first batch of weight loads (chunk indices clamped, as in gemv_tile)
@@ -325,66 +310,34 @@ __device__ __forceinline__ void gemv_tile_fused(const uint8_t* __restrict__ w, i
   __builtin_amdgcn_sched_barrier(0);
 
   const bool write_q = tile == 0 && q_out != nullptr;
-  if constexpr (kOwnChunks) {
-    // 3. quantize this wavefront's chunks into the table (MX layout of gemv_tile).  Only
-    //    this wavefront reads them, so no block barrier: chunks past the row go to the
-    //    spare slot nch, groups past the row's end (K % 128 == 64) get zero codes and scale.
-    auto quant_put = [&](const float4& v, int c) {
-      const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-      const float d = div127(a);  // = fl(amax / 127)
-      const uint32_t pk = q8_0_pack4(v, d);
-      const int g4 = 32 * c + xl, cs = min(c, nch), o = 4 * xl;
-      const bool in_row = g4 < n4;
-      *reinterpret_cast<uint32_t*>(tab + cs * 256 + o) = in_row ? act_hi_e4m3(pk) : 0u;
-      *reinterpret_cast<uint32_t*>(tab + cs * 256 + 128 + o) = in_row ? pk & 0x0F0F0F0Fu : 0u;
-      const _Float16 dh = (_Float16)d;  // the stored binary16 scale (round to nearest even)
-      if ((xl & 7) == 0) dtab[4 * cs + (xl >> 3)] = in_row ? (float)dh : 0.0f;
-      if (write_q && in_row) {
-        *reinterpret_cast<uint32_t*>(q_out + 4 * g4) = pk;
-        if ((xl & 7) == 0) d_out[g4 >> 3] = __builtin_bit_cast(uint16_t, dh);
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < XU; ++u) quant_put(xv[u], wave + W * (2 * u + xh));
-    for (int u = XU; wave + W * 2 * u < nch; ++u) {
-      const int c = wave + W * (2 * u + xh);
-      quant_put(x4[min(32 * c + xl, n4 - 1)], c);
+  // 3. quantize this wavefront's chunks into the table (MX layout of gemv_tile).  Only
+  //    this wavefront reads them, so no block barrier: chunks past the row go to the
+  //    spare slot nch, groups past the row's end (K % 128 == 64) get zero codes and scale.
+  auto quant_put = [&](const float4& v, int c) {
+    const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const float d = div127(a);  // = fl(amax / 127)
+    const uint32_t pk = q8_0_pack4(v, d);
+    const int g4 = 32 * c + xl, cs = min(c, nch), o = 4 * xl;
+    const bool in_row = g4 < n4;
+    *reinterpret_cast<uint32_t*>(tab + cs * 256 + o) = in_row ? act_hi_e4m3(pk) : 0u;
+    *reinterpret_cast<uint32_t*>(tab + cs * 256 + 128 + o) = in_row ? pk & 0x0F0F0F0Fu : 0u;
+    const _Float16 dh = (_Float16)d;  // the stored binary16 scale (round to nearest even)
+    if ((xl & 7) == 0) dtab[4 * cs + (xl >> 3)] = in_row ? (float)dh : 0.0f;
+    if (write_q && in_row) {
+      *reinterpret_cast<uint32_t*>(q_out + 4 * g4) = pk;
+      if ((xl & 7) == 0) d_out[g4 >> 3] = __builtin_bit_cast(uint16_t, dh);
     }
-    if (lane < 4) reinterpret_cast<uint32_t*>(zero16)[lane] = 0u;  // every wavefront writes the same zeros
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
-    // 3. quantize into the table (MX layout of gemv_tile)
-    auto quant_put = [&](const float4& v, int g4) {
-      const float a = max8(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-      const float d = div127(a);  // = fl(amax / 127)
-      const uint32_t pk = q8_0_pack4(v, d);
-      if (g4 < n4) {
-        const int k = 4 * g4, c = k >> 7, o = k & 127;
-        *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = act_hi_e4m3(pk);
-        *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = pk & 0x0F0F0F0Fu;
-        const _Float16 dh = (_Float16)d;  // the stored binary16 scale (round to nearest even)
-        if ((g4 & 7) == 0) dtab[g4 >> 3] = (float)dh;
-        if (write_q) {
-          *reinterpret_cast<uint32_t*>(q_out + k) = pk;
-          if ((g4 & 7) == 0) d_out[g4 >> 3] = __builtin_bit_cast(uint16_t, dh);
-        }
-      }
-    };
+  };
 #pragma unroll
-    for (int u = 0; u < XU; ++u) quant_put(xv[u], tid + NT * u);
-    for (int g4 = tid + NT * XU; g4 < n4; g4 += NT) quant_put(x4[g4], g4);
-    // the part of the last chunk past the row's end (K % 128 == 64): zero codes and scales
-    for (int g4 = n4 + tid; g4 < nch * 32; g4 += NT) {
-      const int k = 4 * g4, c = k >> 7, o = k & 127;
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + o) = 0u;
-      *reinterpret_cast<uint32_t*>(tab + c * 256 + 128 + o) = 0u;
-    }
-    for (int b = nd + tid; b < nch * 4; b += NT) dtab[b] = 0.0f;
-    if (tid < 4) reinterpret_cast<uint32_t*>(zero16)[tid] = 0u;
-    __syncthreads();
+  for (int u = 0; u < XU; ++u) quant_put(xv[u], wave + W * (2 * u + xh));
+  for (int u = XU; wave + W * 2 * u < nch; ++u) {
+    const int c = wave + W * (2 * u + xh);
+    quant_put(x4[min(32 * c + xl, n4 - 1)], c);
   }
+  if (lane < 4) reinterpret_cast<uint32_t*>(zero16)[lane] = 0u;  // every wavefront writes the same zeros
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // 4. compute (the MX loop of gemv_tile)
   const int sbv = nl >> 1, part = nl & 1;
@@ -435,8 +388,12 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
 }
 
 // Fused quantization + decode GEMV (one token): y = S * W . Q8_0(x).
+// At least 8 wavefronts per SIMD (at most 64 VGPRs): two 16-wavefront blocks must share
+// a compute unit on the down projection's grid (320 blocks), and the wavefront-owned
+// quantization would otherwise take 65 VGPRs there (down 13.0 us with this bound and
+// one spilled register, 15.7 without it)
 template <int W, int P, int XU>
-__global__ __launch_bounds__(64 * W) void gemv_nvfp4_fused_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
+__global__ __launch_bounds__(64 * W, 8) void gemv_nvfp4_fused_kernel(const uint8_t* __restrict__ w, int64_t N, int K,
                                                                   const float* __restrict__ x, float w_scale,
                                                                   float* __restrict__ y, int8_t* __restrict__ q_out,
                                                                   uint16_t* __restrict__ d_out) {
