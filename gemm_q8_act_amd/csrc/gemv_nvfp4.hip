@@ -557,7 +557,8 @@ static hipError_t launch_fused_w(const uint8_t* w, float w_scale, const float* x
 // against 3.1 with 4 x 5); fewer than 1024 tiles with long rows 16 x 3 (down 5120 x
 // 17408: 13.3 us against 13.9 with 16 x 2 and 15.1 with 8 x 3), else 8 x 3 (QKV
 // 7168 x 5120 / O 5120 x 5120: 6.7 / 6.5 us against 7.1 / 7.0 with 4 x 5); many tiles
-// 8 x 5 (gate+up 34816 x 5120: 18.2 us against 18.4 with 4 x 5 and 8 x 3).  The layer
+// 8 x 5 (gate+up 34816 x 5120: 18.2 us against 18.4 with 4 x 5 and 8 x 3; 17.8 against 21.5
+// with 16 x 3 on another box).  The layer
 // step of the four took 44.1 us against 44.8 with the former 16 x 2 / 4 x 5 choice.
 hipError_t launch_gemv_nvfp4_fused(const uint8_t* w, float w_scale, const float* x, int64_t N, int64_t K, float* y,
                                    int8_t* q_out, uint16_t* d_out, hipStream_t stream) {
