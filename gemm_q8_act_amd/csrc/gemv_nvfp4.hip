@@ -112,8 +112,9 @@ __device__ __forceinline__ uint32_t q8_0_pack4(const float4& v, float d) {
   return packed ^ 0x80808080u;
 }
 
-// One 16-row tile of the product (the body of both kernels below).
-template <int MODE, bool DEBUG, int W, int P>
+// One 16-row tile of the product (the body of both kernels below).  OWN: the activation
+// table is built per wavefront (below) instead of by the whole block.
+template <int MODE, bool DEBUG, int W, int P, bool OWN>
 __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ w, int64_t N, int K,
                                           const int8_t* __restrict__ q, const uint16_t* __restrict__ d16,
                                           float w_scale, float* __restrict__ y, int32_t* __restrict__ isums,
@@ -134,15 +135,15 @@ __device__ __forceinline__ void gemv_tile(const uint8_t* __restrict__ w, int64_t
   const uint8_t* __restrict__ wt = w + tile * nch * 1024 + 16 * lane;
   const uint8_t* __restrict__ st = w + ntiles * nch * 1024 + tile * nch * 128 + 2 * lane;
 
-  // Many-tile launch shape (8 wavefronts x 5-chunk batches, matrix-core loop, no debug
-  // sums): each wavefront builds the table entries of the chunks it consumes (v, v + W,
+  // OWN (the plain kernel's many-tile launch shape, 8 wavefronts x 5-chunk batches, and
+  // the expert-routed kernel; matrix-core loop, no debug sums): each wavefront builds the table entries of the chunks it consumes (v, v + W,
   // ...) and needs no block barrier, since no wavefront reads another's entries.  Lane l
   // takes 16-code group l % 8 of the chunks v + W (l / 8 + 8 u) and activation scale l % 4
   // of the chunks v + W (l / 4 + 16 u); the first two code groups and the first scale are
   // loaded before the weights.  Measured against the block-cooperative build: gate+up
   // 34816 x 5120 17.1 -> 16.75 us; on the other shapes it was 0.5-1.6 % slower (down
-  // 11.70 -> 11.89 us), so they keep the cooperative build.
-  constexpr bool kOwn = MODE == 0 && !DEBUG && W == 8 && P == 5;
+  // 11.70 -> 11.89 us), so they keep the cooperative build.  Routed 6 of 256 experts (2048 x 2048): 5.12 -> 5.05 us.
+  constexpr bool kOwn = OWN && MODE == 0 && !DEBUG;
   const u32x4* __restrict__ q16 = reinterpret_cast<const u32x4*>(q);
   const int oc = lane >> 3, og = lane & 7;  // chunk slot (of 8 per pass) and 16-code group
   // 1. activation codes and scales first (at most two 16-code groups per thread here)
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_kernel(const uint8_t* __res
                                                             const uint16_t* __restrict__ d16,
                                                             float w_scale, float* __restrict__ y,
                                                             int32_t* __restrict__ isums) {
-  gemv_tile<MODE, DEBUG, W, P>(w, N, K, q, d16, w_scale, y, isums, blockIdx.x);
+  gemv_tile<MODE, DEBUG, W, P, W == 8 && P == 5>(w, N, K, q, d16, w_scale, y, isums, blockIdx.x);
 }
 
 // Fused quantization + decode GEMV (one token): y = S * W . Q8_0(x).
@@ -470,8 +471,8 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_routed_kernel(const uint8_t
     return;
   }
   const int64_t m = job / A;
-  gemv_tile<0, false, W, P>(w + (int64_t)e * expert_bytes, N, K, q + m * K, d16 + m * (K >> 5), w_scales[e], yj,
-                            nullptr, blockIdx.x);
+  gemv_tile<0, false, W, P, true>(w + (int64_t)e * expert_bytes, N, K, q + m * K, d16 + m * (K >> 5), w_scales[e],
+                                  yj, nullptr, blockIdx.x);
 }
 
 // Launch shape: 4 wavefronts x 5-chunk batches; 8 x 3 for long rows over few tiles
